@@ -1,0 +1,191 @@
+"""Benchmark: GEMM TFLOPS (2MNK/t) on one MI355X.
+
+Default run: the 4096^3 fp32 SGEMM (the pages' headline shape) is the timed
+step; the 4096^3 bf16 GEMM is timed the same way and reported beside it.
+Inputs are seeded synthetic matrices already resident in HBM. A step is one
+library call (one kernel launch) on torch's current stream, timed with HIP
+events over exactly --steps calls after --warmup untimed calls.
+
+Also reported:
+  roofline      the timed kernel against MI355X's published fp32 matrix peak;
+  cpu_baseline  the CPU oracle (fp64, OpenMP over all host threads) timed on a
+                bounded sample of the same workload: full rows of C, scaled to
+                TFLOPS by 2 * rows * N * K / seconds.
+
+``--all`` prints one JSON line per workload instead (for the design notes).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s).
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}
+PEAK_HBM_GBS = 8000.0
+METRIC = "GEMM TFLOPS (2MNK/t) fp32 & bf16 at 4096³ + % of MI355X matrix peak"
+
+
+def gemm_flops(M: int, N: int, K: int) -> int:
+    """2*M*N*K: one multiply and one add per (i, j, k), as the SGEMM article counts."""
+    return 2 * M * N * K
+
+
+def tflops(flops: float, seconds: float) -> float:
+    return flops / seconds / 1e12
+
+
+def _time_calls(call, steps: int, warmup: int, stream):
+    import torch
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        call()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / 1e3 / steps     # seconds per call
+
+
+def _device_call(w, sets: int = 1):
+    """Allocate `sets` independent operand sets on the GPU and return a callable
+    that runs the library on the next set each time."""
+    import torch
+    import dense_gemm_04_amd as dg
+    import gemm_inputs as gi
+    inp = gi.make(w)
+    bufs = []
+    for _ in range(sets):
+        A = inp["A"].cuda()
+        B = inp["B"].cuda()
+        C = inp["C0"].cuda() if inp["C0"] is not None else torch.zeros(
+            w.M, w.N, dtype=A.dtype, device="cuda")
+        bufs.append((A, B, C))
+    stream = torch.cuda.current_stream()
+    h = int(stream.cuda_stream)
+    fn = dg.gemm_f32 if w.dtype == "f32" else dg.gemm_bf16
+    state = {"i": 0}
+
+    def call():
+        A, B, C = bufs[state["i"] % sets]
+        state["i"] += 1
+        st = fn(w.M, w.N, w.K, w.alpha, A.data_ptr(), w.K, B.data_ptr(), w.N, w.beta,
+                C.data_ptr(), w.N, h)
+        if st != dg.GEMM_OK:
+            raise RuntimeError(f"gemm returned {st}: {dg.gemm_status_string(st)}")
+    return call, stream, inp
+
+
+def measure(w, steps: int, warmup: int, sets: int = 1) -> dict:
+    call, stream, _ = _device_call(w, sets)
+    sec = _time_calls(call, steps, warmup, stream)
+    out = {"workload": w.name, "dtype": w.dtype, "M": w.M, "N": w.N, "K": w.K,
+           "alpha": w.alpha, "beta": w.beta, "ms": sec * 1e3,
+           "tflops": tflops(gemm_flops(w.M, w.N, w.K), sec),
+           "gbs": w.algorithmic_bytes / sec / 1e9}
+    out["frac_matrix_peak"] = out["tflops"] / PEAK_TFLOPS[w.dtype]
+    out["frac_hbm"] = out["gbs"] / PEAK_HBM_GBS
+    return out
+
+
+def cpu_baseline(w, target_seconds: float = 12.0) -> dict:
+    """Time the oracle on full rows of C for this workload (bounded sample)."""
+    import oracle
+    import gemm_inputs as gi
+    import numpy as np
+    inp = gi.make(w)
+    A, B = gi.as_numpy(inp["A"]), gi.as_numpy(inp["B"])
+    C0 = gi.as_numpy(inp["C0"]) if inp["C0"] is not None else None
+    threads = oracle.max_threads()
+    rows = max(1, min(w.M, 2 * threads))
+    t0 = time.perf_counter()
+    oracle.gemm(A, B, C0, w.alpha, w.beta, w.dtype, rows=list(range(rows)))
+    t1 = time.perf_counter() - t0
+    # Scale the sample so the timed call takes about target_seconds.
+    rows2 = int(min(w.M, max(rows, rows * target_seconds / max(t1, 1e-3))))
+    rows2 = max(threads, (rows2 // threads) * threads) if rows2 >= threads else rows2
+    sel = list(np.linspace(0, w.M - 1, rows2).astype(np.int64))
+    t0 = time.perf_counter()
+    oracle.gemm(A, B, C0, w.alpha, w.beta, w.dtype, rows=sel)
+    sec = time.perf_counter() - t0
+    return {"value": tflops(gemm_flops(rows2, w.N, w.K), sec), "unit": "TFLOPS",
+            "cores": threads, "kind": "oracle",
+            "sample": f"{rows2} full rows of C ({rows2}x{w.N}x{w.K}, fp64 accumulate) "
+                      f"in {sec:.1f} s"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--all", action="store_true", help="one JSON line per workload")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the GEMM path runs on a single device and "
+              "this build has no multi-GPU leg (run with --gpus 1).", file=sys.stderr)
+        return 2
+
+    import torch
+    import gemm_inputs as gi
+    import dense_gemm_04_amd as dg
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    dg.load()
+
+    if args.all:
+        for wid in (1, 2, 3, 4, 51, 52):
+            w = gi.WORKLOADS[wid]
+            # The small-M workload streams 128 MiB of B: rotate 4 sets (512 MiB)
+            # so the 256 MB Infinity Cache cannot serve it.
+            sets = 4 if wid == 52 else 1
+            r = measure(w, args.steps, args.warmup, sets)
+            print(json.dumps(r), flush=True)
+        return 0
+
+    w = gi.WORKLOADS[2]
+    main_r = measure(w, args.steps, args.warmup)
+    bf = measure(gi.WORKLOADS[3], args.steps, args.warmup)
+    line = {
+        "metric": METRIC,
+        "value": round(main_r["tflops"], 3),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_r["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded U[-1,1] fp32 A and B, resident in HBM)",
+        "config": {"workload": "SGEMM fp32 row-major M=N=K=4096, alpha=1, beta=0",
+                   "M": w.M, "N": w.N, "K": w.K, "kernel": "gemm_f32 (MFMA 16x16x4 f32)"},
+        "frac_of_matrix_peak": round(main_r["frac_matrix_peak"], 4),
+        "roofline": {"bound": "mfma", "achieved": round(main_r["tflops"], 3),
+                     "peak": PEAK_TFLOPS["f32"], "unit": "TFLOP/s",
+                     "frac": round(main_r["frac_matrix_peak"], 4), "traffic": None},
+        "bf16_4096": {"workload": "BF16 GEMM M=N=K=4096, fp32 accumulate, bf16 out",
+                      "tflops": round(bf["tflops"], 3), "ms": round(bf["ms"], 4),
+                      "peak": PEAK_TFLOPS["bf16"], "frac": round(bf["frac_matrix_peak"], 4)},
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,176 @@
+// C-ABI entry points: argument validation, kernel-family planning, device
+// check and launch. Validation and planning touch no HIP API, so every error
+// path can be exercised without a GPU.
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <climits>
+#include <cstring>
+
+#include "../../include/gemm.h"
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace {
+
+bool aligned(const void* p, size_t bytes) {
+    return (reinterpret_cast<uintptr_t>(p) % bytes) == 0;
+}
+
+int64_t max1(int64_t x) { return x > 1 ? x : 1; }
+
+// What a call has to do once its arguments are known to be valid.
+enum class Work { kNone, kScale, kGemm };
+
+Work work_of(int64_t M, int64_t N, int64_t K, float alpha, float beta) {
+    if (M == 0 || N == 0) return Work::kNone;
+    if (K == 0 || alpha == 0.f) return beta == 1.f ? Work::kNone : Work::kScale;
+    return Work::kGemm;
+}
+
+// Returns true when the arguments are valid (header: GEMM_ERR_INVALID_VALUE).
+bool valid_args(int esz, int64_t M, int64_t N, int64_t K, float alpha, const void* A,
+                int64_t lda, const void* B, int64_t ldb, float beta, const void* C,
+                int64_t ldc) {
+    if (M < 0 || N < 0 || K < 0) return false;
+    if (M > INT_MAX || N > INT_MAX || K > INT_MAX) return false;
+    if (lda < max1(K) || ldb < max1(N) || ldc < max1(N)) return false;
+    const Work w = work_of(M, N, K, alpha, beta);
+    if (w != Work::kNone && C == nullptr) return false;
+    if (w == Work::kGemm && (A == nullptr || B == nullptr)) return false;
+    if (!aligned(A, esz) || !aligned(B, esz) || !aligned(C, esz)) return false;
+    return true;
+}
+
+// 128-bit global accesses need 16-byte aligned bases and rows.
+bool vector_ok(int esz, const void* A, int64_t lda, const void* B, int64_t ldb,
+               const void* C, int64_t ldc) {
+    const int64_t per = 16 / esz;
+    return aligned(A, 16) && aligned(B, 16) && aligned(C, 16) && lda % per == 0 &&
+           ldb % per == 0 && ldc % per == 0;
+}
+
+// The kernel family for a valid call that has GEMM work, or -1 if the
+// requested family cannot run it.
+int choose(int esz, int64_t M, bool vec, int variant) {
+    switch (variant) {
+        case GEMM_VARIANT_AUTO:
+            if (esz == 2 && M <= dg::kSkinnyMaxM) return GEMM_VARIANT_SKINNY;
+            return vec ? GEMM_VARIANT_MFMA : GEMM_VARIANT_GENERAL;
+        case GEMM_VARIANT_MFMA:
+            return vec ? GEMM_VARIANT_MFMA : -1;
+        case GEMM_VARIANT_GENERAL:
+            return GEMM_VARIANT_GENERAL;
+        case GEMM_VARIANT_VALU:
+            return esz == 4 ? GEMM_VARIANT_VALU : -1;
+        case GEMM_VARIANT_SKINNY:
+            return (esz == 2 && M <= dg::kSkinnyMaxM) ? GEMM_VARIANT_SKINNY : -1;
+        default:
+            return -1;
+    }
+}
+
+int plan_impl(int esz, int64_t M, int64_t N, int64_t K, float alpha, const void* A,
+              int64_t lda, const void* B, int64_t ldb, float beta, const void* C,
+              int64_t ldc, int variant) {
+    if (esz != 2 && esz != 4) return -1;
+    if (variant < GEMM_VARIANT_AUTO || variant > GEMM_VARIANT_SKINNY) return -1;
+    if (!valid_args(esz, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc)) return -1;
+    if (work_of(M, N, K, alpha, beta) != Work::kGemm) return GEMM_VARIANT_AUTO;
+    return choose(esz, M, vector_ok(esz, A, lda, B, ldb, C, ldc), variant);
+}
+
+// Per-device cache of "is this a gfx950": 0 unknown, 1 yes, 2 no.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch[kMaxDevices];
+
+gemm_status_t check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GEMM_ERR_UNSUPPORTED_DEVICE;
+    if (dev >= kMaxDevices) return GEMM_ERR_UNSUPPORTED_DEVICE;
+    int state = g_arch[dev].load(std::memory_order_acquire);
+    if (state == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GEMM_ERR_UNSUPPORTED_DEVICE;
+        state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_arch[dev].store(state, std::memory_order_release);
+    }
+    return state == 1 ? GEMM_OK : GEMM_ERR_UNSUPPORTED_DEVICE;
+}
+
+template <typename T>
+gemm_status_t run(int64_t M, int64_t N, int64_t K, float alpha, const T* A, int64_t lda,
+                  const T* B, int64_t ldb, float beta, T* C, int64_t ldc, void* stream,
+                  int variant) {
+    constexpr int esz = (int)sizeof(T);
+    const int v = plan_impl(esz, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, variant);
+    if (v < 0) return GEMM_ERR_INVALID_VALUE;
+    const Work w = work_of(M, N, K, alpha, beta);
+    if (w == Work::kNone) return GEMM_OK;
+    const gemm_status_t dev = check_device();
+    if (dev != GEMM_OK) return dev;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (w == Work::kScale) {
+        if constexpr (esz == 4) e = dg::launch_scale_f32(M, N, beta, C, ldc, s);
+        else e = dg::launch_scale_bf16(M, N, beta, C, ldc, s);
+    } else {
+        dg::GemmArgs<T> a{M, N, K, alpha, beta, A, lda, B, ldb, C, ldc};
+        const bool vec = vector_ok(esz, A, lda, B, ldb, C, ldc);
+        if constexpr (esz == 4) {
+            e = (v == GEMM_VARIANT_VALU) ? dg::launch_f32_valu(a, vec, s)
+                                         : dg::launch_f32_mfma(a, v == GEMM_VARIANT_MFMA, s);
+        } else {
+            e = (v == GEMM_VARIANT_SKINNY) ? dg::launch_bf16_skinny(a, vec, s)
+                                           : dg::launch_bf16_mfma(a, v == GEMM_VARIANT_MFMA, s);
+        }
+    }
+    return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+gemm_status_t gemm_f32_ex(int64_t M, int64_t N, int64_t K, float alpha, const float* A,
+                          int64_t lda, const float* B, int64_t ldb, float beta, float* C,
+                          int64_t ldc, void* stream, int variant) {
+    return run<float>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, variant);
+}
+
+gemm_status_t gemm_bf16_ex(int64_t M, int64_t N, int64_t K, float alpha, const uint16_t* A,
+                           int64_t lda, const uint16_t* B, int64_t ldb, float beta, uint16_t* C,
+                           int64_t ldc, void* stream, int variant) {
+    return run<uint16_t>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, variant);
+}
+
+gemm_status_t gemm_f32(int64_t M, int64_t N, int64_t K, float alpha, const float* A,
+                       int64_t lda, const float* B, int64_t ldb, float beta, float* C,
+                       int64_t ldc, void* stream) {
+    return gemm_f32_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, GEMM_VARIANT_AUTO);
+}
+
+gemm_status_t gemm_bf16(int64_t M, int64_t N, int64_t K, float alpha, const uint16_t* A,
+                        int64_t lda, const uint16_t* B, int64_t ldb, float beta, uint16_t* C,
+                        int64_t ldc, void* stream) {
+    return gemm_bf16_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, GEMM_VARIANT_AUTO);
+}
+
+int gemm_plan(int elem_bytes, int64_t M, int64_t N, int64_t K, float alpha, const void* A,
+              int64_t lda, const void* B, int64_t ldb, float beta, const void* C, int64_t ldc,
+              int variant) {
+    return plan_impl(elem_bytes, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, variant);
+}
+
+const char* gemm_status_string(int status) {
+    switch (status) {
+        case GEMM_OK: return "success";
+        case GEMM_ERR_INVALID_VALUE: return "invalid argument";
+        case GEMM_ERR_UNSUPPORTED_DEVICE: return "current device is not a gfx950 GPU";
+        case GEMM_ERR_LAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Shared device/host helpers for the gfx950 GEMM kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dg {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Arguments every GEMM kernel receives, by value (kernarg segment).
+template <typename T>
+struct GemmArgs {
+    int64_t M, N, K;
+    float alpha, beta;
+    const T* A; int64_t lda;
+    const T* B; int64_t ldb;
+    T* C; int64_t ldc;
+};
+
+// ---- bf16 helpers ---------------------------------------------------------
+
+// bf16 bit pattern -> fp32 (exact: the pattern is the top half of the word).
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __builtin_bit_cast(float, (uint32_t)h << 16);
+}
+
+// fp32 -> bf16 bit pattern, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// ---- workgroup -> output tile mapping ----------------------------------------
+//
+// The dispatcher hands workgroup w to XCD (w mod 8), and each of the 8 XCDs has
+// its own L2. The linear id is first renumbered so that every XCD owns one
+// contiguous run of ids; the run is then walked in groups of `group_m` tile
+// rows, so the tiles that share an XCD also share A rows and B columns.
+__device__ __forceinline__ void tile_coords(int wg, int nwg, int tiles_m, int tiles_n,
+                                            int group_m, int& tm, int& tn) {
+    constexpr int kXcds = 8;
+    int per = nwg / kXcds, rem = nwg % kXcds;
+    int xcd = wg % kXcds, idx = wg / kXcds;
+    int id = (xcd < rem) ? xcd * (per + 1) + idx
+                         : rem * (per + 1) + (xcd - rem) * per + idx;
+    int group = group_m * tiles_n;
+    int gid = id / group;
+    int first_m = gid * group_m;
+    int gsz = tiles_m - first_m < group_m ? tiles_m - first_m : group_m;
+    int in_group = id - gid * group;
+    tm = first_m + in_group % gsz;
+    tn = in_group / gsz;
+}
+
+}  // namespace dg

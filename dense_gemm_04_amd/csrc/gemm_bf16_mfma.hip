@@ -1,0 +1,252 @@
+// bf16 GEMM on gfx950 matrix cores: C = alpha * A * B + beta * C, row-major,
+// fp32 accumulation, one rounding to bf16 at the end.
+//
+// Structure (the tiling recipe of the RTX 3090 SGEMM article, sections 3-5,
+// and the pipelining of the Blackwell BF16 GEMM notes, section 2.3, rebuilt
+// for CDNA4):
+//   * one workgroup per BM x BN tile of C, tiles renumbered per XCD;
+//   * K walked in slabs of BK = 64: A slab (BM x 64) and B slab (64 x BN) are
+//     fetched with 128-bit loads into registers while the previous slab is
+//     being multiplied, then written to the other half of a double-buffered
+//     LDS (one barrier per slab);
+//   * both slabs are stored k-contiguous in LDS ([row][k] for A, [col][k] for
+//     B), so every MFMA operand fragment is one 128-bit LDS read. Row-major B
+//     is transposed in registers (8 x 8 blocks of bf16) on its way to LDS;
+//   * each LDS row is 8 chunks of 16 bytes whose position is XOR-swizzled with
+//     the row index, so the 128-bit reads and writes of a wave hit distinct
+//     banks (the padding idea of the article's section 4.3, without the
+//     wasted bytes);
+//   * each wave owns a (BM / WAVES_M) x (BN / WAVES_N) block of C held as
+//     16x16 fp32 accumulators of v_mfma_f32_16x16x32_bf16;
+//   * the epilogue forms alpha * acc + beta * C0 in fp32 and rounds to bf16
+//     (notes, section 1.2 and 6.3), storing 16 bytes per lane.
+//
+// Operand layout of v_mfma_f32_16x16x32_bf16 used here: lane l = p + 16 g
+// (p in 0..15, g in 0..3) supplies A(row p, k = 8g .. 8g+7) and B(k = 8g ..
+// 8g+7, col p), and receives D(row 4g + i, col p) in accumulator register i.
+// Which k the hardware pairs is irrelevant to the result as long as A and B
+// use the same assignment, which they do.
+//
+// The n index inside a wave is interleaved: MFMA block tn covers the columns
+// wn0 + FN * p + tn (p = 0..15), so after the loop each lane holds FN
+// consecutive columns of one row and can store them as one vector.
+//
+// Edges (Z-Turbo CUDA tuning page, section 3.1; Blackwell notes, section
+// 4.3): rows of A past M, columns of B past N and k past K are loaded as zero,
+// and the epilogue stores only in-range elements.
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace dg {
+namespace {
+
+constexpr int kBK = 64;            // k per slab (8 chunks of 8 bf16)
+constexpr int kGroupM = 4;         // tile rows per raster group
+
+// Element offset of chunk `c` (8 bf16) of row `row` in a [rows][64] LDS tile.
+__device__ __forceinline__ int lds_off(int row, int c) {
+    return row * kBK + ((c ^ ((row ^ (row >> 3)) & 7)) << 3);
+}
+
+// 8 consecutive bf16 from p, of which the first `valid` are in range.
+__device__ __forceinline__ u32x4 load8_elems(const uint16_t* p, int valid) {
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        uint32_t lo = (2 * e < valid) ? (uint32_t)p[2 * e] : 0u;
+        uint32_t hi = (2 * e + 1 < valid) ? (uint32_t)p[2 * e + 1] : 0u;
+        w[e] = lo | (hi << 16);
+    }
+    return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+template <bool VEC>
+__device__ __forceinline__ u32x4 load8(const uint16_t* p, int valid) {
+    if (VEC && valid >= 8) return *reinterpret_cast<const u32x4*>(p);
+    if (valid <= 0) return u32x4{0u, 0u, 0u, 0u};
+    return load8_elems(p, valid);
+}
+
+// 8 x 8 transpose of bf16: x[r] holds row r (8 columns, two per dword);
+// y[j] receives column j (8 rows, two per dword).
+__device__ __forceinline__ void transpose8x8(const u32x4 (&x)[8], u32x4 (&y)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t lo = x[2 * q][j >> 1], hi = x[2 * q + 1][j >> 1];
+            y[j][q] = (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u))
+                              : ((lo & 0xffffu) | (hi << 16));
+        }
+    }
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool VEC>
+__global__ __launch_bounds__(WAVES_M * WAVES_N * 64)
+void gemm_bf16_mfma_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
+    constexpr int NT = WAVES_M * WAVES_N * 64;
+    constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+    constexpr int FM = WTM / 16, FN = WTN / 16;
+    constexpr int A_CHUNKS = BM * (kBK / 8) / NT;          // 16-byte A chunks per thread
+    constexpr int B_BLOCKS = (kBK / 8) * (BN / 8) / NT;    // 8x8 B blocks per thread
+    constexpr int STAGE = (BM + BN) * kBK;                 // bf16 elements per LDS stage
+    static_assert(A_CHUNKS * NT == BM * (kBK / 8), "A slab must split evenly");
+    static_assert(B_BLOCKS * NT == (kBK / 8) * (BN / 8), "B slab must split evenly");
+    static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be 16-aligned");
+
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+
+    int tm, tn;
+    tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, kGroupM, tm, tn);
+    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+    const int64_t M = p.M, N = p.N, K = p.K;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+
+    u32x4 ra[A_CHUNKS];
+    u32x4 rb[B_BLOCKS][8];
+
+    auto gload = [&](int64_t k0) {
+#pragma unroll
+        for (int i = 0; i < A_CHUNKS; ++i) {
+            const int r = t / 8 + i * (NT / 8), c = t % 8;
+            const int64_t gm = m0 + r, gk = k0 + 8 * c;
+            int valid = (gm < M) ? (int)(K - gk < 8 ? K - gk : 8) : 0;
+            const uint16_t* src = p.A + (valid > 0 ? gm * p.lda + gk : 0);
+            ra[i] = load8<VEC>(src, valid);
+        }
+#pragma unroll
+        for (int bi = 0; bi < B_BLOCKS; ++bi) {
+            const int blk = t + bi * NT;
+            const int kb = blk / (BN / 8), nb = blk % (BN / 8);
+            const int64_t gn = n0 + 8 * nb;
+            const int nvalid = (int)(N - gn < 8 ? (N - gn < 0 ? 0 : N - gn) : 8);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const int64_t gk = k0 + 8 * kb + r;
+                const int valid = gk < K ? nvalid : 0;
+                const uint16_t* src = p.B + (valid > 0 ? gk * p.ldb + gn : 0);
+                rb[bi][r] = load8<VEC>(src, valid);
+            }
+        }
+    };
+
+    auto sstore = [&](int stage) {
+        uint16_t* As = smem + stage * STAGE;
+        uint16_t* Bs = As + BM * kBK;
+#pragma unroll
+        for (int i = 0; i < A_CHUNKS; ++i) {
+            const int r = t / 8 + i * (NT / 8), c = t % 8;
+            *reinterpret_cast<u32x4*>(As + lds_off(r, c)) = ra[i];
+        }
+#pragma unroll
+        for (int bi = 0; bi < B_BLOCKS; ++bi) {
+            const int blk = t + bi * NT;
+            const int kb = blk / (BN / 8), nb = blk % (BN / 8);
+            u32x4 y[8];
+            transpose8x8(rb[bi], y);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                *reinterpret_cast<u32x4*>(Bs + lds_off(8 * nb + j, kb)) = y[j];
+        }
+    };
+
+    f32x4 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int wm0 = (wave / WAVES_N) * WTM, wn0 = (wave % WAVES_N) * WTN;
+    const int pl = lane & 15, g = lane >> 4;
+
+    auto compute = [&](int stage) {
+        const uint16_t* As = smem + stage * STAGE;
+        const uint16_t* Bs = As + BM * kBK;
+#pragma unroll
+        for (int ks = 0; ks < kBK / 32; ++ks) {
+            bf16x8 a[FM], b[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                a[i] = *reinterpret_cast<const bf16x8*>(As + lds_off(wm0 + 16 * i + pl, 4 * ks + g));
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                b[j] = *reinterpret_cast<const bf16x8*>(Bs + lds_off(wn0 + FN * pl + j, 4 * ks + g));
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+    };
+
+    const int64_t nk = (K + kBK - 1) / kBK;
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int64_t kt = 0; kt < nk; ++kt) {
+        const int cur = (int)(kt & 1);
+        if (kt + 1 < nk) gload((kt + 1) * kBK);
+        compute(cur);
+        if (kt + 1 < nk) sstore(cur ^ 1);
+        __syncthreads();
+    }
+
+    // Epilogue: lane (pl, g) holds rows 4g + i of each 16-row block and the FN
+    // consecutive columns wn0 + FN * pl .. + FN - 1.
+    const float alpha = p.alpha, beta = p.beta;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t row = m0 + wm0 + 16 * i + 4 * g + r;
+            const int64_t col = n0 + wn0 + FN * pl;
+            if (row >= M) continue;
+            float v[FN];
+#pragma unroll
+            for (int j = 0; j < FN; ++j) v[j] = alpha * acc[i][j][r];
+            uint16_t* dst = p.C + row * p.ldc + col;
+            if (VEC && FN == 8 && col + 8 <= N) {
+                if (beta != 0.f) {
+                    const u32x4 c0 = *reinterpret_cast<const u32x4*>(dst);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        v[j] += beta * bf16_to_f32((uint16_t)(c0[j >> 1] >> (16 * (j & 1))));
+                }
+                u32x4 o;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
+                *reinterpret_cast<u32x4*>(dst) = o;
+            } else {
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    if (col + j < N) {
+                        float x = v[j];
+                        if (beta != 0.f) x += beta * bf16_to_f32(dst[j]);
+                        dst[j] = f32_to_bf16(x);
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N>
+hipError_t launch_tiles(const GemmArgs<uint16_t>& a, bool vec, hipStream_t s) {
+    const int64_t tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
+    int tm = (int)tiles_m, tn = (int)tiles_n;
+    GemmArgs<uint16_t> args = a;
+    void* kargs[] = {&args, &tm, &tn};
+    const void* fn = vec ? (const void*)&gemm_bf16_mfma_kernel<BM, BN, WAVES_M, WAVES_N, true>
+                         : (const void*)&gemm_bf16_mfma_kernel<BM, BN, WAVES_M, WAVES_N, false>;
+    return hipLaunchKernel(fn, dim3((unsigned)(tiles_m * tiles_n)), dim3(WAVES_M * WAVES_N * 64),
+                           kargs, 0, s);
+}
+
+}  // namespace
+
+hipError_t launch_bf16_mfma(const GemmArgs<uint16_t>& a, bool vec, hipStream_t s) {
+    return launch_tiles<256, 256, 2, 2>(a, vec, s);
+}
+
+}  // namespace dg

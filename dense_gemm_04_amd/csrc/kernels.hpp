@@ -1,0 +1,28 @@
+// Host-side launchers for the gfx950 GEMM kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace dg {
+
+// `vec` selects 128-bit global loads/stores; the caller guarantees 16-byte
+// aligned base pointers and leading dimensions that keep every row 16-byte
+// aligned. Without it every global access is element-wise.
+hipError_t launch_bf16_mfma(const GemmArgs<uint16_t>& a, bool vec, hipStream_t s);
+hipError_t launch_f32_mfma(const GemmArgs<float>& a, bool vec, hipStream_t s);
+hipError_t launch_f32_valu(const GemmArgs<float>& a, bool vec, hipStream_t s);
+hipError_t launch_bf16_skinny(const GemmArgs<uint16_t>& a, bool vec, hipStream_t s);
+
+// C <- beta * C (beta == 0 writes zeros without reading C).
+hipError_t launch_scale_f32(int64_t M, int64_t N, float beta, float* C, int64_t ldc,
+                            hipStream_t s);
+hipError_t launch_scale_bf16(int64_t M, int64_t N, float beta, uint16_t* C, int64_t ldc,
+                             hipStream_t s);
+
+// Largest M the small-M kernel accepts.
+constexpr int64_t kSkinnyMaxM = 32;
+
+}  // namespace dg

@@ -1,0 +1,121 @@
+/*
+ * dense_gemm_04_amd — dense GEMM for AMD Instinct MI355X (gfx950), C ABI.
+ *
+ * Operation (Blackwell BF16 GEMM notes, section 1.1: "C = Alpha*A*B + Beta*C"):
+ *
+ *     C(i,j) <- alpha * sum_k A(i,k) * B(k,j) + beta * C(i,j)
+ *
+ * for 0 <= i < M, 0 <= j < N, 0 <= k < K. All three matrices are ROW-MAJOR
+ * with unit column stride and a leading dimension (the element distance
+ * between the starts of two rows), as in the RTX 3090 SGEMM article's
+ * indexing A[row*K + k], B[k*N + col] (section 2.1), generalised to
+ * A(i,k) = A[i*lda + k], B(k,j) = B[k*ldb + j], C(i,j) = C[i*ldc + j].
+ *
+ * gemm_f32  : A, B, C are IEEE fp32; products and sums in fp32.
+ * gemm_bf16 : A, B, C hold bf16 bit patterns (1 sign, 8 exponent, 7 mantissa
+ *             bits; same notes, section 1.2). Products and sums are fp32;
+ *             the result alpha*acc + beta*C is formed in fp32 and rounded once
+ *             to bf16, to nearest with ties to even (same notes, sections 1.2
+ *             and 6.3: accumulate in FP32, convert back to BF16 at the end).
+ * alpha and beta are fp32 on both paths.
+ *
+ * Summation order over k is unspecified; results agree with an exact-product,
+ * binary64-sum reference to within |alpha| * sum_k |A(i,k)||B(k,j)| *
+ * (a small multiple of K * 2^-24) plus the output rounding.
+ *
+ * Special values of the arguments (BLAS convention):
+ *   - M == 0 or N == 0: nothing is read or written.
+ *   - beta == 0: C is write-only; its old contents (even NaN) are not read.
+ *   - K == 0 or alpha == 0: A and B are not read; C <- beta * C
+ *     (beta == 1 leaves C untouched and launches nothing).
+ *
+ * Ownership and memory: every pointer is a DEVICE pointer owned by the
+ * caller, valid on the current HIP device for the duration of the work.
+ * The library keeps no reference after the work completes and allocates no
+ * device memory. C must not overlap A or B (undefined results otherwise).
+ *
+ * Streams and errors: `stream` is a hipStream_t passed as void* (NULL = the
+ * null stream). Calls are asynchronous: they validate the arguments, enqueue
+ * one or more kernels on `stream` and return; completion and device-side
+ * faults are observed at the caller's next synchronisation. On any error
+ * status nothing has been enqueued. The library is reentrant; its only
+ * global state is a per-device cache of the device architecture.
+ */
+#ifndef DENSE_GEMM_04_AMD_GEMM_H
+#define DENSE_GEMM_04_AMD_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GEMM_OK = 0,
+    /* A size is negative, a leading dimension is smaller than max(1, row
+     * length), a pointer that must be read or written is NULL, a pointer is
+     * not aligned to its element size, or `variant` is unknown or does not
+     * apply to the call. */
+    GEMM_ERR_INVALID_VALUE = 1,
+    /* No HIP device is current, or it is not a gfx950 (MI355X-class) device. */
+    GEMM_ERR_UNSUPPORTED_DEVICE = 2,
+    /* The kernel launch was rejected by the HIP runtime. */
+    GEMM_ERR_LAUNCH = 3
+} gemm_status_t;
+
+/* Kernel family selection for the *_ex entry points. AUTO is what gemm_f32 and
+ * gemm_bf16 use; the others force one family (for measurements and tests). */
+typedef enum {
+    GEMM_VARIANT_AUTO = 0,
+    /* LDS-tiled MFMA kernel with 128-bit global loads; needs every pointer
+     * 16-byte aligned and lda, ldb, ldc multiples of 16 bytes / element size. */
+    GEMM_VARIANT_MFMA = 1,
+    /* The same MFMA tiling with element-wise global loads and stores: any
+     * alignment and leading dimension (RTX 3090 SGEMM article, section 6.2:
+     * a scalar fallback when float4 alignment does not hold). */
+    GEMM_VARIANT_GENERAL = 2,
+    /* fp32 only: vector-FMA (non-matrix-core) kernel with per-thread register
+     * micro-tiles, kept as a measured comparison (same article, sections 5.1-5.3). */
+    GEMM_VARIANT_VALU = 3,
+    /* bf16 only, M <= 32: small-M kernel that streams B once (Blackwell BF16
+     * GEMM notes, section 5.2: small-batch GEMMs are bandwidth bound). */
+    GEMM_VARIANT_SKINNY = 4
+} gemm_variant_t;
+
+/* fp32 GEMM. A: M x K (lda >= max(1,K)), B: K x N (ldb >= max(1,N)),
+ * C: M x N (ldc >= max(1,N)); all fp32, 4-byte aligned. */
+gemm_status_t gemm_f32(int64_t M, int64_t N, int64_t K, float alpha,
+                       const float* A, int64_t lda, const float* B, int64_t ldb,
+                       float beta, float* C, int64_t ldc, void* stream);
+
+/* bf16 GEMM with fp32 accumulation. A, B, C hold bf16 bit patterns
+ * (uint16_t), 2-byte aligned; shapes and leading dimensions as for gemm_f32. */
+gemm_status_t gemm_bf16(int64_t M, int64_t N, int64_t K, float alpha,
+                        const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                        float beta, uint16_t* C, int64_t ldc, void* stream);
+
+/* As above with an explicit kernel family (gemm_variant_t). A forced variant
+ * whose preconditions do not hold returns GEMM_ERR_INVALID_VALUE. */
+gemm_status_t gemm_f32_ex(int64_t M, int64_t N, int64_t K, float alpha,
+                          const float* A, int64_t lda, const float* B, int64_t ldb,
+                          float beta, float* C, int64_t ldc, void* stream, int variant);
+gemm_status_t gemm_bf16_ex(int64_t M, int64_t N, int64_t K, float alpha,
+                           const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                           float beta, uint16_t* C, int64_t ldc, void* stream, int variant);
+
+/* Host-only planning (no HIP call): the variant a call with these arguments
+ * would run (a gemm_variant_t value; GEMM_VARIANT_AUTO when the call would
+ * launch no GEMM kernel), or -1 when the arguments are invalid. `elem_bytes`
+ * is 4 (fp32) or 2 (bf16); pointers are used only for their alignment. */
+int gemm_plan(int elem_bytes, int64_t M, int64_t N, int64_t K, float alpha,
+              const void* A, int64_t lda, const void* B, int64_t ldb,
+              float beta, const void* C, int64_t ldc, int variant);
+
+/* Static string for a gemm_status_t value ("unknown status" otherwise). */
+const char* gemm_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DENSE_GEMM_04_AMD_GEMM_H */

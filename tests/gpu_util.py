@@ -1,0 +1,67 @@
+"""Helpers shared by the GPU tests: run the library on torch CUDA buffers and
+compare against the CPU oracle."""
+import sys
+
+import numpy as np
+import torch
+
+import dense_gemm_04_amd as dg
+import gemm_inputs as gi
+import oracle
+
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def note(msg: str) -> None:
+    """Name the case on the real stderr before a GPU step (survives a lost box)."""
+    sys.__stderr__.write(f"[gpu-case] {msg}\n")
+    sys.__stderr__.flush()
+
+
+def padded(rows: int, cols: int, ld: int, dtype: str, offset: int = 0, fill=0.0):
+    """A (rows x cols) CUDA view with leading dimension ld inside a larger
+    buffer filled with `fill`; `offset` elements shift the base pointer."""
+    buf = torch.full((rows * ld + offset + 64,), fill, dtype=TORCH_DT[dtype], device="cuda")
+    view = buf[offset:offset + rows * ld].view(rows, ld)[:, :cols]
+    return buf, view
+
+
+def run(dtype, A, B, C0, alpha, beta, variant=0, ld_pad=(0, 0, 0), offset=0,
+        c_fill=None, stream=None):
+    """Run C = alpha*A*B + beta*C0 on the GPU. A, B, C0 are CPU tensors
+    (C0 may be None when beta == 0). Returns (C as CPU tensor, status)."""
+    M, K = A.shape
+    N = B.shape[1]
+    lda, ldb, ldc = max(K, 1) + ld_pad[0], max(N, 1) + ld_pad[1], max(N, 1) + ld_pad[2]
+    _, a = padded(M, K, lda, dtype, offset)
+    _, b = padded(K, N, ldb, dtype, offset)
+    cbuf, c = padded(M, N, ldc, dtype, offset,
+                     fill=float("nan") if c_fill is None else c_fill)
+    if M and K:
+        a.copy_(A.to("cuda"))
+    if K and N:
+        b.copy_(B.to("cuda"))
+    if C0 is not None and M and N:
+        c.copy_(C0.to("cuda"))
+    fn = dg.gemm_f32_ex if dtype == "f32" else dg.gemm_bf16_ex
+    h = 0 if stream is None else int(stream.cuda_stream)
+    st = fn(M, N, K, float(alpha), a.data_ptr(), lda, b.data_ptr(), ldb, float(beta),
+            c.data_ptr(), ldc, h, int(variant))
+    torch.cuda.synchronize()
+    return c.cpu(), st, cbuf
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.to(torch.float64).numpy()
+
+
+def oracle_ref(dtype, A, B, C0, alpha, beta, rows=None, cols=None):
+    a32 = float(np.float32(alpha))
+    b32 = float(np.float32(beta))
+    return oracle.gemm(gi.as_numpy(A), gi.as_numpy(B),
+                       None if (C0 is None or beta == 0) else gi.as_numpy(C0),
+                       a32, b32, dtype, rows=rows, cols=cols)
+
+
+def tol(dtype: str) -> float:
+    return oracle.TOL_F32 if dtype == "f32" else oracle.TOL_BF16

@@ -1,0 +1,135 @@
+"""C-ABI checks that need no GPU: the library loads, exports what the header
+declares, validates its arguments before touching HIP, and plans the kernel
+family from shape and alignment alone."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dense_gemm_04_amd as dg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemm.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dg.LIB_PATH):
+        from dense_gemm_04_amd import build
+        build.build()
+    return dg.load()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert header_functions() == sorted(dg.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    assert dg.gemm_status_string(0) == "success"
+    assert dg.gemm_status_string(1) == "invalid argument"
+    assert "gfx950" in dg.gemm_status_string(2)
+    assert dg.gemm_status_string(3) == "kernel launch failed"
+    assert dg.gemm_status_string(99) == "unknown status"
+
+
+# Fake, suitably aligned device addresses: planning only inspects alignment.
+A, B, C = 0x10000, 0x20000, 0x30000
+
+
+def plan(esz=4, M=64, N=64, K=64, alpha=1.0, a=A, lda=None, b=B, ldb=None, beta=0.0, c=C,
+         ldc=None, variant=0):
+    lda = K if lda is None else lda
+    ldb = N if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    return dg.gemm_plan(esz, M, N, K, alpha, a, lda, b, ldb, beta, c, ldc, variant)
+
+
+def test_plan_rejects_invalid_arguments(lib):
+    assert plan(M=-1) == -1
+    assert plan(N=-1) == -1
+    assert plan(K=-1) == -1
+    assert plan(lda=63) == -1                 # lda < K
+    assert plan(ldb=63) == -1                 # ldb < N
+    assert plan(ldc=63) == -1                 # ldc < N
+    assert plan(K=0, lda=0) == -1             # lda < max(1, K)
+    assert plan(a=None) == -1
+    assert plan(b=None) == -1
+    assert plan(c=None) == -1
+    assert plan(a=A + 2) == -1                # fp32 pointer not 4-byte aligned
+    assert plan(esz=2, a=A + 1) == -1         # bf16 pointer not 2-byte aligned
+    assert plan(esz=3) == -1
+    assert plan(variant=9) == -1
+    assert plan(M=1 << 31) == -1
+
+
+def test_plan_quick_paths(lib):
+    # Nothing to do: M or N empty, or C <- 1 * C.
+    assert plan(M=0, c=None) == dg.VARIANT_AUTO
+    assert plan(N=0, c=None, ldb=1, ldc=1) == dg.VARIANT_AUTO
+    assert plan(K=0, lda=1, a=None, b=None, beta=1.0, c=None) == dg.VARIANT_AUTO
+    # alpha == 0 or K == 0: A and B may be NULL, C is scaled.
+    assert plan(alpha=0.0, a=None, b=None, beta=0.5) == dg.VARIANT_AUTO
+    assert plan(K=0, lda=1, a=None, b=None, beta=0.0) == dg.VARIANT_AUTO
+    assert plan(K=0, lda=1, a=None, b=None, beta=0.0, c=None) == -1
+
+
+def test_plan_chooses_family(lib):
+    assert plan() == dg.VARIANT_MFMA
+    assert plan(esz=2, M=16) == dg.VARIANT_SKINNY             # bf16, M <= 32
+    assert plan(esz=2, M=32) == dg.VARIANT_SKINNY
+    assert plan(esz=2, M=33) == dg.VARIANT_MFMA
+    assert plan(M=4095, N=4097, K=1023) == dg.VARIANT_GENERAL  # ld not a multiple of 4 floats
+    assert plan(a=A + 4) == dg.VARIANT_GENERAL                 # base not 16-byte aligned
+    assert plan(lda=68) == dg.VARIANT_MFMA
+    assert plan(lda=66) == dg.VARIANT_GENERAL
+    assert plan(variant=dg.VARIANT_VALU) == dg.VARIANT_VALU
+    assert plan(esz=2, variant=dg.VARIANT_VALU) == -1
+    assert plan(M=16, variant=dg.VARIANT_SKINNY) == -1
+    assert plan(esz=2, M=33, variant=dg.VARIANT_SKINNY) == -1
+    assert plan(a=A + 4, variant=dg.VARIANT_MFMA) == -1
+    assert plan(variant=dg.VARIANT_GENERAL) == dg.VARIANT_GENERAL
+
+
+def test_invalid_calls_return_before_any_hip_call(lib):
+    # These return from validation; no device is touched.
+    assert dg.gemm_f32(-1, 4, 4, 1.0, A, 4, B, 4, 0.0, C, 4, 0) == dg.GEMM_ERR_INVALID_VALUE
+    assert dg.gemm_bf16(4, 4, 4, 1.0, A, 3, B, 4, 0.0, C, 4, 0) == dg.GEMM_ERR_INVALID_VALUE
+    assert dg.gemm_f32_ex(4, 4, 4, 1.0, A, 4, B, 4, 0.0, C, 4, 0, 7) == dg.GEMM_ERR_INVALID_VALUE
+    assert dg.gemm_bf16_ex(64, 64, 64, 1.0, A, 64, B, 64, 0.0, C, 64, 0,
+                           dg.VARIANT_VALU) == dg.GEMM_ERR_INVALID_VALUE
+    # Empty problems succeed without touching the device either.
+    assert dg.gemm_f32(0, 4, 4, 1.0, None, 4, None, 4, 0.0, None, 4, 0) == dg.GEMM_OK
+
+
+def test_valid_call_without_gpu_reports_unsupported_device(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    st = dg.gemm_f32(64, 64, 64, 1.0, A, 64, B, 64, 0.0, C, 64, 0)
+    assert st == dg.GEMM_ERR_UNSUPPORTED_DEVICE
+
+
+def test_oracle_and_library_share_nothing():
+    """The oracle and the HIP sources must not include, import or link each other."""
+    csrc = os.path.join(ROOT, "dense_gemm_04_amd")
+    for dirpath, _, files in os.walk(csrc):
+        for f in files:
+            if f.endswith((".hip", ".hpp", ".py", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), f
+    for f in os.listdir(os.path.join(ROOT, "oracle")):
+        if f.endswith((".c", ".py")):
+            text = open(os.path.join(ROOT, "oracle", f)).read()
+            assert "dense_gemm_04_amd" not in text and "gemm.h" not in text, f
