@@ -22,6 +22,28 @@ struct GemmArgs {
     T* C; int64_t ldc;
 };
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+// ---- buffer (descriptor-based) global loads ---------------------------------
+//
+// A raw buffer descriptor covers [base, base + bytes). Loads whose offset lies
+// past `bytes` return zero instead of touching memory, which is how the tiled
+// kernels read the ragged edges of A and B without branches.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Descriptor word 3 for gfx9-family raw buffers (32-bit data format, no swizzle).
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             kRsrcWord3);
+}
+
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
 // ---- bf16 helpers ---------------------------------------------------------
 
 // bf16 bit pattern -> fp32 (exact: the pattern is the top half of the word).
@@ -56,8 +78,11 @@ __device__ __forceinline__ void tile_coords(int wg, int nwg, int tiles_m, int ti
     int first_m = gid * group_m;
     int gsz = tiles_m - first_m < group_m ? tiles_m - first_m : group_m;
     int in_group = id - gid * group;
-    tm = first_m + in_group % gsz;
-    tn = in_group / gsz;
+    // The divisions above run on the vector ALU; pin the (wave-uniform)
+    // results to scalar registers so everything derived from them, buffer
+    // descriptors included, stays scalar.
+    tm = __builtin_amdgcn_readfirstlane(first_m + in_group % gsz);
+    tn = __builtin_amdgcn_readfirstlane(in_group / gsz);
 }
 
 }  // namespace dg

@@ -245,8 +245,13 @@ hipError_t launch_tiles(const GemmArgs<uint16_t>& a, bool vec, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_bf16_mfma(const GemmArgs<uint16_t>& a, bool vec, hipStream_t s) {
+hipError_t launch_bf16_general(const GemmArgs<uint16_t>& a, bool vec, hipStream_t s) {
     return launch_tiles<256, 256, 2, 2>(a, vec, s);
+}
+
+hipError_t launch_bf16_mfma(const GemmArgs<uint16_t>& a, bool vec, hipStream_t s) {
+    if (vec && bf16_tiled_fits(a)) return launch_bf16_tiled(a, s);
+    return launch_bf16_general(a, vec, s);
 }
 
 }  // namespace dg

@@ -1,0 +1,334 @@
+// bf16 GEMM on gfx950 matrix cores, vector path: C = alpha * A * B + beta * C,
+// row-major, fp32 accumulation, one rounding to bf16 at the end.
+//
+// Used when A, B and C rows are 16-byte aligned (the common case, and every
+// workload shape of interest). The element-wise kernel in gemm_bf16_mfma.hip
+// covers everything else.
+//
+// Tiling (the shared-memory tiling, float4 loads, register blocking and
+// double buffering of the RTX 3090 SGEMM article, sections 3-5, and the
+// asynchronous load/compute pipelining of the Blackwell BF16 GEMM notes,
+// section 2.3, re-planned for CDNA4):
+//   * one workgroup of 4 waves per 256 x 256 tile of C, tiles renumbered per
+//     XCD and rastered in groups of 4 tile rows for L2 reuse;
+//   * K in slabs of 64. Slab t+1 is fetched with 128-bit buffer loads into
+//     registers while slab t is multiplied out of LDS; the registers are then
+//     written to the other half of a double-buffered LDS and one barrier
+//     closes the slab;
+//   * A is stored [m][k] (128-byte rows) and B [k][n] exactly as it lies in
+//     memory (512-byte rows); each 16-byte chunk is placed at an XOR-swizzled
+//     position within its row so that the 128-bit A reads, the B stores and
+//     the transposing B reads of a wave spread over all LDS banks;
+//   * MFMA fragments: A(m, k..k+7) is one ds_read_b128; B(k..k+7, n) is two
+//     ds_read_b64_tr_b16, which hand lane i of each 16-lane group column i of
+//     a 4 x 16 block of row-major B. The next k step's fragments are read
+//     while the current step's MFMAs run;
+//   * v_mfma_f32_16x16x32_bf16 is issued with B as the first operand, so each
+//     16 x 16 accumulator is a block of C transposed and every lane ends up
+//     holding 4 consecutive columns of one row of C: the fused epilogue
+//     (alpha * acc + beta * C0, then RNE to bf16) uses 8-byte loads/stores;
+//   * edges: the descriptors end where the matrices end, so rows of A past M
+//     and rows of B past K read as zero; columns of B past N only feed output
+//     columns that are never stored; k past K in the last slab is masked to
+//     zero in A (Z-Turbo CUDA tuning page, section 3.1: zero-filled tile
+//     edges; Blackwell notes, section 4.3: predicate the tail).
+//
+// Operand layout of v_mfma_f32_16x16x32_bf16: lane l = p + 16 g supplies
+// X(row p, k = 8g .. 8g+7) as its first operand and Y(k = 8g .. 8g+7, col p)
+// as its second, and receives D(row 4g + r, col p) in register r. A and B use
+// the same k assignment, so the hardware's internal pairing does not matter.
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace dg {
+namespace {
+
+constexpr int kBK = 64;
+constexpr int kGroupM = 4;
+
+// A tile [256][64]: chunk c (8 bf16) of row `row`. XOR with row mod 8 keeps
+// the eight 16-byte reads of 8 consecutive rows on distinct banks, and keeps
+// every address affine in the 16-row block index (one address register).
+__device__ __forceinline__ int a_off(int row, int c) {
+    return row * kBK + ((c ^ (row & 7)) << 3);
+}
+
+// B tile [64][256]: chunk c (8 bf16, c in 0..31) of row k. The XOR term is
+// even and depends on k mod 4 and k / 8 mod 4, the two indices that vary
+// across the 16-lane groups of a transposing read.
+__device__ __forceinline__ int b_swz(int k) {
+    return ((k & 3) | (((k >> 3) & 3) << 2)) << 1;
+}
+template <int BN>
+__device__ __forceinline__ int b_off(int k, int c) {
+    return k * BN + ((c ^ b_swz(k)) << 3);
+}
+
+// Zero the bf16 elements at positions >= valid (0..8) of an 8-element chunk.
+__device__ __forceinline__ u32x4 mask_tail(u32x4 v, int valid) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t keep = (2 * q + 1 < valid) ? 0xffffffffu : (2 * q < valid ? 0x0000ffffu : 0u);
+        v[q] &= keep;
+    }
+    return v;
+}
+
+template <int BN>
+__device__ __forceinline__ bf16x8 read_b_frag(const uint16_t* Bs, int k0, int col) {
+    // Lane 4r + q of each 16-lane group addresses row k0 + r (+4), columns col .. col+3.
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(Bs + b_off<BN>(k0, col >> 3) + (col & 7)));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(Bs + b_off<BN>(k0 + 4, col >> 3) + (col & 7)));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Workgroup barrier for the LDS pipeline: first wait until this wave's
+// LDS-destined buffer loads have landed (vmcnt, which the LDS-scoped fence
+// does not cover), then the LDS-scoped release/acquire around the barrier
+// retires this wave's LDS reads and keeps later LDS reads below it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's LDS-destined loads have landed
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS byte address of a __shared__ object (what m0 expects).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(size_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// One global -> LDS copy of 16 bytes per lane: lane l's bytes land at
+// lds + 16 l; out-of-range dwords (per the descriptor) land as zeros.
+// Issued as inline assembly so that the compiler neither reorders LDS
+// accesses across it nor inserts waits for it: the kernel's own vmcnt wait
+// plus barrier (lds_barrier) is the only thing that consumes these copies.
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t soff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :: "v"(voff), "s"(r), "s"(soff), "s"(lds) : "memory", "m0");
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N>
+__global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1)
+void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
+    constexpr int kNT = WAVES_M * WAVES_N * 64;
+    constexpr int kWaves = WAVES_M * WAVES_N;
+    constexpr int kBM = BM, kBN = BN;
+    constexpr int kWTM = BM / WAVES_M, kWTN = BN / WAVES_N;   // wave tile
+    constexpr int kFM = kWTM / 16, kFN = kWTN / 16;
+    constexpr int kAStage = BM * kBK;                         // bf16 elements
+    constexpr int kBStage = kBK * BN;
+    constexpr int kACopies = kAStage * 2 / 1024 / kWaves;     // 1 KB LDS copies per wave
+    constexpr int kBCopies = kBStage * 2 / 1024 / kWaves;
+    constexpr int kBRowsPerCopy = 1024 / (BN * 2);            // B rows filled by one copy
+    static_assert(kACopies * kWaves * 1024 == kAStage * 2, "A slab must split evenly");
+    static_assert(kBCopies * kWaves * 1024 == kBStage * 2, "B slab must split evenly");
+    static_assert(BN == 256 || BN == 128, "B row length");
+    static_assert(kWTM % 16 == 0 && kWTN % 16 == 0, "wave tile");
+    // One array per operand and pipeline stage, so the compiler can tell which
+    // stage an LDS-destined load writes and does not make reads of the other
+    // stage wait for it. Laid out [A0 | A1 | B0 | B1]: stage 1 is 32 KB past
+    // stage 0, within reach of the LDS instructions' immediate offset.
+    __shared__ __attribute__((aligned(16))) uint16_t a_st0[kAStage];
+    __shared__ __attribute__((aligned(16))) uint16_t a_st1[kAStage];
+    __shared__ __attribute__((aligned(16))) uint16_t b_st0[kBStage];
+    __shared__ __attribute__((aligned(16))) uint16_t b_st1[kBStage];
+
+    int tm, tn;
+    tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, kGroupM, tm, tn);
+    const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
+    const int64_t M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb;
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    auto a_stage = [&](int stage) -> uint16_t* { return stage == 0 ? a_st0 : a_st1; };
+    auto b_stage = [&](int stage) -> uint16_t* { return stage == 0 ? b_st0 : b_st1; };
+
+    // A descriptor: rows m0 .. min(M, m0 + 256) - 1, ending after element K of
+    // the last row (rounded up to its 16-byte chunk, which stays in its page).
+    // Rows past M therefore arrive in LDS as zeros.
+    const int64_t rows_a = (M - m0 < kBM) ? M - m0 : kBM;
+    (void)kNT;
+    const uint32_t a_bytes = (uint32_t)((((rows_a - 1) * lda + K) * 2 + 15) & ~(int64_t)15);
+    const rsrc_t a_desc = make_rsrc(p.A + m0 * lda, a_bytes);
+
+    // Global -> LDS copies. One buffer_load_dwordx4 ... lds moves 1 KB: lane l
+    // fills bytes [16 l, 16 l + 16) of the destination, so each lane fetches
+    // the global chunk that the swizzle puts at its LDS position.
+    //   A: copy I fills rows 8 I .. 8 I + 7; lane -> row 8 I + l / 8.
+    //   B: copy I fills rows R I .. R I + R - 1 (R = 1024 / row bytes);
+    //      lane -> row R I + l / (64 / R).
+    const int a_lrow = lane >> 3, a_pos = lane & 7;
+    const int b_lrow = lane / (64 / kBRowsPerCopy), b_pos = lane % (64 / kBRowsPerCopy);
+    auto dma = [&](int64_t kt, int stage) {
+        const int64_t k0 = kt * kBK;
+        const uint32_t As = lds_addr(a_stage(stage));
+        const uint32_t Bs = lds_addr(b_stage(stage));
+#pragma unroll
+        for (int i = 0; i < kACopies; ++i) {
+            const int I = wave * kACopies + i;
+            const int c = a_pos ^ a_lrow;       // (8 I + a_lrow) mod 8 == a_lrow
+            dma16(a_desc, (uint32_t)(a_lrow * lda * 2 + c * 16),
+                  (uint32_t)(((8 * I) * lda + k0) * 2), As + I * 1024);
+        }
+        // B descriptor for this slab: rows k0 .. K - 1, ending after column N of
+        // row K - 1, so rows past K arrive as zeros.
+        const int64_t rem = (((K - k0 - 1) * ldb + (N - n0)) * 2 + 15) & ~(int64_t)15;
+        const uint32_t b_bytes = rem < ((int64_t)1 << 31) ? (uint32_t)rem : 0x80000000u;
+        const rsrc_t b_desc = make_rsrc(p.B + k0 * ldb + n0, b_bytes);
+#pragma unroll
+        for (int i = 0; i < kBCopies; ++i) {
+            const int I = wave * kBCopies + i;
+            const int row = kBRowsPerCopy * I + b_lrow;
+            const int c = b_pos ^ b_swz(row);
+            dma16(b_desc, (uint32_t)(b_lrow * ldb * 2 + c * 16),
+                  (uint32_t)((kBRowsPerCopy * I) * ldb * 2), Bs + I * 1024);
+        }
+    };
+
+    // In the last slab of a ragged K, A(m, k >= K) would hold the next row's
+    // values: zero them in LDS (threads stride over the rows). B is already
+    // zero there.
+    auto zero_a_tail = [&](int stage, int kr) {
+        uint16_t* As = a_stage(stage);
+        for (int row = t; row < kBM; row += kNT) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                if (8 * c + 8 <= kr) continue;
+                u32x4* q = reinterpret_cast<u32x4*>(As + a_off(row, c));
+                *q = mask_tail(*q, kr - 8 * c);
+            }
+        }
+    };
+
+    f32x4 acc[kFN][kFM];
+#pragma unroll
+    for (int j = 0; j < kFN; ++j)
+#pragma unroll
+        for (int i = 0; i < kFM; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int wm0 = (wave / WAVES_N) * kWTM, wn0 = (wave % WAVES_N) * kWTN;
+    const int pl = lane & 15, g = lane >> 4;
+    const int tr_row = pl >> 2, tr_col = (pl & 3) * 4;   // transposing-read role of this lane
+
+    bf16x8 fa[2][kFM], fb[2][kFN];
+    auto read_frags = [&](int stage, int ks, int buf) {
+        const uint16_t* As = a_stage(stage);
+        const uint16_t* Bs = b_stage(stage);
+#pragma unroll
+        for (int i = 0; i < kFM; ++i)
+            fa[buf][i] = *reinterpret_cast<const bf16x8*>(As + a_off(wm0 + 16 * i + pl, 4 * ks + g));
+#pragma unroll
+        for (int j = 0; j < kFN; ++j)
+            fb[buf][j] = read_b_frag<BN>(Bs, 32 * ks + 8 * g + tr_row, wn0 + 16 * j + tr_col);
+    };
+    auto mfmas = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < kFM; ++i)
+#pragma unroll
+            for (int j = 0; j < kFN; ++j)
+                acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[buf][j], fa[buf][i],
+                                                                    acc[j][i], 0, 0, 0);
+    };
+
+    // Pipeline (two LDS stages): while slab t is multiplied, slab t + 1 is in
+    // flight to the other stage. The barrier in the middle of each slab both
+    // publishes slab t + 1 and retires every read of slab t, after which slab
+    // t + 2 may overwrite it. Fragments of the next k step are always read one
+    // step ahead of the MFMAs that use them.
+    const int64_t nk = (K + kBK - 1) / kBK;
+    const int k_tail = (int)(K - (nk - 1) * kBK);   // 1 .. 64
+    dma(0, 0);
+    lds_barrier();
+    if (nk == 1 && k_tail < kBK) {
+        zero_a_tail(0, k_tail);
+        lds_barrier();
+    }
+    if (nk > 1) dma(1, 1);
+    read_frags(0, 0, 0);
+    // One slab; `cur` is a literal at both call sites (the loop is unrolled by
+    // two), so every LDS access names its stage array statically.
+    auto slab = [&](int64_t kt, int cur) {
+        read_frags(cur, 1, 1);
+        mfmas(0);
+        if (kt + 1 < nk) {
+            lds_barrier();
+            if (kt + 2 == nk && k_tail < kBK) {
+                zero_a_tail(cur ^ 1, k_tail);
+                lds_barrier();
+            }
+            if (kt + 2 < nk) dma(kt + 2, cur);
+            read_frags(cur ^ 1, 0, 0);
+        }
+        mfmas(1);
+    };
+    for (int64_t kt = 0; kt < nk; kt += 2) {
+        slab(kt, 0);
+        if (kt + 1 < nk) slab(kt + 1, 1);
+    }
+
+    // Epilogue: acc[j][i] register r holds C(m0 + wm0 + 16 i + pl, n0 + wn0 + 16 j + 4 g + r).
+    const float alpha = p.alpha, beta = p.beta;
+#pragma unroll
+    for (int i = 0; i < kFM; ++i) {
+        const int64_t row = m0 + wm0 + 16 * i + pl;
+        if (row >= M) continue;
+        uint16_t* crow = p.C + row * p.ldc;
+#pragma unroll
+        for (int j = 0; j < kFN; ++j) {
+            const int64_t col = n0 + wn0 + 16 * j + 4 * g;
+            float v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = alpha * acc[j][i][r];
+            if (col + 4 <= N) {
+                u32x2* dst = reinterpret_cast<u32x2*>(crow + col);
+                if (beta != 0.f) {
+                    const u32x2 c0 = *dst;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        v[r] += beta * bf16_to_f32((uint16_t)(c0[r >> 1] >> (16 * (r & 1))));
+                }
+                *dst = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    if (col + r < N) {
+                        float x = v[r];
+                        if (beta != 0.f) x += beta * bf16_to_f32(crow[col + r]);
+                        crow[col + r] = f32_to_bf16(x);
+                    }
+                }
+            }
+        }
+    }
+}
+
+}  // namespace
+
+// True when every buffer offset the tiled kernel forms fits in 31 bits.
+bool bf16_tiled_fits(const GemmArgs<uint16_t>& a) {
+    const int64_t lim = (int64_t)1 << 31;
+    return (256 * a.lda + a.K) * 2 < lim && (kBK * a.ldb + a.N) * 2 < lim;
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N>
+hipError_t launch_cfg(const GemmArgs<uint16_t>& a, hipStream_t s) {
+    const int64_t tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
+    int tm = (int)tiles_m, tn = (int)tiles_n;
+    GemmArgs<uint16_t> args = a;
+    void* kargs[] = {&args, &tm, &tn};
+    return hipLaunchKernel((const void*)&gemm_bf16_tiled_kernel<BM, BN, WAVES_M, WAVES_N>,
+                           dim3((unsigned)(tiles_m * tiles_n)), dim3(WAVES_M * WAVES_N * 64), kargs,
+                           0, s);
+}
+
+hipError_t launch_bf16_tiled(const GemmArgs<uint16_t>& a, hipStream_t s) {
+    return launch_cfg<256, 256, 2, 4>(a, s);
+}
+
+}  // namespace dg

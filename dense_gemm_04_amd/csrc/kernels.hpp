@@ -12,6 +12,12 @@ namespace dg {
 // aligned base pointers and leading dimensions that keep every row 16-byte
 // aligned. Without it every global access is element-wise.
 hipError_t launch_bf16_mfma(const GemmArgs<uint16_t>& a, bool vec, hipStream_t s);
+// The two bf16 MFMA kernels behind launch_bf16_mfma: the tiled vector kernel
+// (needs `vec` and offsets that fit its 31-bit buffer offsets) and the
+// element-wise one that takes any alignment.
+hipError_t launch_bf16_tiled(const GemmArgs<uint16_t>& a, hipStream_t s);
+bool bf16_tiled_fits(const GemmArgs<uint16_t>& a);
+hipError_t launch_bf16_general(const GemmArgs<uint16_t>& a, bool vec, hipStream_t s);
 hipError_t launch_f32_mfma(const GemmArgs<float>& a, bool vec, hipStream_t s);
 hipError_t launch_f32_valu(const GemmArgs<float>& a, bool vec, hipStream_t s);
 hipError_t launch_bf16_skinny(const GemmArgs<uint16_t>& a, bool vec, hipStream_t s);

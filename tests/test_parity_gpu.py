@@ -21,7 +21,9 @@ BF16_VARIANTS = [dg.VARIANT_AUTO, dg.VARIANT_MFMA, dg.VARIANT_GENERAL]
 # Shapes that span several tiles in each direction and end in ragged tails
 # (the 256x256 bf16 tile, the 128x128 fp32 tile, K slabs of 32/64).
 RAGGED = [(1, 1, 1), (3, 5, 7), (17, 33, 65), (129, 257, 63), (300, 200, 100),
-          (257, 520, 129), (513, 384, 1000), (640, 136, 72)]
+          (257, 520, 129), (513, 384, 1000), (640, 136, 72),
+          # 16-byte-aligned rows in both dtypes (vector path) with ragged tiles:
+          (64, 64, 8), (520, 264, 40), (256, 256, 64), (1000, 1032, 136), (264, 776, 200)]
 
 
 def check(dtype, M, N, K, alpha, beta, variant, seed, ld_pad=(0, 0, 0), offset=0):
