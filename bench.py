@@ -97,6 +97,36 @@ def measure(w, steps: int, warmup: int, sets: int = 1) -> dict:
     return out
 
 
+def kernel_source_sha(path: str) -> str:
+    import hashlib
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(summary: str, source: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary.
+
+    The summary holds `source_sha: <hash>`, `fetch_bytes_per_launch: <n>` and
+    `write_bytes_per_launch: <n>` lines (FETCH_SIZE and WRITE_SIZE already
+    scaled by the copy-kernel calibration). Returns None when the summary is
+    missing or was taken on a different kernel source than the one built now.
+    """
+    path = os.path.join(ROOT, "profiles", summary)
+    src = os.path.join(ROOT, "dense_gemm_04_amd", "csrc", source)
+    if not (os.path.exists(path) and os.path.exists(src)):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            fields[k.strip().strip("-* `")] = v.strip().strip("`")
+    if fields.get("source_sha") != kernel_source_sha(src):
+        return None
+    try:
+        return int(fields["fetch_bytes_per_launch"]) + int(fields["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(w, target_seconds: float = 12.0) -> dict:
     """Time the oracle on full rows of C for this workload (bounded sample)."""
     import oracle
@@ -130,6 +160,10 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--all", action="store_true", help="one JSON line per workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only", type=int, default=None,
+                    help="time one workload id (1, 2, 3, 4, 51, 52) and print its line")
+    ap.add_argument("--copy-mib", type=int, default=None,
+                    help="time a plain device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py measures one GPU only: the GEMM path runs on a single device and "
@@ -144,6 +178,21 @@ def main(argv=None) -> int:
         return 2
     torch.cuda.set_device(0)
     dg.load()
+
+    if args.copy_mib is not None:
+        n = args.copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        stream = torch.cuda.current_stream()
+        sec = _time_calls(lambda: dst.copy_(src), args.steps, args.warmup, stream)
+        print(json.dumps({"copy_bytes": n, "ms": sec * 1e3, "gbs": 2 * n / sec / 1e9}), flush=True)
+        return 0
+
+    if args.only is not None:
+        w = gi.WORKLOADS[args.only]
+        r = measure(w, args.steps, args.warmup, 4 if args.only == 52 else 1)
+        print(json.dumps(r), flush=True)
+        return 0
 
     if args.all:
         for wid in (1, 2, 3, 4, 51, 52):
@@ -176,7 +225,8 @@ def main(argv=None) -> int:
         "frac_of_matrix_peak": round(main_r["frac_matrix_peak"], 4),
         "roofline": {"bound": "mfma", "achieved": round(main_r["tflops"], 3),
                      "peak": PEAK_TFLOPS["f32"], "unit": "TFLOP/s",
-                     "frac": round(main_r["frac_matrix_peak"], 4), "traffic": None},
+                     "frac": round(main_r["frac_matrix_peak"], 4),
+                     "traffic": measured_traffic("gemm_f32_mfma_4096.md", "gemm_f32_mfma.hip")},
         "bf16_4096": {"workload": "BF16 GEMM M=N=K=4096, fp32 accumulate, bf16 out",
                       "tflops": round(bf["tflops"], 3), "ms": round(bf["ms"], 4),
                       "peak": PEAK_TFLOPS["bf16"], "frac": round(bf["frac_matrix_peak"], 4)},

@@ -8,7 +8,7 @@
 #include <climits>
 #include <cstring>
 
-#include "../../include/gemm.h"
+#include "gemm.h"
 #include "common.hpp"
 #include "kernels.hpp"
 
