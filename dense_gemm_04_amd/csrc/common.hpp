@@ -60,6 +60,48 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
 
+// ---- LDS pipelines ----------------------------------------------------------
+
+// Zero the bf16 elements at positions >= valid (0..8) of an 8-element chunk.
+__device__ __forceinline__ u32x4 mask_tail(u32x4 v, int valid) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t keep = (2 * q + 1 < valid) ? 0xffffffffu : (2 * q < valid ? 0x0000ffffu : 0u);
+        v[q] &= keep;
+    }
+    return v;
+}
+
+// LDS byte address of a __shared__ object (what m0 expects).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(size_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// One global -> LDS copy of 16 bytes per lane: lane l's bytes land at
+// lds + 16 l; out-of-range dwords (per the descriptor) land as zeros.
+// Issued as inline assembly so that the compiler neither reorders LDS
+// accesses across it nor inserts waits for it: the kernel's own vmcnt wait
+// plus barrier (lds_barrier) is the only thing that consumes these copies.
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t soff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :: "v"(voff), "s"(r), "s"(soff), "s"(lds) : "memory", "m0");
+}
+
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt << 4 | lgkmcnt << 8 | vmcnt[5:4] << 14).
+constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+constexpr int kWaitLgkm0 = 0xC07F;
+
+// Workgroup barrier ordering LDS traffic only: the release half retires this
+// wave's LDS accesses, the acquire half keeps later LDS accesses below the
+// barrier. LDS-destined buffer loads are NOT covered (they count in vmcnt):
+// callers wait for those explicitly first.
+__device__ __forceinline__ void lds_only_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ---- workgroup -> output tile mapping ----------------------------------------
 //
 // The dispatcher hands workgroup w to XCD (w mod 8), and each of the 8 XCDs has

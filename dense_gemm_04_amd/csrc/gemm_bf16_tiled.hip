@@ -65,15 +65,6 @@ __device__ __forceinline__ int b_off(int k, int c) {
     return k * BN + ((c ^ b_swz(k)) << 3);
 }
 
-// Zero the bf16 elements at positions >= valid (0..8) of an 8-element chunk.
-__device__ __forceinline__ u32x4 mask_tail(u32x4 v, int valid) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const uint32_t keep = (2 * q + 1 < valid) ? 0xffffffffu : (2 * q < valid ? 0x0000ffffu : 0u);
-        v[q] &= keep;
-    }
-    return v;
-}
 
 template <int BN>
 __device__ __forceinline__ bf16x8 read_b_frag(const uint16_t* Bs, int k0, int col) {
@@ -86,32 +77,11 @@ __device__ __forceinline__ bf16x8 read_b_frag(const uint16_t* Bs, int k0, int co
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// Workgroup barrier for the LDS pipeline: first wait until this wave's
-// LDS-destined buffer loads have landed (vmcnt, which the LDS-scoped fence
-// does not cover), then the LDS-scoped release/acquire around the barrier
-// retires this wave's LDS reads and keeps later LDS reads below it.
+// Barrier for the two-stage pipeline: this wave's LDS-destined copies have
+// landed (vmcnt 0), then an LDS-only workgroup barrier.
 __device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's LDS-destined loads have landed
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// LDS byte address of a __shared__ object (what m0 expects).
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(size_t)(const __attribute__((address_space(3))) char*)p;
-}
-
-// One global -> LDS copy of 16 bytes per lane: lane l's bytes land at
-// lds + 16 l; out-of-range dwords (per the descriptor) land as zeros.
-// Issued as inline assembly so that the compiler neither reorders LDS
-// accesses across it nor inserts waits for it: the kernel's own vmcnt wait
-// plus barrier (lds_barrier) is the only thing that consumes these copies.
-__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t soff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-                 :: "v"(voff), "s"(r), "s"(soff), "s"(lds) : "memory", "m0");
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    lds_only_barrier();
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N>

@@ -63,12 +63,26 @@ def test_bf16_ragged(shape, variant):
     check("bf16", M, N, K, 1.0, 0.0, variant, seed=400 + N)
 
 
+# (N, K) for the small-M kernels: element-wise rows (N or K not a multiple of
+# 8) and 16-byte rows (the copy-ring path) with ragged K tails, K spanning
+# more 256-row chunks than the ring holds, and N ending in a partial strip.
+SKINNY_NK = [(1, 1), (31, 33), (200, 1100), (1000, 520), (8, 8), (40, 264),
+             (264, 2000), (1032, 4104), (96, 1536)]
+
+
 @pytest.mark.parametrize("M", [1, 2, 5, 15, 16, 17, 31, 32])
-@pytest.mark.parametrize("NK", [(1, 1), (31, 33), (200, 1100), (1000, 520)])
+@pytest.mark.parametrize("NK", SKINNY_NK, ids=lambda s: "x".join(map(str, s)))
 def test_bf16_skinny(M, NK):
     N, K = NK
     check("bf16", M, N, K, 1.5, -0.5, dg.VARIANT_SKINNY, seed=500 + M + N)
     check("bf16", M, N, K, 1.0, 0.0, dg.VARIANT_AUTO, seed=600 + M + K)
+
+
+@pytest.mark.parametrize("M", [7, 16, 29])
+def test_bf16_skinny_padded(M):
+    # 16-byte padded rows keep the copy-ring path; odd padding takes the other.
+    check("bf16", M, 264, 1000, 1.0, 1.0, dg.VARIANT_SKINNY, 720 + M, ld_pad=(8, 16, 24))
+    check("bf16", M, 264, 1000, 1.0, 1.0, dg.VARIANT_SKINNY, 730 + M, ld_pad=(1, 3, 5))
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
