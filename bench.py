@@ -56,9 +56,10 @@ def _time_calls(call, steps: int, warmup: int, stream):
     return start.elapsed_time(end) / 1e3 / steps     # seconds per call
 
 
-def _device_call(w, sets: int = 1):
+def _device_call(w, sets: int = 1, use_ws: bool = False):
     """Allocate `sets` independent operand sets on the GPU and return a callable
-    that runs the library on the next set each time."""
+    that runs the library on the next set each time (through gemm_bf16_ws with
+    a zeroed workspace when `use_ws`)."""
     import torch
     import dense_gemm_04_amd as dg
     import gemm_inputs as gi
@@ -74,6 +75,13 @@ def _device_call(w, sets: int = 1):
     h = int(stream.cuda_stream)
     fn = dg.gemm_f32 if w.dtype == "f32" else dg.gemm_bf16
     state = {"i": 0}
+    if use_ws:
+        nbytes = dg.gemm_bf16_workspace_size(w.M, w.N, w.K)
+        ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+
+        def fn(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream):
+            return dg.gemm_bf16_ws(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                                   ws.data_ptr() if nbytes else None, nbytes, stream)
 
     def call():
         A, B, C = bufs[state["i"] % sets]
@@ -85,10 +93,11 @@ def _device_call(w, sets: int = 1):
     return call, stream, inp
 
 
-def measure(w, steps: int, warmup: int, sets: int = 1) -> dict:
-    call, stream, _ = _device_call(w, sets)
+def measure(w, steps: int, warmup: int, sets: int = 1, use_ws: bool = False) -> dict:
+    call, stream, _ = _device_call(w, sets, use_ws)
     sec = _time_calls(call, steps, warmup, stream)
-    out = {"workload": w.name, "dtype": w.dtype, "M": w.M, "N": w.N, "K": w.K,
+    out = {"workload": w.name + (" (gemm_bf16_ws, split-K)" if use_ws else ""),
+           "dtype": w.dtype, "M": w.M, "N": w.N, "K": w.K,
            "alpha": w.alpha, "beta": w.beta, "ms": sec * 1e3,
            "tflops": tflops(gemm_flops(w.M, w.N, w.K), sec),
            "gbs": w.algorithmic_bytes / sec / 1e9}
@@ -192,6 +201,8 @@ def main(argv=None) -> int:
         w = gi.WORKLOADS[args.only]
         r = measure(w, args.steps, args.warmup, 4 if args.only == 52 else 1)
         print(json.dumps(r), flush=True)
+        if args.only == 52:
+            print(json.dumps(measure(w, args.steps, args.warmup, 4, use_ws=True)), flush=True)
         return 0
 
     if args.all:
@@ -202,6 +213,9 @@ def main(argv=None) -> int:
             sets = 4 if wid == 52 else 1
             r = measure(w, args.steps, args.warmup, sets)
             print(json.dumps(r), flush=True)
+            if wid == 52:
+                print(json.dumps(measure(w, args.steps, args.warmup, sets, use_ws=True)),
+                      flush=True)
         return 0
 
     w = gi.WORKLOADS[2]

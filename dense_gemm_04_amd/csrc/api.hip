@@ -102,7 +102,7 @@ gemm_status_t check_device() {
 template <typename T>
 gemm_status_t run(int64_t M, int64_t N, int64_t K, float alpha, const T* A, int64_t lda,
                   const T* B, int64_t ldb, float beta, T* C, int64_t ldc, void* stream,
-                  int variant) {
+                  int variant, void* ws = nullptr, size_t ws_bytes = 0) {
     constexpr int esz = (int)sizeof(T);
     const int v = plan_impl(esz, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, variant);
     if (v < 0) return GEMM_ERR_INVALID_VALUE;
@@ -122,7 +122,7 @@ gemm_status_t run(int64_t M, int64_t N, int64_t K, float alpha, const T* A, int6
             e = (v == GEMM_VARIANT_VALU) ? dg::launch_f32_valu(a, vec, s)
                                          : dg::launch_f32_mfma(a, v == GEMM_VARIANT_MFMA, s);
         } else {
-            e = (v == GEMM_VARIANT_SKINNY) ? dg::launch_bf16_skinny(a, vec, s)
+            e = (v == GEMM_VARIANT_SKINNY) ? dg::launch_bf16_skinny(a, vec, ws, ws_bytes, s)
                                            : dg::launch_bf16_mfma(a, v == GEMM_VARIANT_MFMA, s);
         }
     }
@@ -143,6 +143,22 @@ gemm_status_t gemm_bf16_ex(int64_t M, int64_t N, int64_t K, float alpha, const u
                            int64_t lda, const uint16_t* B, int64_t ldb, float beta, uint16_t* C,
                            int64_t ldc, void* stream, int variant) {
     return run<uint16_t>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, variant);
+}
+
+size_t gemm_bf16_workspace_size(int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N < 0 || K < 0 || M > INT_MAX || N > INT_MAX || K > INT_MAX) return 0;
+    return dg::bf16_skinny_workspace(M, N, K);
+}
+
+gemm_status_t gemm_bf16_ws(int64_t M, int64_t N, int64_t K, float alpha, const uint16_t* A,
+                           int64_t lda, const uint16_t* B, int64_t ldb, float beta, uint16_t* C,
+                           int64_t ldc, void* workspace, size_t workspace_bytes, void* stream) {
+    if (workspace == nullptr ? workspace_bytes != 0 : !aligned(workspace, 256))
+        return GEMM_ERR_INVALID_VALUE;
+    if (workspace != nullptr && workspace_bytes < gemm_bf16_workspace_size(M, N, K))
+        return GEMM_ERR_INVALID_VALUE;
+    return run<uint16_t>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, GEMM_VARIANT_AUTO,
+                         workspace, workspace_bytes);
 }
 
 gemm_status_t gemm_f32(int64_t M, int64_t N, int64_t K, float alpha, const float* A,

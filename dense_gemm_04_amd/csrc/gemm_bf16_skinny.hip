@@ -170,55 +170,110 @@ void gemm_bf16_skinny_kernel(GemmArgs<uint16_t> p, int strips) {
 }
 
 // ---- vector path -------------------------------------------------------------
+//
+// Work is cut into units: a strip of 64 columns of C (one 128-byte line of
+// every B row; a half line costs a whole line's worth of HBM bandwidth) times
+// a segment of K made of whole 128-row chunks, one unit per workgroup.
+// Without a workspace a unit is a whole strip. With one, K is cut into
+// segments so that the units fill the chip; each workgroup stores its fp32
+// partial tile in its unit's slot, and the last workgroup to finish a strip's
+// segments (an atomic counter per strip) adds the slots in segment order and
+// applies the epilogue.
+//
+// Wave w owns strip columns 16 w .. 16 w + 15 and all k of each chunk, so no
+// partial sums cross waves.
 
-constexpr int kDmaKC = 256;                       // k rows per chunk
-template <int MB> struct SmallMDma {
-    static constexpr int kBStage = kDmaKC * kBN;          // bf16, [256][32] row-major
-    static constexpr int kAStage = 16 * MB * kDmaKC;      // bf16, [16 MB][256]
-    static constexpr int kStages = MB == 1 ? 6 : 4;       // 144 / 128 KB of ring
-    static constexpr int kBCopies = kBStage * 2 / 1024 / (kNT / 64);   // per wave per chunk
+constexpr int kVBN = 64;                 // strip width (columns)
+constexpr int kVKC = 128;                // k rows per chunk
+constexpr int kMaxWorkgroups = 256;      // one per compute unit
+constexpr int kMaxSegments = 64;
+
+template <int MB> struct SmallM {
+    static constexpr int kBStage = kVKC * kVBN;           // bf16, [128][64] row-major
+    static constexpr int kAStage = 16 * MB * kVKC;        // bf16, [16 MB][128]
+    static constexpr int kStages = MB == 1 ? 6 : 5;       // 120 KB of ring
+    static constexpr int kBCopies = kBStage * 2 / 1024 / (kNT / 64);   // 1 KB copies per wave
     static constexpr int kACopies = kAStage * 2 / 1024 / (kNT / 64);
     static constexpr int kCopies = kBCopies + kACopies;
-    static constexpr int kSteps = kDmaKC / 32 / (kNT / 64);            // k-steps per wave per chunk
 };
 
-// A stage row of 256 bf16 = 32 chunks of 16 bytes, XORed with row mod 16 so
-// the 16 rows of an MFMA fragment read land on distinct banks.
-__device__ __forceinline__ int sa_off(int row, int c) {
-    return row * kDmaKC + ((c ^ (row & 15)) << 3);
-}
+// B stage rows are 128 bytes = 8 chunks of 16 bytes; chunk c of row r sits in
+// slot c ^ b_swz(r), which spreads the 16 rows one transposing read touches
+// over all LDS banks. A stage rows are 256 bytes; chunk c of row r sits in
+// slot c ^ (r mod 16), spreading the 16 rows of a fragment read.
+__device__ __forceinline__ int b_swz(int r) { return (((r >> 1) & 1) | (((r >> 3) & 1) << 1)) << 1; }
+__device__ __forceinline__ int a_off(int row, int c) { return row * kVKC + ((c ^ (row & 15)) << 3); }
+
+// How the work is cut (identical on host and device): workgroup w takes
+// segment w / strips of strip w % strips.
+struct SmallMWork {
+    int strips;   // 64-column strips
+    int segs;     // K segments per strip (1: no split)
+    int cps;      // chunks per segment
+};
 
 template <int MB>
+__device__ __forceinline__ void store_row4(const GemmArgs<uint16_t>& p, int64_t row, int64_t gc,
+                                           f32x4 s) {
+    if (row >= p.M) return;
+    uint16_t* dst = p.C + row * p.ldc + gc;
+    if (gc + 3 < p.N) {
+        // Four bf16 = 8 bytes, aligned: rows are 16-byte aligned and gc % 4 == 0.
+        float v[4] = {p.alpha * s[0], p.alpha * s[1], p.alpha * s[2], p.alpha * s[3]};
+        if (p.beta != 0.f) {
+            const u32x2 c0 = *reinterpret_cast<const u32x2*>(dst);
+            v[0] += p.beta * bf16_to_f32((uint16_t)(c0[0] & 0xffffu));
+            v[1] += p.beta * bf16_to_f32((uint16_t)(c0[0] >> 16));
+            v[2] += p.beta * bf16_to_f32((uint16_t)(c0[1] & 0xffffu));
+            v[3] += p.beta * bf16_to_f32((uint16_t)(c0[1] >> 16));
+        }
+        *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            if (gc + r >= p.N) break;
+            float v = p.alpha * s[r];
+            if (p.beta != 0.f) v += p.beta * bf16_to_f32(dst[r]);
+            dst[r] = f32_to_bf16(v);
+        }
+    }
+}
+
+// ws (only used when wk.segs > 1): [counters: one int per strip, padded to
+// 256 bytes][slots: segs x strips tiles of 16 MB x 64 fp32, slot s * strips + strip].
+template <int MB>
 __global__ __launch_bounds__(kNT, 1)
-void gemm_bf16_skinny_dma_kernel(GemmArgs<uint16_t> p, int strips) {
-    using S = SmallMDma<MB>;
+void gemm_bf16_smallm_kernel(GemmArgs<uint16_t> p, SmallMWork wk, unsigned char* ws) {
+    using S = SmallM<MB>;
     __shared__ __attribute__((aligned(16))) uint16_t lds_b[S::kStages * S::kBStage];
     __shared__ __attribute__((aligned(16))) uint16_t lds_a[S::kStages * S::kAStage];
-    __shared__ __attribute__((aligned(16))) float part[kNT / 64][MB * 16 * kBN];
+    __shared__ int last_flag;
 
-    int tm, strip;
-    tile_coords(blockIdx.x, gridDim.x, 1, strips, 1, tm, strip);
-    const int64_t n0 = (int64_t)strip * kBN;
     const int64_t M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb;
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int pl = lane & 15, g = lane >> 4;
+    const int seg = __builtin_amdgcn_readfirstlane((int)blockIdx.x / wk.strips);
+    const int strip = __builtin_amdgcn_readfirstlane((int)blockIdx.x - seg * wk.strips);
+    const int64_t n0 = (int64_t)strip * kVBN;
+    const int64_t nck = (K + kVKC - 1) / kVKC;
+    const int64_t cb = (int64_t)seg * wk.cps;
+    const int64_t nc = (cb + wk.cps < nck ? cb + wk.cps : nck) - cb;   // >= 1
 
-    // A descriptor covers rows 0 .. M - 1 up to element K of the last row
+    // A descriptor: rows 0 .. M - 1, ending at element K of the last row
     // (rounded up to its 16-byte chunk), so rows past M arrive as zeros.
     const uint32_t a_bytes = (uint32_t)((((M - 1) * lda + K) * 2 + 15) & ~(int64_t)15);
     const rsrc_t a_desc = make_rsrc(p.A, a_bytes);
 
-    // The whole offset of every copy goes in the per-lane offset, which the
-    // descriptor's range check always covers.
-    // Copies (1 KB each; lane l fills bytes [16 l, 16 l + 16) of the slot):
-    //   B: copy I fills chunk rows 16 I .. 16 I + 15 (64 bytes each); lane ->
-    //      row 16 I + l / 4, 16-byte column block l % 4.
-    //   A: copy J fills rows 2 J, 2 J + 1 (512 bytes each); lane -> row
-    //      2 J + l / 32, slot l % 32 holding global chunk (l % 32) ^ (row % 16).
-    const uint32_t b_voff = (uint32_t)(((lane >> 2) * ldb + (lane & 3) * 8) * 2);
+    // Copies are 1 KB; lane l fills bytes [16 l, 16 l + 16) of the slot, and
+    // each copy's whole offset sits in the per-lane offset, which the
+    // descriptor's range check covers.
+    //   B: copy I fills chunk rows 8 I .. 8 I + 7; lane -> row 8 I + l / 8,
+    //      slot l % 8 holding 16-byte chunk (l % 8) ^ b_swz(row).
+    //   A: copy J fills rows 4 J .. 4 J + 3; lane -> row 4 J + l / 16, slot
+    //      l % 16 holding chunk (l % 16) ^ (row % 16).
     auto dma = [&](int64_t chunk, int stage) {
-        const int64_t k0 = chunk * kDmaKC;
+        const int64_t k0 = chunk * kVKC;
         const int64_t rem = (((K - k0 - 1) * ldb + (N - n0)) * 2 + 15) & ~(int64_t)15;
         const uint32_t b_bytes = rem < ((int64_t)1 << 31) ? (uint32_t)rem : 0x80000000u;
         const rsrc_t b_desc = make_rsrc(p.B + k0 * ldb + n0, b_bytes);
@@ -227,63 +282,63 @@ void gemm_bf16_skinny_dma_kernel(GemmArgs<uint16_t> p, int strips) {
 #pragma unroll
         for (int i = 0; i < S::kBCopies; ++i) {
             const int I = wave * S::kBCopies + i;
-            dma16(b_desc, b_voff + (uint32_t)(16 * I * ldb * 2), 0, Bs + I * 1024);
+            const int row = 8 * I + (lane >> 3);
+            const int c = (lane & 7) ^ b_swz(row);
+            dma16(b_desc, (uint32_t)(row * ldb * 2 + c * 16), 0, Bs + I * 1024);
         }
 #pragma unroll
         for (int i = 0; i < S::kACopies; ++i) {
             const int J = wave * S::kACopies + i;
-            const int row = 2 * J + (lane >> 5);
-            const int c = (lane & 31) ^ (row & 15);
-            dma16(a_desc, (uint32_t)(((row * lda + k0) + c * 8) * 2), 0, As + J * 1024);
+            const int row = 4 * J + (lane >> 4);
+            const int c = (lane & 15) ^ (row & 15);
+            dma16(a_desc, (uint32_t)((row * lda + k0 + c * 8) * 2), 0, As + J * 1024);
         }
     };
 
-    f32x4 acc[MB][2];
+    f32x4 acc[MB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[mb][0] = acc[mb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-    const int tr_row = pl >> 2, tr_col = (pl & 3) * 4;   // transposing-read role of this lane
-    const int64_t nc = (K + kDmaKC - 1) / kDmaKC;
+    // Transposing-read role: lane 4 r + q of a 16-lane group addresses 4
+    // consecutive columns (4 q ..) of row r of a 4 x 16 block.
+    const int tr_row = pl >> 2, tr_c = 2 * wave + ((pl >> 1) & 1), tr_in = (pl & 1) * 4;
     auto compute = [&](int64_t chunk, int stage) {
         const uint16_t* Bs = lds_b + stage * S::kBStage;
         const uint16_t* As = lds_a + stage * S::kAStage;
 #pragma unroll
-        for (int s = 0; s < S::kSteps; ++s) {
-            const int ks = wave * S::kSteps + s;                // k-step (32 k) within the chunk
-            bf16x8 fa[MB], fb[2];
+        for (int ks = 0; ks < kVKC / 32; ++ks) {
+            bf16x8 fa[MB];
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
-                fa[mb] = *reinterpret_cast<const bf16x8*>(As + sa_off(16 * mb + pl, 4 * ks + g));
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const uint16_t* q = Bs + (32 * ks + 8 * g + tr_row) * kBN + 16 * h + tr_col;
-                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)q);
-                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(q + 4 * kBN));
-                fb[h] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            }
-            const int64_t kfirst = chunk * kDmaKC + 32 * ks + 8 * g;   // k of this lane's first element
+                fa[mb] = *reinterpret_cast<const bf16x8*>(As + a_off(16 * mb + pl, 4 * ks + g));
+            // Rows 32 ks + 8 g + tr_row and 4 further down; columns 16 wave + 4 q.
+            const int r0 = 32 * ks + 8 * g + tr_row, r1 = r0 + 4;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4*)(Bs + r0 * kVBN + ((tr_c ^ b_swz(r0)) << 3) + tr_in));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4*)(Bs + r1 * kVBN + ((tr_c ^ b_swz(r1)) << 3) + tr_in));
+            const bf16x8 fb = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            const int64_t kfirst = chunk * kVKC + 32 * ks + 8 * g;   // k of this lane's first element
             if (kfirst + 8 > K) {
                 // Ragged K: A(m, k >= K) holds the next row's values.
+                const int valid = kfirst >= K ? 0 : (int)(K - kfirst);
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb)
-                    fa[mb] = __builtin_bit_cast(
-                        bf16x8, mask_tail(__builtin_bit_cast(u32x4, fa[mb]), (int)(K - kfirst)));
+                    fa[mb] = __builtin_bit_cast(bf16x8, mask_tail(__builtin_bit_cast(u32x4, fa[mb]), valid));
             }
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-                    acc[mb][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[h], fa[mb], acc[mb][h], 0, 0, 0);
+                acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb, fa[mb], acc[mb], 0, 0, 0);
         }
     };
 
     // Ring of kStages chunk slots; copies run kStages - 1 chunks ahead. At
-    // chunk c each wave waits for its own copies of chunk c (the later ones
-    // may stay in flight), then the barrier publishes chunk c and retires all
+    // chunk c each wave waits for its own copies of chunk c (later ones may
+    // stay in flight), then the barrier publishes chunk c and retires all
     // reads of chunk c - 1, whose slot the copy for chunk c + kStages - 1 reuses.
     const int64_t pre = nc < S::kStages - 1 ? nc : S::kStages - 1;
-    for (int64_t c = 0; c < pre; ++c) dma(c, (int)c);
+    for (int64_t c = 0; c < pre; ++c) dma(cb + c, (int)c);
     int stage = 0;
     for (int64_t c = 0; c < nc; ++c) {
         if (c + S::kStages - 2 <= nc - 1)
@@ -291,61 +346,126 @@ void gemm_bf16_skinny_dma_kernel(GemmArgs<uint16_t> p, int strips) {
         else
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         lds_only_barrier();
-        if (c + S::kStages - 1 < nc) dma(c + S::kStages - 1, stage == 0 ? S::kStages - 1 : stage - 1);
-        compute(c, stage);
+        if (c + S::kStages - 1 < nc) dma(cb + c + S::kStages - 1, stage == 0 ? S::kStages - 1 : stage - 1);
+        compute(cb + c, stage);
         stage = stage + 1 == S::kStages ? 0 : stage + 1;
     }
 
-    // Sum the four waves' partial tiles in a fixed order, then the epilogue.
-    // acc[mb][h] register r holds C(16 mb + pl, 16 h + 4 g + r) of the strip.
+    // acc[mb] register r holds C(16 mb + pl, n0 + 16 wave + 4 g + r).
+    const int tcol = 16 * wave + 4 * g;
+    if (wk.segs == 1) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                part[wave][(16 * mb + pl) * kBN + 16 * h + 4 * g + r] = acc[mb][h][r];
-    __syncthreads();
-    const float alpha = p.alpha, beta = p.beta;
-    for (int e = t; e < MB * 16 * kBN; e += kNT) {
-        const int row = e / kBN, col = e % kBN;
-        const int64_t gc = n0 + col;
-        if (row >= M || gc >= N) continue;
-        float sum = part[0][e];
-#pragma unroll
-        for (int w = 1; w < kNT / 64; ++w) sum += part[w][e];
-        float v = alpha * sum;
-        uint16_t* dst = p.C + row * p.ldc + gc;
-        if (beta != 0.f) v += beta * bf16_to_f32(*dst);
-        *dst = f32_to_bf16(v);
+        for (int mb = 0; mb < MB; ++mb) store_row4<MB>(p, 16 * mb + pl, n0 + tcol, acc[mb]);
+        return;
     }
+
+    // Split K: store the partial tile to this unit's slot, count in once the
+    // stores have completed, and let a strip's last arrival add its segments
+    // in order. Slots and counters are only touched through agent-scope
+    // atomics (device-coherent accesses that bypass the per-XCD L2's
+    // write-back caching), so no cache write-back or invalidate is needed.
+    int* counters = reinterpret_cast<int*>(ws);
+    float* slots = reinterpret_cast<float*>(ws + (((int64_t)wk.strips * 4 + 255) & ~(int64_t)255));
+    auto slot = [&](int sg, int mb) {
+        return slots + ((int64_t)sg * wk.strips + strip) * (16 * MB * kVBN) + (16 * mb + pl) * kVBN + tcol;
+    };
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        float* dst = slot(seg, mb);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            __hip_atomic_store(dst + r, acc[mb][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+    if (t == 0)
+        last_flag = __hip_atomic_fetch_add(counters + strip, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                    wk.segs - 1;
+    __syncthreads();
+    if (!last_flag) return;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        // Eight slots' loads in flight at a time; the sum runs in segment order.
+        f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int sg0 = 0; sg0 < wk.segs; sg0 += 8) {
+            f32x4 v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                v[i] = acc[mb];
+                if (sg0 + i < wk.segs && sg0 + i != seg) {
+                    const float* src = slot(sg0 + i, mb);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        v[i][r] = __hip_atomic_load(src + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (sg0 + i < wk.segs) sum += v[i];
+        }
+        store_row4<MB>(p, 16 * mb + pl, n0 + tcol, sum);
+    }
+    // Leave the counter at zero for the next call that uses this workspace.
+    if (t == 0) __hip_atomic_store(counters + strip, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace
 
-// True when every buffer offset the vector kernel forms fits in 31 bits: A
-// copies reach row 31 (rows past M included) and one chunk past K; B copies
-// reach 256 rows below a chunk's first row.
-static bool skinny_dma_fits(const GemmArgs<uint16_t>& a) {
-    const int64_t lim = (int64_t)1 << 31;
-    return (32 * a.lda + a.K + kDmaKC) * 2 < lim && (kDmaKC * a.ldb + a.N) * 2 < lim;
+// Work decomposition of the vector small-M kernel: 64-column strips; with a
+// workspace and fewer strips than compute units, K segments (whole chunks,
+// every segment non-empty) so that strips x segments fills the chip.
+static SmallMWork plan_smallm(int64_t N, int64_t K, bool split) {
+    SmallMWork w;
+    w.strips = (int)((N + kVBN - 1) / kVBN);
+    const int64_t nck = (K + kVKC - 1) / kVKC;
+    int64_t segs = 1;
+    if (split && w.strips < kMaxWorkgroups) {
+        segs = (kMaxWorkgroups + w.strips - 1) / w.strips;
+        if (segs > kMaxSegments) segs = kMaxSegments;
+        if (segs > nck) segs = nck;
+    }
+    w.cps = (int)((nck + segs - 1) / segs);
+    w.segs = (int)((nck + w.cps - 1) / w.cps);
+    return w;
 }
 
-hipError_t launch_bf16_skinny(const GemmArgs<uint16_t>& a, bool vec, hipStream_t s) {
+// True when every buffer offset the vector kernel forms fits in 31 bits: A
+// copies reach row 31 (rows past M included) and one chunk past K; B copies
+// reach 128 rows below a chunk's first row.
+static bool smallm_fits(const GemmArgs<uint16_t>& a) {
+    const int64_t lim = (int64_t)1 << 31;
+    return (32 * a.lda + a.K + kVKC) * 2 < lim && (kVKC * a.ldb + a.N) * 2 < lim;
+}
+
+size_t bf16_skinny_workspace(int64_t M, int64_t N, int64_t K) {
+    if (M < 1 || M > kSkinnyMaxM || N < 1 || K < 1) return 0;
+    const SmallMWork w = plan_smallm(N, K, true);
+    if (w.segs < 2) return 0;
+    const int64_t mb = M <= 16 ? 1 : 2;
+    return (size_t)((((int64_t)w.strips * 4 + 255) & ~(int64_t)255) +
+                    (int64_t)w.segs * w.strips * 16 * mb * kVBN * 4);
+}
+
+hipError_t launch_bf16_skinny(const GemmArgs<uint16_t>& a, bool vec, void* ws, size_t ws_bytes,
+                              hipStream_t s) {
+    GemmArgs<uint16_t> args = a;
+    if (vec && smallm_fits(a)) {
+        const size_t need = bf16_skinny_workspace(a.M, a.N, a.K);
+        const bool split = ws != nullptr && need > 0 && ws_bytes >= need;
+        SmallMWork w = plan_smallm(a.N, a.K, split);
+        unsigned char* wsp = split ? static_cast<unsigned char*>(ws) : nullptr;
+        void* kargs[] = {&args, &w, &wsp};
+        const void* fn = a.M <= 16 ? (const void*)&gemm_bf16_smallm_kernel<1>
+                                   : (const void*)&gemm_bf16_smallm_kernel<2>;
+        return hipLaunchKernel(fn, dim3((unsigned)(w.strips * w.segs)), dim3(kNT), kargs, 0, s);
+    }
     const int64_t strips = (a.N + kBN - 1) / kBN;
     int st = (int)strips;
-    GemmArgs<uint16_t> args = a;
     void* kargs[] = {&args, &st};
-    const void* fn;
-    if (vec && skinny_dma_fits(a))
-        fn = a.M <= 16 ? (const void*)&gemm_bf16_skinny_dma_kernel<1>
-                       : (const void*)&gemm_bf16_skinny_dma_kernel<2>;
-    else if (a.M <= 16)
-        fn = vec ? (const void*)&gemm_bf16_skinny_kernel<1, true>
-                 : (const void*)&gemm_bf16_skinny_kernel<1, false>;
-    else
-        fn = vec ? (const void*)&gemm_bf16_skinny_kernel<2, true>
-                 : (const void*)&gemm_bf16_skinny_kernel<2, false>;
+    const void* fn = a.M <= 16 ? (vec ? (const void*)&gemm_bf16_skinny_kernel<1, true>
+                                      : (const void*)&gemm_bf16_skinny_kernel<1, false>)
+                               : (vec ? (const void*)&gemm_bf16_skinny_kernel<2, true>
+                                      : (const void*)&gemm_bf16_skinny_kernel<2, false>);
     return hipLaunchKernel(fn, dim3((unsigned)strips), dim3(kNT), kargs, 0, s);
 }
 

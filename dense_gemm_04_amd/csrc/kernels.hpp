@@ -20,7 +20,13 @@ bool bf16_tiled_fits(const GemmArgs<uint16_t>& a);
 hipError_t launch_bf16_general(const GemmArgs<uint16_t>& a, bool vec, hipStream_t s);
 hipError_t launch_f32_mfma(const GemmArgs<float>& a, bool vec, hipStream_t s);
 hipError_t launch_f32_valu(const GemmArgs<float>& a, bool vec, hipStream_t s);
-hipError_t launch_bf16_skinny(const GemmArgs<uint16_t>& a, bool vec, hipStream_t s);
+// Small-M bf16 (M <= kSkinnyMaxM). With `vec` the 64-column copy-ring kernel
+// runs; given a workspace of at least bf16_skinny_workspace(M, N, K) bytes
+// (256-byte aligned, counters zero) it splits K over several workgroups.
+hipError_t launch_bf16_skinny(const GemmArgs<uint16_t>& a, bool vec, void* ws, size_t ws_bytes,
+                              hipStream_t s);
+// Workspace bytes with which launch_bf16_skinny splits K (0: no split for this shape).
+size_t bf16_skinny_workspace(int64_t M, int64_t N, int64_t K);
 
 // C <- beta * C (beta == 0 writes zeros without reading C).
 hipError_t launch_scale_f32(int64_t M, int64_t N, float beta, float* C, int64_t ldc,

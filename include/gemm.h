@@ -32,7 +32,8 @@
  * Ownership and memory: every pointer is a DEVICE pointer owned by the
  * caller, valid on the current HIP device for the duration of the work.
  * The library keeps no reference after the work completes and allocates no
- * device memory. C must not overlap A or B (undefined results otherwise).
+ * device memory; gemm_bf16_ws takes a caller-owned workspace instead. C must
+ * not overlap A, B or the workspace (undefined results otherwise).
  *
  * Streams and errors: `stream` is a hipStream_t passed as void* (NULL = the
  * null stream). Calls are asynchronous: they validate the arguments, enqueue
@@ -44,6 +45,7 @@
 #ifndef DENSE_GEMM_04_AMD_GEMM_H
 #define DENSE_GEMM_04_AMD_GEMM_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -102,6 +104,33 @@ gemm_status_t gemm_f32_ex(int64_t M, int64_t N, int64_t K, float alpha,
 gemm_status_t gemm_bf16_ex(int64_t M, int64_t N, int64_t K, float alpha,
                            const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                            float beta, uint16_t* C, int64_t ldc, void* stream, int variant);
+
+/* Split-K for small M (RTX 3090 SGEMM article, section 7.2: cutting K into
+ * pieces that run in parallel and summing their partial results brings more
+ * multiprocessors to work). With M <= 32 one workgroup per 64-column strip of
+ * C leaves most of the GPU idle when N is small; a workspace lets the bf16
+ * small-M kernel give each strip several workgroups, each over a range of K.
+ * Each stores its fp32 partial tile in the workspace, and the strip's last
+ * workgroup to finish adds the partials in a fixed order (so results do not
+ * depend on timing) and forms alpha * sum + beta * C.
+ *
+ * gemm_bf16_workspace_size: workspace bytes gemm_bf16_ws needs to split this
+ * shape; 0 when it would not split (M > 32, N already fills the GPU, or K is
+ * a single 128-row chunk) or the sizes are invalid. Host only, no HIP call. */
+size_t gemm_bf16_workspace_size(int64_t M, int64_t N, int64_t K);
+
+/* gemm_bf16 with a workspace: device memory owned by the caller, 256-byte
+ * aligned, at least gemm_bf16_workspace_size(M, N, K) bytes, and filled with
+ * zeros before its first use (every call leaves it ready for the next). With
+ * workspace == NULL (and workspace_bytes == 0) this is gemm_bf16. Calls that
+ * share a workspace must not overlap in time (same stream, or ordered by the
+ * caller). GEMM_ERR_INVALID_VALUE also when the workspace is misaligned, too
+ * small, or NULL with a non-zero size. Alignment and shape rules otherwise as
+ * for gemm_bf16; shapes that do not take the split leave the workspace unused. */
+gemm_status_t gemm_bf16_ws(int64_t M, int64_t N, int64_t K, float alpha,
+                           const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                           float beta, uint16_t* C, int64_t ldc,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* Host-only planning (no HIP call): the variant a call with these arguments
  * would run (a gemm_variant_t value; GEMM_VARIANT_AUTO when the call would

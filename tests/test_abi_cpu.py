@@ -133,3 +133,39 @@ def test_oracle_and_library_share_nothing():
         if f.endswith((".c", ".py")):
             text = open(os.path.join(ROOT, "oracle", f)).read()
             assert "dense_gemm_04_amd" not in text and "gemm.h" not in text, f
+
+
+def test_workspace_size(lib):
+    # 16 x 8192 x 8192: 128 strips of 64 columns, K cut into 2 segments of
+    # 4096 to give 256 workgroups: a 512-byte counter block, then 2 x 128 fp32
+    # tiles of 16 x 64.
+    assert dg.gemm_bf16_workspace_size(16, 8192, 8192) == 512 + 2 * 128 * 16 * 64 * 4
+    # 17..32 rows use 32-row tiles.
+    assert dg.gemm_bf16_workspace_size(32, 8192, 8192) == 512 + 2 * 128 * 32 * 64 * 4
+    # No split: M too large, strips already fill the GPU, one K chunk, empty
+    # or invalid sizes.
+    assert dg.gemm_bf16_workspace_size(33, 8192, 8192) == 0
+    assert dg.gemm_bf16_workspace_size(16, 16384, 8192) == 0
+    assert dg.gemm_bf16_workspace_size(16, 64, 128) == 0
+    assert dg.gemm_bf16_workspace_size(0, 64, 1024) == 0
+    assert dg.gemm_bf16_workspace_size(16, 0, 1024) == 0
+    assert dg.gemm_bf16_workspace_size(16, 64, 0) == 0
+    assert dg.gemm_bf16_workspace_size(-1, 64, 1024) == 0
+    # Segments are capped at 64 (N = 64, K = 2^20: 64 segments of 128 chunks).
+    assert dg.gemm_bf16_workspace_size(16, 64, 1 << 20) == 256 + 64 * 1 * 16 * 64 * 4
+    # Every segment is non-empty: K = 300 is 3 chunks, so 3 segments.
+    assert dg.gemm_bf16_workspace_size(16, 64, 300) == 256 + 3 * 16 * 64 * 4
+    # 17 strips want 16 segments; K = 4104 has 33 chunks: 11 segments of 3.
+    assert dg.gemm_bf16_workspace_size(16, 1032, 4104) == 256 + 11 * 17 * 16 * 64 * 4
+
+
+def test_workspace_validation(lib):
+    # Rejected before any HIP call, so these run without a GPU.
+    args = (16, 8192, 8192, 1.0, A, 8192, B, 8192, 0.0, C, 8192)
+    need = dg.gemm_bf16_workspace_size(16, 8192, 8192)
+    ws = 0x400000
+    assert dg.gemm_bf16_ws(*args, None, 64, 0) == dg.GEMM_ERR_INVALID_VALUE       # NULL, size > 0
+    assert dg.gemm_bf16_ws(*args, ws + 128, need, 0) == dg.GEMM_ERR_INVALID_VALUE  # misaligned
+    assert dg.gemm_bf16_ws(*args, ws, need - 1, 0) == dg.GEMM_ERR_INVALID_VALUE    # too small
+    bad = (16, 64, 64, 1.0, A, 63, B, 64, 0.0, C, 64)                                # lda < K
+    assert dg.gemm_bf16_ws(*bad, ws, 1 << 20, 0) == dg.GEMM_ERR_INVALID_VALUE

@@ -1,0 +1,98 @@
+"""GPU parity of gemm_bf16_ws (split-K over a caller workspace) against the
+CPU oracle, plus the workspace contract: repeated calls reuse it without
+clearing (the counters are left at zero), results do not depend on timing
+(partials are added in a fixed order), and shapes that do not split ignore it.
+"""
+import pytest
+import torch
+
+import dense_gemm_04_amd as dg
+import gemm_inputs as gi
+import oracle
+from gpu_util import note, oracle_ref, padded, to_f64, tol
+
+pytestmark = pytest.mark.gpu
+
+
+def workspace(M, N, K):
+    n = dg.gemm_bf16_workspace_size(M, N, K)
+    # torch's allocations are 256-byte aligned; zero-filled before first use.
+    return torch.zeros(max(n, 1), dtype=torch.uint8, device="cuda"), n
+
+
+def run_ws(A, B, C0, alpha, beta, ws, nbytes, ld_pad=(0, 0, 0)):
+    M, K = A.shape
+    N = B.shape[1]
+    lda, ldb, ldc = K + ld_pad[0], N + ld_pad[1], N + ld_pad[2]
+    _, a = padded(M, K, lda, "bf16", fill=float("nan"))
+    _, b = padded(K, N, ldb, "bf16", fill=float("nan"))
+    _, c = padded(M, N, ldc, "bf16", fill=float("nan"))
+    a.copy_(A.cuda())
+    b.copy_(B.cuda())
+    if C0 is not None:
+        c.copy_(C0.cuda())
+    st = dg.gemm_bf16_ws(M, N, K, alpha, a.data_ptr(), lda, b.data_ptr(), ldb, beta,
+                         c.data_ptr(), ldc, ws.data_ptr() if nbytes else None, nbytes, 0)
+    torch.cuda.synchronize()
+    return c.cpu(), st
+
+
+SHAPES = [(16, 264, 2000), (1, 1032, 4104), (17, 64, 1000), (32, 8, 520), (5, 4096, 1024),
+          (16, 128, 300), (31, 520, 8192), (3, 1024, 8200)]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_split_k_parity(shape):
+    M, N, K = shape
+    assert dg.gemm_bf16_workspace_size(M, N, K) > 0       # these shapes do split
+    ws, n = workspace(M, N, K)
+    for rep, (alpha, beta) in enumerate(((1.5, -0.5), (1.0, 0.0), (0.25, 1.0))):
+        seed = 900 + 10 * M + rep
+        A = gi.random_matrix(M, K, "bf16", seed, dist="n")
+        B = gi.random_matrix(K, N, "bf16", seed + 1)
+        C0 = gi.random_matrix(M, N, "bf16", seed + 2) if beta != 0 else None
+        note(f"gemm_bf16_ws M={M} N={N} K={K} alpha={alpha} beta={beta} ws={n}")
+        C, st = run_ws(A, B, C0, alpha, beta, ws, n)
+        assert st == dg.GEMM_OK, dg.gemm_status_string(st)
+        R, D = oracle_ref("bf16", A, B, C0, alpha, beta)
+        err = oracle.max_rel_err(to_f64(C), R, D)
+        assert err <= tol("bf16"), f"call {rep}: max error ratio {err:.3e}"
+    # Every counter is back at zero after the calls.
+    strips = (N + 63) // 64
+    assert int(ws[:4 * strips].view(torch.int32).abs().sum()) == 0
+
+
+def test_split_k_is_deterministic():
+    M, N, K = 16, 1032, 4104
+    ws, n = workspace(M, N, K)
+    A = gi.random_matrix(M, K, "bf16", 990, dist="n")
+    B = gi.random_matrix(K, N, "bf16", 991)
+    note(f"gemm_bf16_ws determinism M={M} N={N} K={K}")
+    first, st = run_ws(A, B, None, 1.0, 0.0, ws, n)
+    assert st == dg.GEMM_OK
+    for _ in range(3):
+        again, st = run_ws(A, B, None, 1.0, 0.0, ws, n)
+        assert st == dg.GEMM_OK
+        assert torch.equal(first.view(torch.int16), again.view(torch.int16))
+
+
+def test_padded_rows_and_no_split_shapes():
+    # Padded 16-byte rows keep the split; a shape that fills the GPU ignores the workspace.
+    M, N, K = 20, 264, 1000
+    ws, n = workspace(M, N, K)
+    A = gi.random_matrix(M, K, "bf16", 995, dist="n")
+    B = gi.random_matrix(K, N, "bf16", 996)
+    C0 = gi.random_matrix(M, N, "bf16", 997)
+    note(f"gemm_bf16_ws padded M={M} N={N} K={K}")
+    C, st = run_ws(A, B, C0, 1.0, 1.0, ws, n, ld_pad=(8, 16, 24))
+    assert st == dg.GEMM_OK
+    R, D = oracle_ref("bf16", A, B, C0, 1.0, 1.0)
+    assert oracle.max_rel_err(to_f64(C), R, D) <= tol("bf16")
+    # M > 32: the workspace is not needed (size 0) and a NULL workspace is accepted.
+    M2 = 40
+    A2 = gi.random_matrix(M2, K, "bf16", 998, dist="n")
+    note(f"gemm_bf16_ws no-split M={M2} N={N} K={K}")
+    C2, st = run_ws(A2, B, None, 1.0, 0.0, ws, 0)
+    assert st == dg.GEMM_OK
+    R2, D2 = oracle_ref("bf16", A2, B, None, 1.0, 0.0)
+    assert oracle.max_rel_err(to_f64(C2), R2, D2) <= tol("bf16")
