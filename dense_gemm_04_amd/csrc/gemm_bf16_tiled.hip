@@ -9,16 +9,17 @@
 // double buffering of the RTX 3090 SGEMM article, sections 3-5, and the
 // asynchronous load/compute pipelining of the Blackwell BF16 GEMM notes,
 // section 2.3, re-planned for CDNA4):
-//   * one workgroup of 4 waves per 256 x 256 tile of C, tiles renumbered per
-//     XCD and rastered in groups of 4 tile rows for L2 reuse;
-//   * K in slabs of 64. Slab t+1 is fetched with 128-bit buffer loads into
-//     registers while slab t is multiplied out of LDS; the registers are then
-//     written to the other half of a double-buffered LDS and one barrier
-//     closes the slab;
+//   * one workgroup of 8 waves (2 x 4, each a 128 x 64 block of C) per
+//     256 x 256 tile, tiles renumbered per XCD and rastered in groups of 4
+//     tile rows for L2 reuse;
+//   * K in slabs of 64 held in two LDS stages. Slabs move from global memory
+//     straight into LDS with LDS-destined 128-bit buffer loads (no register
+//     round trip), two slabs ahead of the MFMAs; one barrier per slab
+//     publishes slab t + 1 and retires every read of slab t;
 //   * A is stored [m][k] (128-byte rows) and B [k][n] exactly as it lies in
 //     memory (512-byte rows); each 16-byte chunk is placed at an XOR-swizzled
-//     position within its row so that the 128-bit A reads, the B stores and
-//     the transposing B reads of a wave spread over all LDS banks;
+//     position within its row so that the 128-bit A reads and the
+//     transposing B reads of a wave spread over all LDS banks;
 //   * MFMA fragments: A(m, k..k+7) is one ds_read_b128; B(k..k+7, n) is two
 //     ds_read_b64_tr_b16, which hand lane i of each 16-lane group column i of
 //     a 4 x 16 block of row-major B. The next k step's fragments are read
@@ -29,9 +30,9 @@
 //     (alpha * acc + beta * C0, then RNE to bf16) uses 8-byte loads/stores;
 //   * edges: the descriptors end where the matrices end, so rows of A past M
 //     and rows of B past K read as zero; columns of B past N only feed output
-//     columns that are never stored; k past K in the last slab is masked to
-//     zero in A (Z-Turbo CUDA tuning page, section 3.1: zero-filled tile
-//     edges; Blackwell notes, section 4.3: predicate the tail).
+//     columns that are never stored; k past K in the last slab is zeroed in
+//     the LDS copy of A (Z-Turbo CUDA tuning page, section 3.1: zero-filled
+//     tile edges; Blackwell notes, section 4.3: predicate the tail).
 //
 // Operand layout of v_mfma_f32_16x16x32_bf16: lane l = p + 16 g supplies
 // X(row p, k = 8g .. 8g+7) as its first operand and Y(k = 8g .. 8g+7, col p)
@@ -94,11 +95,16 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
     constexpr int kFM = kWTM / 16, kFN = kWTN / 16;
     constexpr int kAStage = BM * kBK;                         // bf16 elements
     constexpr int kBStage = kBK * BN;
-    constexpr int kACopies = kAStage * 2 / 1024 / kWaves;     // 1 KB LDS copies per wave
-    constexpr int kBCopies = kBStage * 2 / 1024 / kWaves;
+    // Only the first wave of each SIMD (waves 0 .. kWaves / 2 - 1 with two
+    // waves per SIMD) issues the slab copies: a burst of copies fills the
+    // texture unit's queue and stalls the issuing wave, and the other wave on
+    // the SIMD keeps the matrix core busy meanwhile.
+    constexpr int kDmaWaves = kWaves / 2;
+    constexpr int kACopies = kAStage * 2 / 1024 / kDmaWaves;  // 1 KB LDS copies per issuing wave
+    constexpr int kBCopies = kBStage * 2 / 1024 / kDmaWaves;
     constexpr int kBRowsPerCopy = 1024 / (BN * 2);            // B rows filled by one copy
-    static_assert(kACopies * kWaves * 1024 == kAStage * 2, "A slab must split evenly");
-    static_assert(kBCopies * kWaves * 1024 == kBStage * 2, "B slab must split evenly");
+    static_assert(kACopies * kDmaWaves * 1024 == kAStage * 2, "A slab must split evenly");
+    static_assert(kBCopies * kDmaWaves * 1024 == kBStage * 2, "B slab must split evenly");
     static_assert(BN == 256 || BN == 128, "B row length");
     static_assert(kWTM % 16 == 0 && kWTN % 16 == 0, "wave tile");
     // One array per operand and pipeline stage, so the compiler can tell which
@@ -136,6 +142,7 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
     const int a_lrow = lane >> 3, a_pos = lane & 7;
     const int b_lrow = lane / (64 / kBRowsPerCopy), b_pos = lane % (64 / kBRowsPerCopy);
     auto dma = [&](int64_t kt, int stage) {
+        if (wave >= kDmaWaves) return;
         const int64_t k0 = kt * kBK;
         const uint32_t As = lds_addr(a_stage(stage));
         const uint32_t Bs = lds_addr(b_stage(stage));
@@ -197,13 +204,18 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
         for (int j = 0; j < kFN; ++j)
             fb[buf][j] = read_b_frag<BN>(Bs, 32 * ks + 8 * g + tr_row, wn0 + 16 * j + tr_col);
     };
+    // The MFMA runs go at raised wave priority, so that a wave with matrix
+    // work to issue wins the SIMD's issue slot over one that is issuing
+    // copies or LDS reads.
     auto mfmas = [&](int buf) {
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int i = 0; i < kFM; ++i)
 #pragma unroll
             for (int j = 0; j < kFN; ++j)
                 acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[buf][j], fa[buf][i],
                                                                     acc[j][i], 0, 0, 0);
+        __builtin_amdgcn_s_setprio(0);
     };
 
     // Pipeline (two LDS stages): while slab t is multiplied, slab t + 1 is in
