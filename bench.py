@@ -4,7 +4,8 @@ Default run: the 4096^3 fp32 SGEMM (the pages' headline shape) is the timed
 step; the 4096^3 bf16 GEMM is timed the same way and reported beside it.
 Inputs are seeded synthetic matrices already resident in HBM. A step is one
 library call (one kernel launch) on torch's current stream, timed with HIP
-events over exactly --steps calls after --warmup untimed calls.
+events over exactly --steps calls after --warmup untimed calls (each leg first
+runs its call untimed for a quarter second so the GPU clock has settled).
 
 Also reported:
   roofline      the timed kernel against MI355X's published fp32 matrix peak;
@@ -41,8 +42,21 @@ def tflops(flops: float, seconds: float) -> float:
     return flops / seconds / 1e12
 
 
-def _time_calls(call, steps: int, warmup: int, stream):
+SETTLE_SECONDS = 0.25
+
+
+def _time_calls(call, steps: int, warmup: int, stream, settle: float = SETTLE_SECONDS):
+    """Seconds per call over `steps` calls, after the GPU has settled and
+    `warmup` untimed calls. Settling runs the call untimed for `settle`
+    seconds first: from idle the GPU takes tens of milliseconds to reach its
+    steady clock under load, and a 4096^3 bf16 GEMM measured right away runs
+    about 20% slow."""
     import torch
+    t_end = time.perf_counter() + settle
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            call()
+        torch.cuda.synchronize()
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -193,7 +207,7 @@ def main(argv=None) -> int:
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
         stream = torch.cuda.current_stream()
-        sec = _time_calls(lambda: dst.copy_(src), args.steps, args.warmup, stream)
+        sec = _time_calls(lambda: dst.copy_(src), args.steps, args.warmup, stream, settle=0.0)
         print(json.dumps({"copy_bytes": n, "ms": sec * 1e3, "gbs": 2 * n / sec / 1e9}), flush=True)
         return 0
 
