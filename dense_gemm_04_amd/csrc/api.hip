@@ -29,6 +29,15 @@ Work work_of(int64_t M, int64_t N, int64_t K, float alpha, float beta) {
     return Work::kGemm;
 }
 
+// A rows x cols matrix with leading dimension ld spans (rows - 1) * ld + cols
+// elements; every offset the kernels form stays exact while that span, in
+// bytes, is below 2^60.
+bool span_ok(int esz, int64_t rows, int64_t cols, int64_t ld) {
+    if (rows <= 1) return true;
+    const int64_t lim = ((int64_t)1 << 60) / esz;
+    return cols <= lim && ld <= (lim - cols) / (rows - 1);
+}
+
 // Returns true when the arguments are valid (header: GEMM_ERR_INVALID_VALUE).
 bool valid_args(int esz, int64_t M, int64_t N, int64_t K, float alpha, const void* A,
                 int64_t lda, const void* B, int64_t ldb, float beta, const void* C,
@@ -39,6 +48,8 @@ bool valid_args(int esz, int64_t M, int64_t N, int64_t K, float alpha, const voi
     const Work w = work_of(M, N, K, alpha, beta);
     if (w != Work::kNone && C == nullptr) return false;
     if (w == Work::kGemm && (A == nullptr || B == nullptr)) return false;
+    if (!span_ok(esz, M, N, ldc)) return false;
+    if (w == Work::kGemm && (!span_ok(esz, M, K, lda) || !span_ok(esz, K, N, ldb))) return false;
     if (!aligned(A, esz) || !aligned(B, esz) || !aligned(C, esz)) return false;
     return true;
 }

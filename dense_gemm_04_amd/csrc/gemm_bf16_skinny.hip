@@ -457,6 +457,7 @@ hipError_t launch_bf16_skinny(const GemmArgs<uint16_t>& a, bool vec, void* ws, s
         void* kargs[] = {&args, &w, &wsp};
         const void* fn = a.M <= 16 ? (const void*)&gemm_bf16_smallm_kernel<1>
                                    : (const void*)&gemm_bf16_smallm_kernel<2>;
+        if ((int64_t)w.strips * w.segs > kMaxGrid) return hipErrorInvalidConfiguration;
         return hipLaunchKernel(fn, dim3((unsigned)(w.strips * w.segs)), dim3(kNT), kargs, 0, s);
     }
     const int64_t strips = (a.N + kBN - 1) / kBN;
@@ -466,6 +467,7 @@ hipError_t launch_bf16_skinny(const GemmArgs<uint16_t>& a, bool vec, void* ws, s
                                       : (const void*)&gemm_bf16_skinny_kernel<1, false>)
                                : (vec ? (const void*)&gemm_bf16_skinny_kernel<2, true>
                                       : (const void*)&gemm_bf16_skinny_kernel<2, false>);
+    if (strips > kMaxGrid) return hipErrorInvalidConfiguration;
     return hipLaunchKernel(fn, dim3((unsigned)strips), dim3(kNT), kargs, 0, s);
 }
 

@@ -304,6 +304,7 @@ hipError_t launch_cfg(const GemmArgs<uint16_t>& a, hipStream_t s) {
     int tm = (int)tiles_m, tn = (int)tiles_n;
     GemmArgs<uint16_t> args = a;
     void* kargs[] = {&args, &tm, &tn};
+    if (tiles_m * tiles_n > kMaxGrid) return hipErrorInvalidConfiguration;
     return hipLaunchKernel((const void*)&gemm_bf16_tiled_kernel<BM, BN, WAVES_M, WAVES_N>,
                            dim3((unsigned)(tiles_m * tiles_n)), dim3(WAVES_M * WAVES_N * 64), kargs,
                            0, s);

@@ -203,6 +203,7 @@ hipError_t launch_tiles(const GemmArgs<float>& a, bool vec, hipStream_t s) {
     void* kargs[] = {&args, &tm, &tn};
     const void* fn = vec ? (const void*)&gemm_f32_mfma_kernel<BM, BN, WAVES_M, WAVES_N, true>
                          : (const void*)&gemm_f32_mfma_kernel<BM, BN, WAVES_M, WAVES_N, false>;
+    if (tiles_m * tiles_n > kMaxGrid) return hipErrorInvalidConfiguration;
     return hipLaunchKernel(fn, dim3((unsigned)(tiles_m * tiles_n)), dim3(WAVES_M * WAVES_N * 64),
                            kargs, 0, s);
 }

@@ -149,6 +149,7 @@ hipError_t launch_f32_valu(const GemmArgs<float>& a, bool vec, hipStream_t s) {
     void* kargs[] = {&args, &tm, &tn};
     const void* fn = vec ? (const void*)&gemm_f32_valu_kernel<true>
                          : (const void*)&gemm_f32_valu_kernel<false>;
+    if (tiles_m * tiles_n > kMaxGrid) return hipErrorInvalidConfiguration;
     return hipLaunchKernel(fn, dim3((unsigned)(tiles_m * tiles_n)), dim3(kNT), kargs, 0, s);
 }
 

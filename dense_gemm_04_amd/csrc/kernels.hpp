@@ -37,4 +37,8 @@ hipError_t launch_scale_bf16(int64_t M, int64_t N, float beta, uint16_t* C, int6
 // Largest M the small-M kernel accepts.
 constexpr int64_t kSkinnyMaxM = 32;
 
+// Workgroup ids are ints: launchers refuse grids beyond this (a matrix that
+// large cannot exist in device memory, so this only guards the arithmetic).
+constexpr int64_t kMaxGrid = 0x7fffffff;
+
 }  // namespace dg

@@ -54,14 +54,16 @@ extern "C" {
 
 typedef enum {
     GEMM_OK = 0,
-    /* A size is negative, a leading dimension is smaller than max(1, row
-     * length), a pointer that must be read or written is NULL, a pointer is
-     * not aligned to its element size, or `variant` is unknown or does not
-     * apply to the call. */
+    /* A size is negative or above INT_MAX, a leading dimension is smaller
+     * than max(1, row length), a matrix would span 2^60 bytes or more
+     * ((rows - 1) * ld + cols elements), a pointer that must be read or
+     * written is NULL, a pointer is not aligned to its element size, or
+     * `variant` is unknown or does not apply to the call. */
     GEMM_ERR_INVALID_VALUE = 1,
     /* No HIP device is current, or it is not a gfx950 (MI355X-class) device. */
     GEMM_ERR_UNSUPPORTED_DEVICE = 2,
-    /* The kernel launch was rejected by the HIP runtime. */
+    /* The kernel launch was rejected by the HIP runtime (or the grid would
+     * exceed 2^31 - 1 workgroups, which no matrix in device memory needs). */
     GEMM_ERR_LAUNCH = 3
 } gemm_status_t;
 

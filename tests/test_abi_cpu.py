@@ -72,6 +72,11 @@ def test_plan_rejects_invalid_arguments(lib):
     assert plan(esz=3) == -1
     assert plan(variant=9) == -1
     assert plan(M=1 << 31) == -1
+    # Extents of 2^60 bytes or more: leading dimensions that would overflow offsets.
+    assert plan(M=1 << 20, lda=1 << 40) == -1                   # A spans ~2^62 bytes
+    assert plan(K=1 << 20, lda=1 << 20, ldb=1 << 40) == -1      # B
+    assert plan(M=1 << 20, ldc=1 << 40) == -1                   # C
+    assert plan(M=1 << 20, lda=1 << 30) == dg.VARIANT_MFMA       # 2^52 bytes: fine
 
 
 def test_plan_quick_paths(lib):

@@ -1,4 +1,4 @@
-"""The five workloads at full size, in the launch configuration the benchmark
+"""The six workloads at full size, in the launch configuration the benchmark
 times (default kernel choice, packed leading dimensions), checked against the
 oracle on sampled entries that cover every 128-row and 128-column tile band
 (first, last and one random row/column of each), plus every entry finite."""
@@ -48,3 +48,32 @@ def test_workload_full_size(wid):
     err = oracle.max_rel_err(got, R, D)
     note(f"workload {w.name}: {len(rows)}x{len(cols)} sampled entries, max error ratio {err:.3e}")
     assert err <= tol(w.dtype)
+
+
+def test_workload_small_m_split_k():
+    # The small-M workload through gemm_bf16_ws, as the benchmark times it:
+    # 128 strips x 2 K segments; two calls in a row on one workspace (the
+    # second relies on the counters the first left at zero).
+    w = gi.WORKLOADS[52]
+    note(f"workload {w.name} via gemm_bf16_ws")
+    inp = gi.make(w)
+    A, B = inp["A"].cuda(), inp["B"].cuda()
+    nbytes = dg.gemm_bf16_workspace_size(w.M, w.N, w.K)
+    assert nbytes > 0
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    rows = list(range(w.M))
+    cols = sample(w.N, 64, 520)
+    R, D = oracle.gemm(gi.as_numpy(inp["A"]), gi.as_numpy(inp["B"]), None, w.alpha, w.beta,
+                       w.dtype, rows=rows, cols=cols)
+    for call in range(2):
+        C = torch.full((w.M, w.N), float("nan"), dtype=torch.bfloat16, device="cuda")
+        st = dg.gemm_bf16_ws(w.M, w.N, w.K, w.alpha, A.data_ptr(), w.K, B.data_ptr(), w.N,
+                             w.beta, C.data_ptr(), w.N, ws.data_ptr(), nbytes,
+                             int(torch.cuda.current_stream().cuda_stream))
+        torch.cuda.synchronize()
+        assert st == dg.GEMM_OK, dg.gemm_status_string(st)
+        assert bool(torch.isfinite(C.float()).all())
+        got = C[:, cols].cpu().to(torch.float64).numpy()
+        err = oracle.max_rel_err(got, R, D)
+        note(f"call {call}: max error ratio {err:.3e}")
+        assert err <= tol(w.dtype)
