@@ -90,12 +90,14 @@ def _device_call(w, sets: int = 1, use_ws: bool = False):
     fn = dg.gemm_f32 if w.dtype == "f32" else dg.gemm_bf16
     state = {"i": 0}
     if use_ws:
-        nbytes = dg.gemm_bf16_workspace_size(w.M, w.N, w.K)
+        size_fn, ws_fn = ((dg.gemm_f32_workspace_size, dg.gemm_f32_ws) if w.dtype == "f32"
+                          else (dg.gemm_bf16_workspace_size, dg.gemm_bf16_ws))
+        nbytes = size_fn(w.M, w.N, w.K)
         ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device="cuda")
 
         def fn(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream):
-            return dg.gemm_bf16_ws(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
-                                   ws.data_ptr() if nbytes else None, nbytes, stream)
+            return ws_fn(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                         ws.data_ptr() if nbytes else None, nbytes, stream)
 
     def call():
         A, B, C = bufs[state["i"] % sets]
@@ -110,7 +112,8 @@ def _device_call(w, sets: int = 1, use_ws: bool = False):
 def measure(w, steps: int, warmup: int, sets: int = 1, use_ws: bool = False) -> dict:
     call, stream, _ = _device_call(w, sets, use_ws)
     sec = _time_calls(call, steps, warmup, stream)
-    out = {"workload": w.name + (" (gemm_bf16_ws, split-K)" if use_ws else ""),
+    ws_name = "gemm_f32_ws" if w.dtype == "f32" else "gemm_bf16_ws"
+    out = {"workload": w.name + (f" ({ws_name}, split-K)" if use_ws else ""),
            "dtype": w.dtype, "M": w.M, "N": w.N, "K": w.K,
            "alpha": w.alpha, "beta": w.beta, "ms": sec * 1e3,
            "tflops": tflops(gemm_flops(w.M, w.N, w.K), sec),
@@ -215,8 +218,9 @@ def main(argv=None) -> int:
         w = gi.WORKLOADS[args.only]
         r = measure(w, args.steps, args.warmup, 4 if args.only == 52 else 1)
         print(json.dumps(r), flush=True)
-        if args.only == 52:
-            print(json.dumps(measure(w, args.steps, args.warmup, 4, use_ws=True)), flush=True)
+        if args.only in (51, 52):
+            print(json.dumps(measure(w, args.steps, args.warmup, 4 if args.only == 52 else 1,
+                                     use_ws=True)), flush=True)
         return 0
 
     if args.all:
@@ -227,7 +231,7 @@ def main(argv=None) -> int:
             sets = 4 if wid == 52 else 1
             r = measure(w, args.steps, args.warmup, sets)
             print(json.dumps(r), flush=True)
-            if wid == 52:
+            if wid in (51, 52):
                 print(json.dumps(measure(w, args.steps, args.warmup, sets, use_ws=True)),
                       flush=True)
         return 0

@@ -30,7 +30,8 @@ VARIANT_SKINNY = 4
 VARIANT_NAMES = {0: "auto", 1: "mfma", 2: "general", 3: "valu", 4: "skinny"}
 
 EXPORTS = ("gemm_f32", "gemm_bf16", "gemm_f32_ex", "gemm_bf16_ex", "gemm_bf16_ws",
-           "gemm_bf16_workspace_size", "gemm_plan", "gemm_status_string")
+           "gemm_bf16_workspace_size", "gemm_f32_ws", "gemm_f32_workspace_size", "gemm_plan",
+           "gemm_status_string")
 
 _lib = None
 
@@ -58,10 +59,12 @@ def load() -> ctypes.CDLL:
     for name in ("gemm_f32_ex", "gemm_bf16_ex"):
         fn = getattr(lib, name)
         fn.restype, fn.argtypes = ci, base + [ci]
-    lib.gemm_bf16_ws.restype = ci
-    lib.gemm_bf16_ws.argtypes = base[:11] + [vp, ctypes.c_size_t, vp]
-    lib.gemm_bf16_workspace_size.restype = ctypes.c_size_t
-    lib.gemm_bf16_workspace_size.argtypes = [i64, i64, i64]
+    for name in ("gemm_bf16_ws", "gemm_f32_ws"):
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = ci, base[:11] + [vp, ctypes.c_size_t, vp]
+    for name in ("gemm_bf16_workspace_size", "gemm_f32_workspace_size"):
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = ctypes.c_size_t, [i64, i64, i64]
     lib.gemm_plan.restype = ci
     lib.gemm_plan.argtypes = [ci, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64, ci]
     lib.gemm_status_string.restype = ctypes.c_char_p
@@ -94,6 +97,16 @@ def gemm_bf16_ws(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace, worksp
 
 def gemm_bf16_workspace_size(M, N, K) -> int:
     return load().gemm_bf16_workspace_size(M, N, K)
+
+
+def gemm_f32_ws(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace, workspace_bytes,
+                stream=0) -> int:
+    return load().gemm_f32_ws(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace,
+                              workspace_bytes, stream)
+
+
+def gemm_f32_workspace_size(M, N, K) -> int:
+    return load().gemm_f32_workspace_size(M, N, K)
 
 
 def gemm_plan(elem_bytes, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, variant=0) -> int:

@@ -92,11 +92,16 @@ int plan_impl(int esz, int64_t M, int64_t N, int64_t K, float alpha, const void*
     return choose(esz, M, vector_ok(esz, A, lda, B, ldb, C, ldc), variant);
 }
 
-// Per-device cache of "is this a gfx950": 0 unknown, 1 yes, 2 no.
+// Per-device cache of "is this a gfx950" (0 unknown, 1 yes, 2 no) and of its
+// compute-unit count.
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch[kMaxDevices];
+std::atomic<int> g_cus[kMaxDevices];
 
-gemm_status_t check_device() {
+// Compute units of a full MI355X: the workspace sizes are computed for it.
+constexpr int kFullCus = 256;
+
+gemm_status_t check_device(int* cus) {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GEMM_ERR_UNSUPPORTED_DEVICE;
     if (dev >= kMaxDevices) return GEMM_ERR_UNSUPPORTED_DEVICE;
@@ -104,10 +109,19 @@ gemm_status_t check_device() {
     if (state == 0) {
         hipDeviceProp_t prop;
         if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GEMM_ERR_UNSUPPORTED_DEVICE;
+        g_cus[dev].store(prop.multiProcessorCount > 0 ? prop.multiProcessorCount : kFullCus,
+                         std::memory_order_relaxed);
         state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
         g_arch[dev].store(state, std::memory_order_release);
     }
+    *cus = g_cus[dev].load(std::memory_order_relaxed);
     return state == 1 ? GEMM_OK : GEMM_ERR_UNSUPPORTED_DEVICE;
+}
+
+// Shared argument check of the workspace entry points.
+bool workspace_ok(const void* ws, size_t bytes, size_t need) {
+    if (ws == nullptr) return bytes == 0;
+    return aligned(ws, 256) && bytes >= need;
 }
 
 template <typename T>
@@ -119,7 +133,8 @@ gemm_status_t run(int64_t M, int64_t N, int64_t K, float alpha, const T* A, int6
     if (v < 0) return GEMM_ERR_INVALID_VALUE;
     const Work w = work_of(M, N, K, alpha, beta);
     if (w == Work::kNone) return GEMM_OK;
-    const gemm_status_t dev = check_device();
+    int cus = kFullCus;
+    const gemm_status_t dev = check_device(&cus);
     if (dev != GEMM_OK) return dev;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     hipError_t e;
@@ -131,7 +146,8 @@ gemm_status_t run(int64_t M, int64_t N, int64_t K, float alpha, const T* A, int6
         const bool vec = vector_ok(esz, A, lda, B, ldb, C, ldc);
         if constexpr (esz == 4) {
             e = (v == GEMM_VARIANT_VALU) ? dg::launch_f32_valu(a, vec, s)
-                                         : dg::launch_f32_mfma(a, v == GEMM_VARIANT_MFMA, s);
+                                         : dg::launch_f32_mfma(a, v == GEMM_VARIANT_MFMA, ws, ws_bytes,
+                                                               cus, s);
         } else {
             e = (v == GEMM_VARIANT_SKINNY) ? dg::launch_bf16_skinny(a, vec, ws, ws_bytes, s)
                                            : dg::launch_bf16_mfma(a, v == GEMM_VARIANT_MFMA, s);
@@ -164,12 +180,24 @@ size_t gemm_bf16_workspace_size(int64_t M, int64_t N, int64_t K) {
 gemm_status_t gemm_bf16_ws(int64_t M, int64_t N, int64_t K, float alpha, const uint16_t* A,
                            int64_t lda, const uint16_t* B, int64_t ldb, float beta, uint16_t* C,
                            int64_t ldc, void* workspace, size_t workspace_bytes, void* stream) {
-    if (workspace == nullptr ? workspace_bytes != 0 : !aligned(workspace, 256))
-        return GEMM_ERR_INVALID_VALUE;
-    if (workspace != nullptr && workspace_bytes < gemm_bf16_workspace_size(M, N, K))
+    if (!workspace_ok(workspace, workspace_bytes, gemm_bf16_workspace_size(M, N, K)))
         return GEMM_ERR_INVALID_VALUE;
     return run<uint16_t>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, GEMM_VARIANT_AUTO,
                          workspace, workspace_bytes);
+}
+
+size_t gemm_f32_workspace_size(int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N < 0 || K < 0 || M > INT_MAX || N > INT_MAX || K > INT_MAX) return 0;
+    return dg::f32_mfma_workspace(M, N, K, kFullCus);
+}
+
+gemm_status_t gemm_f32_ws(int64_t M, int64_t N, int64_t K, float alpha, const float* A,
+                          int64_t lda, const float* B, int64_t ldb, float beta, float* C,
+                          int64_t ldc, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!workspace_ok(workspace, workspace_bytes, gemm_f32_workspace_size(M, N, K)))
+        return GEMM_ERR_INVALID_VALUE;
+    return run<float>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, GEMM_VARIANT_AUTO,
+                      workspace, workspace_bytes);
 }
 
 gemm_status_t gemm_f32(int64_t M, int64_t N, int64_t K, float alpha, const float* A,

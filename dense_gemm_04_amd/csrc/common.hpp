@@ -108,13 +108,16 @@ __device__ __forceinline__ void lds_only_barrier() {
 // its own L2. The linear id is first renumbered so that every XCD owns one
 // contiguous run of ids; the run is then walked in groups of `group_m` tile
 // rows, so the tiles that share an XCD also share A rows and B columns.
-__device__ __forceinline__ void tile_coords(int wg, int nwg, int tiles_m, int tiles_n,
-                                            int group_m, int& tm, int& tn) {
+__device__ __forceinline__ int xcd_slot(int wg, int nwg) {
     constexpr int kXcds = 8;
     int per = nwg / kXcds, rem = nwg % kXcds;
     int xcd = wg % kXcds, idx = wg / kXcds;
-    int id = (xcd < rem) ? xcd * (per + 1) + idx
-                         : rem * (per + 1) + (xcd - rem) * per + idx;
+    return (xcd < rem) ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+}
+
+// Tile (tm, tn) of linear id `id` walked in groups of `group_m` tile rows.
+__device__ __forceinline__ void raster_tile(int id, int tiles_m, int tiles_n, int group_m,
+                                            int& tm, int& tn) {
     int group = group_m * tiles_n;
     int gid = id / group;
     int first_m = gid * group_m;
@@ -125,6 +128,11 @@ __device__ __forceinline__ void tile_coords(int wg, int nwg, int tiles_m, int ti
     // descriptors included, stays scalar.
     tm = __builtin_amdgcn_readfirstlane(first_m + in_group % gsz);
     tn = __builtin_amdgcn_readfirstlane(in_group / gsz);
+}
+
+__device__ __forceinline__ void tile_coords(int wg, int nwg, int tiles_m, int tiles_n,
+                                            int group_m, int& tm, int& tn) {
+    raster_tile(xcd_slot(wg, nwg), tiles_m, tiles_n, group_m, tm, tn);
 }
 
 }  // namespace dg

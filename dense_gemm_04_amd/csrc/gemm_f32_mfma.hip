@@ -18,6 +18,9 @@
 //   * after the loop each lane holds 4 consecutive columns of a row, so the
 //     fused alpha/beta epilogue uses 128-bit loads and stores.
 //
+// Rows that are not 16-byte aligned (VEC = false) use the same 128-bit
+// accesses at 4-byte alignment, and element-wise ones only at the edges.
+//
 // Operand layout of v_mfma_f32_16x16x4_f32: lane l = p + 16 g supplies A(row p,
 // k_g) and B(k_g, col p) for one k per lane group g, and receives D(row 4g + i,
 // col p) in accumulator register i. A and B use the same k for each g.
@@ -36,6 +39,17 @@ __device__ __forceinline__ int a_off(int row, int c) {
     return row * kBK + ((c ^ ((row ^ (row >> 3)) & 7)) << 2);
 }
 
+// Split of the last, partly filled round of tiles (the simplest form of
+// stream-K): workgroups 0 .. full - 1 each own a whole tile (tiles 0 .. full - 1
+// of the raster order); each of the `tail` remaining tiles is cut into `parts`
+// ranges of `cps` K slabs, one workgroup per range.
+struct TailSplit {
+    int full;
+    int tail;     // 0: no split
+    int parts;
+    int cps;
+};
+
 __device__ __forceinline__ f32x4 load4_elems(const float* p, int valid) {
     f32x4 v;
 #pragma unroll
@@ -43,16 +57,27 @@ __device__ __forceinline__ f32x4 load4_elems(const float* p, int valid) {
     return v;
 }
 
+// Four floats at an address that is only 4-byte aligned. gfx950 under the
+// HSA runtime runs with unaligned global access enabled, and the compiler
+// emits one 128-bit load or store for this type.
+typedef float f32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+
 template <bool VEC>
 __device__ __forceinline__ f32x4 load4(const float* p, int valid) {
-    if (VEC && valid >= 4) return *reinterpret_cast<const f32x4*>(p);
+    if (valid >= 4)
+        return VEC ? *reinterpret_cast<const f32x4*>(p)
+                   : (f32x4)*reinterpret_cast<const f32x4_a4*>(p);
     if (valid <= 0) return f32x4{0.f, 0.f, 0.f, 0.f};
     return load4_elems(p, valid);
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool VEC>
+// ws (only with SPLIT and ts.tail > 0): [counters: one int per split tile,
+// padded to 256 bytes][slots: tail x parts partial tiles of BM x BN fp32,
+// element e of thread t at e * NT + t].
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool VEC, bool SPLIT>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64)
-void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n) {
+void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit ts,
+                          unsigned char* ws) {
     constexpr int NT = WAVES_M * WAVES_N * 64;
     constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
     constexpr int FM = WTM / 16;          // 16-row blocks per wave
@@ -66,10 +91,24 @@ void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n) {
 
     __shared__ __attribute__((aligned(16))) float smem[2 * STAGE];
 
-    int tm, tn;
-    tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, kGroupM, tm, tn);
-    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
     const int64_t M = p.M, N = p.N, K = p.K;
+    const int64_t nk = (K + kBK - 1) / kBK;
+    int tm, tn, ti = 0, part = 0;
+    int64_t kb = 0, ke = nk;                        // k slabs of this workgroup
+    bool split_tile = false;
+    if (!SPLIT || (int)blockIdx.x < ts.full) {
+        tile_coords(blockIdx.x, SPLIT ? ts.full : gridDim.x, tiles_m, tiles_n, kGroupM, tm, tn);
+    } else {
+        // Split tail: consecutive workgroups take the K ranges of one tile.
+        const int u = (int)blockIdx.x - ts.full;
+        ti = __builtin_amdgcn_readfirstlane(u / ts.parts);
+        part = __builtin_amdgcn_readfirstlane(u - ti * ts.parts);
+        raster_tile(ts.full + ti, tiles_m, tiles_n, kGroupM, tm, tn);
+        kb = (int64_t)part * ts.cps;
+        ke = kb + ts.cps < nk ? kb + ts.cps : nk;
+        split_tile = true;
+    }
+    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
 
     f32x4 ra[A_CHUNKS], rb[B_CHUNKS];
@@ -147,16 +186,68 @@ void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n) {
         }
     };
 
-    const int64_t nk = (K + kBK - 1) / kBK;
-    gload(0);
+    gload(kb * kBK);
     sstore(0);
     __syncthreads();
-    for (int64_t kt = 0; kt < nk; ++kt) {
-        const int cur = (int)(kt & 1);
-        if (kt + 1 < nk) gload((kt + 1) * kBK);
+    for (int64_t kt = kb; kt < ke; ++kt) {
+        const int cur = (int)((kt - kb) & 1);
+        if (kt + 1 < ke) gload((kt + 1) * kBK);
         compute(cur);
-        if (kt + 1 < nk) sstore(cur ^ 1);
+        if (kt + 1 < ke) sstore(cur ^ 1);
         __syncthreads();
+    }
+
+    if (SPLIT && split_tile) {
+        // Store this K range's partial tile with device-coherent stores (sc1:
+        // written through the per-XCD L2, as agent-scope atomics are), count
+        // in once they have completed, and let the tile's last arrival read
+        // the ranges back the same way and add them in range order before the
+        // epilogue. No cache write-back or invalidate is needed.
+        constexpr int E4 = FM * NG * 4;                   // f32x4 values per thread
+        constexpr int kSc1 = 16;                          // cache-policy bit sc1
+        int* counters = reinterpret_cast<int*>(ws);
+        const unsigned char* slots = ws + (((int64_t)ts.tail * 4 + 255) & ~(int64_t)255);
+        const rsrc_t sd = make_rsrc(slots + (int64_t)ti * ts.parts * (BM * BN * 4),
+                                    (uint32_t)(ts.parts * BM * BN * 4));
+        // Value c of thread t of range q sits at byte ((q * E4 + c) * NT + t) * 16.
+        auto voff = [&](int q, int c) { return (uint32_t)(((q * E4 + c) * NT + t) * 16); };
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int gq = 0; gq < NG; ++gq)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][gq][j]), sd,
+                                                           voff(part, (i * NG + gq) * 4 + j), 0, kSc1);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        __syncthreads();
+        __shared__ int last_flag;
+        if (t == 0)
+            last_flag = __hip_atomic_fetch_add(counters + ti, 1, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT) == ts.parts - 1;
+        __syncthreads();
+        if (!last_flag) return;
+        // The last arrival reads every range back, its own included (its
+        // stores have completed), so no accumulator stays live meanwhile.
+        f32x4 sum[E4];
+#pragma unroll
+        for (int c = 0; c < E4; ++c) sum[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int q = 0; q < ts.parts; ++q) {
+            f32x4 v[E4];
+#pragma unroll
+            for (int c = 0; c < E4; ++c)
+                v[c] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(sd, voff(q, c), 0, kSc1));
+#pragma unroll
+            for (int c = 0; c < E4; ++c) sum[c] += v[c];
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int gq = 0; gq < NG; ++gq)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][gq][j] = sum[(i * NG + gq) * 4 + j];
+        // Leave the counter at zero for the next call that uses this workspace.
+        if (t == 0) __hip_atomic_store(counters + ti, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
     const float alpha = p.alpha, beta = p.beta;
@@ -173,13 +264,15 @@ void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n) {
                 f32x4 v;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) v[j] = alpha * acc[i][gq][j][r];
-                if (VEC && col + 4 <= N) {
+                if (col + 4 <= N) {
                     if (beta != 0.f) {
-                        const f32x4 c0 = *reinterpret_cast<const f32x4*>(dst);
+                        const f32x4 c0 = VEC ? *reinterpret_cast<const f32x4*>(dst)
+                                             : (f32x4)*reinterpret_cast<const f32x4_a4*>(dst);
 #pragma unroll
                         for (int j = 0; j < 4; ++j) v[j] += beta * c0[j];
                     }
-                    *reinterpret_cast<f32x4*>(dst) = v;
+                    if (VEC) *reinterpret_cast<f32x4*>(dst) = v;
+                    else *reinterpret_cast<f32x4_a4*>(dst) = (f32x4_a4)v;
                 } else {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
@@ -195,23 +288,68 @@ void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n) {
     }
 }
 
+constexpr int kSlotsPerCu = 2;   // resident workgroups per compute unit (64 KB LDS each)
+constexpr int kMaxParts = 8;
+
+// Tail split for a grid of `tiles` tiles over `cus` compute units: when the
+// last round of resident workgroups would be at most half full, its tiles are
+// cut into K ranges so that the round fills up.
+TailSplit plan_tail(int64_t tiles, int64_t nk, int cus) {
+    TailSplit t{(int)tiles, 0, 1, (int)nk};
+    const int64_t slots = (int64_t)cus * kSlotsPerCu;
+    const int64_t tail = tiles % slots;
+    if (tail == 0 || 2 * tail > slots || nk < 2) return t;
+    int64_t parts = slots / tail;
+    if (parts > kMaxParts) parts = kMaxParts;
+    if (parts > nk) parts = nk;
+    const int64_t cps = (nk + parts - 1) / parts;
+    parts = (nk + cps - 1) / cps;                     // every range non-empty
+    if (parts < 2) return t;
+    t.full = (int)(tiles - tail);
+    t.tail = (int)tail;
+    t.parts = (int)parts;
+    t.cps = (int)cps;
+    return t;
+}
+
+size_t tail_workspace(const TailSplit& t, int bm, int bn) {
+    if (t.tail == 0) return 0;
+    return (size_t)((((int64_t)t.tail * 4 + 255) & ~(int64_t)255) +
+                    (int64_t)t.tail * t.parts * bm * bn * 4);
+}
+
 template <int BM, int BN, int WAVES_M, int WAVES_N>
-hipError_t launch_tiles(const GemmArgs<float>& a, bool vec, hipStream_t s) {
+hipError_t launch_tiles(const GemmArgs<float>& a, bool vec, void* ws, size_t ws_bytes, int cus,
+                        hipStream_t s) {
     const int64_t tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
     int tm = (int)tiles_m, tn = (int)tiles_n;
     GemmArgs<float> args = a;
-    void* kargs[] = {&args, &tm, &tn};
-    const void* fn = vec ? (const void*)&gemm_f32_mfma_kernel<BM, BN, WAVES_M, WAVES_N, true>
-                         : (const void*)&gemm_f32_mfma_kernel<BM, BN, WAVES_M, WAVES_N, false>;
-    if (tiles_m * tiles_n > kMaxGrid) return hipErrorInvalidConfiguration;
-    return hipLaunchKernel(fn, dim3((unsigned)(tiles_m * tiles_n)), dim3(WAVES_M * WAVES_N * 64),
-                           kargs, 0, s);
+    TailSplit ts = plan_tail(tiles_m * tiles_n, (a.K + kBK - 1) / kBK, cus);
+    const bool split = ws != nullptr && ts.tail > 0 && ws_bytes >= tail_workspace(ts, BM, BN);
+    if (!split) ts = TailSplit{(int)(tiles_m * tiles_n), 0, 1, 0};
+    unsigned char* wsp = split ? static_cast<unsigned char*>(ws) : nullptr;
+    void* kargs[] = {&args, &tm, &tn, &ts, &wsp};
+    const void* fn = split
+        ? (vec ? (const void*)&gemm_f32_mfma_kernel<BM, BN, WAVES_M, WAVES_N, true, true>
+               : (const void*)&gemm_f32_mfma_kernel<BM, BN, WAVES_M, WAVES_N, false, true>)
+        : (vec ? (const void*)&gemm_f32_mfma_kernel<BM, BN, WAVES_M, WAVES_N, true, false>
+               : (const void*)&gemm_f32_mfma_kernel<BM, BN, WAVES_M, WAVES_N, false, false>);
+    const int64_t grid = split ? (int64_t)ts.full + (int64_t)ts.tail * ts.parts : tiles_m * tiles_n;
+    if (grid > kMaxGrid) return hipErrorInvalidConfiguration;
+    return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(WAVES_M * WAVES_N * 64), kargs, 0, s);
 }
 
 }  // namespace
 
-hipError_t launch_f32_mfma(const GemmArgs<float>& a, bool vec, hipStream_t s) {
-    return launch_tiles<128, 128, 2, 2>(a, vec, s);
+hipError_t launch_f32_mfma(const GemmArgs<float>& a, bool vec, void* ws, size_t ws_bytes, int cus,
+                           hipStream_t s) {
+    return launch_tiles<128, 128, 2, 2>(a, vec, ws, ws_bytes, cus, s);
+}
+
+size_t f32_mfma_workspace(int64_t M, int64_t N, int64_t K, int cus) {
+    if (M < 1 || N < 1 || K < 1) return 0;
+    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    return tail_workspace(plan_tail(tiles, (K + kBK - 1) / kBK, cus), 128, 128);
 }
 
 }  // namespace dg

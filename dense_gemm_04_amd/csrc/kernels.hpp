@@ -18,7 +18,12 @@ hipError_t launch_bf16_mfma(const GemmArgs<uint16_t>& a, bool vec, hipStream_t s
 hipError_t launch_bf16_tiled(const GemmArgs<uint16_t>& a, hipStream_t s);
 bool bf16_tiled_fits(const GemmArgs<uint16_t>& a);
 hipError_t launch_bf16_general(const GemmArgs<uint16_t>& a, bool vec, hipStream_t s);
-hipError_t launch_f32_mfma(const GemmArgs<float>& a, bool vec, hipStream_t s);
+// fp32 MFMA kernel. Given a workspace of at least f32_mfma_workspace(M, N, K,
+// cus) bytes (256-byte aligned, counters zero), a last round of tiles that
+// would leave most of the `cus` compute units idle is split over K.
+hipError_t launch_f32_mfma(const GemmArgs<float>& a, bool vec, void* ws, size_t ws_bytes, int cus,
+                           hipStream_t s);
+size_t f32_mfma_workspace(int64_t M, int64_t N, int64_t K, int cus);
 hipError_t launch_f32_valu(const GemmArgs<float>& a, bool vec, hipStream_t s);
 // Small-M bf16 (M <= kSkinnyMaxM). With `vec` the 64-column copy-ring kernel
 // runs; given a workspace of at least bf16_skinny_workspace(M, N, K) bytes

@@ -32,8 +32,9 @@
  * Ownership and memory: every pointer is a DEVICE pointer owned by the
  * caller, valid on the current HIP device for the duration of the work.
  * The library keeps no reference after the work completes and allocates no
- * device memory; gemm_bf16_ws takes a caller-owned workspace instead. C must
- * not overlap A, B or the workspace (undefined results otherwise).
+ * device memory; gemm_bf16_ws and gemm_f32_ws take a caller-owned workspace
+ * instead. C must not overlap A, B or the workspace (undefined results
+ * otherwise).
  *
  * Streams and errors: `stream` is a hipStream_t passed as void* (NULL = the
  * null stream). Calls are asynchronous: they validate the arguments, enqueue
@@ -133,6 +134,32 @@ gemm_status_t gemm_bf16_ws(int64_t M, int64_t N, int64_t K, float alpha,
                            const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                            float beta, uint16_t* C, int64_t ldc,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Split-K for the last round of tiles (fp32). The fp32 kernel covers C with
+ * 128 x 128 tiles, two resident workgroups per compute unit. When the tiles
+ * leave a last round that is at most half full (4095 x 4097: 1056 tiles on
+ * 512 slots leave 32 tiles for a third round), the tiles of that round are
+ * cut into up to 8 ranges of K (RTX 3090 SGEMM article, section 7.2:
+ * splitting K to bring more multiprocessors to work). Each range's fp32
+ * partial tile goes to the workspace and the last range to finish adds them
+ * in a fixed order before the alpha/beta epilogue. Full tiles are computed as
+ * in gemm_f32.
+ *
+ * gemm_f32_workspace_size: workspace bytes gemm_f32_ws needs for this shape
+ * on a full MI355X (256 compute units); 0 when it would not split (no last
+ * round, or one more than half full, or K below two 32-deep slabs) or the
+ * sizes are invalid. Host only, no HIP call. On a device with fewer compute
+ * units the split is planned for that device and uses the workspace only if
+ * it is large enough.
+ *
+ * gemm_f32_ws: gemm_f32 with such a workspace; the workspace contract
+ * (alignment, zero fill, no overlapping calls, NULL with size 0) is that of
+ * gemm_bf16_ws. */
+size_t gemm_f32_workspace_size(int64_t M, int64_t N, int64_t K);
+gemm_status_t gemm_f32_ws(int64_t M, int64_t N, int64_t K, float alpha,
+                          const float* A, int64_t lda, const float* B, int64_t ldb,
+                          float beta, float* C, int64_t ldc,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* Host-only planning (no HIP call): the variant a call with these arguments
  * would run (a gemm_variant_t value; GEMM_VARIANT_AUTO when the call would

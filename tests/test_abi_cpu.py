@@ -174,3 +174,28 @@ def test_workspace_validation(lib):
     assert dg.gemm_bf16_ws(*args, ws, need - 1, 0) == dg.GEMM_ERR_INVALID_VALUE    # too small
     bad = (16, 64, 64, 1.0, A, 63, B, 64, 0.0, C, 64)                                # lda < K
     assert dg.gemm_bf16_ws(*bad, ws, 1 << 20, 0) == dg.GEMM_ERR_INVALID_VALUE
+
+
+def test_f32_workspace_size(lib):
+    # 4095 x 4097: 32 x 33 = 1056 tiles of 128 x 128 on 512 slots (256 compute
+    # units, 2 workgroups each): 1024 in two full rounds, 32 left, cut into 8
+    # K ranges (K = 1023 is 32 slabs of 32, 4 per range).
+    assert dg.gemm_f32_workspace_size(4095, 4097, 1023) == 256 + 32 * 8 * 128 * 128 * 4
+    # 300 x 200: 6 tiles, K = 100 is 4 slabs: 4 ranges of one slab.
+    assert dg.gemm_f32_workspace_size(300, 200, 100) == 256 + 6 * 4 * 128 * 128 * 4
+    # No split: whole rounds (4096^2 is 1024 tiles), a last round more than half
+    # full, K of one slab, empty or invalid sizes.
+    assert dg.gemm_f32_workspace_size(4096, 4096, 4096) == 0
+    assert dg.gemm_f32_workspace_size(128 * 16, 128 * 20, 4096) == 0     # 320 tiles > 256
+    assert dg.gemm_f32_workspace_size(300, 200, 32) == 0
+    assert dg.gemm_f32_workspace_size(0, 200, 100) == 0
+    assert dg.gemm_f32_workspace_size(-1, 200, 100) == 0
+
+
+def test_f32_workspace_validation(lib):
+    args = (300, 200, 100, 1.0, A, 100, B, 200, 0.0, C, 200)
+    need = dg.gemm_f32_workspace_size(300, 200, 100)
+    ws = 0x400000
+    assert dg.gemm_f32_ws(*args, None, 64, 0) == dg.GEMM_ERR_INVALID_VALUE
+    assert dg.gemm_f32_ws(*args, ws + 64, need, 0) == dg.GEMM_ERR_INVALID_VALUE
+    assert dg.gemm_f32_ws(*args, ws, need - 1, 0) == dg.GEMM_ERR_INVALID_VALUE

@@ -77,3 +77,29 @@ def test_workload_small_m_split_k():
         err = oracle.max_rel_err(got, R, D)
         note(f"call {call}: max error ratio {err:.3e}")
         assert err <= tol(w.dtype)
+
+
+def test_workload_edge_split_k():
+    # 4095 x 4097 x 1023 through gemm_f32_ws: 1024 whole tiles, then the last
+    # 32 tiles (the ragged ones among them) split into 8 K ranges each.
+    w = gi.WORKLOADS[51]
+    note(f"workload {w.name} via gemm_f32_ws")
+    inp = gi.make(w)
+    A, B, C = inp["A"].cuda(), inp["B"].cuda(), inp["C0"].cuda()
+    nbytes = dg.gemm_f32_workspace_size(w.M, w.N, w.K)
+    assert nbytes > 0
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    st = dg.gemm_f32_ws(w.M, w.N, w.K, w.alpha, A.data_ptr(), w.K, B.data_ptr(), w.N, w.beta,
+                        C.data_ptr(), w.N, ws.data_ptr(), nbytes,
+                        int(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    assert st == dg.GEMM_OK, dg.gemm_status_string(st)
+    assert bool(torch.isfinite(C).all())
+    rows = sample(w.M, 128, 610)
+    cols = sample(w.N, 128, 611)
+    got = C[rows][:, cols].cpu().to(torch.float64).numpy()
+    R, D = oracle.gemm(gi.as_numpy(inp["A"]), gi.as_numpy(inp["B"]), gi.as_numpy(inp["C0"]),
+                       w.alpha, w.beta, w.dtype, rows=rows, cols=cols)
+    err = oracle.max_rel_err(got, R, D)
+    note(f"max error ratio {err:.3e}")
+    assert err <= tol(w.dtype)

@@ -96,3 +96,65 @@ def test_padded_rows_and_no_split_shapes():
     assert st == dg.GEMM_OK
     R2, D2 = oracle_ref("bf16", A2, B, None, 1.0, 0.0)
     assert oracle.max_rel_err(to_f64(C2), R2, D2) <= tol("bf16")
+
+
+# ---- fp32: split K for the last round of tiles -------------------------------
+
+def run_ws_f32(A, B, C0, alpha, beta, ws, nbytes, ld_pad=(0, 0, 0)):
+    M, K = A.shape
+    N = B.shape[1]
+    lda, ldb, ldc = K + ld_pad[0], N + ld_pad[1], N + ld_pad[2]
+    _, a = padded(M, K, lda, "f32", fill=float("nan"))
+    _, b = padded(K, N, ldb, "f32", fill=float("nan"))
+    _, c = padded(M, N, ldc, "f32", fill=float("nan"))
+    a.copy_(A.cuda())
+    b.copy_(B.cuda())
+    if C0 is not None:
+        c.copy_(C0.cuda())
+    st = dg.gemm_f32_ws(M, N, K, alpha, a.data_ptr(), lda, b.data_ptr(), ldb, beta,
+                        c.data_ptr(), ldc, ws.data_ptr() if nbytes else None, nbytes, 0)
+    torch.cuda.synchronize()
+    return c.cpu(), st
+
+
+# Aligned (vector) and unaligned (element-wise) rows, ragged tiles, K ranges of
+# one or several slabs, a single tile split in two.
+F32_SHAPES = [((300, 200, 100), (0, 0, 0)), ((1000, 1032, 136), (0, 0, 0)),
+              ((257, 520, 129), (0, 0, 0)), ((130, 70, 64), (0, 0, 0)),
+              ((513, 384, 1000), (4, 8, 12)), ((300, 264, 257), (1, 3, 5))]
+
+
+@pytest.mark.parametrize("case", F32_SHAPES, ids=lambda c: "x".join(map(str, c[0])) + f"_pad{c[1][0]}")
+def test_f32_split_k_parity(case):
+    (M, N, K), pad = case
+    nbytes = dg.gemm_f32_workspace_size(M, N, K)
+    assert nbytes > 0                                      # these shapes do split
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    for rep, (alpha, beta) in enumerate(((0.5, 2.0), (1.0, 0.0))):
+        seed = 1700 + M + rep
+        A = gi.random_matrix(M, K, "f32", seed)
+        B = gi.random_matrix(K, N, "f32", seed + 1)
+        C0 = gi.random_matrix(M, N, "f32", seed + 2) if beta != 0 else None
+        note(f"gemm_f32_ws M={M} N={N} K={K} pad={pad} alpha={alpha} beta={beta} ws={nbytes}")
+        C, st = run_ws_f32(A, B, C0, alpha, beta, ws, nbytes, pad)
+        assert st == dg.GEMM_OK, dg.gemm_status_string(st)
+        R, D = oracle_ref("f32", A, B, C0, alpha, beta)
+        err = oracle.max_rel_err(to_f64(C), R, D)
+        assert err <= tol("f32"), f"call {rep}: max error ratio {err:.3e}"
+    tiles = ((M + 127) // 128) * ((N + 127) // 128)
+    assert int(ws[:4 * tiles].view(torch.int32).abs().sum()) == 0
+
+
+def test_f32_split_k_deterministic():
+    M, N, K = 1000, 1032, 136
+    nbytes = dg.gemm_f32_workspace_size(M, N, K)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    A = gi.random_matrix(M, K, "f32", 1790)
+    B = gi.random_matrix(K, N, "f32", 1791)
+    note(f"gemm_f32_ws determinism M={M} N={N} K={K}")
+    first, st = run_ws_f32(A, B, None, 1.0, 0.0, ws, nbytes)
+    assert st == dg.GEMM_OK
+    for _ in range(3):
+        again, st = run_ws_f32(A, B, None, 1.0, 0.0, ws, nbytes)
+        assert st == dg.GEMM_OK
+        assert torch.equal(first.view(torch.int32), again.view(torch.int32))
