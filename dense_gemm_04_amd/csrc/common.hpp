@@ -22,6 +22,13 @@ struct GemmArgs {
     T* C; int64_t ldc;
 };
 
+// 128-bit vectors at addresses aligned only to their element (4 or 2 bytes).
+// gfx950 under the HSA runtime runs with unaligned global access enabled, and
+// the compiler emits one 128-bit load or store for these types; the kernels
+// use them on rows that are not 16-byte aligned.
+typedef float f32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x4_a2 __attribute__((ext_vector_type(4), aligned(2)));
+
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 

@@ -33,7 +33,9 @@
 //
 // Edges (Z-Turbo CUDA tuning page, section 3.1; Blackwell notes, section
 // 4.3): rows of A past M, columns of B past N and k past K are loaded as zero,
-// and the epilogue stores only in-range elements.
+// and the epilogue stores only in-range elements. Rows that are not 16-byte
+// aligned (VEC = false) use the same 128-bit accesses at 2-byte alignment and
+// element-wise ones only at the edges.
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -63,7 +65,8 @@ __device__ __forceinline__ u32x4 load8_elems(const uint16_t* p, int valid) {
 
 template <bool VEC>
 __device__ __forceinline__ u32x4 load8(const uint16_t* p, int valid) {
-    if (VEC && valid >= 8) return *reinterpret_cast<const u32x4*>(p);
+    if (valid >= 8)
+        return VEC ? *reinterpret_cast<const u32x4*>(p) : (u32x4)*reinterpret_cast<const u32x4_a2*>(p);
     if (valid <= 0) return u32x4{0u, 0u, 0u, 0u};
     return load8_elems(p, valid);
 }
@@ -206,9 +209,10 @@ void gemm_bf16_mfma_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
 #pragma unroll
             for (int j = 0; j < FN; ++j) v[j] = alpha * acc[i][j][r];
             uint16_t* dst = p.C + row * p.ldc + col;
-            if (VEC && FN == 8 && col + 8 <= N) {
+            if (FN == 8 && col + 8 <= N) {
                 if (beta != 0.f) {
-                    const u32x4 c0 = *reinterpret_cast<const u32x4*>(dst);
+                    const u32x4 c0 = VEC ? *reinterpret_cast<const u32x4*>(dst)
+                                         : (u32x4)*reinterpret_cast<const u32x4_a2*>(dst);
 #pragma unroll
                     for (int j = 0; j < 8; ++j)
                         v[j] += beta * bf16_to_f32((uint16_t)(c0[j >> 1] >> (16 * (j & 1))));
@@ -216,7 +220,8 @@ void gemm_bf16_mfma_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
                 u32x4 o;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
-                *reinterpret_cast<u32x4*>(dst) = o;
+                if (VEC) *reinterpret_cast<u32x4*>(dst) = o;
+                else *reinterpret_cast<u32x4_a2*>(dst) = (u32x4_a2)o;
             } else {
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {

@@ -42,7 +42,8 @@ __device__ __forceinline__ int bt_off(int col, int c) {
 
 template <bool VEC>
 __device__ __forceinline__ u32x4 load8(const uint16_t* p, int valid) {
-    if (VEC && valid >= 8) return *reinterpret_cast<const u32x4*>(p);
+    if (valid >= 8)
+        return VEC ? *reinterpret_cast<const u32x4*>(p) : (u32x4)*reinterpret_cast<const u32x4_a2*>(p);
     uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int e = 0; e < 8; ++e)

@@ -57,11 +57,6 @@ __device__ __forceinline__ f32x4 load4_elems(const float* p, int valid) {
     return v;
 }
 
-// Four floats at an address that is only 4-byte aligned. gfx950 under the
-// HSA runtime runs with unaligned global access enabled, and the compiler
-// emits one 128-bit load or store for this type.
-typedef float f32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
-
 template <bool VEC>
 __device__ __forceinline__ f32x4 load4(const float* p, int valid) {
     if (valid >= 4)
