@@ -14,6 +14,11 @@ with D_ij = |alpha| * sum_k |a_ik||b_kj| + |beta||c0_ij|. The bound is the
 usual forward-error bound of a dot product, so it is independent of the
 scale of the inputs.
 
+``gemm(..., bias=, act=)`` runs the epilogue form of the same oracle:
+r = act(alpha * s + bias_j) + beta * c0_ij, with act the identity, ReLU or
+the tanh form of GELU, and D scaled by a bound on the activation's slope (see
+``oracle_gemm.c``).
+
 It also holds ``bf16_round``: round-to-nearest-even of a binary64 value to
 the bf16 grid (1 sign, 8 exponent and 7 stored mantissa bits, as the
 Blackwell BF16 GEMM notes describe in section 1.2), written from that
@@ -46,6 +51,13 @@ def _load():
         fn.restype = ctypes.c_int
         fn.argtypes = [i64, i64, i64, dbl, vp, i64, vp, i64, dbl, vp, i64,
                        vp, i64, vp, i64, vp, vp, ctypes.c_int]
+    for name in ("oracle_gemm_f32_epi", "oracle_gemm_bf16_epi"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [i64, i64, i64, dbl, vp, i64, vp, i64, dbl, vp, i64, vp, ctypes.c_int,
+                       vp, i64, vp, i64, vp, vp, ctypes.c_int]
+    lib.oracle_activate.restype = dbl
+    lib.oracle_activate.argtypes = [dbl, ctypes.c_int]
     lib.oracle_bf16_bits_to_double.restype = dbl
     lib.oracle_bf16_bits_to_double.argtypes = [ctypes.c_uint16]
     lib.oracle_max_threads.restype = ctypes.c_int
@@ -75,22 +87,41 @@ def _ld(x: np.ndarray, itemsize: int) -> int:
     return max(x.strides[0] // itemsize, x.shape[1], 1)
 
 
+# Activation codes of the epilogue form.
+ACTS = {"none": 0, "relu": 1, "gelu_tanh": 2}
+
+
+def activate(z, act: str) -> np.ndarray:
+    """The oracle's activation (binary64), element by element."""
+    lib = _load()
+    code = ACTS[act]
+    flat = np.asarray(z, dtype=np.float64).ravel()
+    out = np.fromiter((lib.oracle_activate(float(v), code) for v in flat), dtype=np.float64,
+                      count=flat.size)
+    return out.reshape(np.shape(z))
+
+
 def gemm(A: np.ndarray, B: np.ndarray, C0: Optional[np.ndarray] = None,
          alpha: float = 1.0, beta: float = 0.0, dtype: str = "f32",
          rows: Optional[Sequence[int]] = None, cols: Optional[Sequence[int]] = None,
-         threads: int = 0):
+         threads: int = 0, bias: Optional[np.ndarray] = None, act: Optional[str] = None):
     """Return (R, D) as float64 arrays of shape (len(rows), len(cols)).
 
     ``dtype`` "f32": A, B, C0 are float32 arrays. ``dtype`` "bf16": they are
     uint16 arrays holding bf16 bit patterns. ``rows``/``cols`` select a
     sub-grid of C (default: all). ``alpha``/``beta`` are taken as given
     (pass the fp32 value the GPU sees). ``beta == 0`` never reads C0.
+    ``bias`` (length N, same element type) and ``act`` (a key of ``ACTS``)
+    select the epilogue form.
     """
     lib = _load()
+    epi = bias is not None or act is not None
     if dtype == "f32":
-        want, fn, isz = np.float32, lib.oracle_gemm_f32, 4
+        want, isz = np.float32, 4
+        fn = lib.oracle_gemm_f32_epi if epi else lib.oracle_gemm_f32
     elif dtype == "bf16":
-        want, fn, isz = np.uint16, lib.oracle_gemm_bf16, 2
+        want, isz = np.uint16, 2
+        fn = lib.oracle_gemm_bf16_epi if epi else lib.oracle_gemm_bf16
     else:
         raise ValueError(dtype)
     for name, x in (("A", A), ("B", B)):
@@ -112,8 +143,16 @@ def gemm(A: np.ndarray, B: np.ndarray, C0: Optional[np.ndarray] = None,
     nc = N if c_idx is None else nc
     R = np.empty((nr, nc), dtype=np.float64)
     D = np.empty((nr, nc), dtype=np.float64)
+    extra = ()
+    if epi:
+        if bias is not None:
+            bias = np.ascontiguousarray(bias)
+            if bias.dtype != want or bias.shape != (N,):
+                raise ValueError("bias must have shape (N,) and the dtype of A and B")
+        code = ACTS[act if act is not None else "none"]
+        extra = (None if bias is None or bias.size == 0 else bias.ctypes.data, code)
     st = fn(M, N, K, float(alpha), A.ctypes.data if A.size else None, lda,
-            B.ctypes.data if B.size else None, ldb, float(beta), c0_ptr, ldc,
+            B.ctypes.data if B.size else None, ldb, float(beta), c0_ptr, ldc, *extra,
             None if r_idx is None else r_idx.ctypes.data, nr,
             None if c_idx is None else c_idx.ctypes.data, nc,
             R.ctypes.data, D.ctypes.data, int(threads))

@@ -21,7 +21,19 @@
  *   r   = alpha * s + beta * c0_ij         (the beta term is skipped when beta == 0,
  *                                           so C0 is never read then)
  *   D   = |alpha| * sum_k |a_ik| * |b_kj| + |beta| * |c0_ij|
- * r and D are returned unrounded. The products of two fp32 (or bf16) values
+ * r and D are returned unrounded.
+ *
+ * The epilogue variant (oracle_gemm_*_epi) adds what a GEMM epilogue can fuse
+ * (Blackwell BF16 GEMM notes, section 3.3: bias, GELU, residual; the Z-Turbo
+ * tuning page, section 2.1: a fused kernel that applies GELU in its tanh form
+ * and then adds the residual):
+ *   z   = alpha * s + bias_j               (no bias term when bias is NULL)
+ *   r   = act(z) + beta * c0_ij            (c0 is the residual)
+ *   D   = L * (|alpha| * sum_k |a_ik| * |b_kj| + |bias_j|) + |beta| * |c0_ij|
+ * with act one of: identity; ReLU, max(z, 0); GELU, tanh form,
+ *   0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))),
+ * and L a bound on |act'| (1, 1 and ORACLE_GELU_SLOPE), so that an error in z
+ * moves r by at most L times as much. The products of two fp32 (or bf16) values
  * are exact in binary64, so contraction into an FMA cannot change r; the
  * file is still built with -ffp-contract=off and without -ffast-math.
  *
@@ -54,15 +66,36 @@ static double from_bf16(const void* base, int64_t idx) {
 
 typedef double (*load_fn)(const void*, int64_t);
 
+#define ACT_NONE 0
+#define ACT_RELU 1
+#define ACT_GELU_TANH 2
+
+/* Upper bound on the slope of the tanh-form GELU over the reals (the maximum
+ * is about 1.1289, near z = 1.5). */
+#define ORACLE_GELU_SLOPE 1.13
+
+static double activate(double z, int act) {
+    if (act == ACT_RELU) return z > 0.0 ? z : 0.0;
+    if (act == ACT_GELU_TANH)
+        return 0.5 * z * (1.0 + tanh(sqrt(2.0 / acos(-1.0)) * (z + 0.044715 * z * z * z)));
+    return z;
+}
+
+static double act_slope(int act) { return act == ACT_GELU_TANH ? ORACLE_GELU_SLOPE : 1.0; }
+
+double oracle_activate(double z, int act) { return activate(z, act); }
+
 double oracle_bf16_bits_to_double(uint16_t bits) { return from_bf16(&bits, 0); }
 
 static int oracle_gemm(load_fn load, int64_t M, int64_t N, int64_t K, double alpha,
                        const void* A, int64_t lda, const void* B, int64_t ldb,
                        double beta, const void* C0, int64_t ldc,
+                       const void* bias, int act,
                        const int64_t* rows, int64_t nrows,
                        const int64_t* cols, int64_t ncols,
                        double* R, double* D, int nthreads) {
     if (M < 0 || N < 0 || K < 0) return ORACLE_BAD_ARG;
+    if (act < ACT_NONE || act > ACT_GELU_TANH) return ORACLE_BAD_ARG;
     if (rows == NULL) nrows = M;
     if (cols == NULL) ncols = N;
     if (nrows < 0 || ncols < 0) return ORACLE_BAD_ARG;
@@ -110,10 +143,17 @@ static int oracle_gemm(load_fn load, int64_t M, int64_t N, int64_t K, double alp
                 }
             }
             for (int64_t c = 0; c < ncols; ++c) {
+                int64_t j = cols ? cols[c] : c;
                 double r = alpha * s[c];
                 double d = fabs(alpha) * mag[c];
+                if (bias) {
+                    double b = load(bias, j);
+                    r += b;
+                    d += fabs(b);
+                }
+                r = activate(r, act);
+                d *= act_slope(act);
                 if (beta != 0.0) {
-                    int64_t j = cols ? cols[c] : c;
                     double c0 = load(C0, i * ldc + j);
                     r += beta * c0;
                     d += fabs(beta) * fabs(c0);
@@ -134,7 +174,7 @@ int oracle_gemm_f32(int64_t M, int64_t N, int64_t K, double alpha,
                     double beta, const float* C0, int64_t ldc,
                     const int64_t* rows, int64_t nrows, const int64_t* cols, int64_t ncols,
                     double* R, double* D, int nthreads) {
-    return oracle_gemm(from_f32, M, N, K, alpha, A, lda, B, ldb, beta, C0, ldc,
+    return oracle_gemm(from_f32, M, N, K, alpha, A, lda, B, ldb, beta, C0, ldc, NULL, ACT_NONE,
                        rows, nrows, cols, ncols, R, D, nthreads);
 }
 
@@ -143,7 +183,26 @@ int oracle_gemm_bf16(int64_t M, int64_t N, int64_t K, double alpha,
                      double beta, const uint16_t* C0, int64_t ldc,
                      const int64_t* rows, int64_t nrows, const int64_t* cols, int64_t ncols,
                      double* R, double* D, int nthreads) {
-    return oracle_gemm(from_bf16, M, N, K, alpha, A, lda, B, ldb, beta, C0, ldc,
+    return oracle_gemm(from_bf16, M, N, K, alpha, A, lda, B, ldb, beta, C0, ldc, NULL, ACT_NONE,
+                       rows, nrows, cols, ncols, R, D, nthreads);
+}
+
+/* The epilogue variants: bias (length N, same element type, or NULL) and act. */
+int oracle_gemm_f32_epi(int64_t M, int64_t N, int64_t K, double alpha,
+                        const float* A, int64_t lda, const float* B, int64_t ldb,
+                        double beta, const float* C0, int64_t ldc, const float* bias, int act,
+                        const int64_t* rows, int64_t nrows, const int64_t* cols, int64_t ncols,
+                        double* R, double* D, int nthreads) {
+    return oracle_gemm(from_f32, M, N, K, alpha, A, lda, B, ldb, beta, C0, ldc, bias, act,
+                       rows, nrows, cols, ncols, R, D, nthreads);
+}
+
+int oracle_gemm_bf16_epi(int64_t M, int64_t N, int64_t K, double alpha,
+                         const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                         double beta, const uint16_t* C0, int64_t ldc, const uint16_t* bias,
+                         int act, const int64_t* rows, int64_t nrows, const int64_t* cols,
+                         int64_t ncols, double* R, double* D, int nthreads) {
+    return oracle_gemm(from_bf16, M, N, K, alpha, A, lda, B, ldb, beta, C0, ldc, bias, act,
                        rows, nrows, cols, ncols, R, D, nthreads);
 }
 
