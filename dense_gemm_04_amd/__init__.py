@@ -29,9 +29,14 @@ VARIANT_VALU = 3
 VARIANT_SKINNY = 4
 VARIANT_NAMES = {0: "auto", 1: "mfma", 2: "general", 3: "valu", 4: "skinny"}
 
+ACT_NONE = 0
+ACT_RELU = 1
+ACT_GELU_TANH = 2
+ACT_NAMES = {0: "none", 1: "relu", 2: "gelu_tanh"}
+
 EXPORTS = ("gemm_f32", "gemm_bf16", "gemm_f32_ex", "gemm_bf16_ex", "gemm_bf16_ws",
-           "gemm_bf16_workspace_size", "gemm_f32_ws", "gemm_f32_workspace_size", "gemm_plan",
-           "gemm_status_string")
+           "gemm_bf16_workspace_size", "gemm_f32_ws", "gemm_f32_workspace_size",
+           "gemm_f32_bias_act", "gemm_bf16_bias_act", "gemm_plan", "gemm_status_string")
 
 _lib = None
 
@@ -62,6 +67,9 @@ def load() -> ctypes.CDLL:
     for name in ("gemm_bf16_ws", "gemm_f32_ws"):
         fn = getattr(lib, name)
         fn.restype, fn.argtypes = ci, base[:11] + [vp, ctypes.c_size_t, vp]
+    for name in ("gemm_f32_bias_act", "gemm_bf16_bias_act"):
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = ci, base[:11] + [vp, ci, vp, ctypes.c_size_t, vp]
     for name in ("gemm_bf16_workspace_size", "gemm_f32_workspace_size"):
         fn = getattr(lib, name)
         fn.restype, fn.argtypes = ctypes.c_size_t, [i64, i64, i64]
@@ -107,6 +115,18 @@ def gemm_f32_ws(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace, workspa
 
 def gemm_f32_workspace_size(M, N, K) -> int:
     return load().gemm_f32_workspace_size(M, N, K)
+
+
+def gemm_f32_bias_act(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, act, workspace=0,
+                      workspace_bytes=0, stream=0) -> int:
+    return load().gemm_f32_bias_act(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, act,
+                                    workspace, workspace_bytes, stream)
+
+
+def gemm_bf16_bias_act(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, act, workspace=0,
+                       workspace_bytes=0, stream=0) -> int:
+    return load().gemm_bf16_bias_act(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, act,
+                                     workspace, workspace_bytes, stream)
 
 
 def gemm_plan(elem_bytes, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, variant=0) -> int:

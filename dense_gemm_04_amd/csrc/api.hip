@@ -20,12 +20,16 @@ bool aligned(const void* p, size_t bytes) {
 
 int64_t max1(int64_t x) { return x > 1 ? x : 1; }
 
-// What a call has to do once its arguments are known to be valid.
+// What a call has to do once its arguments are known to be valid. Every
+// activation maps 0 to 0, so without a bias the product-free case is the plain
+// one: C = beta * C.
 enum class Work { kNone, kScale, kGemm };
 
-Work work_of(int64_t M, int64_t N, int64_t K, float alpha, float beta) {
+Work work_of(int64_t M, int64_t N, int64_t K, float alpha, float beta,
+             const void* bias = nullptr) {
     if (M == 0 || N == 0) return Work::kNone;
-    if (K == 0 || alpha == 0.f) return beta == 1.f ? Work::kNone : Work::kScale;
+    if (K == 0 || alpha == 0.f)
+        return (beta == 1.f && bias == nullptr) ? Work::kNone : Work::kScale;
     return Work::kGemm;
 }
 
@@ -124,14 +128,22 @@ bool workspace_ok(const void* ws, size_t bytes, size_t need) {
     return aligned(ws, 256) && bytes >= need;
 }
 
+// Bias and activation of the epilogue entry points (valid also when unused).
+bool valid_epilogue(int esz, const void* bias, int act) {
+    return act >= GEMM_ACT_NONE && act <= GEMM_ACT_GELU_TANH && aligned(bias, esz);
+}
+
 template <typename T>
 gemm_status_t run(int64_t M, int64_t N, int64_t K, float alpha, const T* A, int64_t lda,
                   const T* B, int64_t ldb, float beta, T* C, int64_t ldc, void* stream,
-                  int variant, void* ws = nullptr, size_t ws_bytes = 0) {
+                  int variant, void* ws = nullptr, size_t ws_bytes = 0,
+                  const T* bias = nullptr, int act = GEMM_ACT_NONE) {
     constexpr int esz = (int)sizeof(T);
     const int v = plan_impl(esz, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, variant);
     if (v < 0) return GEMM_ERR_INVALID_VALUE;
-    const Work w = work_of(M, N, K, alpha, beta);
+    if (!valid_epilogue(esz, bias, act)) return GEMM_ERR_INVALID_VALUE;
+    const Work w = work_of(M, N, K, alpha, beta, bias);
+    if (w == Work::kScale && C == nullptr) return GEMM_ERR_INVALID_VALUE;
     if (w == Work::kNone) return GEMM_OK;
     int cus = kFullCus;
     const gemm_status_t dev = check_device(&cus);
@@ -139,10 +151,10 @@ gemm_status_t run(int64_t M, int64_t N, int64_t K, float alpha, const T* A, int6
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     hipError_t e;
     if (w == Work::kScale) {
-        if constexpr (esz == 4) e = dg::launch_scale_f32(M, N, beta, C, ldc, s);
-        else e = dg::launch_scale_bf16(M, N, beta, C, ldc, s);
+        if constexpr (esz == 4) e = dg::launch_scale_f32(M, N, beta, C, ldc, bias, act, s);
+        else e = dg::launch_scale_bf16(M, N, beta, C, ldc, bias, act, s);
     } else {
-        dg::GemmArgs<T> a{M, N, K, alpha, beta, A, lda, B, ldb, C, ldc};
+        dg::GemmArgs<T> a{M, N, K, alpha, beta, A, lda, B, ldb, C, ldc, bias, act};
         const bool vec = vector_ok(esz, A, lda, B, ldb, C, ldc);
         if constexpr (esz == 4) {
             e = (v == GEMM_VARIANT_VALU) ? dg::launch_f32_valu(a, vec, s)
@@ -198,6 +210,26 @@ gemm_status_t gemm_f32_ws(int64_t M, int64_t N, int64_t K, float alpha, const fl
         return GEMM_ERR_INVALID_VALUE;
     return run<float>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, GEMM_VARIANT_AUTO,
                       workspace, workspace_bytes);
+}
+
+gemm_status_t gemm_f32_bias_act(int64_t M, int64_t N, int64_t K, float alpha, const float* A,
+                                int64_t lda, const float* B, int64_t ldb, float beta, float* C,
+                                int64_t ldc, const float* bias, int act, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    if (!workspace_ok(workspace, workspace_bytes, gemm_f32_workspace_size(M, N, K)))
+        return GEMM_ERR_INVALID_VALUE;
+    return run<float>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, GEMM_VARIANT_AUTO,
+                      workspace, workspace_bytes, bias, act);
+}
+
+gemm_status_t gemm_bf16_bias_act(int64_t M, int64_t N, int64_t K, float alpha,
+                                 const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                                 float beta, uint16_t* C, int64_t ldc, const uint16_t* bias,
+                                 int act, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!workspace_ok(workspace, workspace_bytes, gemm_bf16_workspace_size(M, N, K)))
+        return GEMM_ERR_INVALID_VALUE;
+    return run<uint16_t>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, GEMM_VARIANT_AUTO,
+                         workspace, workspace_bytes, bias, act);
 }
 
 gemm_status_t gemm_f32(int64_t M, int64_t N, int64_t K, float alpha, const float* A,

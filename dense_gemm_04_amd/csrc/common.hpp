@@ -12,7 +12,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// Arguments every GEMM kernel receives, by value (kernarg segment).
+// Arguments every GEMM kernel receives, by value (kernarg segment). `bias`
+// (length N, or null) and `act` are read only by the epilogue instantiations.
 template <typename T>
 struct GemmArgs {
     int64_t M, N, K;
@@ -20,6 +21,8 @@ struct GemmArgs {
     const T* A; int64_t lda;
     const T* B; int64_t ldb;
     T* C; int64_t ldc;
+    const T* bias = nullptr;
+    int act = 0;
 };
 
 // 128-bit vectors at addresses aligned only to their element (4 or 2 bytes).
@@ -65,6 +68,45 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// ---- fused bias + activation epilogue --------------------------------------
+//
+// out = act(alpha * acc + bias[col]) + beta * C0: the bias is added and the
+// activation applied before the residual term, as a fused GELU + residual
+// kernel does (Z-Turbo tuning page, section 2.1).
+
+constexpr int kActNone = 0, kActRelu = 1, kActGeluTanh = 2;
+
+// GELU in its tanh form, 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))).
+// Since 0.5 (1 + tanh u) is the logistic function of 2u, this equals
+// x / (1 + exp(-2u)), evaluated here with the hardware exp2 and reciprocal:
+// no cancellation for negative x, and 0 or x in the limits (exp2 -> inf or 0).
+__device__ __forceinline__ float gelu_tanh(float x) {
+    constexpr float kScale = -2.3022082f;   // -2 sqrt(2/pi) log2(e)
+    const float t = kScale * x * __builtin_fmaf(0.044715f * x, x, 1.f);
+    return x * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(t));
+}
+
+__device__ __forceinline__ float activate(float x, int act) {
+    if (act == kActRelu) return x > 0.f ? x : 0.f;
+    if (act == kActGeluTanh) return gelu_tanh(x);
+    return x;
+}
+
+__device__ __forceinline__ float elem_f32(float v) { return v; }
+__device__ __forceinline__ float elem_f32(uint16_t v) { return bf16_to_f32(v); }
+
+// True when a call needs the epilogue instantiations.
+template <typename T>
+inline bool has_epilogue(const GemmArgs<T>& a) {
+    return a.bias != nullptr || a.act != kActNone;
+}
+
+// Bias of column `col`: 0 past N or without a bias vector.
+template <typename T>
+__device__ __forceinline__ float bias_at(const GemmArgs<T>& p, int64_t col) {
+    return (p.bias != nullptr && col < p.N) ? elem_f32(p.bias[col]) : 0.f;
 }
 
 // ---- LDS pipelines ----------------------------------------------------------

@@ -18,8 +18,9 @@
 //     wasted bytes);
 //   * each wave owns a (BM / WAVES_M) x (BN / WAVES_N) block of C held as
 //     16x16 fp32 accumulators of v_mfma_f32_16x16x32_bf16;
-//   * the epilogue forms alpha * acc + beta * C0 in fp32 and rounds to bf16
-//     (notes, section 1.2 and 6.3), storing 16 bytes per lane.
+//   * the epilogue forms alpha * acc + beta * C0 in fp32 (with EPI, bias and
+//     activation before the beta term) and rounds to bf16 (notes, section
+//     1.2 and 6.3), storing 16 bytes per lane.
 //
 // Operand layout of v_mfma_f32_16x16x32_bf16 used here: lane l = p + 16 g
 // (p in 0..15, g in 0..3) supplies A(row p, k = 8g .. 8g+7) and B(k = 8g ..
@@ -85,7 +86,7 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&x)[8], u32x4 (&y)[8])
     }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool VEC>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool VEC, bool EPI>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64)
 void gemm_bf16_mfma_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
     constexpr int NT = WAVES_M * WAVES_N * 64;
@@ -198,6 +199,11 @@ void gemm_bf16_mfma_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
     // Epilogue: lane (pl, g) holds rows 4g + i of each 16-row block and the FN
     // consecutive columns wn0 + FN * pl .. + FN - 1.
     const float alpha = p.alpha, beta = p.beta;
+    float bv[FN];
+    if constexpr (EPI) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bv[j] = bias_at(p, n0 + wn0 + FN * pl + j);
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -208,6 +214,10 @@ void gemm_bf16_mfma_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
             float v[FN];
 #pragma unroll
             for (int j = 0; j < FN; ++j) v[j] = alpha * acc[i][j][r];
+            if constexpr (EPI) {
+#pragma unroll
+                for (int j = 0; j < FN; ++j) v[j] = activate(v[j] + bv[j], p.act);
+            }
             uint16_t* dst = p.C + row * p.ldc + col;
             if (FN == 8 && col + 8 <= N) {
                 if (beta != 0.f) {
@@ -242,8 +252,12 @@ hipError_t launch_tiles(const GemmArgs<uint16_t>& a, bool vec, hipStream_t s) {
     int tm = (int)tiles_m, tn = (int)tiles_n;
     GemmArgs<uint16_t> args = a;
     void* kargs[] = {&args, &tm, &tn};
-    const void* fn = vec ? (const void*)&gemm_bf16_mfma_kernel<BM, BN, WAVES_M, WAVES_N, true>
-                         : (const void*)&gemm_bf16_mfma_kernel<BM, BN, WAVES_M, WAVES_N, false>;
+    const bool epi = has_epilogue(a);
+    const void* fn =
+        vec ? (epi ? (const void*)&gemm_bf16_mfma_kernel<BM, BN, WAVES_M, WAVES_N, true, true>
+                   : (const void*)&gemm_bf16_mfma_kernel<BM, BN, WAVES_M, WAVES_N, true, false>)
+            : (epi ? (const void*)&gemm_bf16_mfma_kernel<BM, BN, WAVES_M, WAVES_N, false, true>
+                   : (const void*)&gemm_bf16_mfma_kernel<BM, BN, WAVES_M, WAVES_N, false, false>);
     if (tiles_m * tiles_n > kMaxGrid) return hipErrorInvalidConfiguration;
     return hipLaunchKernel(fn, dim3((unsigned)(tiles_m * tiles_n)), dim3(WAVES_M * WAVES_N * 64),
                            kargs, 0, s);

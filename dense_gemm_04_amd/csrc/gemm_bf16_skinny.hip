@@ -5,23 +5,25 @@
 // is to stream B from HBM exactly once with enough of it in flight, while the
 // matrix cores do the little arithmetic there is.
 //
-// Both kernels here give one workgroup (4 waves) a 32-column strip of C and
-// all of K, so no partial sums ever leave the workgroup; strips are renumbered
-// so that neighbouring strips (which share 128-byte lines of B) run on one
-// XCD. The four waves split each chunk's k range, and their fp32 partial tiles
-// are summed in LDS in a fixed order before the alpha/beta epilogue.
+// Vector path (16-byte aligned rows): one workgroup (4 waves) per 64-column
+// strip of C, or per strip and K segment when a workspace lets K be split.
+// Chunks of 128 rows of B (and the matching 128 columns of A) are copied
+// straight from global memory into a deep ring of LDS stages with
+// LDS-destined buffer loads, several chunks ahead of their use. B stays
+// row-major in LDS and its MFMA fragments come from transposing LDS reads
+// (ds_read_b64_tr_b16); A's from 128-bit LDS reads. Rows past K and M arrive
+// as zeros through the descriptor bounds; the ragged K tail of A is masked in
+// registers.
 //
-// Vector path (16-byte aligned rows): chunks of 256 rows of B (and the
-// matching 256 columns of A) are copied straight from global memory into a
-// deep ring of LDS stages with LDS-destined buffer loads, five chunks ahead
-// of their use. B stays row-major in LDS and its MFMA fragments come from
-// transposing LDS reads (ds_read_b64_tr_b16); A's from 128-bit LDS reads.
-// Rows past K and M arrive as zeros through the descriptor bounds; the
-// ragged K tail of A is masked in registers.
+// Element-wise path (any alignment): one workgroup per 32-column strip and
+// all of K; 8 x 8 blocks of B are read with predicated loads, transposed in
+// registers and written k-contiguous to a double-buffered LDS tile; A
+// fragments are loaded from global memory. The four waves split each chunk's
+// k range, and their fp32 partial tiles are summed in LDS in a fixed order
+// before the epilogue.
 //
-// Element-wise path (any alignment): 8 x 8 blocks of B are read with
-// predicated loads, transposed in registers and written k-contiguous to a
-// double-buffered LDS tile; A fragments are loaded from global memory.
+// Both epilogues form alpha * acc + beta * C0 in fp32; with EPI the bias is
+// added and the activation applied before the beta term.
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -51,7 +53,7 @@ __device__ __forceinline__ u32x4 load8(const uint16_t* p, int valid) {
     return u32x4{w[0], w[1], w[2], w[3]};
 }
 
-template <int MB, bool VEC>
+template <int MB, bool VEC, bool EPI>
 __global__ __launch_bounds__(kNT)
 void gemm_bf16_skinny_kernel(GemmArgs<uint16_t> p, int strips) {
     __shared__ __attribute__((aligned(16))) uint16_t bt[2][kBN * kKC];
@@ -164,6 +166,7 @@ void gemm_bf16_skinny_kernel(GemmArgs<uint16_t> p, int strips) {
 #pragma unroll
         for (int w = 1; w < kNT / 64; ++w) s += part[w][e];
         float v = alpha * s;
+        if constexpr (EPI) v = activate(v + bias_at(p, gc), p.act);
         uint16_t* dst = p.C + row * p.ldc + gc;
         if (beta != 0.f) v += beta * bf16_to_f32(*dst);
         *dst = f32_to_bf16(v);
@@ -213,14 +216,20 @@ struct SmallMWork {
     int cps;      // chunks per segment
 };
 
-template <int MB>
+template <bool EPI>
 __device__ __forceinline__ void store_row4(const GemmArgs<uint16_t>& p, int64_t row, int64_t gc,
                                            f32x4 s) {
     if (row >= p.M) return;
+    if constexpr (EPI) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[r] = activate(p.alpha * s[r] + bias_at(p, gc + r), p.act);
+    } else {
+        s *= p.alpha;
+    }
     uint16_t* dst = p.C + row * p.ldc + gc;
     if (gc + 3 < p.N) {
         // Four bf16 = 8 bytes, aligned: rows are 16-byte aligned and gc % 4 == 0.
-        float v[4] = {p.alpha * s[0], p.alpha * s[1], p.alpha * s[2], p.alpha * s[3]};
+        float v[4] = {s[0], s[1], s[2], s[3]};
         if (p.beta != 0.f) {
             const u32x2 c0 = *reinterpret_cast<const u32x2*>(dst);
             v[0] += p.beta * bf16_to_f32((uint16_t)(c0[0] & 0xffffu));
@@ -233,7 +242,7 @@ __device__ __forceinline__ void store_row4(const GemmArgs<uint16_t>& p, int64_t 
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             if (gc + r >= p.N) break;
-            float v = p.alpha * s[r];
+            float v = s[r];
             if (p.beta != 0.f) v += p.beta * bf16_to_f32(dst[r]);
             dst[r] = f32_to_bf16(v);
         }
@@ -242,7 +251,7 @@ __device__ __forceinline__ void store_row4(const GemmArgs<uint16_t>& p, int64_t 
 
 // ws (only used when wk.segs > 1): [counters: one int per strip, padded to
 // 256 bytes][slots: segs x strips tiles of 16 MB x 64 fp32, slot s * strips + strip].
-template <int MB>
+template <int MB, bool EPI>
 __global__ __launch_bounds__(kNT, 1)
 void gemm_bf16_smallm_kernel(GemmArgs<uint16_t> p, SmallMWork wk, unsigned char* ws) {
     using S = SmallM<MB>;
@@ -356,7 +365,7 @@ void gemm_bf16_smallm_kernel(GemmArgs<uint16_t> p, SmallMWork wk, unsigned char*
     const int tcol = 16 * wave + 4 * g;
     if (wk.segs == 1) {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) store_row4<MB>(p, 16 * mb + pl, n0 + tcol, acc[mb]);
+        for (int mb = 0; mb < MB; ++mb) store_row4<EPI>(p, 16 * mb + pl, n0 + tcol, acc[mb]);
         return;
     }
 
@@ -404,7 +413,7 @@ void gemm_bf16_smallm_kernel(GemmArgs<uint16_t> p, SmallMWork wk, unsigned char*
             for (int i = 0; i < 8; ++i)
                 if (sg0 + i < wk.segs) sum += v[i];
         }
-        store_row4<MB>(p, 16 * mb + pl, n0 + tcol, sum);
+        store_row4<EPI>(p, 16 * mb + pl, n0 + tcol, sum);
     }
     // Leave the counter at zero for the next call that uses this workspace.
     if (t == 0) __hip_atomic_store(counters + strip, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -450,24 +459,32 @@ size_t bf16_skinny_workspace(int64_t M, int64_t N, int64_t K) {
 hipError_t launch_bf16_skinny(const GemmArgs<uint16_t>& a, bool vec, void* ws, size_t ws_bytes,
                               hipStream_t s) {
     GemmArgs<uint16_t> args = a;
+    const bool epi = has_epilogue(a);
     if (vec && smallm_fits(a)) {
         const size_t need = bf16_skinny_workspace(a.M, a.N, a.K);
         const bool split = ws != nullptr && need > 0 && ws_bytes >= need;
         SmallMWork w = plan_smallm(a.N, a.K, split);
         unsigned char* wsp = split ? static_cast<unsigned char*>(ws) : nullptr;
         void* kargs[] = {&args, &w, &wsp};
-        const void* fn = a.M <= 16 ? (const void*)&gemm_bf16_smallm_kernel<1>
-                                   : (const void*)&gemm_bf16_smallm_kernel<2>;
+        const void* fn = epi ? (a.M <= 16 ? (const void*)&gemm_bf16_smallm_kernel<1, true>
+                                          : (const void*)&gemm_bf16_smallm_kernel<2, true>)
+                             : (a.M <= 16 ? (const void*)&gemm_bf16_smallm_kernel<1, false>
+                                          : (const void*)&gemm_bf16_smallm_kernel<2, false>);
         if ((int64_t)w.strips * w.segs > kMaxGrid) return hipErrorInvalidConfiguration;
         return hipLaunchKernel(fn, dim3((unsigned)(w.strips * w.segs)), dim3(kNT), kargs, 0, s);
     }
     const int64_t strips = (a.N + kBN - 1) / kBN;
     int st = (int)strips;
     void* kargs[] = {&args, &st};
-    const void* fn = a.M <= 16 ? (vec ? (const void*)&gemm_bf16_skinny_kernel<1, true>
-                                      : (const void*)&gemm_bf16_skinny_kernel<1, false>)
-                               : (vec ? (const void*)&gemm_bf16_skinny_kernel<2, true>
-                                      : (const void*)&gemm_bf16_skinny_kernel<2, false>);
+    const void* fn =
+        epi ? (a.M <= 16 ? (vec ? (const void*)&gemm_bf16_skinny_kernel<1, true, true>
+                                : (const void*)&gemm_bf16_skinny_kernel<1, false, true>)
+                         : (vec ? (const void*)&gemm_bf16_skinny_kernel<2, true, true>
+                                : (const void*)&gemm_bf16_skinny_kernel<2, false, true>))
+            : (a.M <= 16 ? (vec ? (const void*)&gemm_bf16_skinny_kernel<1, true, false>
+                                : (const void*)&gemm_bf16_skinny_kernel<1, false, false>)
+                         : (vec ? (const void*)&gemm_bf16_skinny_kernel<2, true, false>
+                                : (const void*)&gemm_bf16_skinny_kernel<2, false, false>));
     if (strips > kMaxGrid) return hipErrorInvalidConfiguration;
     return hipLaunchKernel(fn, dim3((unsigned)strips), dim3(kNT), kargs, 0, s);
 }

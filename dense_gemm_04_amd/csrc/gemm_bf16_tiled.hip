@@ -27,7 +27,8 @@
 //   * v_mfma_f32_16x16x32_bf16 is issued with B as the first operand, so each
 //     16 x 16 accumulator is a block of C transposed and every lane ends up
 //     holding 4 consecutive columns of one row of C: the fused epilogue
-//     (alpha * acc + beta * C0, then RNE to bf16) uses 8-byte loads/stores;
+//     (alpha * acc + beta * C0, then RNE to bf16; with EPI, bias and
+//     activation before the beta term) uses 8-byte loads/stores;
 //   * edges: the descriptors end where the matrices end, so rows of A past M
 //     and rows of B past K read as zero; columns of B past N only feed output
 //     columns that are never stored; k past K in the last slab is zeroed in
@@ -85,7 +86,7 @@ __device__ __forceinline__ void lds_barrier() {
     lds_only_barrier();
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool EPI>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1)
 void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
     constexpr int kNT = WAVES_M * WAVES_N * 64;
@@ -256,6 +257,13 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
 
     // Epilogue: acc[j][i] register r holds C(m0 + wm0 + 16 i + pl, n0 + wn0 + 16 j + 4 g + r).
     const float alpha = p.alpha, beta = p.beta;
+    float bv[kFN][4];
+    if constexpr (EPI) {
+#pragma unroll
+        for (int j = 0; j < kFN; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) bv[j][r] = bias_at(p, n0 + wn0 + 16 * j + 4 * g + r);
+    }
 #pragma unroll
     for (int i = 0; i < kFM; ++i) {
         const int64_t row = m0 + wm0 + 16 * i + pl;
@@ -267,6 +275,10 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
             float v[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) v[r] = alpha * acc[j][i][r];
+            if constexpr (EPI) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[r] = activate(v[r] + bv[j][r], p.act);
+            }
             if (col + 4 <= N) {
                 u32x2* dst = reinterpret_cast<u32x2*>(crow + col);
                 if (beta != 0.f) {
@@ -298,20 +310,21 @@ bool bf16_tiled_fits(const GemmArgs<uint16_t>& a) {
     return (256 * a.lda + a.K) * 2 < lim && (kBK * a.ldb + a.N) * 2 < lim;
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool EPI>
 hipError_t launch_cfg(const GemmArgs<uint16_t>& a, hipStream_t s) {
     const int64_t tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
     int tm = (int)tiles_m, tn = (int)tiles_n;
     GemmArgs<uint16_t> args = a;
     void* kargs[] = {&args, &tm, &tn};
     if (tiles_m * tiles_n > kMaxGrid) return hipErrorInvalidConfiguration;
-    return hipLaunchKernel((const void*)&gemm_bf16_tiled_kernel<BM, BN, WAVES_M, WAVES_N>,
+    return hipLaunchKernel((const void*)&gemm_bf16_tiled_kernel<BM, BN, WAVES_M, WAVES_N, EPI>,
                            dim3((unsigned)(tiles_m * tiles_n)), dim3(WAVES_M * WAVES_N * 64), kargs,
                            0, s);
 }
 
 hipError_t launch_bf16_tiled(const GemmArgs<uint16_t>& a, hipStream_t s) {
-    return launch_cfg<256, 256, 2, 4>(a, s);
+    if (has_epilogue(a)) return launch_cfg<256, 256, 2, 4, true>(a, s);
+    return launch_cfg<256, 256, 2, 4, false>(a, s);
 }
 
 }  // namespace dg

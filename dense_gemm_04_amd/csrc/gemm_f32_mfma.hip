@@ -16,7 +16,8 @@
 //     of 4 consecutive columns at that k, which feed 4 MFMA blocks whose
 //     columns are interleaved (block j covers columns 4p + j, p = 0..15);
 //   * after the loop each lane holds 4 consecutive columns of a row, so the
-//     fused alpha/beta epilogue uses 128-bit loads and stores.
+//     fused alpha/beta epilogue (with EPI, bias and activation before the
+//     beta term) uses 128-bit loads and stores.
 //
 // Rows that are not 16-byte aligned (VEC = false) use the same 128-bit
 // accesses at 4-byte alignment, and element-wise ones only at the edges.
@@ -69,7 +70,7 @@ __device__ __forceinline__ f32x4 load4(const float* p, int valid) {
 // ws (only with SPLIT and ts.tail > 0): [counters: one int per split tile,
 // padded to 256 bytes][slots: tail x parts partial tiles of BM x BN fp32,
 // element e of thread t at e * NT + t].
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool VEC, bool SPLIT>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool VEC, bool SPLIT, bool EPI>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64)
 void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit ts,
                           unsigned char* ws) {
@@ -246,6 +247,13 @@ void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit
     }
 
     const float alpha = p.alpha, beta = p.beta;
+    float bv[NG][4];
+    if constexpr (EPI) {
+#pragma unroll
+        for (int gq = 0; gq < NG; ++gq)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bv[gq][j] = bias_at(p, n0 + wn0 + 64 * gq + 4 * pl + j);
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -259,6 +267,10 @@ void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit
                 f32x4 v;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) v[j] = alpha * acc[i][gq][j][r];
+                if constexpr (EPI) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) v[j] = activate(v[j] + bv[gq][j], p.act);
+                }
                 if (col + 4 <= N) {
                     if (beta != 0.f) {
                         const f32x4 c0 = VEC ? *reinterpret_cast<const f32x4*>(dst)
@@ -313,6 +325,14 @@ size_t tail_workspace(const TailSplit& t, int bm, int bn) {
                     (int64_t)t.tail * t.parts * bm * bn * 4);
 }
 
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool EPI>
+const void* pick_kernel(bool vec, bool split) {
+    return split ? (vec ? (const void*)&gemm_f32_mfma_kernel<BM, BN, WAVES_M, WAVES_N, true, true, EPI>
+                        : (const void*)&gemm_f32_mfma_kernel<BM, BN, WAVES_M, WAVES_N, false, true, EPI>)
+                 : (vec ? (const void*)&gemm_f32_mfma_kernel<BM, BN, WAVES_M, WAVES_N, true, false, EPI>
+                        : (const void*)&gemm_f32_mfma_kernel<BM, BN, WAVES_M, WAVES_N, false, false, EPI>);
+}
+
 template <int BM, int BN, int WAVES_M, int WAVES_N>
 hipError_t launch_tiles(const GemmArgs<float>& a, bool vec, void* ws, size_t ws_bytes, int cus,
                         hipStream_t s) {
@@ -324,11 +344,8 @@ hipError_t launch_tiles(const GemmArgs<float>& a, bool vec, void* ws, size_t ws_
     if (!split) ts = TailSplit{(int)(tiles_m * tiles_n), 0, 1, 0};
     unsigned char* wsp = split ? static_cast<unsigned char*>(ws) : nullptr;
     void* kargs[] = {&args, &tm, &tn, &ts, &wsp};
-    const void* fn = split
-        ? (vec ? (const void*)&gemm_f32_mfma_kernel<BM, BN, WAVES_M, WAVES_N, true, true>
-               : (const void*)&gemm_f32_mfma_kernel<BM, BN, WAVES_M, WAVES_N, false, true>)
-        : (vec ? (const void*)&gemm_f32_mfma_kernel<BM, BN, WAVES_M, WAVES_N, true, false>
-               : (const void*)&gemm_f32_mfma_kernel<BM, BN, WAVES_M, WAVES_N, false, false>);
+    const void* fn = has_epilogue(a) ? pick_kernel<BM, BN, WAVES_M, WAVES_N, true>(vec, split)
+                                     : pick_kernel<BM, BN, WAVES_M, WAVES_N, false>(vec, split);
     const int64_t grid = split ? (int64_t)ts.full + (int64_t)ts.tail * ts.parts : tiles_m * tiles_n;
     if (grid > kMaxGrid) return hipErrorInvalidConfiguration;
     return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(WAVES_M * WAVES_N * 64), kargs, 0, s);

@@ -8,6 +8,9 @@
 
 namespace dg {
 
+// Every launcher runs the epilogue instantiation of its kernel when the
+// arguments carry a bias or an activation (has_epilogue).
+//
 // `vec` selects 128-bit global loads/stores; the caller guarantees 16-byte
 // aligned base pointers and leading dimensions that keep every row 16-byte
 // aligned. Without it every global access is element-wise.
@@ -33,11 +36,12 @@ hipError_t launch_bf16_skinny(const GemmArgs<uint16_t>& a, bool vec, void* ws, s
 // Workspace bytes with which launch_bf16_skinny splits K (0: no split for this shape).
 size_t bf16_skinny_workspace(int64_t M, int64_t N, int64_t K);
 
-// C <- beta * C (beta == 0 writes zeros without reading C).
+// C <- act(bias[col]) + beta * C, the product-free case (beta == 0 writes
+// without reading C; without bias and activation the first term is 0).
 hipError_t launch_scale_f32(int64_t M, int64_t N, float beta, float* C, int64_t ldc,
-                            hipStream_t s);
+                            const float* bias, int act, hipStream_t s);
 hipError_t launch_scale_bf16(int64_t M, int64_t N, float beta, uint16_t* C, int64_t ldc,
-                             hipStream_t s);
+                             const uint16_t* bias, int act, hipStream_t s);
 
 // Largest M the small-M kernel accepts.
 constexpr int64_t kSkinnyMaxM = 32;

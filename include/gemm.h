@@ -32,8 +32,8 @@
  * Ownership and memory: every pointer is a DEVICE pointer owned by the
  * caller, valid on the current HIP device for the duration of the work.
  * The library keeps no reference after the work completes and allocates no
- * device memory; gemm_bf16_ws and gemm_f32_ws take a caller-owned workspace
- * instead. C must not overlap A, B or the workspace (undefined results
+ * device memory; the *_ws and *_bias_act entry points take a caller-owned
+ * workspace instead. C must not overlap A, B or the workspace (undefined results
  * otherwise).
  *
  * Streams and errors: `stream` is a hipStream_t passed as void* (NULL = the
@@ -160,6 +160,48 @@ gemm_status_t gemm_f32_ws(int64_t M, int64_t N, int64_t K, float alpha,
                           const float* A, int64_t lda, const float* B, int64_t ldb,
                           float beta, float* C, int64_t ldc,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Fused epilogues (Blackwell BF16 GEMM notes, section 3.3: GELU, residual
+ * adds and scaling are the work a GEMM epilogue takes on; Z-Turbo tuning
+ * page, section 2.1: one kernel that applies GELU in its tanh form and then
+ * adds the residual, instead of separate passes over memory):
+ *
+ *     C(i,j) <- act(alpha * sum_k A(i,k) * B(k,j) + bias[j]) + beta * C(i,j)
+ *
+ * The bias is added and the activation applied before the beta * C term,
+ * which plays the residual. Everything is formed in fp32 from the fp32
+ * accumulator and rounded once at the end (to bf16 on the bf16 path). */
+typedef enum {
+    GEMM_ACT_NONE = 0,
+    /* max(x, 0) */
+    GEMM_ACT_RELU = 1,
+    /* GELU, tanh form: 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))),
+     * evaluated in fp32 as x / (1 + exp(-2 sqrt(2/pi) (x + 0.044715 x^3))),
+     * the same function, with the hardware exp2 and reciprocal (a few ulp of
+     * relative error on top of the pre-activation's). */
+    GEMM_ACT_GELU_TANH = 2
+} gemm_act_t;
+
+/* GEMM with a bias and activation epilogue.
+ * bias: device pointer to N elements of the matrices' type (fp32, or bf16
+ *       bit patterns), element-aligned; NULL for no bias.
+ * act:  a gemm_act_t value; anything else is GEMM_ERR_INVALID_VALUE.
+ * workspace, workspace_bytes: as for gemm_f32_ws / gemm_bf16_ws (NULL and 0
+ *       for none); with one, the same shapes take the split-K paths.
+ * Shapes, alignment, streams and errors otherwise as for gemm_f32 / gemm_bf16.
+ * Special values: M == 0 or N == 0 does nothing; K == 0 or alpha == 0 stores
+ * act(bias[j]) + beta * C(i,j) without reading A or B (with no bias that is
+ * beta * C, since every activation maps 0 to 0, and beta == 1 then launches
+ * nothing); beta == 0 never reads C. With bias == NULL and GEMM_ACT_NONE the
+ * results are bit-identical to gemm_f32 / gemm_bf16 (and their _ws forms). */
+gemm_status_t gemm_f32_bias_act(int64_t M, int64_t N, int64_t K, float alpha,
+                                const float* A, int64_t lda, const float* B, int64_t ldb,
+                                float beta, float* C, int64_t ldc, const float* bias, int act,
+                                void* workspace, size_t workspace_bytes, void* stream);
+gemm_status_t gemm_bf16_bias_act(int64_t M, int64_t N, int64_t K, float alpha,
+                                 const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                                 float beta, uint16_t* C, int64_t ldc, const uint16_t* bias,
+                                 int act, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Host-only planning (no HIP call): the variant a call with these arguments
  * would run (a gemm_variant_t value; GEMM_VARIANT_AUTO when the call would

@@ -199,3 +199,34 @@ def test_f32_workspace_validation(lib):
     assert dg.gemm_f32_ws(*args, None, 64, 0) == dg.GEMM_ERR_INVALID_VALUE
     assert dg.gemm_f32_ws(*args, ws + 64, need, 0) == dg.GEMM_ERR_INVALID_VALUE
     assert dg.gemm_f32_ws(*args, ws, need - 1, 0) == dg.GEMM_ERR_INVALID_VALUE
+
+
+def test_bias_act_validation(lib):
+    """Bias alignment, activation code and workspace are checked before any HIP call."""
+    f32 = (300, 200, 100, 1.0, A, 100, B, 200, 0.0, C, 200)
+    bf = (300, 200, 100, 1.0, A, 100, B, 200, 0.0, C, 200)
+    bias = 0x500000
+    bad = dg.GEMM_ERR_INVALID_VALUE
+    assert dg.gemm_f32_bias_act(*f32, bias, 3, None, 0, 0) == bad
+    assert dg.gemm_f32_bias_act(*f32, bias, -1, None, 0, 0) == bad
+    assert dg.gemm_f32_bias_act(*f32, bias + 2, dg.ACT_RELU, None, 0, 0) == bad
+    assert dg.gemm_bf16_bias_act(*bf, bias + 1, dg.ACT_RELU, None, 0, 0) == bad
+    need = dg.gemm_f32_workspace_size(300, 200, 100)
+    assert dg.gemm_f32_bias_act(*f32, bias, dg.ACT_RELU, 0x400000, need - 1, 0) == bad
+    assert dg.gemm_f32_bias_act(*f32, bias, dg.ACT_RELU, None, 64, 0) == bad
+    # Product-free calls: with no bias and beta == 1 nothing runs; a bias needs C.
+    assert dg.gemm_f32_bias_act(4, 4, 0, 1.0, None, 4, None, 4, 1.0, None, 4, None,
+                                dg.ACT_GELU_TANH, None, 0, 0) == dg.GEMM_OK
+    assert dg.gemm_f32_bias_act(4, 4, 0, 1.0, None, 4, None, 4, 1.0, None, 4, bias,
+                                dg.ACT_GELU_TANH, None, 0, 0) == bad
+    assert dg.gemm_bf16_bias_act(0, 4, 4, 1.0, None, 4, None, 4, 0.0, None, 4, None,
+                                 dg.ACT_RELU, None, 0, 0) == dg.GEMM_OK
+
+
+def test_bias_act_without_gpu_reports_unsupported_device(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    st = dg.gemm_bf16_bias_act(64, 64, 64, 1.0, A, 64, B, 64, 0.0, C, 64, 0x500000,
+                               dg.ACT_GELU_TANH, None, 0, 0)
+    assert st == dg.GEMM_ERR_UNSUPPORTED_DEVICE

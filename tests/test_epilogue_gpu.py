@@ -1,0 +1,177 @@
+"""GPU parity of the bias + activation epilogue entry points (gemm_f32_bias_act,
+gemm_bf16_bias_act) against the oracle's epilogue form, through every kernel
+family: the bf16 tiled kernel, the bf16 and fp32 kernels on unaligned rows,
+the small-M kernels (vector, split-K and element-wise), the fp32 split-K tail
+and the product-free path (K == 0 or alpha == 0). Without a bias and with
+GEMM_ACT_NONE the results must be bit-identical to the plain entry points.
+"""
+import pytest
+import torch
+
+import dense_gemm_04_amd as dg
+import gemm_inputs as gi
+import oracle
+from gpu_util import note, padded, to_f64, tol
+
+pytestmark = pytest.mark.gpu
+
+ACTS = {"none": dg.ACT_NONE, "relu": dg.ACT_RELU, "gelu_tanh": dg.ACT_GELU_TANH}
+
+
+def run_epi(dtype, A, B, C0, bias, act, alpha, beta, ld_pad=(0, 0, 0), offset=0, ws=False,
+            plain=False):
+    """C = act(alpha*A@B + bias) + beta*C0 through the C ABI; returns (C, status)."""
+    M, K = A.shape
+    N = B.shape[1]
+    lda, ldb, ldc = max(K, 1) + ld_pad[0], max(N, 1) + ld_pad[1], max(N, 1) + ld_pad[2]
+    _, a = padded(M, K, lda, dtype, offset, fill=float("nan"))
+    _, b = padded(K, N, ldb, dtype, offset, fill=float("nan"))
+    _, c = padded(M, N, ldc, dtype, offset, fill=float("nan"))
+    if M and K:
+        a.copy_(A.cuda())
+    if K and N:
+        b.copy_(B.cuda())
+    if C0 is not None:
+        c.copy_(C0.cuda())
+    bias_buf, bias_ptr = None, None
+    if bias is not None:
+        bias_buf = torch.full((N + offset + 8,), float("nan"), dtype=bias.dtype, device="cuda")
+        bias_buf[offset:offset + N].copy_(bias.cuda())
+        bias_ptr = bias_buf[offset:].data_ptr()
+    size_fn = dg.gemm_f32_workspace_size if dtype == "f32" else dg.gemm_bf16_workspace_size
+    nbytes = size_fn(M, N, K) if ws else 0
+    wbuf = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    if plain:
+        fn = dg.gemm_f32 if dtype == "f32" else dg.gemm_bf16
+        st = fn(M, N, K, float(alpha), a.data_ptr(), lda, b.data_ptr(), ldb, float(beta),
+                c.data_ptr(), ldc, 0)
+    else:
+        fn = dg.gemm_f32_bias_act if dtype == "f32" else dg.gemm_bf16_bias_act
+        st = fn(M, N, K, float(alpha), a.data_ptr(), lda, b.data_ptr(), ldb, float(beta),
+                c.data_ptr(), ldc, bias_ptr, ACTS[act], wbuf.data_ptr() if nbytes else None,
+                nbytes, 0)
+    torch.cuda.synchronize()
+    return c.cpu(), st, nbytes
+
+
+def oracle_epi(dtype, A, B, C0, bias, act, alpha, beta, rows=None, cols=None):
+    return oracle.gemm(gi.as_numpy(A), gi.as_numpy(B),
+                       None if (C0 is None or beta == 0) else gi.as_numpy(C0),
+                       float(alpha), float(beta), dtype, rows=rows, cols=cols,
+                       bias=None if bias is None else gi.as_numpy(bias), act=act)
+
+
+def inputs(dtype, M, N, K, seed, with_c0=True):
+    A = gi.random_matrix(M, K, dtype, seed, dist="n")
+    B = gi.random_matrix(K, N, dtype, seed + 1)
+    C0 = gi.random_matrix(M, N, dtype, seed + 2) if with_c0 else None
+    bias = gi.random_matrix(1, N, dtype, seed + 3)[0].contiguous()
+    return A, B, C0, bias
+
+
+# (dtype, (M, N, K), ld_pad, workspace): one case per kernel family and edge.
+CASES = [
+    ("bf16", (300, 520, 200), (0, 0, 0), False),     # tiled kernel, ragged M and K
+    ("bf16", (257, 264, 130), (8, 8, 8), False),     # tiled kernel, padded 16-byte rows
+    ("bf16", (130, 200, 129), (1, 3, 5), False),     # unaligned rows: general kernel
+    ("bf16", (16, 520, 300), (0, 0, 0), False),      # small-M vector kernel
+    ("bf16", (32, 72, 130), (0, 0, 0), False),       # small-M vector kernel, two row blocks
+    ("bf16", (16, 1032, 2000), (0, 0, 0), True),     # small-M split-K
+    ("bf16", (5, 100, 77), (1, 1, 1), False),        # small-M element-wise kernel
+    ("f32", (300, 264, 100), (0, 0, 0), False),      # fp32 MFMA, aligned
+    ("f32", (257, 130, 65), (1, 3, 5), False),       # fp32 MFMA, unaligned rows
+    ("f32", (300, 200, 100), (0, 0, 0), True),       # fp32 split-K tail
+    ("f32", (513, 384, 1000), (4, 8, 12), True),     # fp32 split-K tail, padded rows
+]
+
+
+def _case_id(c):
+    return f"{c[0]}_{'x'.join(map(str, c[1]))}_pad{c[2][0]}" + ("_ws" if c[3] else "")
+
+
+@pytest.mark.parametrize("case", CASES, ids=_case_id)
+@pytest.mark.parametrize("act", ["none", "relu", "gelu_tanh"])
+def test_bias_act_parity(case, act):
+    dtype, (M, N, K), pad, ws = case
+    for rep, (alpha, beta, with_bias) in enumerate(((1.0, 0.0, True), (0.5, 2.0, True),
+                                                    (-1.25, 1.0, False))):
+        seed = 3100 + 7 * M + N + rep
+        A, B, C0, bias = inputs(dtype, M, N, K, seed, with_c0=beta != 0)
+        bias = bias if with_bias else None
+        note(f"bias_act {dtype} M={M} N={N} K={K} pad={pad} ws={ws} act={act} "
+             f"alpha={alpha} beta={beta} bias={with_bias}")
+        C, st, nbytes = run_epi(dtype, A, B, C0, bias, act, alpha, beta, pad, ws=ws)
+        assert st == dg.GEMM_OK, dg.gemm_status_string(st)
+        assert nbytes > 0 or not ws
+        R, D = oracle_epi(dtype, A, B, C0, bias, act, alpha, beta)
+        err = oracle.max_rel_err(to_f64(C), R, D)
+        assert err <= tol(dtype), f"call {rep}: max error ratio {err:.3e}"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("act", ["relu", "gelu_tanh"])
+def test_product_free_epilogue(dtype, act):
+    """K == 0 and alpha == 0 store act(bias) + beta * C0 without reading A or B."""
+    M, N = 37, 45
+    _, _, C0, bias = inputs(dtype, M, N, 1, 3500)
+    for K, alpha, beta in ((0, 1.0, 0.5), (20, 0.0, 1.0), (0, 1.0, 0.0)):
+        A = gi.random_matrix(M, K, dtype, 3510)
+        B = gi.random_matrix(K, N, dtype, 3511)
+        note(f"bias_act product-free {dtype} K={K} alpha={alpha} beta={beta} act={act}")
+        C, st, _ = run_epi(dtype, A, B, C0 if beta else None, bias, act, alpha, beta)
+        assert st == dg.GEMM_OK
+        R, D = oracle_epi(dtype, A, B, C0, bias, act, alpha, beta)
+        assert oracle.max_rel_err(to_f64(C), R, D) <= tol(dtype)
+
+
+@pytest.mark.parametrize("case", [("bf16", (300, 520, 200), (0, 0, 0)),
+                                  ("bf16", (130, 200, 129), (1, 3, 5)),
+                                  ("bf16", (16, 520, 300), (0, 0, 0)),
+                                  ("bf16", (5, 100, 77), (1, 1, 1)),
+                                  ("f32", (300, 264, 100), (0, 0, 0)),
+                                  ("f32", (257, 130, 65), (1, 3, 5))],
+                         ids=lambda c: f"{c[0]}_{'x'.join(map(str, c[1]))}_pad{c[2][0]}")
+def test_identity_epilogue_is_bit_identical_to_plain(case):
+    dtype, (M, N, K), pad = case
+    A, B, C0, _ = inputs(dtype, M, N, K, 3600 + M)
+    note(f"bias_act identity vs plain {dtype} M={M} N={N} K={K} pad={pad}")
+    C1, st1, _ = run_epi(dtype, A, B, C0, None, "none", 0.75, -0.5, pad)
+    C2, st2, _ = run_epi(dtype, A, B, C0, None, "none", 0.75, -0.5, pad, plain=True)
+    assert st1 == st2 == dg.GEMM_OK
+    iv = torch.int32 if dtype == "f32" else torch.int16
+    assert torch.equal(C1.view(iv), C2.view(iv))
+
+
+def test_misaligned_bias_and_bad_act_rejected():
+    M, N, K = 64, 64, 64
+    A, B, C0, bias = inputs("bf16", M, N, K, 3700)
+    note("bias_act argument checks")
+    c = torch.zeros(M, N, dtype=torch.bfloat16, device="cuda")
+    a, b = A.cuda(), B.cuda()
+    bb = torch.zeros(N + 1, dtype=torch.bfloat16, device="cuda")
+    st = dg.gemm_bf16_bias_act(M, N, K, 1.0, a.data_ptr(), K, b.data_ptr(), N, 0.0,
+                               c.data_ptr(), N, bb.data_ptr() + 1, dg.ACT_RELU, None, 0, 0)
+    assert st == dg.GEMM_ERR_INVALID_VALUE
+    st = dg.gemm_bf16_bias_act(M, N, K, 1.0, a.data_ptr(), K, b.data_ptr(), N, 0.0,
+                               c.data_ptr(), N, bb.data_ptr(), 7, None, 0, 0)
+    assert st == dg.GEMM_ERR_INVALID_VALUE
+    torch.cuda.synchronize()
+    assert int(c.view(torch.int16).abs().sum()) == 0          # nothing was launched
+
+
+def test_projection_gelu_full_size_sampled():
+    """The 8192 x 12288 x 4096 projection (beta = 1 residual) with bias + GELU,
+    in the launch configuration the benchmark times, on sampled entries."""
+    w = gi.WORKLOADS[4]
+    d = gi.make(w)
+    bias = gi.random_matrix(1, w.N, "bf16", 1000 * w.wid + 4)[0].contiguous()
+    note("bias_act bf16 8192x12288x4096 gelu_tanh full size")
+    C, st, _ = run_epi("bf16", d["A"], d["B"], d["C0"], bias, "gelu_tanh", w.alpha, w.beta)
+    assert st == dg.GEMM_OK
+    g = torch.Generator().manual_seed(3801)
+    rows = sorted(set(torch.randint(0, w.M, (48,), generator=g).tolist()) | {0, w.M - 1})
+    cols = sorted(set(torch.randint(0, w.N, (48,), generator=g).tolist()) | {0, w.N - 1})
+    R, D = oracle_epi("bf16", d["A"], d["B"], d["C0"], bias, "gelu_tanh", w.alpha, w.beta,
+                      rows=rows, cols=cols)
+    Cs = to_f64(C[rows][:, cols])
+    assert oracle.max_rel_err(Cs, R, D) <= tol("bf16")
