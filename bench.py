@@ -44,6 +44,10 @@ def tflops(flops: float, seconds: float) -> float:
 
 SETTLE_SECONDS = 0.25
 
+# Workloads also timed with the fused bias + GELU epilogue (--only, --all):
+# the fp32 4096^3 SGEMM and the bf16 projection with its beta = 1 residual.
+EPILOGUE_WORKLOADS = (2, 4)
+
 
 def _time_calls(call, steps: int, warmup: int, stream, settle: float = SETTLE_SECONDS):
     """Seconds per call over `steps` calls, after the GPU has settled and
@@ -70,10 +74,11 @@ def _time_calls(call, steps: int, warmup: int, stream, settle: float = SETTLE_SE
     return start.elapsed_time(end) / 1e3 / steps     # seconds per call
 
 
-def _device_call(w, sets: int = 1, use_ws: bool = False):
+def _device_call(w, sets: int = 1, use_ws: bool = False, act=None):
     """Allocate `sets` independent operand sets on the GPU and return a callable
-    that runs the library on the next set each time (through gemm_bf16_ws with
-    a zeroed workspace when `use_ws`)."""
+    that runs the library on the next set each time (through gemm_*_ws with a
+    zeroed workspace when `use_ws`; through gemm_*_bias_act with a seeded bias
+    vector and activation `act` when `act` is given)."""
     import torch
     import dense_gemm_04_amd as dg
     import gemm_inputs as gi
@@ -98,6 +103,14 @@ def _device_call(w, sets: int = 1, use_ws: bool = False):
         def fn(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream):
             return ws_fn(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                          ws.data_ptr() if nbytes else None, nbytes, stream)
+    if act is not None:
+        bias = gi.random_matrix(1, w.N, w.dtype, 1000 * w.wid + 4)[0].cuda()
+        epi_fn = dg.gemm_f32_bias_act if w.dtype == "f32" else dg.gemm_bf16_bias_act
+        code = {v: k for k, v in dg.ACT_NAMES.items()}[act]
+
+        def fn(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream):
+            return epi_fn(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias.data_ptr(), code,
+                          None, 0, stream)
 
     def call():
         A, B, C = bufs[state["i"] % sets]
@@ -109,11 +122,15 @@ def _device_call(w, sets: int = 1, use_ws: bool = False):
     return call, stream, inp
 
 
-def measure(w, steps: int, warmup: int, sets: int = 1, use_ws: bool = False) -> dict:
-    call, stream, _ = _device_call(w, sets, use_ws)
+def measure(w, steps: int, warmup: int, sets: int = 1, use_ws: bool = False, act=None) -> dict:
+    call, stream, _ = _device_call(w, sets, use_ws, act)
     sec = _time_calls(call, steps, warmup, stream)
     ws_name = "gemm_f32_ws" if w.dtype == "f32" else "gemm_bf16_ws"
-    out = {"workload": w.name + (f" ({ws_name}, split-K)" if use_ws else ""),
+    epi_name = "gemm_f32_bias_act" if w.dtype == "f32" else "gemm_bf16_bias_act"
+    label = f" ({ws_name}, split-K)" if use_ws else ""
+    if act is not None:
+        label = f" ({epi_name}, bias + {act})"
+    out = {"workload": w.name + label,
            "dtype": w.dtype, "M": w.M, "N": w.N, "K": w.K,
            "alpha": w.alpha, "beta": w.beta, "ms": sec * 1e3,
            "tflops": tflops(gemm_flops(w.M, w.N, w.K), sec),
@@ -187,7 +204,8 @@ def main(argv=None) -> int:
     ap.add_argument("--all", action="store_true", help="one JSON line per workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", type=int, default=None,
-                    help="time one workload id (1, 2, 3, 4, 51, 52) and print its line")
+                    help="time one workload id (1, 2, 3, 4, 51, 52) and print its line "
+                         "(with the split-K line for 51 and 52, the bias + GELU line for 2 and 4)")
     ap.add_argument("--copy-mib", type=int, default=None,
                     help="time a plain device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args(argv)
@@ -221,6 +239,8 @@ def main(argv=None) -> int:
         if args.only in (51, 52):
             print(json.dumps(measure(w, args.steps, args.warmup, 4 if args.only == 52 else 1,
                                      use_ws=True)), flush=True)
+        if args.only in EPILOGUE_WORKLOADS:
+            print(json.dumps(measure(w, args.steps, args.warmup, act="gelu_tanh")), flush=True)
         return 0
 
     if args.all:
@@ -233,6 +253,9 @@ def main(argv=None) -> int:
             print(json.dumps(r), flush=True)
             if wid in (51, 52):
                 print(json.dumps(measure(w, args.steps, args.warmup, sets, use_ws=True)),
+                      flush=True)
+            if wid in EPILOGUE_WORKLOADS:
+                print(json.dumps(measure(w, args.steps, args.warmup, sets, act="gelu_tanh")),
                       flush=True)
         return 0
 
