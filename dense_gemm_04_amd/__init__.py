@@ -34,9 +34,13 @@ ACT_RELU = 1
 ACT_GELU_TANH = 2
 ACT_NAMES = {0: "none", 1: "relu", 2: "gelu_tanh"}
 
+OP_N = 0
+OP_T = 1
+
 EXPORTS = ("gemm_f32", "gemm_bf16", "gemm_f32_ex", "gemm_bf16_ex", "gemm_bf16_ws",
            "gemm_bf16_workspace_size", "gemm_f32_ws", "gemm_f32_workspace_size",
-           "gemm_f32_bias_act", "gemm_bf16_bias_act", "gemm_plan", "gemm_status_string")
+           "gemm_f32_bias_act", "gemm_bf16_bias_act", "gemm_f32_op", "gemm_bf16_op", "gemm_plan",
+           "gemm_status_string")
 
 _lib = None
 
@@ -70,6 +74,9 @@ def load() -> ctypes.CDLL:
     for name in ("gemm_f32_bias_act", "gemm_bf16_bias_act"):
         fn = getattr(lib, name)
         fn.restype, fn.argtypes = ci, base[:11] + [vp, ci, vp, ctypes.c_size_t, vp]
+    for name in ("gemm_f32_op", "gemm_bf16_op"):
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = ci, [ci, ci] + base[:11] + [vp, ci, vp, ctypes.c_size_t, vp]
     for name in ("gemm_bf16_workspace_size", "gemm_f32_workspace_size"):
         fn = getattr(lib, name)
         fn.restype, fn.argtypes = ctypes.c_size_t, [i64, i64, i64]
@@ -127,6 +134,18 @@ def gemm_bf16_bias_act(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, act, 
                        workspace_bytes=0, stream=0) -> int:
     return load().gemm_bf16_bias_act(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, act,
                                      workspace, workspace_bytes, stream)
+
+
+def gemm_f32_op(opa, opb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias=None, act=0,
+                workspace=None, workspace_bytes=0, stream=0) -> int:
+    return load().gemm_f32_op(opa, opb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, act,
+                              workspace, workspace_bytes, stream)
+
+
+def gemm_bf16_op(opa, opb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias=None, act=0,
+                 workspace=None, workspace_bytes=0, stream=0) -> int:
+    return load().gemm_bf16_op(opa, opb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, act,
+                               workspace, workspace_bytes, stream)
 
 
 def gemm_plan(elem_bytes, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, variant=0) -> int:

@@ -43,17 +43,20 @@ bool span_ok(int esz, int64_t rows, int64_t cols, int64_t ld) {
 }
 
 // Returns true when the arguments are valid (header: GEMM_ERR_INVALID_VALUE).
+// With ta, A is stored K x M (lda >= M); with tb, B is stored N x K (ldb >= K).
 bool valid_args(int esz, int64_t M, int64_t N, int64_t K, float alpha, const void* A,
                 int64_t lda, const void* B, int64_t ldb, float beta, const void* C,
-                int64_t ldc) {
+                int64_t ldc, bool ta = false, bool tb = false) {
     if (M < 0 || N < 0 || K < 0) return false;
     if (M > INT_MAX || N > INT_MAX || K > INT_MAX) return false;
-    if (lda < max1(K) || ldb < max1(N) || ldc < max1(N)) return false;
+    if (lda < max1(ta ? M : K) || ldb < max1(tb ? K : N) || ldc < max1(N)) return false;
     const Work w = work_of(M, N, K, alpha, beta);
     if (w != Work::kNone && C == nullptr) return false;
     if (w == Work::kGemm && (A == nullptr || B == nullptr)) return false;
     if (!span_ok(esz, M, N, ldc)) return false;
-    if (w == Work::kGemm && (!span_ok(esz, M, K, lda) || !span_ok(esz, K, N, ldb))) return false;
+    const bool a_ok = ta ? span_ok(esz, K, M, lda) : span_ok(esz, M, K, lda);
+    const bool b_ok = tb ? span_ok(esz, N, K, ldb) : span_ok(esz, K, N, ldb);
+    if (w == Work::kGemm && (!a_ok || !b_ok)) return false;
     if (!aligned(A, esz) || !aligned(B, esz) || !aligned(C, esz)) return false;
     return true;
 }
@@ -67,11 +70,12 @@ bool vector_ok(int esz, const void* A, int64_t lda, const void* B, int64_t ldb,
 }
 
 // The kernel family for a valid call that has GEMM work, or -1 if the
-// requested family cannot run it.
-int choose(int esz, int64_t M, bool vec, int variant) {
+// requested family cannot run it. The small-M kernel reads row-major A and B
+// only; transposed operands go to the tiled kernels.
+int choose(int esz, int64_t M, bool vec, int variant, bool trans = false) {
     switch (variant) {
         case GEMM_VARIANT_AUTO:
-            if (esz == 2 && M <= dg::kSkinnyMaxM) return GEMM_VARIANT_SKINNY;
+            if (esz == 2 && M <= dg::kSkinnyMaxM && !trans) return GEMM_VARIANT_SKINNY;
             return vec ? GEMM_VARIANT_MFMA : GEMM_VARIANT_GENERAL;
         case GEMM_VARIANT_MFMA:
             return vec ? GEMM_VARIANT_MFMA : -1;
@@ -88,12 +92,12 @@ int choose(int esz, int64_t M, bool vec, int variant) {
 
 int plan_impl(int esz, int64_t M, int64_t N, int64_t K, float alpha, const void* A,
               int64_t lda, const void* B, int64_t ldb, float beta, const void* C,
-              int64_t ldc, int variant) {
+              int64_t ldc, int variant, bool ta = false, bool tb = false) {
     if (esz != 2 && esz != 4) return -1;
     if (variant < GEMM_VARIANT_AUTO || variant > GEMM_VARIANT_SKINNY) return -1;
-    if (!valid_args(esz, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc)) return -1;
+    if (!valid_args(esz, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, ta, tb)) return -1;
     if (work_of(M, N, K, alpha, beta) != Work::kGemm) return GEMM_VARIANT_AUTO;
-    return choose(esz, M, vector_ok(esz, A, lda, B, ldb, C, ldc), variant);
+    return choose(esz, M, vector_ok(esz, A, lda, B, ldb, C, ldc), variant, ta || tb);
 }
 
 // Per-device cache of "is this a gfx950" (0 unknown, 1 yes, 2 no) and of its
@@ -122,6 +126,9 @@ gemm_status_t check_device(int* cus) {
     return state == 1 ? GEMM_OK : GEMM_ERR_UNSUPPORTED_DEVICE;
 }
 
+// Operation codes of the *_op entry points (gemm_op_t).
+bool valid_op(int op) { return op == GEMM_OP_N || op == GEMM_OP_T; }
+
 // Shared argument check of the workspace entry points.
 bool workspace_ok(const void* ws, size_t bytes, size_t need) {
     if (ws == nullptr) return bytes == 0;
@@ -137,9 +144,10 @@ template <typename T>
 gemm_status_t run(int64_t M, int64_t N, int64_t K, float alpha, const T* A, int64_t lda,
                   const T* B, int64_t ldb, float beta, T* C, int64_t ldc, void* stream,
                   int variant, void* ws = nullptr, size_t ws_bytes = 0,
-                  const T* bias = nullptr, int act = GEMM_ACT_NONE) {
+                  const T* bias = nullptr, int act = GEMM_ACT_NONE, bool ta = false,
+                  bool tb = false) {
     constexpr int esz = (int)sizeof(T);
-    const int v = plan_impl(esz, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, variant);
+    const int v = plan_impl(esz, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, variant, ta, tb);
     if (v < 0) return GEMM_ERR_INVALID_VALUE;
     if (!valid_epilogue(esz, bias, act)) return GEMM_ERR_INVALID_VALUE;
     const Work w = work_of(M, N, K, alpha, beta, bias);
@@ -154,7 +162,7 @@ gemm_status_t run(int64_t M, int64_t N, int64_t K, float alpha, const T* A, int6
         if constexpr (esz == 4) e = dg::launch_scale_f32(M, N, beta, C, ldc, bias, act, s);
         else e = dg::launch_scale_bf16(M, N, beta, C, ldc, bias, act, s);
     } else {
-        dg::GemmArgs<T> a{M, N, K, alpha, beta, A, lda, B, ldb, C, ldc, bias, act};
+        dg::GemmArgs<T> a{M, N, K, alpha, beta, A, lda, B, ldb, C, ldc, bias, act, ta, tb};
         const bool vec = vector_ok(esz, A, lda, B, ldb, C, ldc);
         if constexpr (esz == 4) {
             e = (v == GEMM_VARIANT_VALU) ? dg::launch_f32_valu(a, vec, s)
@@ -230,6 +238,29 @@ gemm_status_t gemm_bf16_bias_act(int64_t M, int64_t N, int64_t K, float alpha,
         return GEMM_ERR_INVALID_VALUE;
     return run<uint16_t>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, GEMM_VARIANT_AUTO,
                          workspace, workspace_bytes, bias, act);
+}
+
+gemm_status_t gemm_f32_op(int opa, int opb, int64_t M, int64_t N, int64_t K, float alpha,
+                          const float* A, int64_t lda, const float* B, int64_t ldb, float beta,
+                          float* C, int64_t ldc, const float* bias, int act, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    if (!valid_op(opa) || !valid_op(opb)) return GEMM_ERR_INVALID_VALUE;
+    if (!workspace_ok(workspace, workspace_bytes, gemm_f32_workspace_size(M, N, K)))
+        return GEMM_ERR_INVALID_VALUE;
+    return run<float>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, GEMM_VARIANT_AUTO,
+                      workspace, workspace_bytes, bias, act, opa == GEMM_OP_T, opb == GEMM_OP_T);
+}
+
+gemm_status_t gemm_bf16_op(int opa, int opb, int64_t M, int64_t N, int64_t K, float alpha,
+                           const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                           float beta, uint16_t* C, int64_t ldc, const uint16_t* bias, int act,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    if (!valid_op(opa) || !valid_op(opb)) return GEMM_ERR_INVALID_VALUE;
+    if (!workspace_ok(workspace, workspace_bytes, gemm_bf16_workspace_size(M, N, K)))
+        return GEMM_ERR_INVALID_VALUE;
+    return run<uint16_t>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, GEMM_VARIANT_AUTO,
+                         workspace, workspace_bytes, bias, act, opa == GEMM_OP_T,
+                         opb == GEMM_OP_T);
 }
 
 gemm_status_t gemm_f32(int64_t M, int64_t N, int64_t K, float alpha, const float* A,

@@ -23,6 +23,9 @@ struct GemmArgs {
     T* C; int64_t ldc;
     const T* bias = nullptr;
     int act = 0;
+    // Transposed storage: A(i,k) = A[k*lda + i] (A is K x M) when ta, and
+    // B(k,j) = B[j*ldb + k] (B is N x K) when tb.
+    bool ta = false, tb = false;
 };
 
 // 128-bit vectors at addresses aligned only to their element (4 or 2 bytes).

@@ -37,6 +37,12 @@
 // and the epilogue stores only in-range elements. Rows that are not 16-byte
 // aligned (VEC = false) use the same 128-bit accesses at 2-byte alignment and
 // element-wise ones only at the edges.
+//
+// Transposed operands (TA: A stored K x M; TB: B stored N x K) only change the
+// global loads: an operand whose memory rows run along k (row-major A,
+// transposed B) is loaded in 8-element chunks of a row, one whose rows run
+// along m or n (row-major B, transposed A) in 8 x 8 blocks that are transposed
+// in registers. Both land k-contiguous in LDS, so the MFMA loop is the same.
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -86,7 +92,7 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&x)[8], u32x4 (&y)[8])
     }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool VEC, bool EPI>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool VEC, bool EPI, bool TA, bool TB>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64)
 void gemm_bf16_mfma_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
     constexpr int NT = WAVES_M * WAVES_N * 64;
@@ -98,6 +104,9 @@ void gemm_bf16_mfma_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
     static_assert(A_CHUNKS * NT == BM * (kBK / 8), "A slab must split evenly");
     static_assert(B_BLOCKS * NT == (kBK / 8) * (BN / 8), "B slab must split evenly");
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be 16-aligned");
+    // A transposed A uses the block loader and a transposed B the chunk
+    // loader; with BM == BN both take 8 registers of 16 bytes per thread.
+    static_assert(BM == BN && A_CHUNKS == 8 * B_BLOCKS, "loaders share register shapes");
 
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
 
@@ -110,49 +119,76 @@ void gemm_bf16_mfma_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
     u32x4 ra[A_CHUNKS];
     u32x4 rb[B_BLOCKS][8];
 
-    auto gload = [&](int64_t k0) {
+    // Chunk loader (memory rows along k): thread t's chunk i is tile row
+    // t / 8 + i * NT / 8 (of `extent` rows from r0), k chunk t % 8.
+    auto load_chunks = [&](const uint16_t* base, int64_t ld, int64_t extent, int64_t r0,
+                           int64_t k0, u32x4* regs) {
 #pragma unroll
         for (int i = 0; i < A_CHUNKS; ++i) {
             const int r = t / 8 + i * (NT / 8), c = t % 8;
-            const int64_t gm = m0 + r, gk = k0 + 8 * c;
-            int valid = (gm < M) ? (int)(K - gk < 8 ? K - gk : 8) : 0;
-            const uint16_t* src = p.A + (valid > 0 ? gm * p.lda + gk : 0);
-            ra[i] = load8<VEC>(src, valid);
+            const int64_t gm = r0 + r, gk = k0 + 8 * c;
+            int valid = (gm < extent) ? (int)(K - gk < 8 ? K - gk : 8) : 0;
+            const uint16_t* src = base + (valid > 0 ? gm * ld + gk : 0);
+            regs[i] = load8<VEC>(src, valid);
         }
+    };
+    // Block loader (memory rows along m or n): thread t's block bi is the 8 x 8
+    // block (kb, nb) of the 64 x BN slab; register r holds its row k = 8 kb + r.
+    auto load_blocks = [&](const uint16_t* base, int64_t ld, int64_t extent, int64_t c0,
+                           int64_t k0, u32x4 (*regs)[8]) {
 #pragma unroll
         for (int bi = 0; bi < B_BLOCKS; ++bi) {
             const int blk = t + bi * NT;
             const int kb = blk / (BN / 8), nb = blk % (BN / 8);
-            const int64_t gn = n0 + 8 * nb;
-            const int nvalid = (int)(N - gn < 8 ? (N - gn < 0 ? 0 : N - gn) : 8);
+            const int64_t gn = c0 + 8 * nb;
+            const int nvalid = (int)(extent - gn < 8 ? (extent - gn < 0 ? 0 : extent - gn) : 8);
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
                 const int64_t gk = k0 + 8 * kb + r;
                 const int valid = gk < K ? nvalid : 0;
-                const uint16_t* src = p.B + (valid > 0 ? gk * p.ldb + gn : 0);
-                rb[bi][r] = load8<VEC>(src, valid);
+                const uint16_t* src = base + (valid > 0 ? gk * ld + gn : 0);
+                regs[bi][r] = load8<VEC>(src, valid);
             }
         }
     };
-
-    auto sstore = [&](int stage) {
-        uint16_t* As = smem + stage * STAGE;
-        uint16_t* Bs = As + BM * kBK;
+    auto store_chunks = [&](uint16_t* S, const u32x4* regs) {
 #pragma unroll
         for (int i = 0; i < A_CHUNKS; ++i) {
             const int r = t / 8 + i * (NT / 8), c = t % 8;
-            *reinterpret_cast<u32x4*>(As + lds_off(r, c)) = ra[i];
+            *reinterpret_cast<u32x4*>(S + lds_off(r, c)) = regs[i];
         }
+    };
+    auto store_blocks = [&](uint16_t* S, const u32x4 (*regs)[8]) {
 #pragma unroll
         for (int bi = 0; bi < B_BLOCKS; ++bi) {
             const int blk = t + bi * NT;
             const int kb = blk / (BN / 8), nb = blk % (BN / 8);
             u32x4 y[8];
-            transpose8x8(rb[bi], y);
+            transpose8x8(regs[bi], y);
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                *reinterpret_cast<u32x4*>(Bs + lds_off(8 * nb + j, kb)) = y[j];
+                *reinterpret_cast<u32x4*>(S + lds_off(8 * nb + j, kb)) = y[j];
         }
+    };
+    // With TA the A registers hold blocks and with TB the B registers hold
+    // chunks (same register count, viewed through the other shape).
+    u32x4 (*ra_blocks)[8] = reinterpret_cast<u32x4 (*)[8]>(ra);
+    u32x4* rb_chunks = &rb[0][0];
+
+    auto gload = [&](int64_t k0) {
+        if constexpr (TA) load_blocks(p.A, p.lda, M, m0, k0, ra_blocks);
+        else load_chunks(p.A, p.lda, M, m0, k0, ra);
+        if constexpr (TB) load_chunks(p.B, p.ldb, N, n0, k0, rb_chunks);
+        else load_blocks(p.B, p.ldb, N, n0, k0, rb);
+    };
+
+    auto sstore = [&](int stage) {
+        uint16_t* As = smem + stage * STAGE;
+        uint16_t* Bs = As + BM * kBK;
+        if constexpr (TA) store_blocks(As, ra_blocks);
+        else store_chunks(As, ra);
+        if constexpr (TB) store_chunks(Bs, rb_chunks);
+        else store_blocks(Bs, rb);
     };
 
     f32x4 acc[FM][FN];
@@ -246,6 +282,14 @@ void gemm_bf16_mfma_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
     }
 }
 
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool VEC, bool EPI>
+const void* pick_general(bool ta, bool tb) {
+    return ta ? (tb ? (const void*)&gemm_bf16_mfma_kernel<BM, BN, WAVES_M, WAVES_N, VEC, EPI, true, true>
+                    : (const void*)&gemm_bf16_mfma_kernel<BM, BN, WAVES_M, WAVES_N, VEC, EPI, true, false>)
+              : (tb ? (const void*)&gemm_bf16_mfma_kernel<BM, BN, WAVES_M, WAVES_N, VEC, EPI, false, true>
+                    : (const void*)&gemm_bf16_mfma_kernel<BM, BN, WAVES_M, WAVES_N, VEC, EPI, false, false>);
+}
+
 template <int BM, int BN, int WAVES_M, int WAVES_N>
 hipError_t launch_tiles(const GemmArgs<uint16_t>& a, bool vec, hipStream_t s) {
     const int64_t tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
@@ -254,10 +298,10 @@ hipError_t launch_tiles(const GemmArgs<uint16_t>& a, bool vec, hipStream_t s) {
     void* kargs[] = {&args, &tm, &tn};
     const bool epi = has_epilogue(a);
     const void* fn =
-        vec ? (epi ? (const void*)&gemm_bf16_mfma_kernel<BM, BN, WAVES_M, WAVES_N, true, true>
-                   : (const void*)&gemm_bf16_mfma_kernel<BM, BN, WAVES_M, WAVES_N, true, false>)
-            : (epi ? (const void*)&gemm_bf16_mfma_kernel<BM, BN, WAVES_M, WAVES_N, false, true>
-                   : (const void*)&gemm_bf16_mfma_kernel<BM, BN, WAVES_M, WAVES_N, false, false>);
+        vec ? (epi ? pick_general<BM, BN, WAVES_M, WAVES_N, true, true>(a.ta, a.tb)
+                   : pick_general<BM, BN, WAVES_M, WAVES_N, true, false>(a.ta, a.tb))
+            : (epi ? pick_general<BM, BN, WAVES_M, WAVES_N, false, true>(a.ta, a.tb)
+                   : pick_general<BM, BN, WAVES_M, WAVES_N, false, false>(a.ta, a.tb));
     if (tiles_m * tiles_n > kMaxGrid) return hipErrorInvalidConfiguration;
     return hipLaunchKernel(fn, dim3((unsigned)(tiles_m * tiles_n)), dim3(WAVES_M * WAVES_N * 64),
                            kargs, 0, s);

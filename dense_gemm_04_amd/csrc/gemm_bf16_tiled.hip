@@ -34,6 +34,13 @@
 //     columns that are never stored; k past K in the last slab is zeroed in
 //     the LDS copy of A (Z-Turbo CUDA tuning page, section 3.1: zero-filled
 //     tile edges; Blackwell notes, section 4.3: predicate the tail).
+//   * transposed operands (TA: A stored K x M; TB: B stored N x K) change only
+//     where a slab's contiguous dimension lies. An operand whose rows run
+//     along k (row-major A, transposed B) is copied and read the way A is
+//     above: [row][k] in LDS, 128-bit fragment reads, the K tail zeroed in
+//     LDS. An operand whose rows run along m or n (row-major B, transposed A)
+//     is copied and read the way B is: [k][row] in LDS, transposing reads,
+//     rows past K cut off by its descriptor.
 //
 // Operand layout of v_mfma_f32_16x16x32_bf16: lane l = p + 16 g supplies
 // X(row p, k = 8g .. 8g+7) as its first operand and Y(k = 8g .. 8g+7, col p)
@@ -86,7 +93,7 @@ __device__ __forceinline__ void lds_barrier() {
     lds_only_barrier();
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool EPI>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool EPI, bool TA, bool TB>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1)
 void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
     constexpr int kNT = WAVES_M * WAVES_N * 64;
@@ -103,10 +110,11 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
     constexpr int kDmaWaves = kWaves / 2;
     constexpr int kACopies = kAStage * 2 / 1024 / kDmaWaves;  // 1 KB LDS copies per issuing wave
     constexpr int kBCopies = kBStage * 2 / 1024 / kDmaWaves;
-    constexpr int kBRowsPerCopy = 1024 / (BN * 2);            // B rows filled by one copy
+    constexpr int kBRowsPerCopy = 1024 / (BN * 2);            // rows of a [64][BN] slab per copy
     static_assert(kACopies * kDmaWaves * 1024 == kAStage * 2, "A slab must split evenly");
     static_assert(kBCopies * kDmaWaves * 1024 == kBStage * 2, "B slab must split evenly");
     static_assert(BN == 256 || BN == 128, "B row length");
+    static_assert(BM == 256 && (!TA || BM == BN), "operand tile sizes");
     static_assert(kWTM % 16 == 0 && kWTN % 16 == 0, "wave tile");
     // One array per operand and pipeline stage, so the compiler can tell which
     // stage an LDS-destined load writes and does not make reads of the other
@@ -126,20 +134,27 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
     auto a_stage = [&](int stage) -> uint16_t* { return stage == 0 ? a_st0 : a_st1; };
     auto b_stage = [&](int stage) -> uint16_t* { return stage == 0 ? b_st0 : b_st1; };
 
-    // A descriptor: rows m0 .. min(M, m0 + 256) - 1, ending after element K of
-    // the last row (rounded up to its 16-byte chunk, which stays in its page).
-    // Rows past M therefore arrive in LDS as zeros.
+    // A descriptor (row-major A): rows m0 .. min(M, m0 + 256) - 1, ending
+    // after element K of the last row (rounded up to its 16-byte chunk, which
+    // stays in its page). Rows past M therefore arrive in LDS as zeros. The
+    // same for a transposed B (rows n0 .. of the N x K storage). Each is dead
+    // code when its operand is not k-contiguous.
     const int64_t rows_a = (M - m0 < kBM) ? M - m0 : kBM;
     (void)kNT;
     const uint32_t a_bytes = (uint32_t)((((rows_a - 1) * lda + K) * 2 + 15) & ~(int64_t)15);
     const rsrc_t a_desc = make_rsrc(p.A + m0 * lda, a_bytes);
+    const int64_t rows_bt = (N - n0 < kBN) ? N - n0 : kBN;
+    const uint32_t bt_bytes = (uint32_t)((((rows_bt - 1) * ldb + K) * 2 + 15) & ~(int64_t)15);
+    const rsrc_t bt_desc = make_rsrc(p.B + n0 * ldb, bt_bytes);
 
     // Global -> LDS copies. One buffer_load_dwordx4 ... lds moves 1 KB: lane l
     // fills bytes [16 l, 16 l + 16) of the destination, so each lane fetches
     // the global chunk that the swizzle puts at its LDS position.
-    //   A: copy I fills rows 8 I .. 8 I + 7; lane -> row 8 I + l / 8.
-    //   B: copy I fills rows R I .. R I + R - 1 (R = 1024 / row bytes);
-    //      lane -> row R I + l / (64 / R).
+    //   k-contiguous tile ([256][64], row-major A or transposed B): copy I
+    //      fills rows 8 I .. 8 I + 7; lane -> row 8 I + l / 8.
+    //   m/n-contiguous slab ([64][R], row-major B or transposed A): copy I
+    //      fills rows Q I .. Q I + Q - 1 (Q = 1024 / row bytes); lane -> row
+    //      Q I + l / (64 / Q).
     const int a_lrow = lane >> 3, a_pos = lane & 7;
     const int b_lrow = lane / (64 / kBRowsPerCopy), b_pos = lane % (64 / kBRowsPerCopy);
     auto dma = [&](int64_t kt, int stage) {
@@ -147,39 +162,79 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
         const int64_t k0 = kt * kBK;
         const uint32_t As = lds_addr(a_stage(stage));
         const uint32_t Bs = lds_addr(b_stage(stage));
+        if constexpr (!TA) {
 #pragma unroll
-        for (int i = 0; i < kACopies; ++i) {
-            const int I = wave * kACopies + i;
-            const int c = a_pos ^ a_lrow;       // (8 I + a_lrow) mod 8 == a_lrow
-            dma16(a_desc, (uint32_t)(a_lrow * lda * 2 + c * 16),
-                  (uint32_t)(((8 * I) * lda + k0) * 2), As + I * 1024);
+            for (int i = 0; i < kACopies; ++i) {
+                const int I = wave * kACopies + i;
+                const int c = a_pos ^ a_lrow;       // (8 I + a_lrow) mod 8 == a_lrow
+                dma16(a_desc, (uint32_t)(a_lrow * lda * 2 + c * 16),
+                      (uint32_t)(((8 * I) * lda + k0) * 2), As + I * 1024);
+            }
+        } else {
+            // Transposed A, slab rows k0 .. K - 1 of the K x M storage.
+            const int64_t rem = (((K - k0 - 1) * lda + (M - m0)) * 2 + 15) & ~(int64_t)15;
+            const uint32_t bytes = rem < ((int64_t)1 << 31) ? (uint32_t)rem : 0x80000000u;
+            const rsrc_t desc = make_rsrc(p.A + k0 * lda + m0, bytes);
+#pragma unroll
+            for (int i = 0; i < kACopies; ++i) {
+                const int I = wave * kACopies + i;
+                const int row = kBRowsPerCopy * I + b_lrow;
+                const int c = b_pos ^ b_swz(row);
+                dma16(desc, (uint32_t)(b_lrow * lda * 2 + c * 16),
+                      (uint32_t)((kBRowsPerCopy * I) * lda * 2), As + I * 1024);
+            }
         }
-        // B descriptor for this slab: rows k0 .. K - 1, ending after column N of
-        // row K - 1, so rows past K arrive as zeros.
-        const int64_t rem = (((K - k0 - 1) * ldb + (N - n0)) * 2 + 15) & ~(int64_t)15;
-        const uint32_t b_bytes = rem < ((int64_t)1 << 31) ? (uint32_t)rem : 0x80000000u;
-        const rsrc_t b_desc = make_rsrc(p.B + k0 * ldb + n0, b_bytes);
+        if constexpr (!TB) {
+            // B descriptor for this slab: rows k0 .. K - 1, ending after column N of
+            // row K - 1, so rows past K arrive as zeros.
+            const int64_t rem = (((K - k0 - 1) * ldb + (N - n0)) * 2 + 15) & ~(int64_t)15;
+            const uint32_t b_bytes = rem < ((int64_t)1 << 31) ? (uint32_t)rem : 0x80000000u;
+            const rsrc_t b_desc = make_rsrc(p.B + k0 * ldb + n0, b_bytes);
 #pragma unroll
-        for (int i = 0; i < kBCopies; ++i) {
-            const int I = wave * kBCopies + i;
-            const int row = kBRowsPerCopy * I + b_lrow;
-            const int c = b_pos ^ b_swz(row);
-            dma16(b_desc, (uint32_t)(b_lrow * ldb * 2 + c * 16),
-                  (uint32_t)((kBRowsPerCopy * I) * ldb * 2), Bs + I * 1024);
+            for (int i = 0; i < kBCopies; ++i) {
+                const int I = wave * kBCopies + i;
+                const int row = kBRowsPerCopy * I + b_lrow;
+                const int c = b_pos ^ b_swz(row);
+                dma16(b_desc, (uint32_t)(b_lrow * ldb * 2 + c * 16),
+                      (uint32_t)((kBRowsPerCopy * I) * ldb * 2), Bs + I * 1024);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kBCopies; ++i) {
+                const int I = wave * kBCopies + i;
+                const int c = a_pos ^ a_lrow;
+                dma16(bt_desc, (uint32_t)(a_lrow * ldb * 2 + c * 16),
+                      (uint32_t)(((8 * I) * ldb + k0) * 2), Bs + I * 1024);
+            }
         }
     };
 
-    // In the last slab of a ragged K, A(m, k >= K) would hold the next row's
-    // values: zero them in LDS (threads stride over the rows). B is already
+    // In the last slab of a ragged K, a k-contiguous tile (row-major A,
+    // transposed B) would hold the next row's values at k >= K: zero them in
+    // LDS (threads stride over the rows). An m/n-contiguous slab is already
     // zero there.
+    constexpr bool kZeroTail = !TA || TB;
     auto zero_a_tail = [&](int stage, int kr) {
-        uint16_t* As = a_stage(stage);
-        for (int row = t; row < kBM; row += kNT) {
+        if constexpr (!TA) {
+            uint16_t* As = a_stage(stage);
+            for (int row = t; row < kBM; row += kNT) {
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                if (8 * c + 8 <= kr) continue;
-                u32x4* q = reinterpret_cast<u32x4*>(As + a_off(row, c));
-                *q = mask_tail(*q, kr - 8 * c);
+                for (int c = 0; c < 8; ++c) {
+                    if (8 * c + 8 <= kr) continue;
+                    u32x4* q = reinterpret_cast<u32x4*>(As + a_off(row, c));
+                    *q = mask_tail(*q, kr - 8 * c);
+                }
+            }
+        }
+        if constexpr (TB) {
+            uint16_t* Bs = b_stage(stage);
+            for (int row = t; row < kBN; row += kNT) {
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    if (8 * c + 8 <= kr) continue;
+                    u32x4* q = reinterpret_cast<u32x4*>(Bs + a_off(row, c));
+                    *q = mask_tail(*q, kr - 8 * c);
+                }
             }
         }
     };
@@ -199,11 +254,19 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
         const uint16_t* As = a_stage(stage);
         const uint16_t* Bs = b_stage(stage);
 #pragma unroll
-        for (int i = 0; i < kFM; ++i)
-            fa[buf][i] = *reinterpret_cast<const bf16x8*>(As + a_off(wm0 + 16 * i + pl, 4 * ks + g));
+        for (int i = 0; i < kFM; ++i) {
+            if constexpr (TA)
+                fa[buf][i] = read_b_frag<BM>(As, 32 * ks + 8 * g + tr_row, wm0 + 16 * i + tr_col);
+            else
+                fa[buf][i] = *reinterpret_cast<const bf16x8*>(As + a_off(wm0 + 16 * i + pl, 4 * ks + g));
+        }
 #pragma unroll
-        for (int j = 0; j < kFN; ++j)
-            fb[buf][j] = read_b_frag<BN>(Bs, 32 * ks + 8 * g + tr_row, wn0 + 16 * j + tr_col);
+        for (int j = 0; j < kFN; ++j) {
+            if constexpr (TB)
+                fb[buf][j] = *reinterpret_cast<const bf16x8*>(Bs + a_off(wn0 + 16 * j + pl, 4 * ks + g));
+            else
+                fb[buf][j] = read_b_frag<BN>(Bs, 32 * ks + 8 * g + tr_row, wn0 + 16 * j + tr_col);
+        }
     };
     // The MFMA runs go at raised wave priority, so that a wave with matrix
     // work to issue wins the SIMD's issue slot over one that is issuing
@@ -228,7 +291,7 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
     const int k_tail = (int)(K - (nk - 1) * kBK);   // 1 .. 64
     dma(0, 0);
     lds_barrier();
-    if (nk == 1 && k_tail < kBK) {
+    if (kZeroTail && nk == 1 && k_tail < kBK) {
         zero_a_tail(0, k_tail);
         lds_barrier();
     }
@@ -241,7 +304,7 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
         mfmas(0);
         if (kt + 1 < nk) {
             lds_barrier();
-            if (kt + 2 == nk && k_tail < kBK) {
+            if (kZeroTail && kt + 2 == nk && k_tail < kBK) {
                 zero_a_tail(cur ^ 1, k_tail);
                 lds_barrier();
             }
@@ -304,10 +367,22 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
 
 }  // namespace
 
-// True when every buffer offset the tiled kernel forms fits in 31 bits.
+// True when every buffer offset the tiled kernel forms fits in 31 bits: a
+// k-contiguous tile spans 256 rows plus K elements, an m/n-contiguous slab 64
+// rows plus its tile width (at least 256 elements).
 bool bf16_tiled_fits(const GemmArgs<uint16_t>& a) {
     const int64_t lim = (int64_t)1 << 31;
-    return (256 * a.lda + a.K) * 2 < lim && (kBK * a.ldb + a.N) * 2 < lim;
+    auto kc = [&](int64_t ld) { return (256 * ld + a.K) * 2 < lim; };
+    auto mc = [&](int64_t ld, int64_t extent) { return (kBK * ld + 256 + extent) * 2 < lim; };
+    return (a.ta ? mc(a.lda, a.M) : kc(a.lda)) && (a.tb ? kc(a.ldb) : mc(a.ldb, a.N));
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool EPI>
+const void* pick_tiled(bool ta, bool tb) {
+    return ta ? (tb ? (const void*)&gemm_bf16_tiled_kernel<BM, BN, WAVES_M, WAVES_N, EPI, true, true>
+                    : (const void*)&gemm_bf16_tiled_kernel<BM, BN, WAVES_M, WAVES_N, EPI, true, false>)
+              : (tb ? (const void*)&gemm_bf16_tiled_kernel<BM, BN, WAVES_M, WAVES_N, EPI, false, true>
+                    : (const void*)&gemm_bf16_tiled_kernel<BM, BN, WAVES_M, WAVES_N, EPI, false, false>);
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool EPI>
@@ -317,7 +392,7 @@ hipError_t launch_cfg(const GemmArgs<uint16_t>& a, hipStream_t s) {
     GemmArgs<uint16_t> args = a;
     void* kargs[] = {&args, &tm, &tn};
     if (tiles_m * tiles_n > kMaxGrid) return hipErrorInvalidConfiguration;
-    return hipLaunchKernel((const void*)&gemm_bf16_tiled_kernel<BM, BN, WAVES_M, WAVES_N, EPI>,
+    return hipLaunchKernel(pick_tiled<BM, BN, WAVES_M, WAVES_N, EPI>(a.ta, a.tb),
                            dim3((unsigned)(tiles_m * tiles_n)), dim3(WAVES_M * WAVES_N * 64), kargs,
                            0, s);
 }

@@ -22,6 +22,10 @@
 // Rows that are not 16-byte aligned (VEC = false) use the same 128-bit
 // accesses at 4-byte alignment, and element-wise ones only at the edges.
 //
+// Transposed operands (TA: A stored K x M; TB: B stored N x K) are loaded as
+// 4 x 4 blocks (four 128-bit loads along the contiguous dimension) and
+// transposed in registers, so the LDS layout and the MFMA loop stay the same.
+//
 // Operand layout of v_mfma_f32_16x16x4_f32: lane l = p + 16 g supplies A(row p,
 // k_g) and B(k_g, col p) for one k per lane group g, and receives D(row 4g + i,
 // col p) in accumulator register i. A and B use the same k for each g.
@@ -70,7 +74,14 @@ __device__ __forceinline__ f32x4 load4(const float* p, int valid) {
 // ws (only with SPLIT and ts.tail > 0): [counters: one int per split tile,
 // padded to 256 bytes][slots: tail x parts partial tiles of BM x BN fp32,
 // element e of thread t at e * NT + t].
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool VEC, bool SPLIT, bool EPI>
+// 4 x 4 transpose: y[j][i] = x[i][j].
+__device__ __forceinline__ void transpose4x4(const f32x4 (&x)[4], f32x4 (&y)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) y[j] = f32x4{x[0][j], x[1][j], x[2][j], x[3][j]};
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool VEC, bool SPLIT, bool EPI, bool TA,
+          bool TB>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64)
 void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit ts,
                           unsigned char* ws) {
@@ -84,6 +95,10 @@ void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit
     static_assert(A_CHUNKS * NT == BM * (kBK / 4), "A slab must split evenly");
     static_assert(B_CHUNKS * NT == kBK * (BN / 4), "B slab must split evenly");
     static_assert(WTM % 16 == 0 && WTN % 64 == 0, "wave tile shape");
+    // The transposed loaders give each thread one 4 x 4 block of the slab.
+    static_assert(!TA || (kBK / 4) * (BM / 4) == NT, "transposed A: one block per thread");
+    static_assert(!TB || (kBK / 4) * (BN / 4) == NT, "transposed B: one block per thread");
+    static_assert(A_CHUNKS == 4 && B_CHUNKS == 4, "block loaders reuse the chunk registers");
 
     __shared__ __attribute__((aligned(16))) float smem[2 * STAGE];
 
@@ -109,37 +124,82 @@ void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit
 
     f32x4 ra[A_CHUNKS], rb[B_CHUNKS];
 
+    // Transposed A (K x M storage): thread t loads rows k0 + 4 (t / (BM / 4)) + r,
+    // r = 0..3, at columns m0 + 4 (t % (BM / 4)) .. + 3.
+    // Transposed B (N x K storage): thread t loads rows n0 + 4 (t / 8) + r at
+    // columns k0 + 4 (t % 8) .. + 3.
+    const int ta_kb = t / (BM / 4), ta_mb = t % (BM / 4);
+    const int tb_nb = t / (kBK / 4), tb_kb = t % (kBK / 4);
+
     auto gload = [&](int64_t k0) {
+        if constexpr (TA) {
+            const int64_t gm = m0 + 4 * ta_mb;
+            const int mvalid = (int)(M - gm < 4 ? (M - gm < 0 ? 0 : M - gm) : 4);
 #pragma unroll
-        for (int i = 0; i < A_CHUNKS; ++i) {
-            const int r = t / 8 + i * (NT / 8), c = t % 8;
-            const int64_t gm = m0 + r, gk = k0 + 4 * c;
-            const int valid = (gm < M) ? (int)(K - gk < 4 ? K - gk : 4) : 0;
-            ra[i] = load4<VEC>(p.A + (valid > 0 ? gm * p.lda + gk : 0), valid);
+            for (int r = 0; r < 4; ++r) {
+                const int64_t gk = k0 + 4 * ta_kb + r;
+                const int valid = gk < K ? mvalid : 0;
+                ra[r] = load4<VEC>(p.A + (valid > 0 ? gk * p.lda + gm : 0), valid);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < A_CHUNKS; ++i) {
+                const int r = t / 8 + i * (NT / 8), c = t % 8;
+                const int64_t gm = m0 + r, gk = k0 + 4 * c;
+                const int valid = (gm < M) ? (int)(K - gk < 4 ? K - gk : 4) : 0;
+                ra[i] = load4<VEC>(p.A + (valid > 0 ? gm * p.lda + gk : 0), valid);
+            }
         }
+        if constexpr (TB) {
+            const int64_t gk = k0 + 4 * tb_kb;
+            const int kvalid = (int)(K - gk < 4 ? (K - gk < 0 ? 0 : K - gk) : 4);
 #pragma unroll
-        for (int i = 0; i < B_CHUNKS; ++i) {
-            const int idx = t + i * NT;
-            const int kr = idx / (BN / 4), c = idx % (BN / 4);
-            const int64_t gk = k0 + kr, gn = n0 + 4 * c;
-            const int valid = (gk < K) ? (int)(N - gn < 4 ? N - gn : 4) : 0;
-            rb[i] = load4<VEC>(p.B + (valid > 0 ? gk * p.ldb + gn : 0), valid);
+            for (int r = 0; r < 4; ++r) {
+                const int64_t gn = n0 + 4 * tb_nb + r;
+                const int valid = gn < N ? kvalid : 0;
+                rb[r] = load4<VEC>(p.B + (valid > 0 ? gn * p.ldb + gk : 0), valid);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < B_CHUNKS; ++i) {
+                const int idx = t + i * NT;
+                const int kr = idx / (BN / 4), c = idx % (BN / 4);
+                const int64_t gk = k0 + kr, gn = n0 + 4 * c;
+                const int valid = (gk < K) ? (int)(N - gn < 4 ? N - gn : 4) : 0;
+                rb[i] = load4<VEC>(p.B + (valid > 0 ? gk * p.ldb + gn : 0), valid);
+            }
         }
     };
 
     auto sstore = [&](int stage) {
         float* As = smem + stage * STAGE;
         float* Bs = As + BM * kBK;
+        if constexpr (TA) {
+            f32x4 y[4];
+            transpose4x4(ra, y);     // y[j] = A(m0 + 4 ta_mb + j, 4 ta_kb .. + 3)
 #pragma unroll
-        for (int i = 0; i < A_CHUNKS; ++i) {
-            const int r = t / 8 + i * (NT / 8), c = t % 8;
-            *reinterpret_cast<f32x4*>(As + a_off(r, c)) = ra[i];
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<f32x4*>(As + a_off(4 * ta_mb + j, ta_kb)) = y[j];
+        } else {
+#pragma unroll
+            for (int i = 0; i < A_CHUNKS; ++i) {
+                const int r = t / 8 + i * (NT / 8), c = t % 8;
+                *reinterpret_cast<f32x4*>(As + a_off(r, c)) = ra[i];
+            }
         }
+        if constexpr (TB) {
+            f32x4 y[4];
+            transpose4x4(rb, y);     // y[j] = B(4 tb_kb + j, n0 + 4 tb_nb .. + 3)
 #pragma unroll
-        for (int i = 0; i < B_CHUNKS; ++i) {
-            const int idx = t + i * NT;
-            const int kr = idx / (BN / 4), c = idx % (BN / 4);
-            *reinterpret_cast<f32x4*>(Bs + kr * BN + 4 * c) = rb[i];
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<f32x4*>(Bs + (4 * tb_kb + j) * BN + 4 * tb_nb) = y[j];
+        } else {
+#pragma unroll
+            for (int i = 0; i < B_CHUNKS; ++i) {
+                const int idx = t + i * NT;
+                const int kr = idx / (BN / 4), c = idx % (BN / 4);
+                *reinterpret_cast<f32x4*>(Bs + kr * BN + 4 * c) = rb[i];
+            }
         }
     };
 
@@ -325,12 +385,21 @@ size_t tail_workspace(const TailSplit& t, int bm, int bn) {
                     (int64_t)t.tail * t.parts * bm * bn * 4);
 }
 
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool VEC, bool SPLIT, bool EPI>
+const void* pick_layout(bool ta, bool tb) {
+#define DG_F32_KERNEL(TA, TB) \
+    (const void*)&gemm_f32_mfma_kernel<BM, BN, WAVES_M, WAVES_N, VEC, SPLIT, EPI, TA, TB>
+    return ta ? (tb ? DG_F32_KERNEL(true, true) : DG_F32_KERNEL(true, false))
+              : (tb ? DG_F32_KERNEL(false, true) : DG_F32_KERNEL(false, false));
+#undef DG_F32_KERNEL
+}
+
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool EPI>
-const void* pick_kernel(bool vec, bool split) {
-    return split ? (vec ? (const void*)&gemm_f32_mfma_kernel<BM, BN, WAVES_M, WAVES_N, true, true, EPI>
-                        : (const void*)&gemm_f32_mfma_kernel<BM, BN, WAVES_M, WAVES_N, false, true, EPI>)
-                 : (vec ? (const void*)&gemm_f32_mfma_kernel<BM, BN, WAVES_M, WAVES_N, true, false, EPI>
-                        : (const void*)&gemm_f32_mfma_kernel<BM, BN, WAVES_M, WAVES_N, false, false, EPI>);
+const void* pick_kernel(bool vec, bool split, bool ta, bool tb) {
+    return split ? (vec ? pick_layout<BM, BN, WAVES_M, WAVES_N, true, true, EPI>(ta, tb)
+                        : pick_layout<BM, BN, WAVES_M, WAVES_N, false, true, EPI>(ta, tb))
+                 : (vec ? pick_layout<BM, BN, WAVES_M, WAVES_N, true, false, EPI>(ta, tb)
+                        : pick_layout<BM, BN, WAVES_M, WAVES_N, false, false, EPI>(ta, tb));
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N>
@@ -344,8 +413,9 @@ hipError_t launch_tiles(const GemmArgs<float>& a, bool vec, void* ws, size_t ws_
     if (!split) ts = TailSplit{(int)(tiles_m * tiles_n), 0, 1, 0};
     unsigned char* wsp = split ? static_cast<unsigned char*>(ws) : nullptr;
     void* kargs[] = {&args, &tm, &tn, &ts, &wsp};
-    const void* fn = has_epilogue(a) ? pick_kernel<BM, BN, WAVES_M, WAVES_N, true>(vec, split)
-                                     : pick_kernel<BM, BN, WAVES_M, WAVES_N, false>(vec, split);
+    const void* fn = has_epilogue(a)
+                         ? pick_kernel<BM, BN, WAVES_M, WAVES_N, true>(vec, split, a.ta, a.tb)
+                         : pick_kernel<BM, BN, WAVES_M, WAVES_N, false>(vec, split, a.ta, a.tb);
     const int64_t grid = split ? (int64_t)ts.full + (int64_t)ts.tail * ts.parts : tiles_m * tiles_n;
     if (grid > kMaxGrid) return hipErrorInvalidConfiguration;
     return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(WAVES_M * WAVES_N * 64), kargs, 0, s);

@@ -29,6 +29,8 @@
  *   - K == 0 or alpha == 0: A and B are not read; C <- beta * C
  *     (beta == 1 leaves C untouched and launches nothing).
  *
+ * gemm_f32_op and gemm_bf16_op (below) also take transposed A or B.
+ *
  * Ownership and memory: every pointer is a DEVICE pointer owned by the
  * caller, valid on the current HIP device for the duration of the work.
  * The library keeps no reference after the work completes and allocates no
@@ -202,6 +204,34 @@ gemm_status_t gemm_bf16_bias_act(int64_t M, int64_t N, int64_t K, float alpha,
                                  const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                                  float beta, uint16_t* C, int64_t ldc, const uint16_t* bias,
                                  int act, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Transposed operands: C <- act(alpha * op(A) op(B) + bias) + beta * C, where
+ * op(X) is X (GEMM_OP_N) or its transpose (GEMM_OP_T). op(A) is M x K and
+ * op(B) is K x N:
+ *   opa == GEMM_OP_N: A is M x K row-major, A(i,k) = A[i*lda + k], lda >= max(1,K);
+ *   opa == GEMM_OP_T: A is stored K x M row-major, op(A)(i,k) = A[k*lda + i],
+ *                     lda >= max(1,M);
+ *   opb == GEMM_OP_N: B is K x N row-major, B(k,j) = B[k*ldb + j], ldb >= max(1,N);
+ *   opb == GEMM_OP_T: B is stored N x K row-major, op(B)(k,j) = B[j*ldb + k],
+ *                     ldb >= max(1,K). A column-major K x N matrix with leading
+ *                     dimension ldb is exactly this storage.
+ * The backward pass of y = x W needs both forms (dx = dy W^T, dW = x^T dy),
+ * and the CUTLASS example of the Blackwell BF16 GEMM notes (section 3.3)
+ * takes B column-major. bias, act, workspace and all other rules are those of
+ * gemm_*_bias_act (with opa == opb == GEMM_OP_N the two calls are the same);
+ * an opa or opb other than the two codes is GEMM_ERR_INVALID_VALUE. The
+ * small-M kernel (M <= 32, bf16) reads row-major A and B only: transposed
+ * small-M calls run on the tiled kernels. */
+typedef enum { GEMM_OP_N = 0, GEMM_OP_T = 1 } gemm_op_t;
+
+gemm_status_t gemm_f32_op(int opa, int opb, int64_t M, int64_t N, int64_t K, float alpha,
+                          const float* A, int64_t lda, const float* B, int64_t ldb,
+                          float beta, float* C, int64_t ldc, const float* bias, int act,
+                          void* workspace, size_t workspace_bytes, void* stream);
+gemm_status_t gemm_bf16_op(int opa, int opb, int64_t M, int64_t N, int64_t K, float alpha,
+                           const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                           float beta, uint16_t* C, int64_t ldc, const uint16_t* bias, int act,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* Host-only planning (no HIP call): the variant a call with these arguments
  * would run (a gemm_variant_t value; GEMM_VARIANT_AUTO when the call would

@@ -230,3 +230,29 @@ def test_bias_act_without_gpu_reports_unsupported_device(lib):
     st = dg.gemm_bf16_bias_act(64, 64, 64, 1.0, A, 64, B, 64, 0.0, C, 64, 0x500000,
                                dg.ACT_GELU_TANH, None, 0, 0)
     assert st == dg.GEMM_ERR_UNSUPPORTED_DEVICE
+
+
+def test_op_validation(lib):
+    """Operation codes and the transposed leading-dimension rules are checked
+    before any HIP call."""
+    bad = dg.GEMM_ERR_INVALID_VALUE
+    M, N, K = 300, 200, 100
+    # op(A) = A^T: A stored K x M needs lda >= M; op(B) = B^T: B stored N x K needs ldb >= K.
+    assert dg.gemm_f32_op(1, 0, M, N, K, 1.0, A, M - 1, B, N, 0.0, C, N) == bad
+    assert dg.gemm_f32_op(0, 1, M, N, K, 1.0, A, K, B, K - 1, 0.0, C, N) == bad
+    assert dg.gemm_bf16_op(3, 0, M, N, K, 1.0, A, K, B, N, 0.0, C, N) == bad
+    assert dg.gemm_bf16_op(0, -1, M, N, K, 1.0, A, K, B, N, 0.0, C, N) == bad
+    # A K x M storage may have lda < K (e.g. a wide, short A^T).
+    st = dg.gemm_f32_op(1, 1, 8, 4, 1000, 1.0, A, 8, B, 1000, 0.0, C, 4)
+    assert st in (dg.GEMM_OK, dg.GEMM_ERR_UNSUPPORTED_DEVICE)
+    assert dg.gemm_f32_op(1, 1, 8, 4, 1000, 1.0, A, 7, B, 1000, 0.0, C, 4) == bad
+    assert dg.gemm_bf16_op(1, 1, 0, 4, 4, 1.0, None, 1, None, 4, 0.0, None, 4) == dg.GEMM_OK
+
+
+def test_op_without_gpu_reports_unsupported_device(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    for opa, opb in ((0, 0), (0, 1), (1, 0), (1, 1)):
+        st = dg.gemm_bf16_op(opa, opb, 64, 64, 64, 1.0, A, 64, B, 64, 0.0, C, 64)
+        assert st == dg.GEMM_ERR_UNSUPPORTED_DEVICE
