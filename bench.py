@@ -47,6 +47,8 @@ SETTLE_SECONDS = 0.25
 # Workloads also timed with the fused bias + GELU epilogue (--only, --all):
 # the fp32 4096^3 SGEMM and the bf16 projection with its beta = 1 residual.
 EPILOGUE_WORKLOADS = (2, 4)
+# Workloads also timed with transposed operand storage (A^T B, A B^T, A^T B^T).
+LAYOUT_WORKLOADS = (2, 3)
 
 
 def _time_calls(call, steps: int, warmup: int, stream, settle: float = SETTLE_SECONDS):
@@ -74,19 +76,21 @@ def _time_calls(call, steps: int, warmup: int, stream, settle: float = SETTLE_SE
     return start.elapsed_time(end) / 1e3 / steps     # seconds per call
 
 
-def _device_call(w, sets: int = 1, use_ws: bool = False, act=None):
+def _device_call(w, sets: int = 1, use_ws: bool = False, act=None, ops=None):
     """Allocate `sets` independent operand sets on the GPU and return a callable
     that runs the library on the next set each time (through gemm_*_ws with a
     zeroed workspace when `use_ws`; through gemm_*_bias_act with a seeded bias
-    vector and activation `act` when `act` is given)."""
+    vector and activation `act` when `act` is given; through gemm_*_op with A
+    stored K x M and/or B stored N x K when `ops` = (opa, opb) is given)."""
     import torch
     import dense_gemm_04_amd as dg
     import gemm_inputs as gi
     inp = gi.make(w)
     bufs = []
+    opa, opb = ops if ops is not None else (0, 0)
     for _ in range(sets):
-        A = inp["A"].cuda()
-        B = inp["B"].cuda()
+        A = (inp["A"].t().contiguous() if opa else inp["A"]).cuda()
+        B = (inp["B"].t().contiguous() if opb else inp["B"]).cuda()
         C = inp["C0"].cuda() if inp["C0"] is not None else torch.zeros(
             w.M, w.N, dtype=A.dtype, device="cuda")
         bufs.append((A, B, C))
@@ -112,24 +116,36 @@ def _device_call(w, sets: int = 1, use_ws: bool = False, act=None):
             return epi_fn(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias.data_ptr(), code,
                           None, 0, stream)
 
+    lda, ldb = (w.M if opa else w.K), (w.K if opb else w.N)
+    if ops is not None:
+        op_fn = dg.gemm_f32_op if w.dtype == "f32" else dg.gemm_bf16_op
+
+        def fn(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream):
+            return op_fn(opa, opb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, None, 0, None, 0,
+                         stream)
+
     def call():
         A, B, C = bufs[state["i"] % sets]
         state["i"] += 1
-        st = fn(w.M, w.N, w.K, w.alpha, A.data_ptr(), w.K, B.data_ptr(), w.N, w.beta,
+        st = fn(w.M, w.N, w.K, w.alpha, A.data_ptr(), lda, B.data_ptr(), ldb, w.beta,
                 C.data_ptr(), w.N, h)
         if st != dg.GEMM_OK:
             raise RuntimeError(f"gemm returned {st}: {dg.gemm_status_string(st)}")
     return call, stream, inp
 
 
-def measure(w, steps: int, warmup: int, sets: int = 1, use_ws: bool = False, act=None) -> dict:
-    call, stream, _ = _device_call(w, sets, use_ws, act)
+def measure(w, steps: int, warmup: int, sets: int = 1, use_ws: bool = False, act=None,
+            ops=None) -> dict:
+    call, stream, _ = _device_call(w, sets, use_ws, act, ops)
     sec = _time_calls(call, steps, warmup, stream)
     ws_name = "gemm_f32_ws" if w.dtype == "f32" else "gemm_bf16_ws"
     epi_name = "gemm_f32_bias_act" if w.dtype == "f32" else "gemm_bf16_bias_act"
     label = f" ({ws_name}, split-K)" if use_ws else ""
     if act is not None:
         label = f" ({epi_name}, bias + {act})"
+    if ops is not None:
+        op_name = "gemm_f32_op" if w.dtype == "f32" else "gemm_bf16_op"
+        label = f" ({op_name}, {'A^T' if ops[0] else 'A'} {'B^T' if ops[1] else 'B'})"
     out = {"workload": w.name + label,
            "dtype": w.dtype, "M": w.M, "N": w.N, "K": w.K,
            "alpha": w.alpha, "beta": w.beta, "ms": sec * 1e3,
@@ -205,7 +221,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", type=int, default=None,
                     help="time one workload id (1, 2, 3, 4, 51, 52) and print its line "
-                         "(with the split-K line for 51 and 52, the bias + GELU line for 2 and 4)")
+                         "(with the split-K line for 51 and 52, the bias + GELU line for 2 and 4, "
+                         "the transposed-layout lines for 2 and 3)")
     ap.add_argument("--copy-mib", type=int, default=None,
                     help="time a plain device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args(argv)
@@ -241,6 +258,9 @@ def main(argv=None) -> int:
                                      use_ws=True)), flush=True)
         if args.only in EPILOGUE_WORKLOADS:
             print(json.dumps(measure(w, args.steps, args.warmup, act="gelu_tanh")), flush=True)
+        if args.only in LAYOUT_WORKLOADS:
+            for ops in ((0, 1), (1, 0), (1, 1)):
+                print(json.dumps(measure(w, args.steps, args.warmup, ops=ops)), flush=True)
         return 0
 
     if args.all:
@@ -257,6 +277,10 @@ def main(argv=None) -> int:
             if wid in EPILOGUE_WORKLOADS:
                 print(json.dumps(measure(w, args.steps, args.warmup, sets, act="gelu_tanh")),
                       flush=True)
+            if wid in LAYOUT_WORKLOADS:
+                for ops in ((0, 1), (1, 0), (1, 1)):
+                    print(json.dumps(measure(w, args.steps, args.warmup, sets, ops=ops)),
+                          flush=True)
         return 0
 
     w = gi.WORKLOADS[2]

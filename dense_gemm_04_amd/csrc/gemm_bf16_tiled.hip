@@ -86,6 +86,14 @@ __device__ __forceinline__ bf16x8 read_b_frag(const uint16_t* Bs, int k0, int co
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// The lane index, computed afresh (mbcnt) from an operand the compiler cannot
+// see through, so that it is not kept live in a register across the main loop.
+__device__ __forceinline__ int opaque_lane() {
+    unsigned m = ~0u;
+    asm volatile("" : "+s"(m));
+    return (int)__builtin_amdgcn_mbcnt_hi(m, __builtin_amdgcn_mbcnt_lo(m, 0u));
+}
+
 // Barrier for the two-stage pipeline: this wave's LDS-destined copies have
 // landed (vmcnt 0), then an LDS-only workgroup barrier.
 __device__ __forceinline__ void lds_barrier() {
@@ -171,16 +179,22 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
                       (uint32_t)(((8 * I) * lda + k0) * 2), As + I * 1024);
             }
         } else {
-            // Transposed A, slab rows k0 .. K - 1 of the K x M storage.
+            // Transposed A, slab rows k0 .. K - 1 of the K x M storage. The
+            // per-copy lane offsets are recomputed here from an opaque copy
+            // of the lane index rather than kept live across the loop: with
+            // both operands copied this way they would not fit in registers,
+            // and a spilled offset's reload waits for every copy in flight.
             const int64_t rem = (((K - k0 - 1) * lda + (M - m0)) * 2 + 15) & ~(int64_t)15;
             const uint32_t bytes = rem < ((int64_t)1 << 31) ? (uint32_t)rem : 0x80000000u;
             const rsrc_t desc = make_rsrc(p.A + k0 * lda + m0, bytes);
+            const int ln = opaque_lane();
+            const int lrow = ln / (64 / kBRowsPerCopy), pos = ln % (64 / kBRowsPerCopy);
 #pragma unroll
             for (int i = 0; i < kACopies; ++i) {
                 const int I = wave * kACopies + i;
-                const int row = kBRowsPerCopy * I + b_lrow;
-                const int c = b_pos ^ b_swz(row);
-                dma16(desc, (uint32_t)(b_lrow * lda * 2 + c * 16),
+                const int row = kBRowsPerCopy * I + lrow;
+                const int c = pos ^ b_swz(row);
+                dma16(desc, (uint32_t)(lrow * lda * 2 + c * 16),
                       (uint32_t)((kBRowsPerCopy * I) * lda * 2), As + I * 1024);
             }
         }
@@ -190,13 +204,28 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
             const int64_t rem = (((K - k0 - 1) * ldb + (N - n0)) * 2 + 15) & ~(int64_t)15;
             const uint32_t b_bytes = rem < ((int64_t)1 << 31) ? (uint32_t)rem : 0x80000000u;
             const rsrc_t b_desc = make_rsrc(p.B + k0 * ldb + n0, b_bytes);
+            if constexpr (TA) {
+                // Both operands copied as m/n-contiguous slabs: recompute the
+                // lane offsets here too (see the transposed A copies).
+                const int ln = opaque_lane();
+                const int lrow = ln / (64 / kBRowsPerCopy), pos = ln % (64 / kBRowsPerCopy);
 #pragma unroll
-            for (int i = 0; i < kBCopies; ++i) {
-                const int I = wave * kBCopies + i;
-                const int row = kBRowsPerCopy * I + b_lrow;
-                const int c = b_pos ^ b_swz(row);
-                dma16(b_desc, (uint32_t)(b_lrow * ldb * 2 + c * 16),
-                      (uint32_t)((kBRowsPerCopy * I) * ldb * 2), Bs + I * 1024);
+                for (int i = 0; i < kBCopies; ++i) {
+                    const int I = wave * kBCopies + i;
+                    const int row = kBRowsPerCopy * I + lrow;
+                    const int c = pos ^ b_swz(row);
+                    dma16(b_desc, (uint32_t)(lrow * ldb * 2 + c * 16),
+                          (uint32_t)((kBRowsPerCopy * I) * ldb * 2), Bs + I * 1024);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < kBCopies; ++i) {
+                    const int I = wave * kBCopies + i;
+                    const int row = kBRowsPerCopy * I + b_lrow;
+                    const int c = b_pos ^ b_swz(row);
+                    dma16(b_desc, (uint32_t)(b_lrow * ldb * 2 + c * 16),
+                          (uint32_t)((kBRowsPerCopy * I) * ldb * 2), Bs + I * 1024);
+                }
             }
         } else {
 #pragma unroll
