@@ -47,8 +47,9 @@ SETTLE_SECONDS = 0.25
 # Workloads also timed with the fused bias + GELU epilogue (--only, --all):
 # the fp32 4096^3 SGEMM and the bf16 projection with its beta = 1 residual.
 EPILOGUE_WORKLOADS = (2, 4)
-# Workloads also timed with transposed operand storage (A^T B, A B^T, A^T B^T).
-LAYOUT_WORKLOADS = (2, 3)
+# Workloads also timed with transposed operand storage (A^T B, A B^T, A^T B^T);
+# the small-M workload with B stored N x K (a weight kept as [out][in]), split-K.
+LAYOUT_WORKLOADS = {2: ((0, 1), (1, 0), (1, 1)), 3: ((0, 1), (1, 0), (1, 1)), 52: ((0, 1),)}
 
 
 def _time_calls(call, steps: int, warmup: int, stream, settle: float = SETTLE_SECONDS):
@@ -119,10 +120,13 @@ def _device_call(w, sets: int = 1, use_ws: bool = False, act=None, ops=None):
     lda, ldb = (w.M if opa else w.K), (w.K if opb else w.N)
     if ops is not None:
         op_fn = dg.gemm_f32_op if w.dtype == "f32" else dg.gemm_bf16_op
+        op_size = dg.gemm_f32_workspace_size if w.dtype == "f32" else dg.gemm_bf16_workspace_size
+        op_bytes = op_size(w.M, w.N, w.K) if use_ws else 0
+        op_ws = torch.zeros(max(op_bytes, 1), dtype=torch.uint8, device="cuda")
 
         def fn(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream):
-            return op_fn(opa, opb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, None, 0, None, 0,
-                         stream)
+            return op_fn(opa, opb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, None, 0,
+                         op_ws.data_ptr() if op_bytes else None, op_bytes, stream)
 
     def call():
         A, B, C = bufs[state["i"] % sets]
@@ -145,7 +149,8 @@ def measure(w, steps: int, warmup: int, sets: int = 1, use_ws: bool = False, act
         label = f" ({epi_name}, bias + {act})"
     if ops is not None:
         op_name = "gemm_f32_op" if w.dtype == "f32" else "gemm_bf16_op"
-        label = f" ({op_name}, {'A^T' if ops[0] else 'A'} {'B^T' if ops[1] else 'B'})"
+        label = (f" ({op_name}, {'A^T' if ops[0] else 'A'} {'B^T' if ops[1] else 'B'}"
+                 + (", split-K)" if use_ws else ")"))
     out = {"workload": w.name + label,
            "dtype": w.dtype, "M": w.M, "N": w.N, "K": w.K,
            "alpha": w.alpha, "beta": w.beta, "ms": sec * 1e3,
@@ -222,7 +227,7 @@ def main(argv=None) -> int:
     ap.add_argument("--only", type=int, default=None,
                     help="time one workload id (1, 2, 3, 4, 51, 52) and print its line "
                          "(with the split-K line for 51 and 52, the bias + GELU line for 2 and 4, "
-                         "the transposed-layout lines for 2 and 3)")
+                         "the transposed-layout lines for 2, 3 and 52)")
     ap.add_argument("--copy-mib", type=int, default=None,
                     help="time a plain device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args(argv)
@@ -259,8 +264,9 @@ def main(argv=None) -> int:
         if args.only in EPILOGUE_WORKLOADS:
             print(json.dumps(measure(w, args.steps, args.warmup, act="gelu_tanh")), flush=True)
         if args.only in LAYOUT_WORKLOADS:
-            for ops in ((0, 1), (1, 0), (1, 1)):
-                print(json.dumps(measure(w, args.steps, args.warmup, ops=ops)), flush=True)
+            for ops in LAYOUT_WORKLOADS[args.only]:
+                print(json.dumps(measure(w, args.steps, args.warmup, 4 if args.only == 52 else 1,
+                                         use_ws=args.only == 52, ops=ops)), flush=True)
         return 0
 
     if args.all:
@@ -278,9 +284,9 @@ def main(argv=None) -> int:
                 print(json.dumps(measure(w, args.steps, args.warmup, sets, act="gelu_tanh")),
                       flush=True)
             if wid in LAYOUT_WORKLOADS:
-                for ops in ((0, 1), (1, 0), (1, 1)):
-                    print(json.dumps(measure(w, args.steps, args.warmup, sets, ops=ops)),
-                          flush=True)
+                for ops in LAYOUT_WORKLOADS[wid]:
+                    print(json.dumps(measure(w, args.steps, args.warmup, sets, use_ws=wid == 52,
+                                             ops=ops)), flush=True)
         return 0
 
     w = gi.WORKLOADS[2]

@@ -70,12 +70,13 @@ bool vector_ok(int esz, const void* A, int64_t lda, const void* B, int64_t ldb,
 }
 
 // The kernel family for a valid call that has GEMM work, or -1 if the
-// requested family cannot run it. The small-M kernel reads row-major A and B
-// only; transposed operands go to the tiled kernels.
-int choose(int esz, int64_t M, bool vec, int variant, bool trans = false) {
+// requested family cannot run it. The small-M kernel reads row-major A and
+// either a row-major B or, with 16-byte rows, a transposed one; other
+// transposed small-M calls go to the tiled kernels.
+int choose(int esz, int64_t M, bool vec, int variant, bool ta = false, bool tb = false) {
     switch (variant) {
         case GEMM_VARIANT_AUTO:
-            if (esz == 2 && M <= dg::kSkinnyMaxM && !trans) return GEMM_VARIANT_SKINNY;
+            if (esz == 2 && M <= dg::kSkinnyMaxM && !ta && (!tb || vec)) return GEMM_VARIANT_SKINNY;
             return vec ? GEMM_VARIANT_MFMA : GEMM_VARIANT_GENERAL;
         case GEMM_VARIANT_MFMA:
             return vec ? GEMM_VARIANT_MFMA : -1;
@@ -97,7 +98,7 @@ int plan_impl(int esz, int64_t M, int64_t N, int64_t K, float alpha, const void*
     if (variant < GEMM_VARIANT_AUTO || variant > GEMM_VARIANT_SKINNY) return -1;
     if (!valid_args(esz, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, ta, tb)) return -1;
     if (work_of(M, N, K, alpha, beta) != Work::kGemm) return GEMM_VARIANT_AUTO;
-    return choose(esz, M, vector_ok(esz, A, lda, B, ldb, C, ldc), variant, ta || tb);
+    return choose(esz, M, vector_ok(esz, A, lda, B, ldb, C, ldc), variant, ta, tb);
 }
 
 // Per-device cache of "is this a gfx950" (0 unknown, 1 yes, 2 no) and of its

@@ -15,6 +15,10 @@
 // as zeros through the descriptor bounds; the ragged K tail of A is masked in
 // registers.
 //
+// Transposed B (TB: B stored N x K, the layout of a weight matrix kept as
+// [out][in]) takes the same vector kernel: a chunk is then 64 rows of B's
+// storage (one per output column) times 128 k, copied and read the way A is.
+//
 // Element-wise path (any alignment): one workgroup per 32-column strip and
 // all of K; 8 x 8 blocks of B are read with predicated loads, transposed in
 // registers and written k-contiguous to a double-buffered LDS tile; A
@@ -251,7 +255,7 @@ __device__ __forceinline__ void store_row4(const GemmArgs<uint16_t>& p, int64_t 
 
 // ws (only used when wk.segs > 1): [counters: one int per strip, padded to
 // 256 bytes][slots: segs x strips tiles of 16 MB x 64 fp32, slot s * strips + strip].
-template <int MB, bool EPI>
+template <int MB, bool EPI, bool TB>
 __global__ __launch_bounds__(kNT, 1)
 void gemm_bf16_smallm_kernel(GemmArgs<uint16_t> p, SmallMWork wk, unsigned char* ws) {
     using S = SmallM<MB>;
@@ -274,6 +278,11 @@ void gemm_bf16_smallm_kernel(GemmArgs<uint16_t> p, SmallMWork wk, unsigned char*
     // (rounded up to its 16-byte chunk), so rows past M arrive as zeros.
     const uint32_t a_bytes = (uint32_t)((((M - 1) * lda + K) * 2 + 15) & ~(int64_t)15);
     const rsrc_t a_desc = make_rsrc(p.A, a_bytes);
+    // Transposed B: rows n0 .. min(N, n0 + 64) - 1 of the N x K storage, the
+    // same way (dead code without TB).
+    const int64_t rows_bt = N - n0 < kVBN ? N - n0 : kVBN;
+    const uint32_t bt_bytes = (uint32_t)((((rows_bt - 1) * ldb + K) * 2 + 15) & ~(int64_t)15);
+    const rsrc_t bt_desc = make_rsrc(p.B + n0 * ldb, bt_bytes);
 
     // Copies are 1 KB; lane l fills bytes [16 l, 16 l + 16) of the slot, and
     // each copy's whole offset sits in the per-lane offset, which the
@@ -282,19 +291,30 @@ void gemm_bf16_smallm_kernel(GemmArgs<uint16_t> p, SmallMWork wk, unsigned char*
     //      slot l % 8 holding 16-byte chunk (l % 8) ^ b_swz(row).
     //   A: copy J fills rows 4 J .. 4 J + 3; lane -> row 4 J + l / 16, slot
     //      l % 16 holding chunk (l % 16) ^ (row % 16).
+    //   Transposed B ([64 n][128 k] chunks): as A.
     auto dma = [&](int64_t chunk, int stage) {
         const int64_t k0 = chunk * kVKC;
-        const int64_t rem = (((K - k0 - 1) * ldb + (N - n0)) * 2 + 15) & ~(int64_t)15;
-        const uint32_t b_bytes = rem < ((int64_t)1 << 31) ? (uint32_t)rem : 0x80000000u;
-        const rsrc_t b_desc = make_rsrc(p.B + k0 * ldb + n0, b_bytes);
         const uint32_t Bs = lds_addr(lds_b + stage * S::kBStage);
         const uint32_t As = lds_addr(lds_a + stage * S::kAStage);
+        if constexpr (TB) {
 #pragma unroll
-        for (int i = 0; i < S::kBCopies; ++i) {
-            const int I = wave * S::kBCopies + i;
-            const int row = 8 * I + (lane >> 3);
-            const int c = (lane & 7) ^ b_swz(row);
-            dma16(b_desc, (uint32_t)(row * ldb * 2 + c * 16), 0, Bs + I * 1024);
+            for (int i = 0; i < S::kBCopies; ++i) {
+                const int J = wave * S::kBCopies + i;
+                const int row = 4 * J + (lane >> 4);
+                const int c = (lane & 15) ^ (row & 15);
+                dma16(bt_desc, (uint32_t)((row * ldb + k0 + c * 8) * 2), 0, Bs + J * 1024);
+            }
+        } else {
+            const int64_t rem = (((K - k0 - 1) * ldb + (N - n0)) * 2 + 15) & ~(int64_t)15;
+            const uint32_t b_bytes = rem < ((int64_t)1 << 31) ? (uint32_t)rem : 0x80000000u;
+            const rsrc_t b_desc = make_rsrc(p.B + k0 * ldb + n0, b_bytes);
+#pragma unroll
+            for (int i = 0; i < S::kBCopies; ++i) {
+                const int I = wave * S::kBCopies + i;
+                const int row = 8 * I + (lane >> 3);
+                const int c = (lane & 7) ^ b_swz(row);
+                dma16(b_desc, (uint32_t)(row * ldb * 2 + c * 16), 0, Bs + I * 1024);
+            }
         }
 #pragma unroll
         for (int i = 0; i < S::kACopies; ++i) {
@@ -322,20 +342,28 @@ void gemm_bf16_smallm_kernel(GemmArgs<uint16_t> p, SmallMWork wk, unsigned char*
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
                 fa[mb] = *reinterpret_cast<const bf16x8*>(As + a_off(16 * mb + pl, 4 * ks + g));
-            // Rows 32 ks + 8 g + tr_row and 4 further down; columns 16 wave + 4 q.
-            const int r0 = 32 * ks + 8 * g + tr_row, r1 = r0 + 4;
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4*)(Bs + r0 * kVBN + ((tr_c ^ b_swz(r0)) << 3) + tr_in));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4*)(Bs + r1 * kVBN + ((tr_c ^ b_swz(r1)) << 3) + tr_in));
-            const bf16x8 fb = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            bf16x8 fb;
+            if constexpr (TB) {
+                // B(k = 32 ks + 8 g .. + 7, n = 16 wave + pl): one 128-bit read of row n.
+                fb = *reinterpret_cast<const bf16x8*>(Bs + a_off(16 * wave + pl, 4 * ks + g));
+            } else {
+                // Rows 32 ks + 8 g + tr_row and 4 further down; columns 16 wave + 4 q.
+                const int r0 = 32 * ks + 8 * g + tr_row, r1 = r0 + 4;
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4*)(Bs + r0 * kVBN + ((tr_c ^ b_swz(r0)) << 3) + tr_in));
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4*)(Bs + r1 * kVBN + ((tr_c ^ b_swz(r1)) << 3) + tr_in));
+                fb = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
             const int64_t kfirst = chunk * kVKC + 32 * ks + 8 * g;   // k of this lane's first element
             if (kfirst + 8 > K) {
-                // Ragged K: A(m, k >= K) holds the next row's values.
+                // Ragged K: A(m, k >= K) holds the next row's values, and so
+                // does a transposed B(k >= K, n).
                 const int valid = kfirst >= K ? 0 : (int)(K - kfirst);
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb)
                     fa[mb] = __builtin_bit_cast(bf16x8, mask_tail(__builtin_bit_cast(u32x4, fa[mb]), valid));
+                if constexpr (TB) fb = __builtin_bit_cast(bf16x8, mask_tail(__builtin_bit_cast(u32x4, fb), valid));
             }
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
@@ -347,8 +375,18 @@ void gemm_bf16_smallm_kernel(GemmArgs<uint16_t> p, SmallMWork wk, unsigned char*
     // chunk c each wave waits for its own copies of chunk c (later ones may
     // stay in flight), then the barrier publishes chunk c and retires all
     // reads of chunk c - 1, whose slot the copy for chunk c + kStages - 1 reuses.
+    //
+    // With a transposed B, the strips' row blocks lie 64 rows (1 MB at
+    // K = 8192) apart, so strips walking their chunks in step would all read
+    // at the same offset within their rows. Each group of 8 strips (one per
+    // XCD) therefore starts its segment one chunk later than the group
+    // before, wrapping around: measured 36.6 -> 29.2 us at 16 x 8192 x 8192.
+    // Row-major B reads contiguous rows across strips and keeps the plain
+    // order (a rotation measured slower there).
+    const int64_t rot = TB ? (int64_t)(strip >> 3) % nc : 0;
+    auto rc = [&](int64_t c) { return cb + (c + rot >= nc ? c + rot - nc : c + rot); };
     const int64_t pre = nc < S::kStages - 1 ? nc : S::kStages - 1;
-    for (int64_t c = 0; c < pre; ++c) dma(cb + c, (int)c);
+    for (int64_t c = 0; c < pre; ++c) dma(rc(c), (int)c);
     int stage = 0;
     for (int64_t c = 0; c < nc; ++c) {
         if (c + S::kStages - 2 <= nc - 1)
@@ -356,8 +394,8 @@ void gemm_bf16_smallm_kernel(GemmArgs<uint16_t> p, SmallMWork wk, unsigned char*
         else
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         lds_only_barrier();
-        if (c + S::kStages - 1 < nc) dma(cb + c + S::kStages - 1, stage == 0 ? S::kStages - 1 : stage - 1);
-        compute(cb + c, stage);
+        if (c + S::kStages - 1 < nc) dma(rc(c + S::kStages - 1), stage == 0 ? S::kStages - 1 : stage - 1);
+        compute(rc(c), stage);
         stage = stage + 1 == S::kStages ? 0 : stage + 1;
     }
 
@@ -441,10 +479,12 @@ static SmallMWork plan_smallm(int64_t N, int64_t K, bool split) {
 
 // True when every buffer offset the vector kernel forms fits in 31 bits: A
 // copies reach row 31 (rows past M included) and one chunk past K; B copies
-// reach 128 rows below a chunk's first row.
+// reach 128 rows below a chunk's first row, or with a transposed B row 63 of
+// the strip and one chunk past K.
 static bool smallm_fits(const GemmArgs<uint16_t>& a) {
     const int64_t lim = (int64_t)1 << 31;
-    return (32 * a.lda + a.K + kVKC) * 2 < lim && (kVKC * a.ldb + a.N) * 2 < lim;
+    const bool b_ok = a.tb ? (kVBN * a.ldb + a.K + kVKC) * 2 < lim : (kVKC * a.ldb + a.N) * 2 < lim;
+    return (32 * a.lda + a.K + kVKC) * 2 < lim && b_ok;
 }
 
 size_t bf16_skinny_workspace(int64_t M, int64_t N, int64_t K) {
@@ -460,16 +500,20 @@ hipError_t launch_bf16_skinny(const GemmArgs<uint16_t>& a, bool vec, void* ws, s
                               hipStream_t s) {
     GemmArgs<uint16_t> args = a;
     const bool epi = has_epilogue(a);
+    // A transposed B is read only by the vector kernel; otherwise the tiled
+    // kernels take the call.
+    if (a.tb && !(vec && smallm_fits(a))) return launch_bf16_mfma(a, vec, s);
     if (vec && smallm_fits(a)) {
         const size_t need = bf16_skinny_workspace(a.M, a.N, a.K);
         const bool split = ws != nullptr && need > 0 && ws_bytes >= need;
         SmallMWork w = plan_smallm(a.N, a.K, split);
         unsigned char* wsp = split ? static_cast<unsigned char*>(ws) : nullptr;
         void* kargs[] = {&args, &w, &wsp};
-        const void* fn = epi ? (a.M <= 16 ? (const void*)&gemm_bf16_smallm_kernel<1, true>
-                                          : (const void*)&gemm_bf16_smallm_kernel<2, true>)
-                             : (a.M <= 16 ? (const void*)&gemm_bf16_smallm_kernel<1, false>
-                                          : (const void*)&gemm_bf16_smallm_kernel<2, false>);
+#define DG_SMALLM(MB, EPI) (a.tb ? (const void*)&gemm_bf16_smallm_kernel<MB, EPI, true> \
+                              : (const void*)&gemm_bf16_smallm_kernel<MB, EPI, false>)
+        const void* fn = epi ? (a.M <= 16 ? DG_SMALLM(1, true) : DG_SMALLM(2, true))
+                             : (a.M <= 16 ? DG_SMALLM(1, false) : DG_SMALLM(2, false));
+#undef DG_SMALLM
         if ((int64_t)w.strips * w.segs > kMaxGrid) return hipErrorInvalidConfiguration;
         return hipLaunchKernel(fn, dim3((unsigned)(w.strips * w.segs)), dim3(kNT), kargs, 0, s);
     }

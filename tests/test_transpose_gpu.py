@@ -85,7 +85,7 @@ SHAPES = [
     ((300, 520, 200), (0, 0, 0)),     # vector kernels, ragged M, N and K
     ((257, 264, 136), (8, 8, 8)),     # padded 16-byte rows
     ((130, 200, 129), (1, 3, 5)),     # unaligned rows
-    ((16, 264, 300), (0, 0, 0)),      # small M (bf16: tiled kernel, not the small-M one)
+    ((16, 264, 300), (0, 0, 0)),      # small M (bf16: small-M kernel for A B and A B^T)
     ((1, 1, 1), (0, 0, 0)),
     ((3, 5, 7), (0, 0, 0)),
     ((64, 1, 65), (0, 0, 0)),
@@ -166,3 +166,50 @@ def test_op_full_size_sampled(dtype, ops):
     cols = sorted(set(torch.randint(0, w.N, (40,), generator=g).tolist()) | {0, w.N - 1})
     R, D = oracle_op(dtype, d["A"], d["B"], None, 1.0, 0.0, rows=rows, cols=cols)
     assert oracle.max_rel_err(to_f64(C[rows][:, cols]), R, D) <= tol(dtype)
+
+
+# Small M with B stored N x K (x W^T with W kept as [out][in]): the small-M
+# vector kernel reads the transposed B directly; unaligned rows fall back to
+# the tiled kernels.
+SMALL_M_TB = [((16, 520, 300), (0, 0, 0), False), ((32, 72, 130), (0, 0, 0), False),
+              ((1, 1032, 4104), (0, 0, 0), True), ((17, 64, 1000), (0, 0, 0), True),
+              ((5, 200, 77), (8, 8, 8), False), ((5, 100, 77), (1, 1, 1), False),
+              ((3, 1024, 8200), (0, 0, 0), True)]
+
+
+@pytest.mark.parametrize("case", SMALL_M_TB,
+                         ids=lambda c: "x".join(map(str, c[0])) + f"_pad{c[1][0]}" + ("_ws" if c[2] else ""))
+def test_small_m_transposed_b(case):
+    (M, N, K), pad, ws = case
+    for rep, (alpha, beta) in enumerate(((1.0, 0.0), (0.5, 2.0))):
+        nbytes = check("bf16", 0, 1, M, N, K, 4800 + M + rep, alpha, beta, pad, ws=ws)
+        assert nbytes > 0 or not ws
+    check("bf16", 0, 1, M, N, K, 4850 + M, 1.0, 1.0, pad, bias=True, act="gelu_tanh", ws=ws)
+
+
+def test_small_m_transposed_b_is_deterministic():
+    """Repeated calls give the same bits, with and without split K (partials
+    are added in a fixed order; each strip's chunk order is fixed)."""
+    M, N, K = 16, 1032, 4104
+    A = gi.random_matrix(M, K, "bf16", 4900, dist="n")
+    B = gi.random_matrix(K, N, "bf16", 4901)
+    for ws in (False, True):
+        note(f"gemm_bf16_op NT small M determinism ws={ws}")
+        first, st, _ = run_op("bf16", 0, 1, A, B, None, 1.0, 0.0, ws=ws)
+        assert st == dg.GEMM_OK
+        for _ in range(2):
+            again, st, _ = run_op("bf16", 0, 1, A, B, None, 1.0, 0.0, ws=ws)
+            assert st == dg.GEMM_OK
+            assert torch.equal(first.view(torch.int16), again.view(torch.int16))
+
+
+def test_small_m_transposed_b_full_size():
+    """16 x 8192 x 8192 with B stored N x K, split-K, as the benchmark times it."""
+    w = gi.WORKLOADS[52]
+    d = gi.make(w)
+    note("gemm_bf16_op NT 16x8192x8192 full size, split-K")
+    C, st, nbytes = run_op("bf16", 0, 1, d["A"], d["B"], None, 1.0, 0.0, ws=True)
+    assert st == dg.GEMM_OK and nbytes > 0
+    cols = list(range(0, w.N, 61)) + [w.N - 1]
+    R, D = oracle_op("bf16", d["A"], d["B"], None, 1.0, 0.0, cols=cols)
+    assert oracle.max_rel_err(to_f64(C[:, cols]), R, D) <= tol("bf16")
