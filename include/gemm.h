@@ -236,7 +236,10 @@ gemm_status_t gemm_bf16_op(int opa, int opb, int64_t M, int64_t N, int64_t K, fl
 /* Host-only planning (no HIP call): the variant a call with these arguments
  * would run (a gemm_variant_t value; GEMM_VARIANT_AUTO when the call would
  * launch no GEMM kernel), or -1 when the arguments are invalid. `elem_bytes`
- * is 4 (fp32) or 2 (bf16); pointers are used only for their alignment. */
+ * is 4 (fp32) or 2 (bf16); pointers are used only for their alignment. The
+ * operands are taken as row-major (gemm_f32 / gemm_bf16 / their _ex forms);
+ * with transposed operands (gemm_*_op) a bf16 small-M call may run on the
+ * tiled families instead (see gemm_bf16_op). */
 int gemm_plan(int elem_bytes, int64_t M, int64_t N, int64_t K, float alpha,
               const void* A, int64_t lda, const void* B, int64_t ldb,
               float beta, const void* C, int64_t ldc, int variant);
