@@ -69,6 +69,13 @@ bool vector_ok(int esz, const void* A, int64_t lda, const void* B, int64_t ldb,
            ldb % per == 0 && ldc % per == 0;
 }
 
+// Whether the small-M kernels take M rows: the vector kernel (16-byte rows)
+// up to kSkinnyMaxM, also with a transposed B; the element-wise one up to
+// kSkinnyElemMaxM, row-major B only.
+bool small_m_ok(int64_t M, bool vec, bool tb) {
+    return vec ? M <= dg::kSkinnyMaxM : (!tb && M <= dg::kSkinnyElemMaxM);
+}
+
 // The kernel family for a valid call that has GEMM work, or -1 if the
 // requested family cannot run it. The small-M kernel reads row-major A and
 // either a row-major B or, with 16-byte rows, a transposed one; other
@@ -76,7 +83,7 @@ bool vector_ok(int esz, const void* A, int64_t lda, const void* B, int64_t ldb,
 int choose(int esz, int64_t M, bool vec, int variant, bool ta = false, bool tb = false) {
     switch (variant) {
         case GEMM_VARIANT_AUTO:
-            if (esz == 2 && M <= dg::kSkinnyMaxM && !ta && (!tb || vec)) return GEMM_VARIANT_SKINNY;
+            if (esz == 2 && !ta && small_m_ok(M, vec, tb)) return GEMM_VARIANT_SKINNY;
             return vec ? GEMM_VARIANT_MFMA : GEMM_VARIANT_GENERAL;
         case GEMM_VARIANT_MFMA:
             return vec ? GEMM_VARIANT_MFMA : -1;
@@ -85,7 +92,7 @@ int choose(int esz, int64_t M, bool vec, int variant, bool ta = false, bool tb =
         case GEMM_VARIANT_VALU:
             return esz == 4 ? GEMM_VARIANT_VALU : -1;
         case GEMM_VARIANT_SKINNY:
-            return (esz == 2 && M <= dg::kSkinnyMaxM) ? GEMM_VARIANT_SKINNY : -1;
+            return (esz == 2 && small_m_ok(M, vec, false)) ? GEMM_VARIANT_SKINNY : -1;
         default:
             return -1;
     }

@@ -1,4 +1,4 @@
-// Small-M bf16 GEMM (M <= 32): C = alpha * A * B + beta * C with fp32
+// Small-M bf16 GEMM (M <= 128): C = alpha * A * B + beta * C with fp32
 // accumulation, for the inference shapes where a few rows of activations meet
 // a large weight matrix. The Blackwell BF16 GEMM notes (section 5.2) point out
 // that such GEMMs reuse almost nothing and are bound by reading B, so the aim
@@ -196,10 +196,12 @@ constexpr int kVKC = 128;                // k rows per chunk
 constexpr int kMaxWorkgroups = 256;      // one per compute unit
 constexpr int kMaxSegments = 64;
 
+// MB 16-row blocks of A (M <= 16 MB). The ring takes what LDS allows: 6, 5,
+// 4 and 3 stages of 20, 24, 32 and 48 KB for MB = 1, 2, 4, 8.
 template <int MB> struct SmallM {
     static constexpr int kBStage = kVKC * kVBN;           // bf16, [128][64] row-major
     static constexpr int kAStage = 16 * MB * kVKC;        // bf16, [16 MB][128]
-    static constexpr int kStages = MB == 1 ? 6 : 5;       // 120 KB of ring
+    static constexpr int kStages = MB == 1 ? 6 : MB == 2 ? 5 : MB == 4 ? 4 : 3;
     static constexpr int kBCopies = kBStage * 2 / 1024 / (kNT / 64);   // 1 KB copies per wave
     static constexpr int kACopies = kAStage * 2 / 1024 / (kNT / 64);
     static constexpr int kCopies = kBCopies + kACopies;
@@ -477,21 +479,24 @@ static SmallMWork plan_smallm(int64_t N, int64_t K, bool split) {
     return w;
 }
 
+// Row blocks of 16 for M rows: 1, 2, 4 or 8.
+static int smallm_blocks(int64_t M) { return M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8; }
+
 // True when every buffer offset the vector kernel forms fits in 31 bits: A
-// copies reach row 31 (rows past M included) and one chunk past K; B copies
-// reach 128 rows below a chunk's first row, or with a transposed B row 63 of
-// the strip and one chunk past K.
+// copies reach row 16 MB - 1 (rows past M included) and one chunk past K; B
+// copies reach 128 rows below a chunk's first row, or with a transposed B row
+// 63 of the strip and one chunk past K.
 static bool smallm_fits(const GemmArgs<uint16_t>& a) {
     const int64_t lim = (int64_t)1 << 31;
     const bool b_ok = a.tb ? (kVBN * a.ldb + a.K + kVKC) * 2 < lim : (kVKC * a.ldb + a.N) * 2 < lim;
-    return (32 * a.lda + a.K + kVKC) * 2 < lim && b_ok;
+    return (16 * smallm_blocks(a.M) * a.lda + a.K + kVKC) * 2 < lim && b_ok;
 }
 
 size_t bf16_skinny_workspace(int64_t M, int64_t N, int64_t K) {
     if (M < 1 || M > kSkinnyMaxM || N < 1 || K < 1) return 0;
     const SmallMWork w = plan_smallm(N, K, true);
     if (w.segs < 2) return 0;
-    const int64_t mb = M <= 16 ? 1 : 2;
+    const int64_t mb = smallm_blocks(M);
     return (size_t)((((int64_t)w.strips * 4 + 255) & ~(int64_t)255) +
                     (int64_t)w.segs * w.strips * 16 * mb * kVBN * 4);
 }
@@ -500,9 +505,10 @@ hipError_t launch_bf16_skinny(const GemmArgs<uint16_t>& a, bool vec, void* ws, s
                               hipStream_t s) {
     GemmArgs<uint16_t> args = a;
     const bool epi = has_epilogue(a);
-    // A transposed B is read only by the vector kernel; otherwise the tiled
-    // kernels take the call.
-    if (a.tb && !(vec && smallm_fits(a))) return launch_bf16_mfma(a, vec, s);
+    // A transposed B, and M > kSkinnyElemMaxM, are handled by the vector
+    // kernel only; otherwise the tiled kernels take the call.
+    if ((a.tb || a.M > kSkinnyElemMaxM) && !(vec && smallm_fits(a)))
+        return launch_bf16_mfma(a, vec, s);
     if (vec && smallm_fits(a)) {
         const size_t need = bf16_skinny_workspace(a.M, a.N, a.K);
         const bool split = ws != nullptr && need > 0 && ws_bytes >= need;
@@ -511,8 +517,11 @@ hipError_t launch_bf16_skinny(const GemmArgs<uint16_t>& a, bool vec, void* ws, s
         void* kargs[] = {&args, &w, &wsp};
 #define DG_SMALLM(MB, EPI) (a.tb ? (const void*)&gemm_bf16_smallm_kernel<MB, EPI, true> \
                               : (const void*)&gemm_bf16_smallm_kernel<MB, EPI, false>)
-        const void* fn = epi ? (a.M <= 16 ? DG_SMALLM(1, true) : DG_SMALLM(2, true))
-                             : (a.M <= 16 ? DG_SMALLM(1, false) : DG_SMALLM(2, false));
+        const int mb = smallm_blocks(a.M);
+        const void* fn = epi ? (mb == 1 ? DG_SMALLM(1, true) : mb == 2 ? DG_SMALLM(2, true)
+                                : mb == 4 ? DG_SMALLM(4, true) : DG_SMALLM(8, true))
+                             : (mb == 1 ? DG_SMALLM(1, false) : mb == 2 ? DG_SMALLM(2, false)
+                                : mb == 4 ? DG_SMALLM(4, false) : DG_SMALLM(8, false));
 #undef DG_SMALLM
         if ((int64_t)w.strips * w.segs > kMaxGrid) return hipErrorInvalidConfiguration;
         return hipLaunchKernel(fn, dim3((unsigned)(w.strips * w.segs)), dim3(kNT), kargs, 0, s);

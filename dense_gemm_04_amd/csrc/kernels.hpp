@@ -28,8 +28,8 @@ hipError_t launch_f32_mfma(const GemmArgs<float>& a, bool vec, void* ws, size_t 
                            hipStream_t s);
 size_t f32_mfma_workspace(int64_t M, int64_t N, int64_t K, int cus);
 hipError_t launch_f32_valu(const GemmArgs<float>& a, bool vec, hipStream_t s);
-// Small-M bf16 (M <= kSkinnyMaxM). With `vec` the 64-column copy-ring kernel
-// runs; given a workspace of at least bf16_skinny_workspace(M, N, K) bytes
+// Small-M bf16 (M <= kSkinnyMaxM; without `vec`, M <= kSkinnyElemMaxM). With
+// `vec` the 64-column copy-ring kernel runs; given a workspace of at least bf16_skinny_workspace(M, N, K) bytes
 // (256-byte aligned, counters zero) it splits K over several workgroups.
 hipError_t launch_bf16_skinny(const GemmArgs<uint16_t>& a, bool vec, void* ws, size_t ws_bytes,
                               hipStream_t s);
@@ -43,8 +43,10 @@ hipError_t launch_scale_f32(int64_t M, int64_t N, float beta, float* C, int64_t 
 hipError_t launch_scale_bf16(int64_t M, int64_t N, float beta, uint16_t* C, int64_t ldc,
                              const uint16_t* bias, int act, hipStream_t s);
 
-// Largest M the small-M kernel accepts.
-constexpr int64_t kSkinnyMaxM = 32;
+// Largest M the small-M kernels accept: the vector kernel (16-byte rows)
+// takes up to 128 rows, the element-wise one up to 32.
+constexpr int64_t kSkinnyMaxM = 128;
+constexpr int64_t kSkinnyElemMaxM = 32;
 
 // Workgroup ids are ints: launchers refuse grids beyond this (a matrix that
 // large cannot exist in device memory, so this only guards the arithmetic).

@@ -84,8 +84,9 @@ typedef enum {
     /* fp32 only: vector-FMA (non-matrix-core) kernel with per-thread register
      * micro-tiles, kept as a measured comparison (same article, sections 5.1-5.3). */
     GEMM_VARIANT_VALU = 3,
-    /* bf16 only, M <= 32: small-M kernel that streams B once (Blackwell BF16
-     * GEMM notes, section 5.2: small-batch GEMMs are bandwidth bound). */
+    /* bf16 only, M <= 128 with 16-byte rows (M <= 32 otherwise): small-M
+     * kernel that streams B once (Blackwell BF16 GEMM notes, section 5.2:
+     * small-batch GEMMs are bandwidth bound). */
     GEMM_VARIANT_SKINNY = 4
 } gemm_variant_t;
 
@@ -112,7 +113,7 @@ gemm_status_t gemm_bf16_ex(int64_t M, int64_t N, int64_t K, float alpha,
 
 /* Split-K for small M (RTX 3090 SGEMM article, section 7.2: cutting K into
  * pieces that run in parallel and summing their partial results brings more
- * multiprocessors to work). With M <= 32 one workgroup per 64-column strip of
+ * multiprocessors to work). With M <= 128 one workgroup per 64-column strip of
  * C leaves most of the GPU idle when N is small; a workspace lets the bf16
  * small-M kernel give each strip several workgroups, each over a range of K.
  * Each stores its fp32 partial tile in the workspace, and the strip's last
@@ -120,7 +121,7 @@ gemm_status_t gemm_bf16_ex(int64_t M, int64_t N, int64_t K, float alpha,
  * depend on timing) and forms alpha * sum + beta * C.
  *
  * gemm_bf16_workspace_size: workspace bytes gemm_bf16_ws needs to split this
- * shape; 0 when it would not split (M > 32, N already fills the GPU, or K is
+ * shape; 0 when it would not split (M > 128, N already fills the GPU, or K is
  * a single 128-row chunk) or the sizes are invalid. Host only, no HIP call. */
 size_t gemm_bf16_workspace_size(int64_t M, int64_t N, int64_t K);
 
@@ -220,8 +221,9 @@ gemm_status_t gemm_bf16_bias_act(int64_t M, int64_t N, int64_t K, float alpha,
  * takes B column-major. bias, act, workspace and all other rules are those of
  * gemm_*_bias_act (with opa == opb == GEMM_OP_N the two calls are the same);
  * an opa or opb other than the two codes is GEMM_ERR_INVALID_VALUE. The
- * small-M kernel (M <= 32, bf16) reads row-major A and B only: transposed
- * small-M calls run on the tiled kernels. */
+ * small-M kernel (bf16, M <= 128) reads a row-major A and a row-major or,
+ * with 16-byte rows, transposed B; other transposed small-M calls run on the
+ * tiled kernels. */
 typedef enum { GEMM_OP_N = 0, GEMM_OP_T = 1 } gemm_op_t;
 
 gemm_status_t gemm_f32_op(int opa, int opb, int64_t M, int64_t N, int64_t K, float alpha,

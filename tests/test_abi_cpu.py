@@ -92,9 +92,13 @@ def test_plan_quick_paths(lib):
 
 def test_plan_chooses_family(lib):
     assert plan() == dg.VARIANT_MFMA
-    assert plan(esz=2, M=16) == dg.VARIANT_SKINNY             # bf16, M <= 32
+    assert plan(esz=2, M=16) == dg.VARIANT_SKINNY             # bf16, M <= 128 (16-byte rows)
     assert plan(esz=2, M=32) == dg.VARIANT_SKINNY
-    assert plan(esz=2, M=33) == dg.VARIANT_MFMA
+    assert plan(esz=2, M=33) == dg.VARIANT_SKINNY
+    assert plan(esz=2, M=128) == dg.VARIANT_SKINNY
+    assert plan(esz=2, M=129) == dg.VARIANT_MFMA
+    assert plan(esz=2, M=32, lda=66) == dg.VARIANT_SKINNY      # unaligned: element-wise, M <= 32
+    assert plan(esz=2, M=33, lda=66) == dg.VARIANT_GENERAL
     assert plan(M=4095, N=4097, K=1023) == dg.VARIANT_GENERAL  # ld not a multiple of 4 floats
     assert plan(a=A + 4) == dg.VARIANT_GENERAL                 # base not 16-byte aligned
     assert plan(lda=68) == dg.VARIANT_MFMA
@@ -102,7 +106,8 @@ def test_plan_chooses_family(lib):
     assert plan(variant=dg.VARIANT_VALU) == dg.VARIANT_VALU
     assert plan(esz=2, variant=dg.VARIANT_VALU) == -1
     assert plan(M=16, variant=dg.VARIANT_SKINNY) == -1
-    assert plan(esz=2, M=33, variant=dg.VARIANT_SKINNY) == -1
+    assert plan(esz=2, M=129, variant=dg.VARIANT_SKINNY) == -1
+    assert plan(esz=2, M=33, lda=66, variant=dg.VARIANT_SKINNY) == -1
     assert plan(a=A + 4, variant=dg.VARIANT_MFMA) == -1
     assert plan(variant=dg.VARIANT_GENERAL) == dg.VARIANT_GENERAL
 
@@ -145,11 +150,13 @@ def test_workspace_size(lib):
     # 4096 to give 256 workgroups: a 512-byte counter block, then 2 x 128 fp32
     # tiles of 16 x 64.
     assert dg.gemm_bf16_workspace_size(16, 8192, 8192) == 512 + 2 * 128 * 16 * 64 * 4
-    # 17..32 rows use 32-row tiles.
+    # 17..32 rows use 32-row tiles, 33..64 64-row and 65..128 128-row tiles.
     assert dg.gemm_bf16_workspace_size(32, 8192, 8192) == 512 + 2 * 128 * 32 * 64 * 4
+    assert dg.gemm_bf16_workspace_size(33, 8192, 8192) == 512 + 2 * 128 * 64 * 64 * 4
+    assert dg.gemm_bf16_workspace_size(128, 8192, 8192) == 512 + 2 * 128 * 128 * 64 * 4
     # No split: M too large, strips already fill the GPU, one K chunk, empty
     # or invalid sizes.
-    assert dg.gemm_bf16_workspace_size(33, 8192, 8192) == 0
+    assert dg.gemm_bf16_workspace_size(129, 8192, 8192) == 0
     assert dg.gemm_bf16_workspace_size(16, 16384, 8192) == 0
     assert dg.gemm_bf16_workspace_size(16, 64, 128) == 0
     assert dg.gemm_bf16_workspace_size(0, 64, 1024) == 0

@@ -78,6 +78,28 @@ def test_bf16_skinny(M, NK):
     check("bf16", M, N, K, 1.0, 0.0, dg.VARIANT_AUTO, seed=600 + M + K)
 
 
+# The vector small-M kernel also takes 33..128 rows (64- and 128-row tiles of A).
+SKINNY_WIDE_NK = [(264, 2000), (1032, 4104), (96, 1536), (40, 264), (8, 8), (1000, 520)]
+
+
+@pytest.mark.parametrize("M", [33, 48, 64, 65, 100, 128])
+@pytest.mark.parametrize("NK", SKINNY_WIDE_NK, ids=lambda s: "x".join(map(str, s)))
+def test_bf16_small_m_up_to_128(M, NK):
+    N, K = NK
+    check("bf16", M, N, K, 1.5, -0.5, dg.VARIANT_SKINNY, seed=800 + M + N)
+    check("bf16", M, N, K, 1.0, 0.0, dg.VARIANT_AUTO, seed=900 + M + K)
+
+
+@pytest.mark.parametrize("M", [33, 64, 128])
+def test_bf16_small_m_wide_unaligned_falls_back(M):
+    # Rows that are not 16-byte aligned: the element-wise small-M kernel stops
+    # at 32 rows, so these run on the unaligned tiled kernel.
+    assert dg.gemm_plan(2, M, 200, 1100, 1.0, 4096, 1100, 8192, 200, 0.0, 16384, 200,
+                        dg.VARIANT_AUTO) == dg.VARIANT_GENERAL
+    check("bf16", M, 200, 1100, 1.0, 1.0, dg.VARIANT_AUTO, 950 + M)
+    check("bf16", M, 264, 1000, 1.0, 1.0, dg.VARIANT_AUTO, 960 + M, ld_pad=(1, 3, 5))
+
+
 @pytest.mark.parametrize("M", [7, 16, 29])
 def test_bf16_skinny_padded(M):
     # 16-byte padded rows keep the copy-ring path; odd padding takes the other.

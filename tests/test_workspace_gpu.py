@@ -38,7 +38,8 @@ def run_ws(A, B, C0, alpha, beta, ws, nbytes, ld_pad=(0, 0, 0)):
 
 
 SHAPES = [(16, 264, 2000), (1, 1032, 4104), (17, 64, 1000), (32, 8, 520), (5, 4096, 1024),
-          (16, 128, 300), (31, 520, 8192), (3, 1024, 8200)]
+          (16, 128, 300), (31, 520, 8192), (3, 1024, 8200), (33, 520, 1000), (64, 264, 2000),
+          (65, 1032, 4104), (100, 72, 300), (128, 520, 8192)]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
@@ -88,7 +89,7 @@ def test_padded_rows_and_no_split_shapes():
     assert st == dg.GEMM_OK
     R, D = oracle_ref("bf16", A, B, C0, 1.0, 1.0)
     assert oracle.max_rel_err(to_f64(C), R, D) <= tol("bf16")
-    # M > 32: the workspace is not needed (size 0) and a NULL workspace is accepted.
+    # A NULL workspace is accepted (no split), here for a 64-row tile.
     M2 = 40
     A2 = gi.random_matrix(M2, K, "bf16", 998, dist="n")
     note(f"gemm_bf16_ws no-split M={M2} N={N} K={K}")
