@@ -47,6 +47,15 @@ SETTLE_SECONDS = 0.25
 # Workloads also timed with the fused bias + GELU epilogue (--only, --all):
 # the fp32 4096^3 SGEMM and the bf16 projection with its beta = 1 residual.
 EPILOGUE_WORKLOADS = (2, 4)
+# Mid-size bf16 shapes with fewer 256 x 256 tiles than compute units, timed
+# by --all with and without a split-K workspace (seed families 61..63).
+def midsize_workloads():
+    import gemm_inputs as gi
+    return [gi.Workload(61, "gemm_bf16_512x8192x8192", "bf16", 512, 8192, 8192, 1.0, 0.0, "n", "n"),
+            gi.Workload(62, "gemm_bf16_2048x2048x8192", "bf16", 2048, 2048, 8192, 1.0, 0.0, "n", "n"),
+            gi.Workload(63, "gemm_bf16_128x8192x8192", "bf16", 128, 8192, 8192, 1.0, 0.0, "n", "n")]
+
+
 # Workloads also timed with transposed operand storage (A^T B, A B^T, A^T B^T);
 # the small-M workload with B stored N x K (a weight kept as [out][in]), split-K.
 LAYOUT_WORKLOADS = {2: ((0, 1), (1, 0), (1, 1)), 3: ((0, 1), (1, 0), (1, 1)), 52: ((0, 1),)}
@@ -225,7 +234,7 @@ def main(argv=None) -> int:
     ap.add_argument("--all", action="store_true", help="one JSON line per workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", type=int, default=None,
-                    help="time one workload id (1, 2, 3, 4, 51, 52) and print its line "
+                    help="time one workload id (1, 2, 3, 4, 51, 52; 61-63 mid-size) and print its line "
                          "(with the split-K line for 51 and 52, the bias + GELU line for 2 and 4, "
                          "the transposed-layout lines for 2, 3 and 52)")
     ap.add_argument("--copy-mib", type=int, default=None,
@@ -255,7 +264,12 @@ def main(argv=None) -> int:
         return 0
 
     if args.only is not None:
-        w = gi.WORKLOADS[args.only]
+        extra = {m.wid: m for m in midsize_workloads()}
+        w = gi.WORKLOADS[args.only] if args.only in gi.WORKLOADS else extra[args.only]
+        if args.only in extra:
+            for use_ws in (False, True):
+                print(json.dumps(measure(w, args.steps, args.warmup, use_ws=use_ws)), flush=True)
+            return 0
         r = measure(w, args.steps, args.warmup, 4 if args.only == 52 else 1)
         print(json.dumps(r), flush=True)
         if args.only in (51, 52):
@@ -287,6 +301,9 @@ def main(argv=None) -> int:
                 for ops in LAYOUT_WORKLOADS[wid]:
                     print(json.dumps(measure(w, args.steps, args.warmup, sets, use_ws=wid == 52,
                                              ops=ops)), flush=True)
+        for w in midsize_workloads():
+            for use_ws in (False, True):
+                print(json.dumps(measure(w, args.steps, args.warmup, use_ws=use_ws)), flush=True)
         return 0
 
     w = gi.WORKLOADS[2]

@@ -177,8 +177,9 @@ gemm_status_t run(int64_t M, int64_t N, int64_t K, float alpha, const T* A, int6
                                          : dg::launch_f32_mfma(a, v == GEMM_VARIANT_MFMA, ws, ws_bytes,
                                                                cus, s);
         } else {
-            e = (v == GEMM_VARIANT_SKINNY) ? dg::launch_bf16_skinny(a, vec, ws, ws_bytes, s)
-                                           : dg::launch_bf16_mfma(a, v == GEMM_VARIANT_MFMA, s);
+            e = (v == GEMM_VARIANT_SKINNY)
+                    ? dg::launch_bf16_skinny(a, vec, ws, ws_bytes, cus, s)
+                    : dg::launch_bf16_mfma(a, v == GEMM_VARIANT_MFMA, ws, ws_bytes, cus, s);
         }
     }
     return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
@@ -202,7 +203,8 @@ gemm_status_t gemm_bf16_ex(int64_t M, int64_t N, int64_t K, float alpha, const u
 
 size_t gemm_bf16_workspace_size(int64_t M, int64_t N, int64_t K) {
     if (M < 0 || N < 0 || K < 0 || M > INT_MAX || N > INT_MAX || K > INT_MAX) return 0;
-    return dg::bf16_skinny_workspace(M, N, K);
+    if (M <= dg::kSkinnyMaxM) return dg::bf16_skinny_workspace(M, N, K);
+    return dg::bf16_tiled_workspace(M, N, K, kFullCus);
 }
 
 gemm_status_t gemm_bf16_ws(int64_t M, int64_t N, int64_t K, float alpha, const uint16_t* A,

@@ -154,6 +154,50 @@ __device__ __forceinline__ void lds_only_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// ---- split of the last round of tiles ---------------------------------------
+//
+// The simplest form of stream-K: workgroups 0 .. full - 1 each own a whole
+// tile (tiles 0 .. full - 1 of the raster order); each of the `tail`
+// remaining tiles is cut into `parts` ranges of `cps` K slabs, one workgroup
+// per range, whose fp32 partial tiles meet in a caller workspace laid out as
+// [counters: one int per split tile, padded to 256 bytes][slots: tail x parts
+// partial tiles].
+struct TailSplit {
+    int full;
+    int tail;     // 0: no split
+    int parts;
+    int cps;
+};
+
+constexpr int kMaxSplitParts = 8;
+
+// Tail split for `tiles` tiles of `nk` K slabs over `slots` resident
+// workgroups: when the last round would be at most half full, its tiles are
+// cut into K ranges (of at least `min_cps` slabs) so that the round fills up.
+inline TailSplit plan_tail_split(int64_t tiles, int64_t nk, int64_t slots, int64_t min_cps = 1) {
+    TailSplit t{(int)tiles, 0, 1, (int)nk};
+    const int64_t tail = tiles % slots;
+    if (tail == 0 || 2 * tail > slots || nk < 2 * min_cps) return t;
+    int64_t parts = slots / tail;
+    if (parts > kMaxSplitParts) parts = kMaxSplitParts;
+    if (parts > nk / min_cps) parts = nk / min_cps;
+    const int64_t cps = (nk + parts - 1) / parts;
+    parts = (nk + cps - 1) / cps;                     // every range non-empty
+    if (parts < 2) return t;
+    t.full = (int)(tiles - tail);
+    t.tail = (int)tail;
+    t.parts = (int)parts;
+    t.cps = (int)cps;
+    return t;
+}
+
+// Workspace bytes of a split with bm x bn fp32 partial tiles.
+inline size_t tail_workspace(const TailSplit& t, int bm, int bn) {
+    if (t.tail == 0) return 0;
+    return (size_t)((((int64_t)t.tail * 4 + 255) & ~(int64_t)255) +
+                    (int64_t)t.tail * t.parts * bm * bn * 4);
+}
+
 // ---- workgroup -> output tile mapping ----------------------------------------
 //
 // The dispatcher hands workgroup w to XCD (w mod 8), and each of the 8 XCDs has

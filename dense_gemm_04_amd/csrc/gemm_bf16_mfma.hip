@@ -313,8 +313,9 @@ hipError_t launch_bf16_general(const GemmArgs<uint16_t>& a, bool vec, hipStream_
     return launch_tiles<256, 256, 2, 2>(a, vec, s);
 }
 
-hipError_t launch_bf16_mfma(const GemmArgs<uint16_t>& a, bool vec, hipStream_t s) {
-    if (vec && bf16_tiled_fits(a)) return launch_bf16_tiled(a, s);
+hipError_t launch_bf16_mfma(const GemmArgs<uint16_t>& a, bool vec, void* ws, size_t ws_bytes,
+                            int cus, hipStream_t s) {
+    if (vec && bf16_tiled_fits(a)) return launch_bf16_tiled(a, ws, ws_bytes, cus, s);
     return launch_bf16_general(a, vec, s);
 }
 

@@ -502,13 +502,13 @@ size_t bf16_skinny_workspace(int64_t M, int64_t N, int64_t K) {
 }
 
 hipError_t launch_bf16_skinny(const GemmArgs<uint16_t>& a, bool vec, void* ws, size_t ws_bytes,
-                              hipStream_t s) {
+                              int cus, hipStream_t s) {
     GemmArgs<uint16_t> args = a;
     const bool epi = has_epilogue(a);
     // A transposed B, and M > kSkinnyElemMaxM, are handled by the vector
     // kernel only; otherwise the tiled kernels take the call.
     if ((a.tb || a.M > kSkinnyElemMaxM) && !(vec && smallm_fits(a)))
-        return launch_bf16_mfma(a, vec, s);
+        return launch_bf16_mfma(a, vec, ws, ws_bytes, cus, s);
     if (vec && smallm_fits(a)) {
         const size_t need = bf16_skinny_workspace(a.M, a.N, a.K);
         const bool split = ws != nullptr && need > 0 && ws_bytes >= need;

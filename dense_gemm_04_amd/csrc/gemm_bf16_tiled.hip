@@ -34,6 +34,12 @@
 //     columns that are never stored; k past K in the last slab is zeroed in
 //     the LDS copy of A (Z-Turbo CUDA tuning page, section 3.1: zero-filled
 //     tile edges; Blackwell notes, section 4.3: predicate the tail).
+//   * split K (SPLIT, with a caller workspace): when the tiles leave the last
+//     round of resident workgroups at most half full, as shapes with fewer
+//     tiles than compute units do, each tile of that round is cut into K
+//     ranges (the RTX 3090 SGEMM article, section 7.2: more multiprocessors
+//     at work on the same tile); their fp32 partial tiles meet in the
+//     workspace and the last range to finish adds them in range order;
 //   * transposed operands (TA: A stored K x M; TB: B stored N x K) change only
 //     where a slab's contiguous dimension lies. An operand whose rows run
 //     along k (row-major A, transposed B) is copied and read the way A is
@@ -101,9 +107,13 @@ __device__ __forceinline__ void lds_barrier() {
     lds_only_barrier();
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool EPI, bool TA, bool TB>
+// ws (only with SPLIT and ts.tail > 0): [counters: one int per split tile,
+// padded to 256 bytes][slots: tail x parts partial tiles of BM x BN fp32,
+// value c of thread t at byte (c * threads + t) * 16 of its slot].
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool EPI, bool TA, bool TB, bool SPLIT>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1)
-void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
+void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, TailSplit ts,
+                            unsigned char* ws) {
     constexpr int kNT = WAVES_M * WAVES_N * 64;
     constexpr int kWaves = WAVES_M * WAVES_N;
     constexpr int kBM = BM, kBN = BN;
@@ -133,10 +143,24 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
     __shared__ __attribute__((aligned(16))) uint16_t b_st0[kBStage];
     __shared__ __attribute__((aligned(16))) uint16_t b_st1[kBStage];
 
-    int tm, tn;
-    tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, kGroupM, tm, tn);
-    const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
     const int64_t M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb;
+    const int64_t nk = (K + kBK - 1) / kBK;
+    int tm, tn, ti = 0, part = 0;
+    int64_t kb = 0, ke = nk;                        // K slabs of this workgroup
+    bool split_tile = false;
+    if (!SPLIT || (int)blockIdx.x < ts.full) {
+        tile_coords(blockIdx.x, SPLIT ? ts.full : gridDim.x, tiles_m, tiles_n, kGroupM, tm, tn);
+    } else {
+        // Split tail: consecutive workgroups take the K ranges of one tile.
+        const int u = (int)blockIdx.x - ts.full;
+        ti = __builtin_amdgcn_readfirstlane(u / ts.parts);
+        part = __builtin_amdgcn_readfirstlane(u - ti * ts.parts);
+        raster_tile(ts.full + ti, tiles_m, tiles_n, kGroupM, tm, tn);
+        kb = (int64_t)part * ts.cps;
+        ke = kb + ts.cps < nk ? kb + ts.cps : nk;
+        split_tile = true;
+    }
+    const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     auto a_stage = [&](int stage) -> uint16_t* { return stage == 0 ? a_st0 : a_st1; };
@@ -316,35 +340,89 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
     // publishes slab t + 1 and retires every read of slab t, after which slab
     // t + 2 may overwrite it. Fragments of the next k step are always read one
     // step ahead of the MFMAs that use them.
-    const int64_t nk = (K + kBK - 1) / kBK;
+    // Slabs kb .. ke - 1 (all of K unless the tile is split); only the range
+    // that ends at nk holds the ragged K tail.
     const int k_tail = (int)(K - (nk - 1) * kBK);   // 1 .. 64
-    dma(0, 0);
+    const bool tail_here = kZeroTail && ke == nk && k_tail < kBK;
+    dma(kb, 0);
     lds_barrier();
-    if (kZeroTail && nk == 1 && k_tail < kBK) {
+    if (tail_here && kb + 1 == ke) {
         zero_a_tail(0, k_tail);
         lds_barrier();
     }
-    if (nk > 1) dma(1, 1);
+    if (kb + 1 < ke) dma(kb + 1, 1);
     read_frags(0, 0, 0);
     // One slab; `cur` is a literal at both call sites (the loop is unrolled by
     // two), so every LDS access names its stage array statically.
     auto slab = [&](int64_t kt, int cur) {
         read_frags(cur, 1, 1);
         mfmas(0);
-        if (kt + 1 < nk) {
+        if (kt + 1 < ke) {
             lds_barrier();
-            if (kZeroTail && kt + 2 == nk && k_tail < kBK) {
+            if (tail_here && kt + 2 == ke) {
                 zero_a_tail(cur ^ 1, k_tail);
                 lds_barrier();
             }
-            if (kt + 2 < nk) dma(kt + 2, cur);
+            if (kt + 2 < ke) dma(kt + 2, cur);
             read_frags(cur ^ 1, 0, 0);
         }
         mfmas(1);
     };
-    for (int64_t kt = 0; kt < nk; kt += 2) {
+    for (int64_t kt = kb; kt < ke; kt += 2) {
         slab(kt, 0);
-        if (kt + 1 < nk) slab(kt + 1, 1);
+        if (kt + 1 < ke) slab(kt + 1, 1);
+    }
+
+    if constexpr (SPLIT) {
+        if (split_tile) {
+            // Store this K range's partial tile with device-coherent stores
+            // (sc1: written through the per-XCD L2), count in once they have
+            // completed, and let the tile's last arrival read the ranges back
+            // the same way and add them in range order before the epilogue.
+            // No cache write-back or invalidate is needed.
+            constexpr int E4 = kFN * kFM;                     // f32x4 values per thread
+            constexpr int kSc1 = 16;                          // cache-policy bit sc1
+            int* counters = reinterpret_cast<int*>(ws);
+            const unsigned char* slots = ws + (((int64_t)ts.tail * 4 + 255) & ~(int64_t)255);
+            const rsrc_t sd = make_rsrc(slots + (int64_t)ti * ts.parts * (kBM * kBN * 4),
+                                        (uint32_t)(ts.parts * kBM * kBN * 4));
+            auto voff = [&](int q, int c) { return (uint32_t)(((q * E4 + c) * kNT + t) * 16); };
+#pragma unroll
+            for (int j = 0; j < kFN; ++j)
+#pragma unroll
+                for (int i = 0; i < kFM; ++i)
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[j][i]), sd,
+                                                           voff(part, j * kFM + i), 0, kSc1);
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+            __syncthreads();
+            __shared__ int last_flag;
+            if (t == 0)
+                last_flag = __hip_atomic_fetch_add(counters + ti, 1, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT) == ts.parts - 1;
+            __syncthreads();
+            if (!last_flag) return;
+            // The last arrival reads every range back, its own included (its
+            // stores have completed): one value of all eight possible ranges
+            // at a time (loads past the tile's `parts` ranges fall outside the
+            // descriptor and read as zeros), added in range order.
+#pragma unroll
+            for (int j = 0; j < kFN; ++j) {
+#pragma unroll
+                for (int i = 0; i < kFM; ++i) {
+                    f32x4 v[kMaxSplitParts];
+#pragma unroll
+                    for (int q = 0; q < kMaxSplitParts; ++q)
+                        v[q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                             sd, voff(q, j * kFM + i), 0, kSc1));
+                    f32x4 sum = v[0];
+#pragma unroll
+                    for (int q = 1; q < kMaxSplitParts; ++q) sum += v[q];
+                    acc[j][i] = sum;
+                }
+            }
+            // Leave the counter at zero for the next call that uses this workspace.
+            if (t == 0) __hip_atomic_store(counters + ti, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 
     // Epilogue: acc[j][i] register r holds C(m0 + wm0 + 16 i + pl, n0 + wn0 + 16 j + 4 g + r).
@@ -406,29 +484,59 @@ bool bf16_tiled_fits(const GemmArgs<uint16_t>& a) {
     return (a.ta ? mc(a.lda, a.M) : kc(a.lda)) && (a.tb ? kc(a.ldb) : mc(a.ldb, a.N));
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool EPI>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool EPI, bool SPLIT>
 const void* pick_tiled(bool ta, bool tb) {
-    return ta ? (tb ? (const void*)&gemm_bf16_tiled_kernel<BM, BN, WAVES_M, WAVES_N, EPI, true, true>
-                    : (const void*)&gemm_bf16_tiled_kernel<BM, BN, WAVES_M, WAVES_N, EPI, true, false>)
-              : (tb ? (const void*)&gemm_bf16_tiled_kernel<BM, BN, WAVES_M, WAVES_N, EPI, false, true>
-                    : (const void*)&gemm_bf16_tiled_kernel<BM, BN, WAVES_M, WAVES_N, EPI, false, false>);
+#define DG_TILED(TA, TB) \
+    (const void*)&gemm_bf16_tiled_kernel<BM, BN, WAVES_M, WAVES_N, EPI, TA, TB, SPLIT>
+    return ta ? (tb ? DG_TILED(true, true) : DG_TILED(true, false))
+              : (tb ? DG_TILED(false, true) : DG_TILED(false, false));
+#undef DG_TILED
+}
+
+// One workgroup per compute unit (8 waves of 256 registers, 128 KB of LDS).
+constexpr int kTiledSlotsPerCu = 1;
+// Each K range spans at least 16 slabs (1024 k). Every range stores a 256 KB
+// fp32 partial tile and the tile's last range reads them all back, which
+// costs a CU 10-30 us whatever the tile count; only ranges with that much
+// MFMA work to save pay for it (1024^3 and 2048^3 measured slower split into
+// ranges of 4 and 8 slabs; 1024 x 4096 x 4096 and 512 x 8192 x 8192 gain
+// 1.2x and 1.7x).
+constexpr int kTiledMinSlabs = 16;
+
+TailSplit plan_tiled(int64_t M, int64_t N, int64_t K, int cus) {
+    const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+    return plan_tail_split(tiles, (K + kBK - 1) / kBK, (int64_t)cus * kTiledSlotsPerCu,
+                           kTiledMinSlabs);
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool EPI>
-hipError_t launch_cfg(const GemmArgs<uint16_t>& a, hipStream_t s) {
+hipError_t launch_cfg(const GemmArgs<uint16_t>& a, void* ws, size_t ws_bytes, int cus,
+                      hipStream_t s) {
+    static_assert(BM == 256 && BN == 256, "plan_tiled assumes 256 x 256 tiles");
     const int64_t tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
     int tm = (int)tiles_m, tn = (int)tiles_n;
     GemmArgs<uint16_t> args = a;
-    void* kargs[] = {&args, &tm, &tn};
-    if (tiles_m * tiles_n > kMaxGrid) return hipErrorInvalidConfiguration;
-    return hipLaunchKernel(pick_tiled<BM, BN, WAVES_M, WAVES_N, EPI>(a.ta, a.tb),
-                           dim3((unsigned)(tiles_m * tiles_n)), dim3(WAVES_M * WAVES_N * 64), kargs,
-                           0, s);
+    TailSplit ts = plan_tiled(a.M, a.N, a.K, cus);
+    const bool split = ws != nullptr && ts.tail > 0 && ws_bytes >= tail_workspace(ts, BM, BN);
+    if (!split) ts = TailSplit{(int)(tiles_m * tiles_n), 0, 1, 0};
+    unsigned char* wsp = split ? static_cast<unsigned char*>(ws) : nullptr;
+    void* kargs[] = {&args, &tm, &tn, &ts, &wsp};
+    const void* fn = split ? pick_tiled<BM, BN, WAVES_M, WAVES_N, EPI, true>(a.ta, a.tb)
+                           : pick_tiled<BM, BN, WAVES_M, WAVES_N, EPI, false>(a.ta, a.tb);
+    const int64_t grid = split ? (int64_t)ts.full + (int64_t)ts.tail * ts.parts : tiles_m * tiles_n;
+    if (grid > kMaxGrid) return hipErrorInvalidConfiguration;
+    return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(WAVES_M * WAVES_N * 64), kargs, 0, s);
 }
 
-hipError_t launch_bf16_tiled(const GemmArgs<uint16_t>& a, hipStream_t s) {
-    if (has_epilogue(a)) return launch_cfg<256, 256, 2, 4, true>(a, s);
-    return launch_cfg<256, 256, 2, 4, false>(a, s);
+hipError_t launch_bf16_tiled(const GemmArgs<uint16_t>& a, void* ws, size_t ws_bytes, int cus,
+                             hipStream_t s) {
+    if (has_epilogue(a)) return launch_cfg<256, 256, 2, 4, true>(a, ws, ws_bytes, cus, s);
+    return launch_cfg<256, 256, 2, 4, false>(a, ws, ws_bytes, cus, s);
+}
+
+size_t bf16_tiled_workspace(int64_t M, int64_t N, int64_t K, int cus) {
+    if (M < 1 || N < 1 || K < 1) return 0;
+    return tail_workspace(plan_tiled(M, N, K, cus), 256, 256);
 }
 
 }  // namespace dg

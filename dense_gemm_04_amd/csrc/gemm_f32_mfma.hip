@@ -57,17 +57,6 @@ __device__ __forceinline__ int b_off(int kr, int col) {
     return kr * BN + col;
 }
 
-// Split of the last, partly filled round of tiles (the simplest form of
-// stream-K): workgroups 0 .. full - 1 each own a whole tile (tiles 0 .. full - 1
-// of the raster order); each of the `tail` remaining tiles is cut into `parts`
-// ranges of `cps` K slabs, one workgroup per range.
-struct TailSplit {
-    int full;
-    int tail;     // 0: no split
-    int parts;
-    int cps;
-};
-
 __device__ __forceinline__ f32x4 load4_elems(const float* p, int valid) {
     f32x4 v;
 #pragma unroll
@@ -369,33 +358,9 @@ void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit
 }
 
 constexpr int kSlotsPerCu = 2;   // resident workgroups per compute unit (64 KB LDS each)
-constexpr int kMaxParts = 8;
 
-// Tail split for a grid of `tiles` tiles over `cus` compute units: when the
-// last round of resident workgroups would be at most half full, its tiles are
-// cut into K ranges so that the round fills up.
 TailSplit plan_tail(int64_t tiles, int64_t nk, int cus) {
-    TailSplit t{(int)tiles, 0, 1, (int)nk};
-    const int64_t slots = (int64_t)cus * kSlotsPerCu;
-    const int64_t tail = tiles % slots;
-    if (tail == 0 || 2 * tail > slots || nk < 2) return t;
-    int64_t parts = slots / tail;
-    if (parts > kMaxParts) parts = kMaxParts;
-    if (parts > nk) parts = nk;
-    const int64_t cps = (nk + parts - 1) / parts;
-    parts = (nk + cps - 1) / cps;                     // every range non-empty
-    if (parts < 2) return t;
-    t.full = (int)(tiles - tail);
-    t.tail = (int)tail;
-    t.parts = (int)parts;
-    t.cps = (int)cps;
-    return t;
-}
-
-size_t tail_workspace(const TailSplit& t, int bm, int bn) {
-    if (t.tail == 0) return 0;
-    return (size_t)((((int64_t)t.tail * 4 + 255) & ~(int64_t)255) +
-                    (int64_t)t.tail * t.parts * bm * bn * 4);
+    return plan_tail_split(tiles, nk, (int64_t)cus * kSlotsPerCu);
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool VEC, bool SPLIT, bool EPI>

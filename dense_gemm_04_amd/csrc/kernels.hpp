@@ -14,11 +14,19 @@ namespace dg {
 // `vec` selects 128-bit global loads/stores; the caller guarantees 16-byte
 // aligned base pointers and leading dimensions that keep every row 16-byte
 // aligned. Without it every global access is element-wise.
-hipError_t launch_bf16_mfma(const GemmArgs<uint16_t>& a, bool vec, hipStream_t s);
+//
+// Workspace arguments (ws may be null): given at least the bytes the matching
+// *_workspace function returns for the shape (256-byte aligned, counters
+// zero), a kernel splits K for the tiles of a last round that would leave
+// most of the `cus` compute units idle; otherwise it runs unsplit.
+hipError_t launch_bf16_mfma(const GemmArgs<uint16_t>& a, bool vec, void* ws, size_t ws_bytes,
+                            int cus, hipStream_t s);
 // The two bf16 MFMA kernels behind launch_bf16_mfma: the tiled vector kernel
-// (needs `vec` and offsets that fit its 31-bit buffer offsets) and the
-// element-wise one that takes any alignment.
-hipError_t launch_bf16_tiled(const GemmArgs<uint16_t>& a, hipStream_t s);
+// (needs `vec` and offsets that fit its 31-bit buffer offsets; splits K with
+// a workspace) and the element-wise one that takes any alignment.
+hipError_t launch_bf16_tiled(const GemmArgs<uint16_t>& a, void* ws, size_t ws_bytes, int cus,
+                             hipStream_t s);
+size_t bf16_tiled_workspace(int64_t M, int64_t N, int64_t K, int cus);
 bool bf16_tiled_fits(const GemmArgs<uint16_t>& a);
 hipError_t launch_bf16_general(const GemmArgs<uint16_t>& a, bool vec, hipStream_t s);
 // fp32 MFMA kernel. Given a workspace of at least f32_mfma_workspace(M, N, K,
@@ -32,7 +40,7 @@ hipError_t launch_f32_valu(const GemmArgs<float>& a, bool vec, hipStream_t s);
 // `vec` the 64-column copy-ring kernel runs; given a workspace of at least bf16_skinny_workspace(M, N, K) bytes
 // (256-byte aligned, counters zero) it splits K over several workgroups.
 hipError_t launch_bf16_skinny(const GemmArgs<uint16_t>& a, bool vec, void* ws, size_t ws_bytes,
-                              hipStream_t s);
+                              int cus, hipStream_t s);
 // Workspace bytes with which launch_bf16_skinny splits K (0: no split for this shape).
 size_t bf16_skinny_workspace(int64_t M, int64_t N, int64_t K);
 

@@ -120,9 +120,16 @@ gemm_status_t gemm_bf16_ex(int64_t M, int64_t N, int64_t K, float alpha,
  * workgroup to finish adds the partials in a fixed order (so results do not
  * depend on timing) and forms alpha * sum + beta * C.
  *
+ * For M > 128 the tiled bf16 kernel splits the same way as the fp32 one (see
+ * gemm_f32_ws): when fewer 256 x 256 tiles than compute units, or a last
+ * round at most half full, would leave CUs idle, each such tile is cut into up
+ * to 8 K ranges of at least 1024 k, with 256 KB fp32 partial tiles.
+ *
  * gemm_bf16_workspace_size: workspace bytes gemm_bf16_ws needs to split this
- * shape; 0 when it would not split (M > 128, N already fills the GPU, or K is
- * a single 128-row chunk) or the sizes are invalid. Host only, no HIP call. */
+ * shape; 0 when it would not split (small M: N already fills the GPU or K is
+ * a single 128-row chunk; M > 128: no idle CUs, or K below 2048) or the sizes
+ * are invalid. Host only, no HIP call. Sized for a full MI355X (256 compute
+ * units). */
 size_t gemm_bf16_workspace_size(int64_t M, int64_t N, int64_t K);
 
 /* gemm_bf16 with a workspace: device memory owned by the caller, 256-byte

@@ -154,9 +154,10 @@ def test_workspace_size(lib):
     assert dg.gemm_bf16_workspace_size(32, 8192, 8192) == 512 + 2 * 128 * 32 * 64 * 4
     assert dg.gemm_bf16_workspace_size(33, 8192, 8192) == 512 + 2 * 128 * 64 * 64 * 4
     assert dg.gemm_bf16_workspace_size(128, 8192, 8192) == 512 + 2 * 128 * 128 * 64 * 4
-    # No split: M too large, strips already fill the GPU, one K chunk, empty
-    # or invalid sizes.
-    assert dg.gemm_bf16_workspace_size(129, 8192, 8192) == 0
+    # M > 128 is sized for the tiled kernel instead (see the next test); no
+    # small-M split when strips already fill the GPU, one K chunk, empty or
+    # invalid sizes.
+    assert dg.gemm_bf16_workspace_size(129, 8192, 8192) == 256 + 32 * 8 * 256 * 256 * 4
     assert dg.gemm_bf16_workspace_size(16, 16384, 8192) == 0
     assert dg.gemm_bf16_workspace_size(16, 64, 128) == 0
     assert dg.gemm_bf16_workspace_size(0, 64, 1024) == 0
@@ -169,6 +170,26 @@ def test_workspace_size(lib):
     assert dg.gemm_bf16_workspace_size(16, 64, 300) == 256 + 3 * 16 * 64 * 4
     # 17 strips want 16 segments; K = 4104 has 33 chunks: 11 segments of 3.
     assert dg.gemm_bf16_workspace_size(16, 1032, 4104) == 256 + 11 * 17 * 16 * 64 * 4
+
+
+def test_tiled_workspace_size(lib):
+    # M > 128: the bf16 tiled kernel's split. 256 x 256 tiles, one workgroup
+    # per compute unit: a last round at most half full (of 256) is cut into
+    # up to 8 K ranges of at least 16 slabs of 64, each with a 256 KB fp32
+    # partial tile.
+    tile = 256 * 256 * 4
+    # 512 x 8192 x 8192: 64 tiles, 128 slabs -> 4 ranges each.
+    assert dg.gemm_bf16_workspace_size(512, 8192, 8192) == 256 + 64 * 4 * tile
+    # 2048^3: 64 tiles, 32 slabs -> 2 ranges.
+    assert dg.gemm_bf16_workspace_size(2048, 2048, 2048) == 256 + 64 * 2 * tile
+    # 129 x 1000 x 8200: 4 tiles, 129 slabs -> 8 ranges of 17 (the last 10).
+    assert dg.gemm_bf16_workspace_size(129, 1000, 8200) == 256 + 4 * 8 * tile
+    # No split: a full round (4096^2 = 256 tiles), a last round more than half
+    # full (3000^2 = 144 tiles), fewer than 32 slabs.
+    assert dg.gemm_bf16_workspace_size(4096, 4096, 4096) == 0
+    assert dg.gemm_bf16_workspace_size(3000, 3000, 3000) == 0
+    assert dg.gemm_bf16_workspace_size(1024, 1024, 1024) == 0
+    assert dg.gemm_bf16_workspace_size(300, 520, 1984) == 0
 
 
 def test_workspace_validation(lib):

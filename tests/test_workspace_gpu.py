@@ -159,3 +159,50 @@ def test_f32_split_k_deterministic():
         again, st = run_ws_f32(A, B, None, 1.0, 0.0, ws, nbytes)
         assert st == dg.GEMM_OK
         assert torch.equal(first.view(torch.int32), again.view(torch.int32))
+
+
+# ---- bf16 tiled kernel: split K when few tiles leave most CUs idle -----------
+
+# (shape, ld padding): ragged M, N and K, K ranges of one or several slabs,
+# the ragged K tail in the last range, padded 16-byte rows.
+TILED_SHAPES = [((300, 520, 2100), (0, 0, 0)), ((257, 264, 4100), (0, 0, 0)),
+                ((512, 512, 4096), (0, 0, 0)), ((1024, 1024, 2048), (8, 16, 24)),
+                ((129, 1000, 8200), (0, 0, 0))]
+
+
+@pytest.mark.parametrize("case", TILED_SHAPES,
+                         ids=lambda c: "x".join(map(str, c[0])) + f"_pad{c[1][0]}")
+@pytest.mark.parametrize("ops", [(0, 0), (0, 1), (1, 0), (1, 1)], ids=["NN", "NT", "TN", "TT"])
+def test_bf16_tiled_split_k_parity(case, ops):
+    from test_transpose_gpu import check
+    (M, N, K), pad = case
+    assert dg.gemm_bf16_workspace_size(M, N, K) > 0          # these shapes do split
+    for rep, (alpha, beta) in enumerate(((1.0, 0.0), (0.5, 2.0))):
+        check("bf16", ops[0], ops[1], M, N, K, 5100 + M + rep, alpha, beta, pad, ws=True)
+    check("bf16", ops[0], ops[1], M, N, K, 5150 + M, 1.0, 1.0, pad, bias=True, act="gelu_tanh",
+          ws=True)
+
+
+def test_bf16_tiled_split_k_deterministic_and_counters_reset():
+    from test_transpose_gpu import run_op
+    M, N, K = 512, 512, 4096
+    A = gi.random_matrix(M, K, "bf16", 5200, dist="n")
+    B = gi.random_matrix(K, N, "bf16", 5201)
+    nbytes = dg.gemm_bf16_workspace_size(M, N, K)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    a, b = A.cuda(), B.cuda()
+    outs = []
+    for _ in range(3):
+        note(f"gemm_bf16_ws tiled split determinism M={M} N={N} K={K}")
+        c = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+        st = dg.gemm_bf16_ws(M, N, K, 1.0, a.data_ptr(), K, b.data_ptr(), N, 0.0, c.data_ptr(), N,
+                             ws.data_ptr(), nbytes, 0)
+        torch.cuda.synchronize()
+        assert st == dg.GEMM_OK
+        outs.append(c.cpu())
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    assert torch.equal(outs[0].view(torch.int16), outs[2].view(torch.int16))
+    assert int(ws[:4 * 4].view(torch.int32).abs().sum()) == 0          # 4 tiles' counters
+    R, D = oracle_ref("bf16", A, B, None, 1.0, 0.0)
+    assert oracle.max_rel_err(to_f64(outs[0]), R, D) <= tol("bf16")
+
