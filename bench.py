@@ -86,7 +86,7 @@ def _time_calls(call, steps: int, warmup: int, stream, settle: float = SETTLE_SE
     return start.elapsed_time(end) / 1e3 / steps     # seconds per call
 
 
-def _device_call(w, sets: int = 1, use_ws: bool = False, act=None, ops=None):
+def _device_call(w, sets: int = 1, use_ws: bool = False, act=None, ops=None, variant=None):
     """Allocate `sets` independent operand sets on the GPU and return a callable
     that runs the library on the next set each time (through gemm_*_ws with a
     zeroed workspace when `use_ws`; through gemm_*_bias_act with a seeded bias
@@ -126,6 +126,11 @@ def _device_call(w, sets: int = 1, use_ws: bool = False, act=None, ops=None):
             return epi_fn(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias.data_ptr(), code,
                           None, 0, stream)
 
+    if variant is not None:
+        ex_fn = dg.gemm_f32_ex if w.dtype == "f32" else dg.gemm_bf16_ex
+
+        def fn(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream):
+            return ex_fn(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, variant)
     lda, ldb = (w.M if opa else w.K), (w.K if opb else w.N)
     if ops is not None:
         op_fn = dg.gemm_f32_op if w.dtype == "f32" else dg.gemm_bf16_op
@@ -148,14 +153,17 @@ def _device_call(w, sets: int = 1, use_ws: bool = False, act=None, ops=None):
 
 
 def measure(w, steps: int, warmup: int, sets: int = 1, use_ws: bool = False, act=None,
-            ops=None) -> dict:
-    call, stream, _ = _device_call(w, sets, use_ws, act, ops)
+            ops=None, variant=None) -> dict:
+    call, stream, _ = _device_call(w, sets, use_ws, act, ops, variant)
     sec = _time_calls(call, steps, warmup, stream)
     ws_name = "gemm_f32_ws" if w.dtype == "f32" else "gemm_bf16_ws"
     epi_name = "gemm_f32_bias_act" if w.dtype == "f32" else "gemm_bf16_bias_act"
     label = f" ({ws_name}, split-K)" if use_ws else ""
     if act is not None:
         label = f" ({epi_name}, bias + {act})"
+    if variant is not None:
+        import dense_gemm_04_amd as dg
+        label = f" (gemm_{w.dtype}_ex, {dg.VARIANT_NAMES[variant]} kernel)"
     if ops is not None:
         op_name = "gemm_f32_op" if w.dtype == "f32" else "gemm_bf16_op"
         label = (f" ({op_name}, {'A^T' if ops[0] else 'A'} {'B^T' if ops[1] else 'B'}"
@@ -277,6 +285,8 @@ def main(argv=None) -> int:
                                      use_ws=True)), flush=True)
         if args.only in EPILOGUE_WORKLOADS:
             print(json.dumps(measure(w, args.steps, args.warmup, act="gelu_tanh")), flush=True)
+        if args.only == 2:
+            print(json.dumps(measure(w, args.steps, args.warmup, variant=dg.VARIANT_VALU)), flush=True)
         if args.only in LAYOUT_WORKLOADS:
             for ops in LAYOUT_WORKLOADS[args.only]:
                 print(json.dumps(measure(w, args.steps, args.warmup, 4 if args.only == 52 else 1,
@@ -296,6 +306,10 @@ def main(argv=None) -> int:
                       flush=True)
             if wid in EPILOGUE_WORKLOADS:
                 print(json.dumps(measure(w, args.steps, args.warmup, sets, act="gelu_tanh")),
+                      flush=True)
+            if wid == 2:
+                # The vector-FMA comparison kernel at the same shape.
+                print(json.dumps(measure(w, args.steps, args.warmup, variant=dg.VARIANT_VALU)),
                       flush=True)
             if wid in LAYOUT_WORKLOADS:
                 for ops in LAYOUT_WORKLOADS[wid]:
