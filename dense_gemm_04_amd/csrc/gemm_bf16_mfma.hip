@@ -44,6 +44,8 @@
 // along m or n (row-major B, transposed A) in 8 x 8 blocks that are transposed
 // in registers. Both land k-contiguous in LDS, so the MFMA loop is the same.
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -119,23 +121,30 @@ void gemm_bf16_mfma_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
     u32x4 ra[A_CHUNKS];
     u32x4 rb[B_BLOCKS][8];
 
+    // 8 consecutive bf16; FULL: known to be in range, loaded with no test.
+    auto ld8 = [&](auto full_tag, const uint16_t* base, int64_t off, int valid) -> u32x4 {
+        if constexpr (decltype(full_tag)::value)
+            return VEC ? *reinterpret_cast<const u32x4*>(base + off)
+                       : (u32x4)*reinterpret_cast<const u32x4_a2*>(base + off);
+        else
+            return load8<VEC>(base + (valid > 0 ? off : 0), valid);
+    };
     // Chunk loader (memory rows along k): thread t's chunk i is tile row
     // t / 8 + i * NT / 8 (of `extent` rows from r0), k chunk t % 8.
-    auto load_chunks = [&](const uint16_t* base, int64_t ld, int64_t extent, int64_t r0,
-                           int64_t k0, u32x4* regs) {
+    auto load_chunks = [&](auto full_tag, const uint16_t* base, int64_t ld, int64_t extent,
+                           int64_t r0, int64_t k0, u32x4* regs) {
 #pragma unroll
         for (int i = 0; i < A_CHUNKS; ++i) {
             const int r = t / 8 + i * (NT / 8), c = t % 8;
             const int64_t gm = r0 + r, gk = k0 + 8 * c;
             int valid = (gm < extent) ? (int)(K - gk < 8 ? K - gk : 8) : 0;
-            const uint16_t* src = base + (valid > 0 ? gm * ld + gk : 0);
-            regs[i] = load8<VEC>(src, valid);
+            regs[i] = ld8(full_tag, base, gm * ld + gk, valid);
         }
     };
     // Block loader (memory rows along m or n): thread t's block bi is the 8 x 8
     // block (kb, nb) of the 64 x BN slab; register r holds its row k = 8 kb + r.
-    auto load_blocks = [&](const uint16_t* base, int64_t ld, int64_t extent, int64_t c0,
-                           int64_t k0, u32x4 (*regs)[8]) {
+    auto load_blocks = [&](auto full_tag, const uint16_t* base, int64_t ld, int64_t extent,
+                           int64_t c0, int64_t k0, u32x4 (*regs)[8]) {
 #pragma unroll
         for (int bi = 0; bi < B_BLOCKS; ++bi) {
             const int blk = t + bi * NT;
@@ -146,8 +155,7 @@ void gemm_bf16_mfma_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
             for (int r = 0; r < 8; ++r) {
                 const int64_t gk = k0 + 8 * kb + r;
                 const int valid = gk < K ? nvalid : 0;
-                const uint16_t* src = base + (valid > 0 ? gk * ld + gn : 0);
-                regs[bi][r] = load8<VEC>(src, valid);
+                regs[bi][r] = ld8(full_tag, base, gk * ld + gn, valid);
             }
         }
     };
@@ -175,11 +183,19 @@ void gemm_bf16_mfma_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
     u32x4 (*ra_blocks)[8] = reinterpret_cast<u32x4 (*)[8]>(ra);
     u32x4* rb_chunks = &rb[0][0];
 
+    // Interior slabs (tile inside M and N, slab inside K) load every chunk
+    // whole with no range test; the edge path's per-lane tests would
+    // otherwise sit in every slab, with waits for all outstanding loads.
+    auto gload_slab = [&](auto full_tag, int64_t k0) {
+        if constexpr (TA) load_blocks(full_tag, p.A, p.lda, M, m0, k0, ra_blocks);
+        else load_chunks(full_tag, p.A, p.lda, M, m0, k0, ra);
+        if constexpr (TB) load_chunks(full_tag, p.B, p.ldb, N, n0, k0, rb_chunks);
+        else load_blocks(full_tag, p.B, p.ldb, N, n0, k0, rb);
+    };
+    const bool full_tile = m0 + BM <= M && n0 + BN <= N;
     auto gload = [&](int64_t k0) {
-        if constexpr (TA) load_blocks(p.A, p.lda, M, m0, k0, ra_blocks);
-        else load_chunks(p.A, p.lda, M, m0, k0, ra);
-        if constexpr (TB) load_chunks(p.B, p.ldb, N, n0, k0, rb_chunks);
-        else load_blocks(p.B, p.ldb, N, n0, k0, rb);
+        if (full_tile && k0 + kBK <= K) gload_slab(std::true_type{}, k0);
+        else gload_slab(std::false_type{}, k0);
     };
 
     auto sstore = [&](int stage) {

@@ -30,6 +30,8 @@
 // k_g) and B(k_g, col p) for one k per lane group g, and receives D(row 4g + i,
 // col p) in accumulator register i. A and B use the same k for each g.
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -133,7 +135,19 @@ void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit
     const int ta_kb = t / (BM / 4), ta_mb = t % (BM / 4);
     const int tb_nb = t / (kBK / 4), tb_kb = t % (kBK / 4);
 
-    auto gload = [&](int64_t k0) {
+    // Global -> register loads of one slab. FULL: the tile lies inside M and
+    // N and the slab inside K, so every chunk is loaded whole with no range
+    // test. The edge path's per-lane tests would otherwise be compiled into
+    // every slab, with a wait for all outstanding loads in the middle.
+    auto gload_slab = [&](auto full_tag, int64_t k0) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        auto ld = [&](const float* base, int64_t off, int valid) -> f32x4 {
+            if constexpr (FULL)
+                return VEC ? *reinterpret_cast<const f32x4*>(base + off)
+                           : (f32x4)*reinterpret_cast<const f32x4_a4*>(base + off);
+            else
+                return load4<VEC>(base + (valid > 0 ? off : 0), valid);
+        };
         if constexpr (TA) {
             const int64_t gm = m0 + 4 * ta_mb;
             const int mvalid = (int)(M - gm < 4 ? (M - gm < 0 ? 0 : M - gm) : 4);
@@ -141,7 +155,7 @@ void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit
             for (int r = 0; r < 4; ++r) {
                 const int64_t gk = k0 + 4 * ta_kb + r;
                 const int valid = gk < K ? mvalid : 0;
-                ra[r] = load4<VEC>(p.A + (valid > 0 ? gk * p.lda + gm : 0), valid);
+                ra[r] = ld(p.A, gk * p.lda + gm, valid);
             }
         } else {
 #pragma unroll
@@ -149,7 +163,7 @@ void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit
                 const int r = t / 8 + i * (NT / 8), c = t % 8;
                 const int64_t gm = m0 + r, gk = k0 + 4 * c;
                 const int valid = (gm < M) ? (int)(K - gk < 4 ? K - gk : 4) : 0;
-                ra[i] = load4<VEC>(p.A + (valid > 0 ? gm * p.lda + gk : 0), valid);
+                ra[i] = ld(p.A, gm * p.lda + gk, valid);
             }
         }
         if constexpr (TB) {
@@ -159,7 +173,7 @@ void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit
             for (int r = 0; r < 4; ++r) {
                 const int64_t gn = n0 + 4 * tb_nb + r;
                 const int valid = gn < N ? kvalid : 0;
-                rb[r] = load4<VEC>(p.B + (valid > 0 ? gn * p.ldb + gk : 0), valid);
+                rb[r] = ld(p.B, gn * p.ldb + gk, valid);
             }
         } else {
 #pragma unroll
@@ -168,9 +182,14 @@ void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit
                 const int kr = idx / (BN / 4), c = idx % (BN / 4);
                 const int64_t gk = k0 + kr, gn = n0 + 4 * c;
                 const int valid = (gk < K) ? (int)(N - gn < 4 ? N - gn : 4) : 0;
-                rb[i] = load4<VEC>(p.B + (valid > 0 ? gk * p.ldb + gn : 0), valid);
+                rb[i] = ld(p.B, gk * p.ldb + gn, valid);
             }
         }
+    };
+    const bool full_tile = m0 + BM <= M && n0 + BN <= N;
+    auto gload = [&](int64_t k0) {
+        if (full_tile && k0 + kBK <= K) gload_slab(std::true_type{}, k0);
+        else gload_slab(std::false_type{}, k0);
     };
 
     auto sstore = [&](int stage) {
