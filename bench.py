@@ -178,6 +178,43 @@ def measure(w, steps: int, warmup: int, sets: int = 1, use_ws: bool = False, act
     return out
 
 
+def vendor_lines(steps: int, warmup: int):
+    """torch's own GEMM (the platform BLAS behind torch.mm / torch.addmm) on the
+    headline workloads' operands, timed like this library's calls. Context only:
+    it is not part of the path and not the benchmark's value."""
+    import torch
+    import gemm_inputs as gi
+    torch.backends.cuda.matmul.allow_tf32 = False
+    for wid, opb in ((2, 0), (3, 0), (4, 0), (51, 0), (52, 0), (52, 1)):
+        w = gi.WORKLOADS[wid]
+        inp = gi.make(w)
+        # As for this library's small-M lines, 4 operand sets (512 MiB of B)
+        # rotate so that the Infinity Cache cannot serve B.
+        sets = 4 if wid == 52 else 1
+        A = inp["A"].cuda()
+        Bs = [(inp["B"].t().contiguous() if opb else inp["B"]).cuda() for _ in range(sets)]
+        Bops = [B.t() if opb else B for B in Bs]
+        C0 = inp["C0"].cuda() if inp["C0"] is not None else None
+        out = torch.empty(w.M, w.N, dtype=A.dtype, device="cuda")
+        state = {"i": 0}
+
+        def call():
+            Bop = Bops[state["i"] % sets]
+            state["i"] += 1
+            if C0 is None or w.beta == 0:
+                torch.mm(A, Bop, out=out)
+                if w.alpha != 1:
+                    out.mul_(w.alpha)
+            else:
+                torch.addmm(C0, A, Bop, beta=w.beta, alpha=w.alpha, out=out)
+        sec = _time_calls(call, steps, warmup, torch.cuda.current_stream())
+        yield {"workload": w.name + (" (B stored N x K)" if opb else ""),
+               "library": "torch.mm / torch.addmm " + torch.__version__,
+               "ms": sec * 1e3, "tflops": tflops(gemm_flops(w.M, w.N, w.K), sec),
+               "gbs": w.algorithmic_bytes / sec / 1e9}
+        del A, Bs, Bops, C0, out
+
+
 def kernel_source_sha(path: str) -> str:
     import hashlib
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
@@ -245,6 +282,9 @@ def main(argv=None) -> int:
                     help="time one workload id (1, 2, 3, 4, 51, 52; 61-63 mid-size) and print its line "
                          "(with the split-K line for 51 and 52, the bias + GELU line for 2 and 4, "
                          "the transposed-layout lines for 2, 3 and 52)")
+    ap.add_argument("--vendor", action="store_true",
+                    help="time torch's own GEMM (torch.mm / torch.addmm, the platform BLAS) on the "
+                         "headline workloads, for context beside this library's lines")
     ap.add_argument("--copy-mib", type=int, default=None,
                     help="time a plain device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args(argv)
@@ -269,6 +309,11 @@ def main(argv=None) -> int:
         stream = torch.cuda.current_stream()
         sec = _time_calls(lambda: dst.copy_(src), args.steps, args.warmup, stream, settle=0.0)
         print(json.dumps({"copy_bytes": n, "ms": sec * 1e3, "gbs": 2 * n / sec / 1e9}), flush=True)
+        return 0
+
+    if args.vendor:
+        for line in vendor_lines(args.steps, args.warmup):
+            print(json.dumps(line), flush=True)
         return 0
 
     if args.only is not None:
