@@ -55,9 +55,18 @@ namespace {
 constexpr int kBK = 64;            // k per slab (8 chunks of 8 bf16)
 constexpr int kGroupM = 4;         // tile rows per raster group
 
-// Element offset of chunk `c` (8 bf16) of row `row` in a [rows][64] LDS tile.
+// Element offset of chunk `c` (8 bf16) of row `row` in a [rows][64] LDS tile,
+// with an XOR-swizzled chunk position per tile. For the A tile, (row ^ row / 4
+// ^ row / 32) mod 8 measures conflict-free on gfx950 (SQ_LDS_BANK_CONFLICT on
+// probes of each pattern) for its fragment reads (16 consecutive rows), its
+// chunk stores and its transposed block stores (rows 8 apart); the B tile's
+// fragment reads take rows 8 apart, which cost one extra cycle per 16 lanes
+// under every chunk XOR tried, and it keeps (row ^ row / 8) mod 8, under
+// which its stores are conflict-free.
+template <bool ATILE>
 __device__ __forceinline__ int lds_off(int row, int c) {
-    return row * kBK + ((c ^ ((row ^ (row >> 3)) & 7)) << 3);
+    const int x = ATILE ? (row ^ (row >> 2) ^ (row >> 5)) : (row ^ (row >> 3));
+    return row * kBK + ((c ^ (x & 7)) << 3);
 }
 
 // 8 consecutive bf16 from p, of which the first `valid` are in range.
@@ -159,14 +168,16 @@ void gemm_bf16_mfma_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
             }
         }
     };
-    auto store_chunks = [&](uint16_t* S, const u32x4* regs) {
+    auto store_chunks = [&](auto a_tile, uint16_t* S, const u32x4* regs) {
+        constexpr bool AT = decltype(a_tile)::value;
 #pragma unroll
         for (int i = 0; i < A_CHUNKS; ++i) {
             const int r = t / 8 + i * (NT / 8), c = t % 8;
-            *reinterpret_cast<u32x4*>(S + lds_off(r, c)) = regs[i];
+            *reinterpret_cast<u32x4*>(S + lds_off<AT>(r, c)) = regs[i];
         }
     };
-    auto store_blocks = [&](uint16_t* S, const u32x4 (*regs)[8]) {
+    auto store_blocks = [&](auto a_tile, uint16_t* S, const u32x4 (*regs)[8]) {
+        constexpr bool AT = decltype(a_tile)::value;
 #pragma unroll
         for (int bi = 0; bi < B_BLOCKS; ++bi) {
             const int blk = t + bi * NT;
@@ -175,7 +186,7 @@ void gemm_bf16_mfma_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
             transpose8x8(regs[bi], y);
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                *reinterpret_cast<u32x4*>(S + lds_off(8 * nb + j, kb)) = y[j];
+                *reinterpret_cast<u32x4*>(S + lds_off<AT>(8 * nb + j, kb)) = y[j];
         }
     };
     // With TA the A registers hold blocks and with TB the B registers hold
@@ -201,10 +212,10 @@ void gemm_bf16_mfma_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
     auto sstore = [&](int stage) {
         uint16_t* As = smem + stage * STAGE;
         uint16_t* Bs = As + BM * kBK;
-        if constexpr (TA) store_blocks(As, ra_blocks);
-        else store_chunks(As, ra);
-        if constexpr (TB) store_chunks(Bs, rb_chunks);
-        else store_blocks(Bs, rb);
+        if constexpr (TA) store_blocks(std::true_type{}, As, ra_blocks);
+        else store_chunks(std::true_type{}, As, ra);
+        if constexpr (TB) store_chunks(std::false_type{}, Bs, rb_chunks);
+        else store_blocks(std::false_type{}, Bs, rb);
     };
 
     f32x4 acc[FM][FN];
@@ -224,10 +235,10 @@ void gemm_bf16_mfma_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
             bf16x8 a[FM], b[FN];
 #pragma unroll
             for (int i = 0; i < FM; ++i)
-                a[i] = *reinterpret_cast<const bf16x8*>(As + lds_off(wm0 + 16 * i + pl, 4 * ks + g));
+                a[i] = *reinterpret_cast<const bf16x8*>(As + lds_off<true>(wm0 + 16 * i + pl, 4 * ks + g));
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                b[j] = *reinterpret_cast<const bf16x8*>(Bs + lds_off(wn0 + FN * pl + j, 4 * ks + g));
+                b[j] = *reinterpret_cast<const bf16x8*>(Bs + lds_off<false>(wn0 + FN * pl + j, 4 * ks + g));
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll

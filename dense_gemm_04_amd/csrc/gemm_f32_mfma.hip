@@ -10,7 +10,8 @@
 //     B slab (32 x BN) [k][col] in a double-buffered LDS, loaded with 128-bit
 //     global loads one slab ahead (one barrier per slab);
 //   * A rows are 8 chunks of 4 floats with an XOR-swizzled chunk position, so
-//     the 128-bit fragment reads of a wave are bank-conflict free;
+//     the 128-bit fragment reads of a wave are bank-conflict free (checked
+//     with SQ_LDS_BANK_CONFLICT on probes of each access pattern);
 //   * each lane reads 4 consecutive k of A with one 128-bit LDS read and uses
 //     them in 4 successive MFMAs; the matching B values are one 128-bit read
 //     of 4 consecutive columns at that k, which feed 4 MFMA blocks whose
@@ -41,21 +42,25 @@ namespace {
 constexpr int kBK = 32;       // k per slab
 constexpr int kGroupM = 4;
 
-// Float offset of chunk `c` (4 floats) of row `row` in a [rows][32] tile.
+// Float offset of chunk `c` (4 floats) of row `row` in a [rows][32] tile. The
+// chunk XOR (row ^ row / 4) mod 8 measures conflict-free on gfx950 for the
+// fragment reads (16 consecutive rows x 4 chunks), the row-major stores (8
+// rows x 8 chunks) and the transposed stores (32 rows 4 apart x 2 chunks);
+// (row ^ row / 8) mod 8 cost the fragment reads 4 extra cycles each.
 __device__ __forceinline__ int a_off(int row, int c) {
-    return row * kBK + ((c ^ ((row ^ (row >> 3)) & 7)) << 2);
+    return row * kBK + ((c ^ ((row ^ (row >> 2)) & 7)) << 2);
 }
 
 // Float offset of column `col` (a multiple of 4) of row `kr` in a [32][BN]
-// tile. With a transposed B (SWZ) chunk positions are XORed with
-// 2 * ((kr / 4) mod 8): a row's 128-bit reads (consecutive chunks) stay
-// conflict-free, and the transposed stores, whose 16-lane phases write the
-// same chunks of 8 rows 4 apart, land on 16 distinct bank groups instead of
-// one (A B^T 111 -> 116 TFLOP/s at 4096^3). Row-major B is stored in plain
-// rows, which measured 1.4% faster for it.
+// tile. With a transposed B (SWZ) chunk positions are XORed with (kr / 4)
+// mod 8: a row's 128-bit reads (consecutive chunks) stay conflict-free, and
+// so do the transposed stores, which write 2 chunks of 8 rows 4 apart per
+// 16 lanes (unswizzled they cost 53 extra cycles per store, an XOR with
+// 2 * ((kr / 4) mod 8) still 7.5). Row-major B is stored in plain rows, whose
+// stores and reads are conflict-free as they are.
 template <int BN, bool SWZ>
 __device__ __forceinline__ int b_off(int kr, int col) {
-    if constexpr (SWZ) return kr * BN + ((((col >> 2) ^ (((kr >> 2) & 7) << 1))) << 2);
+    if constexpr (SWZ) return kr * BN + ((((col >> 2) ^ ((kr >> 2) & 7))) << 2);
     return kr * BN + col;
 }
 
