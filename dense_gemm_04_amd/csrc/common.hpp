@@ -154,6 +154,13 @@ __device__ __forceinline__ void lds_only_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Barrier for a two-stage copy pipeline: this wave's LDS-destined copies have
+// landed (vmcnt 0), then an LDS-only workgroup barrier.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    lds_only_barrier();
+}
+
 // ---- split of the last round of tiles ---------------------------------------
 //
 // The simplest form of stream-K: workgroups 0 .. full - 1 each own a whole

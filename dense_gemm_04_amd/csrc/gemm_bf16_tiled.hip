@@ -100,13 +100,6 @@ __device__ __forceinline__ int opaque_lane() {
     return (int)__builtin_amdgcn_mbcnt_hi(m, __builtin_amdgcn_mbcnt_lo(m, 0u));
 }
 
-// Barrier for the two-stage pipeline: this wave's LDS-destined copies have
-// landed (vmcnt 0), then an LDS-only workgroup barrier.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    lds_only_barrier();
-}
-
 // ws (only with SPLIT and ts.tail > 0): [counters: one int per split tile,
 // padded to 256 bytes][slots: tail x parts partial tiles of BM x BN fp32,
 // value c of thread t at byte (c * threads + t) * 16 of its slot].

@@ -40,7 +40,11 @@ namespace dg {
 namespace {
 
 constexpr int kBK = 32;       // k per slab
-constexpr int kGroupM = 4;
+// Tile rows per raster group. Each XCD owns a contiguous run of tiles and runs
+// 64 workgroups at once (32 CUs x 2), so groups of 8 tile rows make each XCD's
+// round an 8 x 8 block of tiles: at 4096^3 the L2 fetches 537 MB per call
+// against 671 MB with groups of 4 (same time).
+constexpr int kGroupM = 8;
 
 // Float offset of chunk `c` (4 floats) of row `row` in a [rows][32] tile. The
 // chunk XOR (row ^ row / 4) mod 8 measures conflict-free on gfx950 for the
@@ -108,6 +112,10 @@ void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit
     static_assert(!TA || (kBK / 4) * (BM / 4) == NT, "transposed A: one block per thread");
     static_assert(!TB || (kBK / 4) * (BN / 4) == NT, "transposed B: one block per thread");
     static_assert(A_CHUNKS == 4 && B_CHUNKS == 4, "block loaders reuse the chunk registers");
+    // LDS-destined copies for row-major operands with 16-byte rows.
+    constexpr bool DMA = VEC && !TA && !TB;
+    static_assert(!DMA || (BM == 128 && BN == 128 && NT == 256),
+                  "the copy schedule covers 128 x 32 and 32 x 128 slabs with 4 waves");
 
     __shared__ __attribute__((aligned(16))) float smem[2 * STAGE];
 
@@ -268,15 +276,97 @@ void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit
         }
     };
 
-    gload(kb * kBK);
-    sstore(0);
-    __syncthreads();
-    for (int64_t kt = kb; kt < ke; ++kt) {
-        const int cur = (int)((kt - kb) & 1);
-        if (kt + 1 < ke) gload((kt + 1) * kBK);
-        compute(cur);
-        if (kt + 1 < ke) sstore(cur ^ 1);
+    if constexpr (DMA) {
+        // Row-major A and B with 16-byte rows: slabs go straight from global
+        // memory to LDS (buffer_load_dwordx4 ... lds, 1 KB per wave
+        // instruction), with no register staging and no LDS store
+        // instructions. Copy I of A fills tile rows 8 I .. 8 I + 7, lane l the
+        // 16 bytes at physical chunk l % 8 of row 8 I + l / 8, so it fetches
+        // the logical chunk that a_off puts there: l % 8 ^ ((row ^ row / 4)
+        // mod 8), which for row = 8 I + r is l % 8 ^ ((r ^ r / 4) mod 8) ^ 2 I
+        // mod 8. Copy J of B fills rows 2 J and 2 J + 1 in plain order. Each
+        // wave issues copies I, J = 4 wave .. 4 wave + 3 of each slab.
+        // Descriptors are re-based at every slab and end at the last valid
+        // element, so rows past M and K arrive as zeros; A's elements at
+        // k >= K inside rows below M are zeroed in LDS after they land.
+        const int ar = lane >> 3, ap = lane & 7;
+        const int s_ar = (ar ^ (ar >> 2)) & 7;
+        const int wv = __builtin_amdgcn_readfirstlane(wave);   // scalar copy offsets
+        uint32_t a_voff[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            a_voff[i] = (uint32_t)((ar * p.lda + 4 * (ap ^ s_ar ^ (2 * i))) * 4);
+        const uint32_t b_voff = (uint32_t)(((lane >> 5) * p.ldb + 4 * (lane & 31)) * 4);
+        const int64_t rows_a = M - m0 < BM ? M - m0 : BM;
+        const int64_t cols_b = N - n0 < BN ? N - n0 : BN;
+        auto dma = [&](int64_t kt, int stage) {
+            const int64_t k0 = kt * kBK;
+            const uint32_t As = lds_addr(smem + stage * STAGE);
+            const uint32_t Bs = As + BM * kBK * 4;
+            const rsrc_t ad = make_rsrc(p.A + m0 * p.lda + k0,
+                                        (uint32_t)(((rows_a - 1) * p.lda + (K - k0)) * 4));
+            const int64_t rows_b = K - k0 < kBK ? K - k0 : kBK;
+            const rsrc_t bd = make_rsrc(p.B + k0 * p.ldb + n0,
+                                        (uint32_t)(((rows_b - 1) * p.ldb + cols_b) * 4));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int I = 4 * wv + i;
+                dma16(ad, a_voff[i], (uint32_t)(8 * I * p.lda * 4), As + I * 1024);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int J = 4 * wv + j;
+                dma16(bd, b_voff, (uint32_t)(2 * J * p.ldb * 4), Bs + J * 1024);
+            }
+        };
+        // Zero A's elements at k >= K (kr = K - k0 valid) of one stage.
+        auto zero_a_tail = [&](int stage, int kr) {
+            float* As = smem + stage * STAGE;
+            for (int row = t; row < BM; row += NT) {
+#pragma unroll
+                for (int c = 0; c < kBK / 4; ++c) {
+                    if (4 * c + 4 <= kr) continue;
+                    f32x4* q = reinterpret_cast<f32x4*>(As + a_off(row, c));
+                    f32x4 v = *q;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = (4 * c + e < kr) ? v[e] : 0.f;
+                    *q = v;
+                }
+            }
+        };
+        const int k_tail = (int)(K - (nk - 1) * kBK);   // 1 .. kBK
+        const bool tail_here = ke == nk && k_tail < kBK;
+        dma(kb, 0);
+        lds_barrier();
+        if (tail_here && kb + 1 == ke) {
+            zero_a_tail(0, k_tail);
+            __syncthreads();
+        }
+        for (int64_t kt = kb; kt < ke; ++kt) {
+            const int cur = (int)((kt - kb) & 1);
+            // The other stage was last read in slab kt - 1, before the
+            // barrier that ended it.
+            if (kt + 1 < ke) dma(kt + 1, cur ^ 1);
+            compute(cur);
+            if (kt + 1 < ke) {
+                lds_barrier();
+                if (tail_here && kt + 2 == ke) {
+                    zero_a_tail(cur ^ 1, k_tail);
+                    __syncthreads();
+                }
+            }
+        }
+    } else {
+        gload(kb * kBK);
+        sstore(0);
         __syncthreads();
+        for (int64_t kt = kb; kt < ke; ++kt) {
+            const int cur = (int)((kt - kb) & 1);
+            if (kt + 1 < ke) gload((kt + 1) * kBK);
+            compute(cur);
+            if (kt + 1 < ke) sstore(cur ^ 1);
+            __syncthreads();
+        }
     }
 
     if (SPLIT && split_tile) {
@@ -425,8 +515,19 @@ hipError_t launch_tiles(const GemmArgs<float>& a, bool vec, void* ws, size_t ws_
 
 }  // namespace
 
+// True when every offset the LDS-destined copies form (within one slab, from
+// descriptors re-based per slab) fits in 31 bits: 128 rows of A and 32 rows
+// of B.
+static bool f32_copies_fit(const GemmArgs<float>& a) {
+    const int64_t lim = (int64_t)1 << 31;
+    return (128 * a.lda + 32) * 4 < lim && (32 * a.ldb + 128) * 4 < lim;
+}
+
 hipError_t launch_f32_mfma(const GemmArgs<float>& a, bool vec, void* ws, size_t ws_bytes, int cus,
                            hipStream_t s) {
+    // Row-major operands with 16-byte rows take the copy path; past its offset
+    // range they take the register-staged path at element alignment.
+    if (vec && !a.ta && !a.tb && !f32_copies_fit(a)) vec = false;
     return launch_tiles<128, 128, 2, 2>(a, vec, ws, ws_bytes, cus, s);
 }
 
