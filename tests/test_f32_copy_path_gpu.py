@@ -1,0 +1,98 @@
+"""GPU parity of the fp32 kernel's global -> LDS copy path (row-major A and B
+with 16-byte rows) at its edges, against the oracle:
+
+* ragged M, N and K, with every padding element of A and B set to NaN, so a
+  copy that let a padding element into the product (a row past M, a column of
+  A at k >= K, a row of B at k >= K) would show up as NaN in C;
+* split K over a workspace, where only the range that ends at K holds the
+  ragged tail;
+* a leading dimension of A just inside and just past the copies' 31-bit
+  offset range (past it the call takes the register-staged path).
+"""
+import pytest
+import torch
+
+import dense_gemm_04_amd as dg
+import gemm_inputs as gi
+import oracle
+from gpu_util import note, padded, to_f64, tol
+
+pytestmark = pytest.mark.gpu
+
+
+def run_nan_padded(A, B, lda, ldb, ldc, alpha=1.0, beta=0.0, C0=None, ws=False):
+    M, K = A.shape
+    N = B.shape[1]
+    _, a = padded(M, K, lda, "f32", fill=float("nan"))
+    _, b = padded(K, N, ldb, "f32", fill=float("nan"))
+    _, c = padded(M, N, ldc, "f32", fill=float("nan"))
+    a.copy_(A.cuda())
+    b.copy_(B.cuda())
+    if C0 is not None:
+        c.copy_(C0.cuda())
+    nbytes = dg.gemm_f32_workspace_size(M, N, K) if ws else 0
+    wbuf = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    if ws:
+        st = dg.gemm_f32_ws(M, N, K, alpha, a.data_ptr(), lda, b.data_ptr(), ldb, beta,
+                            c.data_ptr(), ldc, wbuf.data_ptr() if nbytes else None, nbytes, 0)
+    else:
+        st = dg.gemm_f32(M, N, K, alpha, a.data_ptr(), lda, b.data_ptr(), ldb, beta,
+                         c.data_ptr(), ldc, 0)
+    torch.cuda.synchronize()
+    return c.cpu(), st, nbytes
+
+
+def check(A, B, C, alpha=1.0, beta=0.0, C0=None):
+    R, D = oracle.gemm(gi.as_numpy(A), gi.as_numpy(B),
+                       None if (C0 is None or beta == 0) else gi.as_numpy(C0),
+                       float(alpha), float(beta), "f32")
+    err = oracle.max_rel_err(to_f64(C), R, D)
+    assert err <= tol("f32"), f"max error ratio {err:.3e}"
+
+
+# (M, N, K): one and several tiles, K from a single partial slab to several
+# slabs with a ragged tail, M and N ragged inside the last tile.
+SHAPES = [(1, 4, 1), (5, 12, 31), (128, 128, 32), (129, 130, 33), (200, 260, 63),
+          (300, 136, 100), (77, 300, 257), (256, 384, 1000)]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_nan_padding_never_reaches_c(shape):
+    M, N, K = shape
+    A = gi.random_matrix(M, K, "f32", 5100 + M)
+    B = gi.random_matrix(K, N, "f32", 5200 + N)
+    # 16-byte rows with at least one padding chunk after each row.
+    lda, ldb, ldc = (K + 3) // 4 * 4 + 4, (N + 3) // 4 * 4 + 8, N + 3
+    note(f"f32 copy path NaN padding M={M} N={N} K={K} lda={lda} ldb={ldb}")
+    C, st, _ = run_nan_padded(A, B, lda, ldb, ldc)
+    assert st == dg.GEMM_OK
+    assert torch.isfinite(C).all()
+    check(A, B, C)
+
+
+@pytest.mark.parametrize("shape", [(300, 200, 1000), (257, 264, 4100), (1100, 1030, 2100)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_split_k_with_ragged_tail_and_nan_padding(shape):
+    M, N, K = shape
+    A = gi.random_matrix(M, K, "f32", 5300 + M)
+    B = gi.random_matrix(K, N, "f32", 5400 + N)
+    C0 = gi.random_matrix(M, N, "f32", 5500 + K)
+    lda, ldb, ldc = (K + 3) // 4 * 4 + 4, (N + 3) // 4 * 4 + 4, N
+    note(f"f32 copy path split K M={M} N={N} K={K}")
+    C, st, nbytes = run_nan_padded(A, B, lda, ldb, ldc, alpha=0.5, beta=-1.5, C0=C0, ws=True)
+    assert st == dg.GEMM_OK
+    check(A, B, C, 0.5, -1.5, C0)
+
+
+@pytest.mark.parametrize("lda", [4_000_000, 4_200_000])
+def test_leading_dimension_at_the_copy_offset_limit(lda):
+    """128 rows of A span (128 * lda + 32) * 4 bytes: inside 2^31 at 4.0 M
+    (copy path), past it at 4.2 M (register-staged path). Only 3 rows exist,
+    so the copies of rows 8 .. 127 fall past the descriptor and read nothing."""
+    M, N, K = 3, 40, 50
+    A = gi.random_matrix(M, K, "f32", 5600)
+    B = gi.random_matrix(K, N, "f32", 5601)
+    note(f"f32 copy path lda={lda}")
+    C, st, _ = run_nan_padded(A, B, lda, N + 4, N)
+    assert st == dg.GEMM_OK
+    check(A, B, C)
