@@ -113,9 +113,13 @@ void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit
     static_assert(!TA || (kBK / 4) * (BM / 4) == NT, "transposed A: one block per thread");
     static_assert(!TB || (kBK / 4) * (BN / 4) == NT, "transposed B: one block per thread");
     static_assert(A_CHUNKS == 4 && B_CHUNKS == 4, "block loaders reuse the chunk registers");
-    // LDS-destined copies for row-major operands with 16-byte rows.
-    constexpr bool DMA = VEC && !TA && !TB;
-    static_assert(!DMA || (BM == 128 && BN == 128 && NT == 256),
+    // LDS-destined copies for operands with 16-byte rows, except a
+    // transposed A. With a transposed B (BKC) the B tile is staged [n][k]
+    // like A and read the way A is, so its MFMA blocks cover 16 consecutive
+    // columns each instead of interleaved ones.
+    constexpr bool DMA = VEC && !TA;
+    constexpr bool BKC = DMA && TB;
+    static_assert(!DMA || (BM == 128 && BN == 128 && NT == 256 && NG == 1),
                   "the copy schedule covers 128 x 32 and 32 x 128 slabs with 4 waves");
 
     __shared__ __attribute__((aligned(16))) float smem[2 * STAGE];
@@ -252,6 +256,30 @@ void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit
     auto compute = [&](int stage) {
         const float* As = smem + stage * STAGE;
         const float* Bs = As + BM * kBK;
+        if constexpr (BKC) {
+            // B^T staged [n][k]: lane (pl, g) reads 4 consecutive k of column
+            // wn0 + 16 j + pl, used in 4 successive MFMAs with A's matching
+            // 4 k; block j covers columns wn0 + 16 j .. + 15.
+#pragma unroll
+            for (int q = 0; q < kBK / 16; ++q) {
+                f32x4 a[FM], b[4];
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+                    a[i] = *reinterpret_cast<const f32x4*>(As + a_off(wm0 + 16 * i + pl, 4 * q + g));
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    b[j] = *reinterpret_cast<const f32x4*>(Bs + a_off(wn0 + 16 * j + pl, 4 * q + g));
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+#pragma unroll
+                    for (int i = 0; i < FM; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            acc[i][0][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                a[i][s], b[j][s], acc[i][0][j], 0, 0, 0);
+            }
+            return;
+        }
 #pragma unroll
         for (int q = 0; q < kBK / 16; ++q) {
             f32x4 a[FM];
@@ -298,32 +326,48 @@ void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit
         for (int i = 0; i < 4; ++i)
             a_voff[i] = (uint32_t)((ar * p.lda + 4 * (ap ^ s_ar ^ (2 * i))) * 4);
         const uint32_t b_voff = (uint32_t)(((lane >> 5) * p.ldb + 4 * (lane & 31)) * 4);
+        uint32_t bt_voff[4];     // transposed B: the A copy pattern over ldb
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            bt_voff[i] = (uint32_t)((ar * p.ldb + 4 * (ap ^ s_ar ^ (2 * i))) * 4);
         const int64_t rows_a = M - m0 < BM ? M - m0 : BM;
-        const int64_t cols_b = N - n0 < BN ? N - n0 : BN;
+        const int64_t cols_b = N - n0 < BN ? N - n0 : BN;   // also B^T's valid rows
         auto dma = [&](int64_t kt, int stage) {
             const int64_t k0 = kt * kBK;
             const uint32_t As = lds_addr(smem + stage * STAGE);
             const uint32_t Bs = As + BM * kBK * 4;
             const rsrc_t ad = make_rsrc(p.A + m0 * p.lda + k0,
                                         (uint32_t)(((rows_a - 1) * p.lda + (K - k0)) * 4));
-            const int64_t rows_b = K - k0 < kBK ? K - k0 : kBK;
-            const rsrc_t bd = make_rsrc(p.B + k0 * p.ldb + n0,
-                                        (uint32_t)(((rows_b - 1) * p.ldb + cols_b) * 4));
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int I = 4 * wv + i;
                 dma16(ad, a_voff[i], (uint32_t)(8 * I * p.lda * 4), As + I * 1024);
             }
+            if constexpr (BKC) {
+                const rsrc_t bd = make_rsrc(p.B + n0 * p.ldb + k0,
+                                            (uint32_t)(((cols_b - 1) * p.ldb + (K - k0)) * 4));
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int J = 4 * wv + j;
-                dma16(bd, b_voff, (uint32_t)(2 * J * p.ldb * 4), Bs + J * 1024);
+                for (int j = 0; j < 4; ++j) {
+                    const int J = 4 * wv + j;
+                    dma16(bd, bt_voff[j], (uint32_t)(8 * J * p.ldb * 4), Bs + J * 1024);
+                }
+            } else {
+                const int64_t rows_b = K - k0 < kBK ? K - k0 : kBK;
+                const rsrc_t bd = make_rsrc(p.B + k0 * p.ldb + n0,
+                                            (uint32_t)(((rows_b - 1) * p.ldb + cols_b) * 4));
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int J = 4 * wv + j;
+                    dma16(bd, b_voff, (uint32_t)(2 * J * p.ldb * 4), Bs + J * 1024);
+                }
             }
         };
-        // Zero A's elements at k >= K (kr = K - k0 valid) of one stage.
+        // Zero the elements at k >= K (kr = K - k0 valid) of one stage's A
+        // tile, and of its B^T tile when B is staged [n][k] too.
         auto zero_a_tail = [&](int stage, int kr) {
             float* As = smem + stage * STAGE;
-            for (int row = t; row < BM; row += NT) {
+            constexpr int kRows = BKC ? BM + BN : BM;    // B^T rows follow A's
+            for (int row = t; row < kRows; row += NT) {
 #pragma unroll
                 for (int c = 0; c < kBK / 4; ++c) {
                     if (4 * c + 4 <= kr) continue;
@@ -424,6 +468,34 @@ void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit
     }
 
     const float alpha = p.alpha, beta = p.beta;
+    if constexpr (BKC) {
+        // Block j of row block i: lane (pl, g) holds rows 16 i + 4 g + r of
+        // column wn0 + 16 j + pl; 16 lanes store 64 consecutive bytes.
+        float bvk[4];
+        if constexpr (EPI) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bvk[j] = bias_at(p, n0 + wn0 + 16 * j + pl);
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t row = m0 + wm0 + 16 * i + 4 * g + r;
+                if (row >= M) continue;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int64_t col = n0 + wn0 + 16 * j + pl;
+                    if (col >= N) continue;
+                    float x = alpha * acc[i][0][j][r];
+                    if constexpr (EPI) x = activate(x + bvk[j], p.act);
+                    float* dst = p.C + row * p.ldc + col;
+                    if (beta != 0.f) x += beta * *dst;
+                    *dst = x;
+                }
+            }
+        }
+        return;
+    }
     float bv[NG][4];
     if constexpr (EPI) {
 #pragma unroll
@@ -517,18 +589,20 @@ hipError_t launch_tiles(const GemmArgs<float>& a, bool vec, void* ws, size_t ws_
 }  // namespace
 
 // True when every offset the LDS-destined copies form (within one slab, from
-// descriptors re-based per slab) fits in 31 bits: 128 rows of A and 32 rows
-// of B.
+// descriptors re-based per slab) fits in 31 bits: 128 rows of A, and 32 rows
+// of B or 128 rows of a transposed B.
 static bool f32_copies_fit(const GemmArgs<float>& a) {
     const int64_t lim = (int64_t)1 << 31;
-    return (128 * a.lda + 32) * 4 < lim && (32 * a.ldb + 128) * 4 < lim;
+    return (128 * a.lda + 32) * 4 < lim &&
+           (a.tb ? 128 * a.ldb + 32 : 32 * a.ldb + 128) * 4 < lim;
 }
 
 hipError_t launch_f32_mfma(const GemmArgs<float>& a, bool vec, void* ws, size_t ws_bytes, int cus,
                            hipStream_t s) {
-    // Row-major operands with 16-byte rows take the copy path; past its offset
-    // range they take the register-staged path at element alignment.
-    if (vec && !a.ta && !a.tb && !f32_copies_fit(a)) vec = false;
+    // Operands with 16-byte rows (A not transposed) take the copy path; past
+    // its offset range they take the register-staged path at element
+    // alignment.
+    if (vec && !a.ta && !f32_copies_fit(a)) vec = false;
     return launch_tiles<128, 128, 2, 2>(a, vec, ws, ws_bytes, cus, s);
 }
 
