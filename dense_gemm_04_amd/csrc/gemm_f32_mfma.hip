@@ -113,12 +113,16 @@ void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit
     static_assert(!TA || (kBK / 4) * (BM / 4) == NT, "transposed A: one block per thread");
     static_assert(!TB || (kBK / 4) * (BN / 4) == NT, "transposed B: one block per thread");
     static_assert(A_CHUNKS == 4 && B_CHUNKS == 4, "block loaders reuse the chunk registers");
-    // LDS-destined copies for operands with 16-byte rows, except a
-    // transposed A. With a transposed B (BKC) the B tile is staged [n][k]
-    // like A and read the way A is, so its MFMA blocks cover 16 consecutive
-    // columns each instead of interleaved ones.
-    constexpr bool DMA = VEC && !TA;
-    constexpr bool BKC = DMA && TB;
+    // LDS-destined copies for operands with 16-byte rows. Each operand is
+    // staged as it is stored: a row-major A as [m][k] and a transposed B as
+    // [n][k] (k-contiguous, swizzled by a_off, read 4 consecutive k per lane),
+    // a row-major B as [k][n] and a transposed A as [k][m] (plain rows, read
+    // 4 consecutive n or m per lane). A k-contiguous operand's MFMA blocks
+    // cover 16 consecutive rows (columns); an m/n-contiguous operand's blocks
+    // are 4-way interleaved.
+    constexpr bool DMA = VEC;
+    constexpr bool AMC = DMA && TA;      // A^T staged [k][m]
+    constexpr bool BKC = DMA && TB;      // B^T staged [n][k]
     static_assert(!DMA || (BM == 128 && BN == 128 && NT == 256 && NG == 1),
                   "the copy schedule covers 128 x 32 and 32 x 128 slabs with 4 waves");
 
@@ -256,27 +260,37 @@ void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit
     auto compute = [&](int stage) {
         const float* As = smem + stage * STAGE;
         const float* Bs = As + BM * kBK;
-        if constexpr (BKC) {
-            // B^T staged [n][k]: lane (pl, g) reads 4 consecutive k of column
-            // wn0 + 16 j + pl, used in 4 successive MFMAs with A's matching
-            // 4 k; block j covers columns wn0 + 16 j .. + 15.
+        if constexpr (AMC || BKC) {
+            // k-contiguous tile: lane (pl, g) reads 4 consecutive k of row
+            // (column) 16 x + pl once per 16 k and uses them in 4 successive
+            // MFMAs. m/n-contiguous tile: one 128-bit read per k of 4
+            // consecutive rows (columns) 4 pl .. 4 pl + 3, one per block.
 #pragma unroll
             for (int q = 0; q < kBK / 16; ++q) {
                 f32x4 a[FM], b[4];
+                if constexpr (!AMC) {
 #pragma unroll
-                for (int i = 0; i < FM; ++i)
-                    a[i] = *reinterpret_cast<const f32x4*>(As + a_off(wm0 + 16 * i + pl, 4 * q + g));
+                    for (int i = 0; i < FM; ++i)
+                        a[i] = *reinterpret_cast<const f32x4*>(As + a_off(wm0 + 16 * i + pl, 4 * q + g));
+                }
+                if constexpr (BKC) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    b[j] = *reinterpret_cast<const f32x4*>(Bs + a_off(wn0 + 16 * j + pl, 4 * q + g));
+                    for (int j = 0; j < 4; ++j)
+                        b[j] = *reinterpret_cast<const f32x4*>(Bs + a_off(wn0 + 16 * j + pl, 4 * q + g));
+                }
 #pragma unroll
-                for (int s = 0; s < 4; ++s)
+                for (int s = 0; s < 4; ++s) {
+                    const int kr = 16 * q + 4 * g + s;
+                    f32x4 a4, b4;
+                    if constexpr (AMC) a4 = *reinterpret_cast<const f32x4*>(As + kr * BM + wm0 + 4 * pl);
+                    if constexpr (!BKC) b4 = *reinterpret_cast<const f32x4*>(Bs + kr * BN + wn0 + 4 * pl);
 #pragma unroll
                     for (int i = 0; i < FM; ++i)
 #pragma unroll
                         for (int j = 0; j < 4; ++j)
                             acc[i][0][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                                a[i][s], b[j][s], acc[i][0][j], 0, 0, 0);
+                                AMC ? a4[i] : a[i][s], BKC ? b[j][s] : b4[j], acc[i][0][j], 0, 0, 0);
+                }
             }
             return;
         }
@@ -326,6 +340,7 @@ void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit
         for (int i = 0; i < 4; ++i)
             a_voff[i] = (uint32_t)((ar * p.lda + 4 * (ap ^ s_ar ^ (2 * i))) * 4);
         const uint32_t b_voff = (uint32_t)(((lane >> 5) * p.ldb + 4 * (lane & 31)) * 4);
+        const uint32_t at_voff = (uint32_t)(((lane >> 5) * p.lda + 4 * (lane & 31)) * 4);
         uint32_t bt_voff[4];     // transposed B: the A copy pattern over ldb
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -336,12 +351,25 @@ void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit
             const int64_t k0 = kt * kBK;
             const uint32_t As = lds_addr(smem + stage * STAGE);
             const uint32_t Bs = As + BM * kBK * 4;
-            const rsrc_t ad = make_rsrc(p.A + m0 * p.lda + k0,
-                                        (uint32_t)(((rows_a - 1) * p.lda + (K - k0)) * 4));
+            const int64_t rows_k = K - k0 < kBK ? K - k0 : kBK;
+            if constexpr (AMC) {
+                // A^T (K x M storage): copy I fills k rows 2 I, 2 I + 1 of
+                // [32][128], plain, like a row-major B.
+                const rsrc_t ad = make_rsrc(p.A + k0 * p.lda + m0,
+                                            (uint32_t)(((rows_k - 1) * p.lda + rows_a) * 4));
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int I = 4 * wv + i;
-                dma16(ad, a_voff[i], (uint32_t)(8 * I * p.lda * 4), As + I * 1024);
+                for (int i = 0; i < 4; ++i) {
+                    const int I = 4 * wv + i;
+                    dma16(ad, at_voff, (uint32_t)(2 * I * p.lda * 4), As + I * 1024);
+                }
+            } else {
+                const rsrc_t ad = make_rsrc(p.A + m0 * p.lda + k0,
+                                            (uint32_t)(((rows_a - 1) * p.lda + (K - k0)) * 4));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int I = 4 * wv + i;
+                    dma16(ad, a_voff[i], (uint32_t)(8 * I * p.lda * 4), As + I * 1024);
+                }
             }
             if constexpr (BKC) {
                 const rsrc_t bd = make_rsrc(p.B + n0 * p.ldb + k0,
@@ -352,9 +380,8 @@ void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit
                     dma16(bd, bt_voff[j], (uint32_t)(8 * J * p.ldb * 4), Bs + J * 1024);
                 }
             } else {
-                const int64_t rows_b = K - k0 < kBK ? K - k0 : kBK;
                 const rsrc_t bd = make_rsrc(p.B + k0 * p.ldb + n0,
-                                            (uint32_t)(((rows_b - 1) * p.ldb + cols_b) * 4));
+                                            (uint32_t)(((rows_k - 1) * p.ldb + cols_b) * 4));
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int J = 4 * wv + j;
@@ -362,12 +389,14 @@ void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit
                 }
             }
         };
-        // Zero the elements at k >= K (kr = K - k0 valid) of one stage's A
-        // tile, and of its B^T tile when B is staged [n][k] too.
+        // Zero the elements at k >= K (kr = K - k0 valid) of one stage's
+        // k-contiguous tiles: A's rows 0 .. BM - 1 unless A is staged [k][m],
+        // B^T's rows after them (a_off(BM + n, c) is B^T's a_off(n, c)) when B
+        // is staged [n][k]. An m/n-contiguous tile has zero rows there already.
+        constexpr int kZeroLo = AMC ? BM : 0, kZeroHi = BKC ? BM + BN : BM;
         auto zero_a_tail = [&](int stage, int kr) {
             float* As = smem + stage * STAGE;
-            constexpr int kRows = BKC ? BM + BN : BM;    // B^T rows follow A's
-            for (int row = t; row < kRows; row += NT) {
+            for (int row = kZeroLo + t; row < kZeroHi; row += NT) {
 #pragma unroll
                 for (int c = 0; c < kBK / 4; ++c) {
                     if (4 * c + 4 <= kr) continue;
@@ -380,7 +409,7 @@ void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit
             }
         };
         const int k_tail = (int)(K - (nk - 1) * kBK);   // 1 .. kBK
-        const bool tail_here = ke == nk && k_tail < kBK;
+        const bool tail_here = kZeroLo < kZeroHi && ke == nk && k_tail < kBK;
         dma(kb, 0);
         lds_barrier();
         if (tail_here && kb + 1 == ke) {
@@ -469,8 +498,9 @@ void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit
 
     const float alpha = p.alpha, beta = p.beta;
     if constexpr (BKC) {
-        // Block j of row block i: lane (pl, g) holds rows 16 i + 4 g + r of
-        // column wn0 + 16 j + pl; 16 lanes store 64 consecutive bytes.
+        // Block j of row block i: lane (pl, g) holds rows 16 i + 4 g + r (or
+        // 16 g + 4 r + i with A staged [k][m]) of column wn0 + 16 j + pl; 16
+        // lanes store 64 consecutive bytes.
         float bvk[4];
         if constexpr (EPI) {
 #pragma unroll
@@ -480,7 +510,7 @@ void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit
         for (int i = 0; i < FM; ++i) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int64_t row = m0 + wm0 + 16 * i + 4 * g + r;
+                const int64_t row = m0 + wm0 + (AMC ? 16 * g + 4 * r + i : 16 * i + 4 * g + r);
                 if (row >= M) continue;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -507,7 +537,8 @@ void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int64_t row = m0 + wm0 + 16 * i + 4 * g + r;
+            // Block i of an m-contiguous A covers rows 4 x + i.
+            const int64_t row = m0 + wm0 + (AMC ? 16 * g + 4 * r + i : 16 * i + 4 * g + r);
             if (row >= M) continue;
 #pragma unroll
             for (int gq = 0; gq < NG; ++gq) {
@@ -589,20 +620,19 @@ hipError_t launch_tiles(const GemmArgs<float>& a, bool vec, void* ws, size_t ws_
 }  // namespace
 
 // True when every offset the LDS-destined copies form (within one slab, from
-// descriptors re-based per slab) fits in 31 bits: 128 rows of A, and 32 rows
-// of B or 128 rows of a transposed B.
+// descriptors re-based per slab) fits in 31 bits: 128 rows of a k-contiguous
+// operand (row-major A, transposed B), 32 rows of the other kind.
 static bool f32_copies_fit(const GemmArgs<float>& a) {
     const int64_t lim = (int64_t)1 << 31;
-    return (128 * a.lda + 32) * 4 < lim &&
+    return (a.ta ? 32 * a.lda + 128 : 128 * a.lda + 32) * 4 < lim &&
            (a.tb ? 128 * a.ldb + 32 : 32 * a.ldb + 128) * 4 < lim;
 }
 
 hipError_t launch_f32_mfma(const GemmArgs<float>& a, bool vec, void* ws, size_t ws_bytes, int cus,
                            hipStream_t s) {
-    // Operands with 16-byte rows (A not transposed) take the copy path; past
-    // its offset range they take the register-staged path at element
-    // alignment.
-    if (vec && !a.ta && !f32_copies_fit(a)) vec = false;
+    // Operands with 16-byte rows take the copy path; past its offset range
+    // they take the register-staged path at element alignment.
+    if (vec && !f32_copies_fit(a)) vec = false;
     return launch_tiles<128, 128, 2, 2>(a, vec, ws, ws_bytes, cus, s);
 }
 

@@ -8,8 +8,9 @@ with 16-byte rows) at its edges, against the oracle:
   ragged tail;
 * a leading dimension of A just inside and just past the copies' 31-bit
   offset range (past it the call takes the register-staged path);
-* B stored N x K (A B^T), whose tile is staged k-contiguous like A's, with
-  the same NaN padding, ragged shapes and split K.
+* B stored N x K (A B^T), A stored K x M (A^T B) and both (A^T B^T), each
+  operand staged in LDS the way it is stored, with the same NaN padding,
+  ragged shapes and split K.
 """
 import pytest
 import torch
@@ -100,36 +101,42 @@ def test_leading_dimension_at_the_copy_offset_limit(lda):
     check(A, B, C)
 
 
-def run_bt_nan_padded(A, Bt, lda, ldb, ldc, alpha=1.0, beta=0.0, C0=None, ws=False):
-    """C = alpha * A * Bt^T + beta * C0 with Bt stored N x K, NaN padding."""
+def run_op_nan_padded(opa, opb, A, B, alpha, beta, C0, ws, pad):
+    """C = alpha * op(A) op(B) + beta * C0 through gemm_f32_op, with A stored
+    K x M when opa and B stored N x K when opb; every padding element NaN."""
     M, K = A.shape
-    N = Bt.shape[0]
-    _, a = padded(M, K, lda, "f32", fill=float("nan"))
-    _, b = padded(N, K, ldb, "f32", fill=float("nan"))
+    N = B.shape[1]
+    As = A.t().contiguous() if opa else A
+    Bs = B.t().contiguous() if opb else B
+    lda = (As.shape[1] + 3) // 4 * 4 + pad
+    ldb = (Bs.shape[1] + 3) // 4 * 4 + 2 * pad
+    ldc = N + 1
+    _, a = padded(As.shape[0], As.shape[1], lda, "f32", fill=float("nan"))
+    _, b = padded(Bs.shape[0], Bs.shape[1], ldb, "f32", fill=float("nan"))
     _, c = padded(M, N, ldc, "f32", fill=float("nan"))
-    a.copy_(A.cuda())
-    b.copy_(Bt.cuda())
+    a.copy_(As.cuda())
+    b.copy_(Bs.cuda())
     if C0 is not None:
         c.copy_(C0.cuda())
     nbytes = dg.gemm_f32_workspace_size(M, N, K) if ws else 0
     wbuf = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device="cuda")
-    st = dg.gemm_f32_op(dg.OP_N, dg.OP_T, M, N, K, alpha, a.data_ptr(), lda, b.data_ptr(), ldb,
+    st = dg.gemm_f32_op(opa, opb, M, N, K, alpha, a.data_ptr(), lda, b.data_ptr(), ldb,
                         beta, c.data_ptr(), ldc, None, 0,
                         wbuf.data_ptr() if nbytes else None, nbytes, 0)
     torch.cuda.synchronize()
     return c.cpu(), st
 
 
+@pytest.mark.parametrize("ops", [(0, 1), (1, 0), (1, 1)], ids=["ABt", "AtB", "AtBt"])
 @pytest.mark.parametrize("shape", SHAPES + [(1100, 1030, 2100)], ids=lambda s: "x".join(map(str, s)))
-def test_transposed_b_nan_padding_never_reaches_c(shape):
+def test_transposed_nan_padding_never_reaches_c(shape, ops):
     M, N, K = shape
     A = gi.random_matrix(M, K, "f32", 5700 + M)
-    Bt = gi.random_matrix(N, K, "f32", 5800 + N)
+    B = gi.random_matrix(K, N, "f32", 5800 + N)
     C0 = gi.random_matrix(M, N, "f32", 5900 + K)
-    lda, ldb, ldc = (K + 3) // 4 * 4 + 4, (K + 3) // 4 * 4 + 8, N + 1
     ws = M * N > 1_000_000
-    note(f"f32 copy path A B^T NaN padding M={M} N={N} K={K} ws={ws}")
-    C, st = run_bt_nan_padded(A, Bt, lda, ldb, ldc, alpha=1.25, beta=0.5, C0=C0, ws=ws)
+    note(f"f32 copy path ops={ops} NaN padding M={M} N={N} K={K} ws={ws}")
+    C, st = run_op_nan_padded(ops[0], ops[1], A, B, 1.25, 0.5, C0, ws, pad=4)
     assert st == dg.GEMM_OK
     assert torch.isfinite(C).all()
-    check(A, Bt.t().contiguous(), C, 1.25, 0.5, C0)
+    check(A, B, C, 1.25, 0.5, C0)
