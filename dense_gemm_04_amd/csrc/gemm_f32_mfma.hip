@@ -1,31 +1,32 @@
-// fp32 GEMM (SGEMM) on gfx950 matrix cores: C = alpha * A * B + beta * C,
-// row-major, fp32 products and fp32 accumulation (v_mfma_f32_16x16x4_f32).
+// fp32 GEMM (SGEMM) on gfx950 matrix cores: C = alpha * op(A) * op(B) + beta * C,
+// fp32 products and fp32 accumulation (v_mfma_f32_16x16x4_f32).
 //
 // The RTX 3090 SGEMM article builds its 10.23 TFLOPS kernel from shared-memory
 // tiles (section 3), float4 loads (section 4), register accumulators and
 // double buffering (section 5). The same ideas are kept here, but the inner
 // product runs on the fp32 matrix cores instead of per-thread FMAs:
 //   * one workgroup per BM x BN tile of C, renumbered per XCD;
-//   * K in slabs of BK = 32; the A slab (BM x 32) is stored [row][k] and the
-//     B slab (32 x BN) [k][col] in a double-buffered LDS, loaded with 128-bit
-//     global loads one slab ahead (one barrier per slab);
-//   * A rows are 8 chunks of 4 floats with an XOR-swizzled chunk position, so
-//     the 128-bit fragment reads of a wave are bank-conflict free (checked
-//     with SQ_LDS_BANK_CONFLICT on probes of each access pattern);
-//   * each lane reads 4 consecutive k of A with one 128-bit LDS read and uses
-//     them in 4 successive MFMAs; the matching B values are one 128-bit read
-//     of 4 consecutive columns at that k, which feed 4 MFMA blocks whose
-//     columns are interleaved (block j covers columns 4p + j, p = 0..15);
-//   * after the loop each lane holds 4 consecutive columns of a row, so the
-//     fused alpha/beta epilogue (with EPI, bias and activation before the
-//     beta term) uses 128-bit loads and stores.
+//   * K in slabs of BK = 32 in a double-buffered LDS (one barrier per slab);
+//   * operands with 16-byte rows are copied from global memory straight into
+//     LDS (buffer_load_dwordx4 ... lds) one slab ahead, each in its stored
+//     layout: a k-contiguous operand (row-major A, transposed B) as [row][k]
+//     with an XOR-swizzled chunk position, an m/n-contiguous one (row-major B,
+//     transposed A) as [k][col] in plain rows;
+//   * a k-contiguous tile gives each lane 4 consecutive k of one row per
+//     128-bit LDS read, used in 4 successive MFMAs (blocks of 16 consecutive
+//     rows); an m/n-contiguous tile gives each lane 4 consecutive rows at one
+//     k, one per MFMA block (blocks interleaved 4 ways);
+//   * every LDS access pattern measures bank-conflict free
+//     (SQ_LDS_BANK_CONFLICT on probes of each pattern);
+//   * the fused alpha/beta epilogue (with EPI, bias and activation before the
+//     beta term) follows the block layout: 128-bit loads and stores when a
+//     lane holds 4 consecutive columns, element-wise ones otherwise.
 //
-// Rows that are not 16-byte aligned (VEC = false) use the same 128-bit
-// accesses at 4-byte alignment, and element-wise ones only at the edges.
-//
-// Transposed operands (TA: A stored K x M; TB: B stored N x K) are loaded as
-// 4 x 4 blocks (four 128-bit loads along the contiguous dimension) and
-// transposed in registers, so the LDS layout and the MFMA loop stay the same.
+// Rows that are not 16-byte aligned (VEC = false) are register-staged: the
+// same 128-bit global accesses at 4-byte alignment (element-wise only at the
+// edges), then LDS stores. Transposed operands on that path are loaded as
+// 4 x 4 blocks and transposed in registers, so the LDS layout is that of
+// row-major operands.
 //
 // Operand layout of v_mfma_f32_16x16x4_f32: lane l = p + 16 g supplies A(row p,
 // k_g) and B(k_g, col p) for one k per lane group g, and receives D(row 4g + i,
