@@ -216,8 +216,17 @@ def vendor_lines(steps: int, warmup: int):
 
 
 def kernel_source_sha(path: str) -> str:
+    """First 16 hex digits of the sha256 of a kernel source's code: `//`
+    comments, trailing blanks and empty lines removed, so that editing a
+    comment leaves a counter summary current while any code change does not."""
     import hashlib
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    import re
+    code = []
+    for line in open(path, encoding="utf-8"):
+        line = re.sub(r"//.*", "", line).rstrip()
+        if line:
+            code.append(line)
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
 def measured_traffic(summary: str, source: str):

@@ -56,3 +56,15 @@ def test_workload_bytes_and_flops():
 def test_multi_gpu_request_is_refused(capsys):
     assert bench.main(["--gpus", "2"]) == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_source_sha_follows_code_not_comments(tmp_path):
+    """A counter summary stays current across comment edits, not code edits."""
+    a = tmp_path / "a.hip"
+    b = tmp_path / "b.hip"
+    c = tmp_path / "c.hip"
+    a.write_text("// header\nint f(int x) {  // trailing\n    return x + 1;\n}\n")
+    b.write_text("// another header\n\nint f(int x) {\n    return x + 1;   \n}\n// end\n")
+    c.write_text("// header\nint f(int x) {  // trailing\n    return x + 2;\n}\n")
+    assert bench.kernel_source_sha(str(a)) == bench.kernel_source_sha(str(b))
+    assert bench.kernel_source_sha(str(a)) != bench.kernel_source_sha(str(c))
