@@ -321,18 +321,21 @@ void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit
     };
 
     if constexpr (DMA) {
-        // Row-major A and B with 16-byte rows: slabs go straight from global
-        // memory to LDS (buffer_load_dwordx4 ... lds, 1 KB per wave
-        // instruction), with no register staging and no LDS store
-        // instructions. Copy I of A fills tile rows 8 I .. 8 I + 7, lane l the
-        // 16 bytes at physical chunk l % 8 of row 8 I + l / 8, so it fetches
-        // the logical chunk that a_off puts there: l % 8 ^ ((row ^ row / 4)
-        // mod 8), which for row = 8 I + r is l % 8 ^ ((r ^ r / 4) mod 8) ^ 2 I
-        // mod 8. Copy J of B fills rows 2 J and 2 J + 1 in plain order. Each
-        // wave issues copies I, J = 4 wave .. 4 wave + 3 of each slab.
-        // Descriptors are re-based at every slab and end at the last valid
-        // element, so rows past M and K arrive as zeros; A's elements at
-        // k >= K inside rows below M are zeroed in LDS after they land.
+        // Operands with 16-byte rows: slabs go straight from global memory to
+        // LDS (buffer_load_dwordx4 ... lds, 1 KB per wave instruction), with
+        // no register staging and no LDS store instructions.
+        //   k-contiguous tile ([128][32]: row-major A, transposed B): copy I
+        //     fills tile rows 8 I .. 8 I + 7, lane l the 16 bytes at physical
+        //     chunk l % 8 of row 8 I + l / 8, so it fetches the logical chunk
+        //     that a_off puts there: l % 8 ^ ((row ^ row / 4) mod 8), which for
+        //     row = 8 I + r is l % 8 ^ ((r ^ r / 4) mod 8) ^ 2 I mod 8.
+        //   m/n-contiguous tile ([32][128]: row-major B, transposed A): copy I
+        //     fills k rows 2 I and 2 I + 1 in plain order.
+        // Each wave issues copies 4 wave .. 4 wave + 3 of each operand and
+        // slab. Descriptors are re-based at every slab and end at the last
+        // valid element, so rows (columns) past M, N and K arrive as zeros;
+        // elements at k >= K inside the valid rows of a k-contiguous tile are
+        // zeroed in LDS after they land.
         const int ar = lane >> 3, ap = lane & 7;
         const int s_ar = (ar ^ (ar >> 2)) & 7;
         const int wv = __builtin_amdgcn_readfirstlane(wave);   // scalar copy offsets
