@@ -5,7 +5,10 @@
 // tiles (section 3), float4 loads (section 4), register accumulators and
 // double buffering (section 5). The same ideas are kept here, but the inner
 // product runs on the fp32 matrix cores instead of per-thread FMAs:
-//   * one workgroup per BM x BN tile of C, renumbered per XCD;
+//   * BM x BN tiles of C, renumbered per XCD; on the copy path without
+//     split-K the grid is as many workgroups as can be resident (two per CU)
+//     and each walks its tiles in turn, so no workgroup is launched between
+//     rounds of tiles;
 //   * K in slabs of BK = 32 in a double-buffered LDS (one barrier per slab);
 //   * operands with 16-byte rows are copied from global memory straight into
 //     LDS (buffer_load_dwordx4 ... lds) one slab ahead, each in its stored
@@ -95,11 +98,11 @@ __device__ __forceinline__ void transpose4x4(const f32x4 (&x)[4], f32x4 (&y)[4])
     for (int j = 0; j < 4; ++j) y[j] = f32x4{x[0][j], x[1][j], x[2][j], x[3][j]};
 }
 
+// One tile (or, with SPLIT, one K range of a tile) for work item bidx of nbid.
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool VEC, bool SPLIT, bool EPI, bool TA,
           bool TB>
-__global__ __launch_bounds__(WAVES_M * WAVES_N * 64)
-void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit ts,
-                          unsigned char* ws) {
+__device__ __forceinline__ void f32_tile(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit ts,
+                                         unsigned char* ws, const int bidx, const int nbid) {
     constexpr int NT = WAVES_M * WAVES_N * 64;
     constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
     constexpr int FM = WTM / 16;          // 16-row blocks per wave
@@ -134,11 +137,11 @@ void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit
     int tm, tn, ti = 0, part = 0;
     int64_t kb = 0, ke = nk;                        // k slabs of this workgroup
     bool split_tile = false;
-    if (!SPLIT || (int)blockIdx.x < ts.full) {
-        tile_coords(blockIdx.x, SPLIT ? ts.full : gridDim.x, tiles_m, tiles_n, kGroupM, tm, tn);
+    if (!SPLIT || bidx < ts.full) {
+        tile_coords(bidx, SPLIT ? ts.full : nbid, tiles_m, tiles_n, kGroupM, tm, tn);
     } else {
         // Split tail: consecutive workgroups take the K ranges of one tile.
-        const int u = (int)blockIdx.x - ts.full;
+        const int u = bidx - ts.full;
         ti = __builtin_amdgcn_readfirstlane(u / ts.parts);
         part = __builtin_amdgcn_readfirstlane(u - ti * ts.parts);
         raster_tile(ts.full + ti, tiles_m, tiles_n, kGroupM, tm, tn);
@@ -581,6 +584,32 @@ void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit
 
 constexpr int kSlotsPerCu = 2;   // resident workgroups per compute unit (64 KB LDS each)
 
+// Whether a workgroup walks several tiles: on the copy path without split-K,
+// workgroup w takes tiles w, w + gridDim.x, ... (the same XCD slot each time).
+// The register-staged path keeps one tile per workgroup: in a tile loop its
+// registers no longer fit two waves per SIMD. With split-K every workgroup is
+// one work item.
+constexpr bool walks_tiles(bool vec, bool split) { return vec && !split; }
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool VEC, bool SPLIT, bool EPI, bool TA,
+          bool TB>
+__global__ __launch_bounds__(WAVES_M * WAVES_N * 64)
+void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit ts,
+                          unsigned char* ws) {
+    if constexpr (!walks_tiles(VEC, SPLIT)) {
+        f32_tile<BM, BN, WAVES_M, WAVES_N, VEC, SPLIT, EPI, TA, TB>(p, tiles_m, tiles_n, ts, ws,
+                                                                  (int)blockIdx.x, (int)gridDim.x);
+    } else {
+        const int64_t total = (int64_t)tiles_m * tiles_n;
+        for (int64_t b = blockIdx.x; b < total; b += gridDim.x) {
+            // The previous tile's last slab may have been read from stage 0.
+            if (b != (int64_t)blockIdx.x) __syncthreads();
+            f32_tile<BM, BN, WAVES_M, WAVES_N, VEC, SPLIT, EPI, TA, TB>(p, tiles_m, tiles_n, ts, ws,
+                                                                      (int)b, (int)total);
+        }
+    }
+}
+
 TailSplit plan_tail(int64_t tiles, int64_t nk, int cus) {
     return plan_tail_split(tiles, nk, (int64_t)cus * kSlotsPerCu);
 }
@@ -616,8 +645,10 @@ hipError_t launch_tiles(const GemmArgs<float>& a, bool vec, void* ws, size_t ws_
     const void* fn = has_epilogue(a)
                          ? pick_kernel<BM, BN, WAVES_M, WAVES_N, true>(vec, split, a.ta, a.tb)
                          : pick_kernel<BM, BN, WAVES_M, WAVES_N, false>(vec, split, a.ta, a.tb);
-    const int64_t grid = split ? (int64_t)ts.full + (int64_t)ts.tail * ts.parts : tiles_m * tiles_n;
-    if (grid > kMaxGrid) return hipErrorInvalidConfiguration;
+    const int64_t items = split ? (int64_t)ts.full + (int64_t)ts.tail * ts.parts : tiles_m * tiles_n;
+    if (items > kMaxGrid) return hipErrorInvalidConfiguration;
+    const int64_t slots = (int64_t)kSlotsPerCu * cus;
+    const int64_t grid = walks_tiles(vec, split) && items > slots ? slots : items;
     return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(WAVES_M * WAVES_N * 64), kargs, 0, s);
 }
 

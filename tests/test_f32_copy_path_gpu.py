@@ -10,7 +10,9 @@ with 16-byte rows) at its edges, against the oracle:
   offset range (past it the call takes the register-staged path);
 * B stored N x K (A B^T), A stored K x M (A^T B) and both (A^T B^T), each
   operand staged in LDS the way it is stored, with the same NaN padding,
-  ragged shapes and split K.
+  ragged shapes and split K;
+* more tiles than resident workgroups, so that each workgroup walks two or
+  three tiles in every layout, with and without the bias/activation epilogue.
 """
 import pytest
 import torch
@@ -19,6 +21,7 @@ import dense_gemm_04_amd as dg
 import gemm_inputs as gi
 import oracle
 from gpu_util import note, padded, to_f64, tol
+from test_transpose_gpu import check as check_op
 
 pytestmark = pytest.mark.gpu
 
@@ -140,3 +143,29 @@ def test_transposed_nan_padding_never_reaches_c(shape, ops):
     assert st == dg.GEMM_OK
     assert torch.isfinite(C).all()
     check(A, B, C, 1.25, 0.5, C0)
+
+
+# More tiles than resident workgroups (two per CU, 512 on a full MI355X): 576,
+# 1089 and 561 tiles of 128 x 128, so workgroups walk two or three tiles, and
+# the ragged last row and column of tiles (and the ragged K tail) fall on
+# workgroups that computed full tiles before them.
+WALK_SHAPES = [(3000, 3000, 70), (4200, 4200, 40), (4100, 2100, 45)]
+
+
+@pytest.mark.parametrize("ops", [(0, 0), (0, 1), (1, 0), (1, 1)], ids=["AB", "ABt", "AtB", "AtBt"])
+@pytest.mark.parametrize("shape", WALK_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_workgroups_walking_several_tiles(shape, ops):
+    M, N, K = shape
+    A = gi.random_matrix(M, K, "f32", 6000 + M)
+    B = gi.random_matrix(K, N, "f32", 6100 + N)
+    C0 = gi.random_matrix(M, N, "f32", 6200 + K)
+    note(f"f32 copy path, tiles walked, ops={ops} M={M} N={N} K={K}")
+    C, st = run_op_nan_padded(ops[0], ops[1], A, B, 0.75, -0.5, C0, False, pad=4)
+    assert st == dg.GEMM_OK
+    assert torch.isfinite(C).all()
+    check(A, B, C, 0.75, -0.5, C0)
+
+
+@pytest.mark.parametrize("act", ["relu", "gelu_tanh"])
+def test_walking_tiles_with_bias_and_activation(act):
+    check_op("f32", 0, 0, 3000, 3000, 72, 6300, alpha=1.25, beta=0.5, bias=True, act=act)
