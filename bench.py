@@ -216,16 +216,26 @@ def vendor_lines(steps: int, warmup: int):
 
 
 def kernel_source_sha(path: str) -> str:
-    """First 16 hex digits of the sha256 of a kernel source's code: `//`
-    comments, trailing blanks and empty lines removed, so that editing a
-    comment leaves a counter summary current while any code change does not."""
+    """First 16 hex digits of the sha256 of a kernel source's code and of the
+    local headers it includes (`#include "..."`, followed through the headers
+    they include): `//` comments, trailing blanks and empty lines removed, so
+    that editing a comment leaves a counter summary current while any code
+    change, in the kernel file or in shared device code, does not."""
     import hashlib
     import re
-    code = []
-    for line in open(path, encoding="utf-8"):
-        line = re.sub(r"//.*", "", line).rstrip()
-        if line:
-            code.append(line)
+    code, seen, todo = [], set(), [os.path.abspath(path)]
+    while todo:
+        f = todo.pop(0)
+        if f in seen or not os.path.exists(f):
+            continue
+        seen.add(f)
+        for line in open(f, encoding="utf-8"):
+            m = re.match(r'\s*#\s*include\s+"([^"]+)"', line)
+            if m:
+                todo.append(os.path.join(os.path.dirname(f), m.group(1)))
+            line = re.sub(r"//.*", "", line).rstrip()
+            if line:
+                code.append(line)
     return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 

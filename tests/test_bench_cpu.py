@@ -68,3 +68,17 @@ def test_source_sha_follows_code_not_comments(tmp_path):
     c.write_text("// header\nint f(int x) {  // trailing\n    return x + 2;\n}\n")
     assert bench.kernel_source_sha(str(a)) == bench.kernel_source_sha(str(b))
     assert bench.kernel_source_sha(str(a)) != bench.kernel_source_sha(str(c))
+
+
+def test_source_sha_follows_included_headers(tmp_path):
+    """A code change in a local header the kernel includes (shared device
+    code) changes the kernel's hash; a comment edit there does not."""
+    k = tmp_path / "k.hip"
+    h = tmp_path / "common.hpp"
+    k.write_text('#include <hip/hip_runtime.h>\n#include "common.hpp"\nint g() { return f(1); }\n')
+    h.write_text("inline int f(int x) { return x; }\n")
+    s0 = bench.kernel_source_sha(str(k))
+    h.write_text("// note\ninline int f(int x) { return x; }  // same\n")
+    assert bench.kernel_source_sha(str(k)) == s0
+    h.write_text("inline int f(int x) { return -x; }\n")
+    assert bench.kernel_source_sha(str(k)) != s0
