@@ -309,7 +309,7 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py measures one GPU only: the GEMM path runs on a single device and "
-              "this build has no multi-GPU leg (run with --gpus 1).", file=sys.stderr)
+              "the library has no multi-GPU leg (run with --gpus 1).", file=sys.stderr)
         return 2
 
     import torch
