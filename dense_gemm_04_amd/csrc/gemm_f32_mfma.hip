@@ -98,6 +98,13 @@ __device__ __forceinline__ void transpose4x4(const f32x4 (&x)[4], f32x4 (&y)[4])
     for (int j = 0; j < 4; ++j) y[j] = f32x4{x[0][j], x[1][j], x[2][j], x[3][j]};
 }
 
+// Whether a workgroup walks several tiles: on the copy path without split-K,
+// workgroup w takes tiles w, w + gridDim.x, ... (the same XCD slot each time).
+// The register-staged path keeps one tile per workgroup: in a tile loop its
+// registers no longer fit two waves per SIMD. With split-K every workgroup is
+// one work item.
+constexpr bool walks_tiles(bool vec, bool split) { return vec && !split; }
+
 // One tile (or, with SPLIT, one K range of a tile) for work item bidx of nbid.
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool VEC, bool SPLIT, bool EPI, bool TA,
           bool TB>
@@ -540,6 +547,30 @@ __device__ __forceinline__ void f32_tile(GemmArgs<float> p, int tiles_m, int til
 #pragma unroll
             for (int j = 0; j < 4; ++j) bv[gq][j] = bias_at(p, n0 + wn0 + 64 * gq + 4 * pl + j);
     }
+    // With beta != 0, a workgroup that computes one tile loads all of its C
+    // values before the first store (the stores could alias later loads, so
+    // the compiler would otherwise wait for each load in turn). A workgroup
+    // that walks tiles skips this: the extra registers would leave room for
+    // only one wave per SIMD.
+    constexpr bool kPreloadC = !walks_tiles(VEC, SPLIT);
+    f32x4 cpre[kPreloadC ? FM : 1][4][NG];
+    if (kPreloadC && beta != 0.f) {
+#pragma unroll
+        for (int i = 0; i < (kPreloadC ? FM : 1); ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t row = m0 + wm0 + (AMC ? 16 * g + 4 * r + i : 16 * i + 4 * g + r);
+#pragma unroll
+                for (int gq = 0; gq < NG; ++gq) {
+                    const int64_t col = n0 + wn0 + 64 * gq + 4 * pl;
+                    const float* src = p.C + row * p.ldc + col;
+                    cpre[i][r][gq] = (row < M && col + 4 <= N)
+                                         ? (VEC ? *reinterpret_cast<const f32x4*>(src)
+                                                : (f32x4)*reinterpret_cast<const f32x4_a4*>(src))
+                                         : f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -560,8 +591,10 @@ __device__ __forceinline__ void f32_tile(GemmArgs<float> p, int tiles_m, int til
                 }
                 if (col + 4 <= N) {
                     if (beta != 0.f) {
-                        const f32x4 c0 = VEC ? *reinterpret_cast<const f32x4*>(dst)
-                                             : (f32x4)*reinterpret_cast<const f32x4_a4*>(dst);
+                        f32x4 c0;
+                        if constexpr (kPreloadC) c0 = cpre[i][r][gq];
+                        else c0 = VEC ? *reinterpret_cast<const f32x4*>(dst)
+                                      : (f32x4)*reinterpret_cast<const f32x4_a4*>(dst);
 #pragma unroll
                         for (int j = 0; j < 4; ++j) v[j] += beta * c0[j];
                     }
@@ -583,13 +616,6 @@ __device__ __forceinline__ void f32_tile(GemmArgs<float> p, int tiles_m, int til
 }
 
 constexpr int kSlotsPerCu = 2;   // resident workgroups per compute unit (64 KB LDS each)
-
-// Whether a workgroup walks several tiles: on the copy path without split-K,
-// workgroup w takes tiles w, w + gridDim.x, ... (the same XCD slot each time).
-// The register-staged path keeps one tile per workgroup: in a tile loop its
-// registers no longer fit two waves per SIMD. With split-K every workgroup is
-// one work item.
-constexpr bool walks_tiles(bool vec, bool split) { return vec && !split; }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool VEC, bool SPLIT, bool EPI, bool TA,
           bool TB>
