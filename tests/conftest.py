@@ -30,3 +30,15 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter):
+    # Full-size parity: every entry of C compared with the oracle; one line
+    # per comparison with the worst error ratio found.
+    mod = sys.modules.get("gpu_util")
+    rows = getattr(mod, "FULL_SIZE_RESULTS", None) if mod is not None else None
+    if not rows:
+        return
+    terminalreporter.write_sep("-", "full-size parity (every entry of C against the oracle)")
+    for test, entries, err in rows:
+        terminalreporter.write_line(f"{test}: {entries} entries, max error ratio {err:.3e}")

@@ -1,5 +1,6 @@
 """Helpers shared by the GPU tests: run the library on torch CUDA buffers and
 compare against the CPU oracle."""
+import os
 import sys
 
 import numpy as np
@@ -65,3 +66,47 @@ def oracle_ref(dtype, A, B, C0, alpha, beta, rows=None, cols=None):
 
 def tol(dtype: str) -> float:
     return oracle.TOL_F32 if dtype == "f32" else oracle.TOL_BF16
+
+
+# Full-size references: the oracle over every entry of a workload's C, kept
+# for the next test that needs the same one (several calls share a workload:
+# the plain call, the split-K call, the transposed layouts).
+_REFERENCES: dict = {}
+
+
+def workload_reference(wid: int, bias=None, act=None, key=None):
+    """(R, D) of the oracle over all M x N entries of workload `wid` (its seeded
+    inputs), optionally in the bias + activation form. At most two results are
+    kept (config 4's pair alone is 1.6 GB)."""
+    k = (wid, key, act)
+    if k not in _REFERENCES:
+        while len(_REFERENCES) >= 2:
+            _REFERENCES.pop(next(iter(_REFERENCES)))
+        w = gi.WORKLOADS[wid]
+        d = gi.make(w)
+        _REFERENCES[k] = oracle.gemm(
+            gi.as_numpy(d["A"]), gi.as_numpy(d["B"]),
+            gi.as_numpy(d["C0"]) if d["C0"] is not None else None,
+            w.alpha, w.beta, w.dtype,
+            bias=None if bias is None else gi.as_numpy(bias), act=act)
+    return _REFERENCES[k]
+
+
+# (test, entries compared, max error ratio) of every full-size comparison in
+# this session; tests/conftest.py prints them at the end of the run.
+FULL_SIZE_RESULTS: list = []
+
+
+def full_max_err(C: torch.Tensor, R: np.ndarray, D: np.ndarray, chunk: int = 1024) -> float:
+    """max |c - r| / D over EVERY entry of C (a CUDA or CPU tensor), compared in
+    row chunks so that only one chunk is held in binary64 at a time. A NaN or
+    inf entry counts as an infinite error. The result is also recorded under
+    the running test's name for the end-of-run summary."""
+    assert tuple(C.shape) == R.shape == D.shape, (tuple(C.shape), R.shape, D.shape)
+    worst = 0.0
+    for r0 in range(0, C.shape[0], chunk):
+        c = C[r0:r0 + chunk].cpu().to(torch.float64).numpy()
+        worst = max(worst, oracle.max_rel_err(c, R[r0:r0 + chunk], D[r0:r0 + chunk]))
+    test = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
+    FULL_SIZE_RESULTS.append((test, int(C.shape[0]) * int(C.shape[1]), worst))
+    return worst
