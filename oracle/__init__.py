@@ -17,7 +17,9 @@ scale of the inputs.
 ``gemm(..., bias=, act=)`` runs the epilogue form of the same oracle:
 r = act(alpha * s + bias_j) + beta * c0_ij, with act the identity, ReLU or
 the tanh form of GELU, and D scaled by a bound on the activation's slope (see
-``oracle_gemm.c``).
+``oracle_gemm.c``). ``row_scale=`` / ``col_scale=`` (fp32 vectors of length
+M and N) add the quantisation scales: r = act(alpha * u_i * v_j * s + bias_j)
++ beta * c0_ij.
 
 It also holds ``bf16_round``: round-to-nearest-even of a binary64 value to
 the bf16 grid (1 sign, 8 exponent and 7 stored mantissa bits, as the
@@ -56,6 +58,11 @@ def _load():
         fn.restype = ctypes.c_int
         fn.argtypes = [i64, i64, i64, dbl, vp, i64, vp, i64, dbl, vp, i64, vp, ctypes.c_int,
                        vp, i64, vp, i64, vp, vp, ctypes.c_int]
+    for name in ("oracle_gemm_f32_scaled", "oracle_gemm_bf16_scaled"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [i64, i64, i64, dbl, vp, i64, vp, i64, dbl, vp, i64, vp, vp, vp,
+                       ctypes.c_int, vp, i64, vp, i64, vp, vp, ctypes.c_int]
     lib.oracle_activate.restype = dbl
     lib.oracle_activate.argtypes = [dbl, ctypes.c_int]
     lib.oracle_bf16_bits_to_double.restype = dbl
@@ -104,7 +111,8 @@ def activate(z, act: str) -> np.ndarray:
 def gemm(A: np.ndarray, B: np.ndarray, C0: Optional[np.ndarray] = None,
          alpha: float = 1.0, beta: float = 0.0, dtype: str = "f32",
          rows: Optional[Sequence[int]] = None, cols: Optional[Sequence[int]] = None,
-         threads: int = 0, bias: Optional[np.ndarray] = None, act: Optional[str] = None):
+         threads: int = 0, bias: Optional[np.ndarray] = None, act: Optional[str] = None,
+         row_scale: Optional[np.ndarray] = None, col_scale: Optional[np.ndarray] = None):
     """Return (R, D) as float64 arrays of shape (len(rows), len(cols)).
 
     ``dtype`` "f32": A, B, C0 are float32 arrays. ``dtype`` "bf16": they are
@@ -112,16 +120,20 @@ def gemm(A: np.ndarray, B: np.ndarray, C0: Optional[np.ndarray] = None,
     sub-grid of C (default: all). ``alpha``/``beta`` are taken as given
     (pass the fp32 value the GPU sees). ``beta == 0`` never reads C0.
     ``bias`` (length N, same element type) and ``act`` (a key of ``ACTS``)
-    select the epilogue form.
+    select the epilogue form. ``row_scale`` (length M) and ``col_scale``
+    (length N), float32, select the scaled form.
     """
     lib = _load()
+    scaled = row_scale is not None or col_scale is not None
     epi = bias is not None or act is not None
     if dtype == "f32":
         want, isz = np.float32, 4
-        fn = lib.oracle_gemm_f32_epi if epi else lib.oracle_gemm_f32
+        fn = (lib.oracle_gemm_f32_scaled if scaled else
+              lib.oracle_gemm_f32_epi if epi else lib.oracle_gemm_f32)
     elif dtype == "bf16":
         want, isz = np.uint16, 2
-        fn = lib.oracle_gemm_bf16_epi if epi else lib.oracle_gemm_bf16
+        fn = (lib.oracle_gemm_bf16_scaled if scaled else
+              lib.oracle_gemm_bf16_epi if epi else lib.oracle_gemm_bf16)
     else:
         raise ValueError(dtype)
     for name, x in (("A", A), ("B", B)):
@@ -144,7 +156,16 @@ def gemm(A: np.ndarray, B: np.ndarray, C0: Optional[np.ndarray] = None,
     R = np.empty((nr, nc), dtype=np.float64)
     D = np.empty((nr, nc), dtype=np.float64)
     extra = ()
-    if epi:
+    scales = ()
+    if scaled:
+        # Contiguous copies held in local names, so they outlive the call.
+        row_scale = None if row_scale is None else np.ascontiguousarray(row_scale)
+        col_scale = None if col_scale is None else np.ascontiguousarray(col_scale)
+        for name, v, n in (("row_scale", row_scale, M), ("col_scale", col_scale, N)):
+            if v is not None and (v.dtype != np.float32 or v.shape != (n,)):
+                raise ValueError(f"{name} must be float32 of shape ({n},)")
+            scales += (None if v is None or v.size == 0 else v.ctypes.data,)
+    if epi or scaled:
         if bias is not None:
             bias = np.ascontiguousarray(bias)
             if bias.dtype != want or bias.shape != (N,):
@@ -152,7 +173,7 @@ def gemm(A: np.ndarray, B: np.ndarray, C0: Optional[np.ndarray] = None,
         code = ACTS[act if act is not None else "none"]
         extra = (None if bias is None or bias.size == 0 else bias.ctypes.data, code)
     st = fn(M, N, K, float(alpha), A.ctypes.data if A.size else None, lda,
-            B.ctypes.data if B.size else None, ldb, float(beta), c0_ptr, ldc, *extra,
+            B.ctypes.data if B.size else None, ldb, float(beta), c0_ptr, ldc, *scales, *extra,
             None if r_idx is None else r_idx.ctypes.data, nr,
             None if c_idx is None else c_idx.ctypes.data, nc,
             R.ctypes.data, D.ctypes.data, int(threads))

@@ -37,6 +37,17 @@
  * are exact in binary64, so contraction into an FMA cannot change r; the
  * file is still built with -ffp-contract=off and without -ffast-math.
  *
+ * The scaled variant (oracle_gemm_*_scaled) adds the third kind of epilogue
+ * work the Blackwell BF16 GEMM notes name in section 3.3, quantisation
+ * scaling: one fp32 factor per row of A (u_i) and one per column of B (v_j),
+ * the dequantisation scales of a row-wise and a column-wise quantised operand,
+ * which multiply the product before anything else is added:
+ *   z   = alpha * u_i * v_j * s + bias_j
+ *   r   = act(z) + beta * c0_ij
+ *   D   = L * (|alpha * u_i * v_j| * sum_k |a_ik| * |b_kj| + |bias_j|) + |beta| * |c0_ij|
+ * A missing scale vector (NULL) is the factor 1 for every row (column). The
+ * factor alpha * u_i * v_j is formed in binary64 (one rounding, at 2^-53).
+ *
  * Rows are independent and are spread over OpenMP threads; within a row the
  * loop order is k outer, j inner, which keeps every entry's own sum in
  * increasing k (the row-wise loop of the CPU matmul in the CUDA shared-memory
@@ -90,6 +101,7 @@ double oracle_bf16_bits_to_double(uint16_t bits) { return from_bf16(&bits, 0); }
 static int oracle_gemm(load_fn load, int64_t M, int64_t N, int64_t K, double alpha,
                        const void* A, int64_t lda, const void* B, int64_t ldb,
                        double beta, const void* C0, int64_t ldc,
+                       const float* row_scale, const float* col_scale,
                        const void* bias, int act,
                        const int64_t* rows, int64_t nrows,
                        const int64_t* cols, int64_t ncols,
@@ -142,10 +154,13 @@ static int oracle_gemm(load_fn load, int64_t M, int64_t N, int64_t K, double alp
                     mag[c] += fabs(a) * fabs(brow[c]);
                 }
             }
+            /* The product's factor for this row: alpha * u_i (u_i = 1 without row scales). */
+            double f_row = alpha * (row_scale ? (double)row_scale[i] : 1.0);
             for (int64_t c = 0; c < ncols; ++c) {
                 int64_t j = cols ? cols[c] : c;
-                double r = alpha * s[c];
-                double d = fabs(alpha) * mag[c];
+                double f = f_row * (col_scale ? (double)col_scale[j] : 1.0);
+                double r = f * s[c];
+                double d = fabs(f) * mag[c];
                 if (bias) {
                     double b = load(bias, j);
                     r += b;
@@ -174,7 +189,8 @@ int oracle_gemm_f32(int64_t M, int64_t N, int64_t K, double alpha,
                     double beta, const float* C0, int64_t ldc,
                     const int64_t* rows, int64_t nrows, const int64_t* cols, int64_t ncols,
                     double* R, double* D, int nthreads) {
-    return oracle_gemm(from_f32, M, N, K, alpha, A, lda, B, ldb, beta, C0, ldc, NULL, ACT_NONE,
+    return oracle_gemm(from_f32, M, N, K, alpha, A, lda, B, ldb, beta, C0, ldc, NULL, NULL,
+                       NULL, ACT_NONE,
                        rows, nrows, cols, ncols, R, D, nthreads);
 }
 
@@ -183,7 +199,8 @@ int oracle_gemm_bf16(int64_t M, int64_t N, int64_t K, double alpha,
                      double beta, const uint16_t* C0, int64_t ldc,
                      const int64_t* rows, int64_t nrows, const int64_t* cols, int64_t ncols,
                      double* R, double* D, int nthreads) {
-    return oracle_gemm(from_bf16, M, N, K, alpha, A, lda, B, ldb, beta, C0, ldc, NULL, ACT_NONE,
+    return oracle_gemm(from_bf16, M, N, K, alpha, A, lda, B, ldb, beta, C0, ldc, NULL, NULL,
+                       NULL, ACT_NONE,
                        rows, nrows, cols, ncols, R, D, nthreads);
 }
 
@@ -193,7 +210,8 @@ int oracle_gemm_f32_epi(int64_t M, int64_t N, int64_t K, double alpha,
                         double beta, const float* C0, int64_t ldc, const float* bias, int act,
                         const int64_t* rows, int64_t nrows, const int64_t* cols, int64_t ncols,
                         double* R, double* D, int nthreads) {
-    return oracle_gemm(from_f32, M, N, K, alpha, A, lda, B, ldb, beta, C0, ldc, bias, act,
+    return oracle_gemm(from_f32, M, N, K, alpha, A, lda, B, ldb, beta, C0, ldc, NULL, NULL,
+                       bias, act,
                        rows, nrows, cols, ncols, R, D, nthreads);
 }
 
@@ -202,8 +220,31 @@ int oracle_gemm_bf16_epi(int64_t M, int64_t N, int64_t K, double alpha,
                          double beta, const uint16_t* C0, int64_t ldc, const uint16_t* bias,
                          int act, const int64_t* rows, int64_t nrows, const int64_t* cols,
                          int64_t ncols, double* R, double* D, int nthreads) {
-    return oracle_gemm(from_bf16, M, N, K, alpha, A, lda, B, ldb, beta, C0, ldc, bias, act,
+    return oracle_gemm(from_bf16, M, N, K, alpha, A, lda, B, ldb, beta, C0, ldc, NULL, NULL,
+                       bias, act,
                        rows, nrows, cols, ncols, R, D, nthreads);
+}
+
+/* The scaled variants: row_scale (length M) and col_scale (length N), fp32,
+ * each NULL for none, then the bias and activation as above. */
+int oracle_gemm_f32_scaled(int64_t M, int64_t N, int64_t K, double alpha,
+                           const float* A, int64_t lda, const float* B, int64_t ldb,
+                           double beta, const float* C0, int64_t ldc, const float* row_scale,
+                           const float* col_scale, const float* bias, int act,
+                           const int64_t* rows, int64_t nrows, const int64_t* cols,
+                           int64_t ncols, double* R, double* D, int nthreads) {
+    return oracle_gemm(from_f32, M, N, K, alpha, A, lda, B, ldb, beta, C0, ldc, row_scale,
+                       col_scale, bias, act, rows, nrows, cols, ncols, R, D, nthreads);
+}
+
+int oracle_gemm_bf16_scaled(int64_t M, int64_t N, int64_t K, double alpha,
+                            const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                            double beta, const uint16_t* C0, int64_t ldc, const float* row_scale,
+                            const float* col_scale, const uint16_t* bias, int act,
+                            const int64_t* rows, int64_t nrows, const int64_t* cols,
+                            int64_t ncols, double* R, double* D, int nthreads) {
+    return oracle_gemm(from_bf16, M, N, K, alpha, A, lda, B, ldb, beta, C0, ldc, row_scale,
+                       col_scale, bias, act, rows, nrows, cols, ncols, R, D, nthreads);
 }
 
 int oracle_max_threads(void) { return omp_get_max_threads(); }
