@@ -13,7 +13,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Arguments every GEMM kernel receives, by value (kernarg segment). `bias`
-// (length N, or null) and `act` are read only by the epilogue instantiations.
+// (length N, or null), `act` and the scale vectors are read only by the
+// epilogue instantiations.
 template <typename T>
 struct GemmArgs {
     int64_t M, N, K;
@@ -26,6 +27,10 @@ struct GemmArgs {
     // Transposed storage: A(i,k) = A[k*lda + i] (A is K x M) when ta, and
     // B(k,j) = B[j*ldb + k] (B is N x K) when tb.
     bool ta = false, tb = false;
+    // Quantisation scales (fp32, or null): the product of row i and column j
+    // is multiplied by row_scale[i] * col_scale[j] along with alpha.
+    const float* row_scale = nullptr;
+    const float* col_scale = nullptr;
 };
 
 // 128-bit vectors at addresses aligned only to their element (4 or 2 bytes).
@@ -105,13 +110,27 @@ __device__ __forceinline__ float elem_f32(uint16_t v) { return bf16_to_f32(v); }
 // True when a call needs the epilogue instantiations.
 template <typename T>
 inline bool has_epilogue(const GemmArgs<T>& a) {
-    return a.bias != nullptr || a.act != kActNone;
+    return a.bias != nullptr || a.act != kActNone || a.row_scale != nullptr ||
+           a.col_scale != nullptr;
 }
 
 // Bias of column `col`: 0 past N or without a bias vector.
 template <typename T>
 __device__ __forceinline__ float bias_at(const GemmArgs<T>& p, int64_t col) {
     return (p.bias != nullptr && col < p.N) ? elem_f32(p.bias[col]) : 0.f;
+}
+
+// The epilogue's factor on the product of row `row`: alpha times the row's
+// quantisation scale (alpha alone without row scales or past M).
+template <typename T>
+__device__ __forceinline__ float row_factor(const GemmArgs<T>& p, int64_t row) {
+    return (p.row_scale != nullptr && row < p.M) ? p.alpha * p.row_scale[row] : p.alpha;
+}
+
+// Quantisation scale of column `col`: 1 past N or without column scales.
+template <typename T>
+__device__ __forceinline__ float col_factor(const GemmArgs<T>& p, int64_t col) {
+    return (p.col_scale != nullptr && col < p.N) ? p.col_scale[col] : 1.f;
 }
 
 // ---- LDS pipelines ----------------------------------------------------------

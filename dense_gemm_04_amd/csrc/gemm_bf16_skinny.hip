@@ -492,13 +492,22 @@ static bool smallm_fits(const GemmArgs<uint16_t>& a) {
     return (16 * smallm_blocks(a.M) * a.lda + a.K + kVKC) * 2 < lim && b_ok;
 }
 
-size_t bf16_skinny_workspace(int64_t M, int64_t N, int64_t K) {
+// Workspace of the 64-column kernel's split.
+static size_t smallm_workspace(int64_t M, int64_t N, int64_t K) {
     if (M < 1 || M > kSkinnyMaxM || N < 1 || K < 1) return 0;
     const SmallMWork w = plan_smallm(N, K, true);
     if (w.segs < 2) return 0;
     const int64_t mb = smallm_blocks(M);
     return (size_t)((((int64_t)w.strips * 4 + 255) & ~(int64_t)255) +
                     (int64_t)w.segs * w.strips * 16 * mb * kVBN * 4);
+}
+
+// The larger of the two small-M splits: the streaming kernel takes row-major
+// B, the 64-column kernel a transposed B (and shapes the streaming one does
+// not cover).
+size_t bf16_skinny_workspace(int64_t M, int64_t N, int64_t K) {
+    const size_t a = smallm_workspace(M, N, K), b = bf16_stream_workspace(M, N, K);
+    return a > b ? a : b;
 }
 
 hipError_t launch_bf16_skinny(const GemmArgs<uint16_t>& a, bool vec, void* ws, size_t ws_bytes,
@@ -509,8 +518,11 @@ hipError_t launch_bf16_skinny(const GemmArgs<uint16_t>& a, bool vec, void* ws, s
     // kernel only; otherwise the tiled kernels take the call.
     if ((a.tb || a.M > kSkinnyElemMaxM) && !(vec && smallm_fits(a)))
         return launch_bf16_mfma(a, vec, ws, ws_bytes, cus, s);
+    if (vec && !a.tb && ws != nullptr && plan_stream(a.N, a.K).phases > 0 &&
+        ws_bytes >= bf16_stream_workspace(a.M, a.N, a.K) && bf16_stream_fits(a))
+        return launch_bf16_stream(a, ws, s);
     if (vec && smallm_fits(a)) {
-        const size_t need = bf16_skinny_workspace(a.M, a.N, a.K);
+        const size_t need = smallm_workspace(a.M, a.N, a.K);
         const bool split = ws != nullptr && need > 0 && ws_bytes >= need;
         SmallMWork w = plan_smallm(a.N, a.K, split);
         unsigned char* wsp = split ? static_cast<unsigned char*>(ws) : nullptr;

@@ -41,8 +41,25 @@ hipError_t launch_f32_valu(const GemmArgs<float>& a, bool vec, hipStream_t s);
 // (256-byte aligned, counters zero) it splits K over several workgroups.
 hipError_t launch_bf16_skinny(const GemmArgs<uint16_t>& a, bool vec, void* ws, size_t ws_bytes,
                               int cus, hipStream_t s);
-// Workspace bytes with which launch_bf16_skinny splits K (0: no split for this shape).
+// Workspace bytes with which launch_bf16_skinny splits K (0: no split for this
+// shape); at least what the streaming kernel below needs when it applies.
 size_t bf16_skinny_workspace(int64_t M, int64_t N, int64_t K);
+
+// Small-M streaming kernel (vector path, row-major B, split K): 256-column
+// strips with K interleaved over `phases` workgroups per strip in 32-row
+// blocks (block b goes to phase b mod phases).
+struct StreamWork {
+    int strips;   // 256-column strips of C
+    int phases;   // workgroups per strip (0: the kernel does not apply)
+    int nblk;     // 32-row blocks of K
+};
+StreamWork plan_stream(int64_t N, int64_t K);
+// Workspace bytes the streaming kernel needs (0 when it does not apply).
+size_t bf16_stream_workspace(int64_t M, int64_t N, int64_t K);
+bool bf16_stream_fits(const GemmArgs<uint16_t>& a);
+// Needs M <= kSkinnyMaxM, 16-byte rows, plan_stream(N, K).phases >= 2 and a
+// workspace of bf16_stream_workspace(M, N, K) bytes (256-byte aligned, zeros).
+hipError_t launch_bf16_stream(const GemmArgs<uint16_t>& a, void* ws, hipStream_t s);
 
 // C <- act(bias[col]) + beta * C, the product-free case (beta == 0 writes
 // without reading C; without bias and activation the first term is 0).

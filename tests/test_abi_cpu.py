@@ -146,19 +146,36 @@ def test_oracle_and_library_share_nothing():
 
 
 def test_workspace_size(lib):
-    # 16 x 8192 x 8192: 128 strips of 64 columns, K cut into 2 segments of
-    # 4096 to give 256 workgroups: a 512-byte counter block, then 2 x 128 fp32
-    # tiles of 16 x 64.
-    assert dg.gemm_bf16_workspace_size(16, 8192, 8192) == 512 + 2 * 128 * 16 * 64 * 4
+    # 16 x 8192 x 8192 runs on the streaming kernel: 32 strips of 256 columns,
+    # K interleaved over 8 phases (256 workgroups): a 256-byte counter block,
+    # then 32 x 8 fp32 partial tiles of 16 x 256.
+    assert dg.gemm_bf16_workspace_size(16, 8192, 8192) == 256 + 32 * 8 * 16 * 256 * 4
     # 17..32 rows use 32-row tiles, 33..64 64-row and 65..128 128-row tiles.
-    assert dg.gemm_bf16_workspace_size(32, 8192, 8192) == 512 + 2 * 128 * 32 * 64 * 4
-    assert dg.gemm_bf16_workspace_size(33, 8192, 8192) == 512 + 2 * 128 * 64 * 64 * 4
-    assert dg.gemm_bf16_workspace_size(128, 8192, 8192) == 512 + 2 * 128 * 128 * 64 * 4
+    assert dg.gemm_bf16_workspace_size(32, 8192, 8192) == 256 + 32 * 8 * 32 * 256 * 4
+    assert dg.gemm_bf16_workspace_size(33, 8192, 8192) == 256 + 32 * 8 * 64 * 256 * 4
+    assert dg.gemm_bf16_workspace_size(128, 8192, 8192) == 256 + 32 * 8 * 128 * 256 * 4
+    # 64 strips of 256 columns: 4 phases fill the chip.
+    assert dg.gemm_bf16_workspace_size(16, 16384, 8192) == 256 + 64 * 4 * 16 * 256 * 4
+    # 16 strips (N = 3841) would take 16 phases, the most; K = 4104 has 129
+    # blocks of 32 rows, K = 700 only 22, enough for 5 phases of 4 blocks.
+    assert dg.gemm_bf16_workspace_size(16, 3841, 4104) == 256 + 16 * 16 * 16 * 256 * 4
+    assert dg.gemm_bf16_workspace_size(16, 3841, 700) == 256 + 16 * 5 * 16 * 256 * 4
+    # K = 260 has 9 blocks: 2 phases. The size is the larger of the two
+    # small-M splits (the 64-column kernel, which a transposed B uses, would
+    # cut 65 strips into 3 segments here). K = 40 (2 blocks) does not split
+    # here, nor in the 64-column kernel (one 128-row chunk).
+    assert dg.gemm_bf16_workspace_size(7, 4104, 260) == max(256 + 17 * 2 * 16 * 256 * 4,
+                                                            512 + 3 * 65 * 16 * 64 * 4)
+    assert dg.gemm_bf16_workspace_size(7, 4104, 40) == 0
+    # N = 3840 is 15 strips: the 64-column kernel's split (60 strips of 64
+    # columns; K = 8192 has 64 chunks of 128: 5 segments of 13 chunks).
+    assert dg.gemm_bf16_workspace_size(16, 3840, 8192) == 256 + 5 * 60 * 16 * 64 * 4
     # M > 128 is sized for the tiled kernel instead (see the next test); no
     # small-M split when strips already fill the GPU, one K chunk, empty or
     # invalid sizes.
     assert dg.gemm_bf16_workspace_size(129, 8192, 8192) == 256 + 32 * 8 * 256 * 256 * 4
-    assert dg.gemm_bf16_workspace_size(16, 16384, 8192) == 0
+    assert dg.gemm_bf16_workspace_size(16, 2048, 8192) > 0
+    assert dg.gemm_bf16_workspace_size(16, 16384, 128) == 0
     assert dg.gemm_bf16_workspace_size(16, 64, 128) == 0
     assert dg.gemm_bf16_workspace_size(0, 64, 1024) == 0
     assert dg.gemm_bf16_workspace_size(16, 0, 1024) == 0

@@ -63,6 +63,51 @@ def test_split_k_parity(shape):
     assert int(ws[:4 * strips].view(torch.int32).abs().sum()) == 0
 
 
+# Shapes with at least 16 strips of 256 columns (N > 3840) and at least 8
+# blocks of 32 rows of K: with a workspace and row-major B they run on the
+# streaming kernel (K interleaved over 2 to 16 workgroups per strip in 32-row
+# blocks), ragged in M, N and K.
+STREAM_SHAPES = [(16, 3841, 700), (1, 4100, 4104), (17, 5000, 1000), (128, 4096, 2056),
+                 (33, 4352, 300), (7, 4104, 260), (64, 6000, 333), (2, 8192, 520),
+                 (100, 4160, 1500)]
+
+
+@pytest.mark.parametrize("shape", STREAM_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_stream_split_parity(shape):
+    M, N, K = shape
+    assert dg.gemm_bf16_workspace_size(M, N, K) > 0
+    ws, n = workspace(M, N, K)
+    for rep, (alpha, beta, pad) in enumerate(((1.5, -0.5, (0, 0, 0)), (1.0, 0.0, (8, 16, 24)),
+                                              (0.25, 1.0, (0, 8, 0)))):
+        seed = 7000 + 10 * M + rep
+        A = gi.random_matrix(M, K, "bf16", seed, dist="n")
+        B = gi.random_matrix(K, N, "bf16", seed + 1)
+        C0 = gi.random_matrix(M, N, "bf16", seed + 2) if beta != 0 else None
+        note(f"gemm_bf16_ws stream M={M} N={N} K={K} alpha={alpha} beta={beta} pad={pad}")
+        C, st = run_ws(A, B, C0, alpha, beta, ws, n, ld_pad=pad)
+        assert st == dg.GEMM_OK, dg.gemm_status_string(st)
+        R, D = oracle_ref("bf16", A, B, C0, alpha, beta)
+        err = oracle.max_rel_err(to_f64(C), R, D)
+        assert err <= tol("bf16"), f"call {rep}: max error ratio {err:.3e}"
+    # The counters (one int per 256-column strip) are back at zero.
+    strips = (N + 255) // 256
+    assert int(ws[:4 * strips].view(torch.int32).abs().sum()) == 0
+
+
+def test_stream_split_is_deterministic():
+    M, N, K = 16, 4352, 4104
+    ws, n = workspace(M, N, K)
+    A = gi.random_matrix(M, K, "bf16", 7990, dist="n")
+    B = gi.random_matrix(K, N, "bf16", 7991)
+    note(f"gemm_bf16_ws stream determinism M={M} N={N} K={K}")
+    first, st = run_ws(A, B, None, 1.0, 0.0, ws, n)
+    assert st == dg.GEMM_OK
+    for _ in range(3):
+        again, st = run_ws(A, B, None, 1.0, 0.0, ws, n)
+        assert st == dg.GEMM_OK
+        assert torch.equal(first.view(torch.int16), again.view(torch.int16))
+
+
 def test_split_k_is_deterministic():
     M, N, K = 16, 1032, 4104
     ws, n = workspace(M, N, K)
