@@ -21,6 +21,9 @@ GEMM_OK = 0
 GEMM_ERR_INVALID_VALUE = 1
 GEMM_ERR_UNSUPPORTED_DEVICE = 2
 GEMM_ERR_LAUNCH = 3
+GEMM_ERR_SCRATCH_LIMIT = 4
+# Size of the static scratch behind gemm_bf16_ws_noalloc (per GPU).
+NOALLOC_SCRATCH_BYTES = (32 << 20) + (64 << 10)
 
 VARIANT_AUTO = 0
 VARIANT_MFMA = 1
@@ -38,7 +41,7 @@ OP_N = 0
 OP_T = 1
 
 EXPORTS = ("gemm_f32", "gemm_bf16", "gemm_f32_ex", "gemm_bf16_ex", "gemm_bf16_ws",
-           "gemm_bf16_workspace_size", "gemm_f32_ws", "gemm_f32_workspace_size",
+           "gemm_bf16_workspace_size", "gemm_bf16_ws_noalloc", "gemm_f32_ws", "gemm_f32_workspace_size",
            "gemm_f32_bias_act", "gemm_bf16_bias_act", "gemm_f32_op", "gemm_bf16_op", "gemm_plan",
            "gemm_status_string")
 
@@ -65,6 +68,7 @@ def load() -> ctypes.CDLL:
     for name in ("gemm_f32", "gemm_bf16"):
         fn = getattr(lib, name)
         fn.restype, fn.argtypes = ci, base
+    lib.gemm_bf16_ws_noalloc.restype, lib.gemm_bf16_ws_noalloc.argtypes = ci, base
     for name in ("gemm_f32_ex", "gemm_bf16_ex"):
         fn = getattr(lib, name)
         fn.restype, fn.argtypes = ci, base + [ci]
@@ -108,6 +112,10 @@ def gemm_bf16_ws(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace, worksp
                  stream=0) -> int:
     return load().gemm_bf16_ws(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace,
                                workspace_bytes, stream)
+
+
+def gemm_bf16_ws_noalloc(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0) -> int:
+    return load().gemm_bf16_ws_noalloc(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
 
 
 def gemm_bf16_workspace_size(M, N, K) -> int:

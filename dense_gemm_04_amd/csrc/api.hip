@@ -117,9 +117,10 @@ std::atomic<int> g_cus[kMaxDevices];
 // Compute units of a full MI355X: the workspace sizes are computed for it.
 constexpr int kFullCus = 256;
 
-gemm_status_t check_device(int* cus) {
+gemm_status_t check_device(int* cus, int* device = nullptr) {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GEMM_ERR_UNSUPPORTED_DEVICE;
+    if (device != nullptr) *device = dev;
     if (dev >= kMaxDevices) return GEMM_ERR_UNSUPPORTED_DEVICE;
     int state = g_arch[dev].load(std::memory_order_acquire);
     if (state == 0) {
@@ -185,9 +186,78 @@ gemm_status_t run(int64_t M, int64_t N, int64_t K, float alpha, const T* A, int6
     return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 
+// ---- static scratch of gemm_bf16_ws_noalloc ---------------------------------
+//
+// The split-K workspace of the entry point for callers that cannot allocate:
+// one array per GPU, allocated with the library's code object on that GPU
+// and held until the process ends. Like any static-storage object it starts
+// zero-filled; every call leaves its counters at zero again.
+constexpr size_t kScratchBytes = GEMM_NOALLOC_SCRATCH_BYTES;
+// The counters of every split sit in the first bytes of a workspace (one int
+// per strip or split tile, padded to 256 bytes); a shape whose slots fit in
+// kScratchBytes has fewer than 16384 of them, so this prefix holds them all.
+constexpr size_t kScratchCounterBytes = 65536;
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Per device: the scratch's device address (host code must use this, never
+// the name `scratch`, which on the host is only a stand-in for the symbol),
+// and whether its counter prefix has been cleared.
+std::atomic<void*> g_scratch[kMaxDevices];
+std::atomic<int> g_scratch_cleared[kMaxDevices];
+
+__global__ void clear_words(uint32_t* p, int n) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+// The scratch of device `dev` (current), its counter prefix cleared once by a
+// kernel on `stream` before the first call that uses it (a fill kernel rather
+// than a memset, so that a call under stream capture records an ordinary
+// kernel node). Returns nullptr if the symbol cannot be resolved or the clear
+// cannot be launched.
+void* scratch_for(int dev, hipStream_t stream) {
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    int expected = 0;
+    if (g_scratch_cleared[dev].compare_exchange_strong(expected, 1, std::memory_order_acq_rel)) {
+        clear_words<<<16, 256, 0, stream>>>(static_cast<uint32_t*>(p), (int)(kScratchCounterBytes / 4));
+        if (hipGetLastError() != hipSuccess) {
+            g_scratch_cleared[dev].store(0, std::memory_order_release);
+            return nullptr;
+        }
+    }
+    return p;
+}
+
 }  // namespace
 
 extern "C" {
+
+gemm_status_t gemm_bf16_ws_noalloc(int64_t M, int64_t N, int64_t K, float alpha,
+                                   const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                                   float beta, uint16_t* C, int64_t ldc, void* stream) {
+    // Host-only checks first: arguments, then whether the split fits the scratch.
+    if (plan_impl(2, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, GEMM_VARIANT_AUTO) < 0)
+        return GEMM_ERR_INVALID_VALUE;
+    if (work_of(M, N, K, alpha, beta) != Work::kGemm)
+        return gemm_bf16_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, GEMM_VARIANT_AUTO);
+    const size_t need = gemm_bf16_workspace_size(M, N, K);
+    if (need > kScratchBytes || (N + 63) / 64 * 4 > (int64_t)kScratchCounterBytes)
+        return GEMM_ERR_SCRATCH_LIMIT;
+    if (need == 0)
+        return gemm_bf16_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, GEMM_VARIANT_AUTO);
+    int cus = 0, dev = -1;
+    const gemm_status_t st = check_device(&cus, &dev);
+    if (st != GEMM_OK) return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    void* ws = scratch_for(dev, s);
+    if (ws == nullptr) return GEMM_ERR_LAUNCH;
+    return run<uint16_t>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, GEMM_VARIANT_AUTO,
+                         ws, kScratchBytes);
+}
 
 gemm_status_t gemm_f32_ex(int64_t M, int64_t N, int64_t K, float alpha, const float* A,
                           int64_t lda, const float* B, int64_t ldb, float beta, float* C,
@@ -297,6 +367,8 @@ const char* gemm_status_string(int status) {
         case GEMM_ERR_INVALID_VALUE: return "invalid argument";
         case GEMM_ERR_UNSUPPORTED_DEVICE: return "current device is not a gfx950 GPU";
         case GEMM_ERR_LAUNCH: return "kernel launch failed";
+        case GEMM_ERR_SCRATCH_LIMIT:
+            return "shape needs more split-K scratch than the library's static buffer holds";
         default: return "unknown status";
     }
 }

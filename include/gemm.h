@@ -35,15 +35,17 @@
  * caller, valid on the current HIP device for the duration of the work.
  * The library keeps no reference after the work completes and allocates no
  * device memory; the *_ws and *_bias_act entry points take a caller-owned
- * workspace instead. C must not overlap A, B or the workspace (undefined results
- * otherwise).
+ * workspace instead, and gemm_bf16_ws_noalloc uses a static array that the
+ * library's code object holds on each GPU. C must not overlap A, B or the
+ * workspace (undefined results otherwise).
  *
  * Streams and errors: `stream` is a hipStream_t passed as void* (NULL = the
  * null stream). Calls are asynchronous: they validate the arguments, enqueue
  * one or more kernels on `stream` and return; completion and device-side
  * faults are observed at the caller's next synchronisation. On any error
- * status nothing has been enqueued. The library is reentrant; its only
- * global state is a per-device cache of the device architecture.
+ * status nothing has been enqueued. The library is reentrant (except that
+ * gemm_bf16_ws_noalloc calls share one scratch per GPU); its global state is
+ * a per-device cache of the device architecture and of the scratch address.
  */
 #ifndef DENSE_GEMM_04_AMD_GEMM_H
 #define DENSE_GEMM_04_AMD_GEMM_H
@@ -67,7 +69,10 @@ typedef enum {
     GEMM_ERR_UNSUPPORTED_DEVICE = 2,
     /* The kernel launch was rejected by the HIP runtime (or the grid would
      * exceed 2^31 - 1 workgroups, which no matrix in device memory needs). */
-    GEMM_ERR_LAUNCH = 3
+    GEMM_ERR_LAUNCH = 3,
+    /* gemm_bf16_ws_noalloc only: the shape's split-K workspace is larger than
+     * GEMM_NOALLOC_SCRATCH_BYTES. Nothing is launched. */
+    GEMM_ERR_SCRATCH_LIMIT = 4
 } gemm_status_t;
 
 /* Kernel family selection for the *_ex entry points. AUTO is what gemm_f32 and
@@ -144,6 +149,29 @@ gemm_status_t gemm_bf16_ws(int64_t M, int64_t N, int64_t K, float alpha,
                            const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                            float beta, uint16_t* C, int64_t ldc,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * gemm_bf16_ws with the library's own scratch instead of a caller workspace.
+ * Each GPU the library runs on holds one static scratch array of
+ * GEMM_NOALLOC_SCRATCH_BYTES (32 MiB + 64 KiB) from the library's load until
+ * the process ends. This call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine); on its first use on a device it looks up that
+ * device's array and enqueues one small kernel on `stream` that clears the
+ * array's counters.
+ * Results are those of gemm_bf16_ws with a workspace of
+ * gemm_bf16_workspace_size(M, N, K) bytes (bit for bit). Shapes whose
+ * workspace would exceed the scratch return GEMM_ERR_SCRATCH_LIMIT and
+ * launch nothing (16 x 8192 x 8192 needs 4 MiB and 128 x 8192 x 8192 32 MiB,
+ * which fit; 512 x 8192 x 8192 needs 64 MiB, which does not; shapes that
+ * would not split need none and run as gemm_bf16). All calls on one GPU share its scratch: calls that overlap
+ * in time on one GPU (different streams, or threads without ordering) race
+ * and give undefined results; calls ordered on one stream are safe. Other
+ * rules as for gemm_bf16. */
+#define GEMM_NOALLOC_SCRATCH_BYTES (((size_t)32 << 20) + ((size_t)64 << 10))
+gemm_status_t gemm_bf16_ws_noalloc(int64_t M, int64_t N, int64_t K, float alpha,
+                                   const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                                   float beta, uint16_t* C, int64_t ldc, void* stream);
 
 /* Split-K for the last round of tiles (fp32). The fp32 kernel covers C with
  * 128 x 128 tiles, two resident workgroups per compute unit. When the tiles

@@ -41,6 +41,7 @@ def test_status_strings(lib):
     assert dg.gemm_status_string(1) == "invalid argument"
     assert "gfx950" in dg.gemm_status_string(2)
     assert dg.gemm_status_string(3) == "kernel launch failed"
+    assert "scratch" in dg.gemm_status_string(4)
     assert dg.gemm_status_string(99) == "unknown status"
 
 
@@ -121,6 +122,26 @@ def test_invalid_calls_return_before_any_hip_call(lib):
                            dg.VARIANT_VALU) == dg.GEMM_ERR_INVALID_VALUE
     # Empty problems succeed without touching the device either.
     assert dg.gemm_f32(0, 4, 4, 1.0, None, 4, None, 4, 0.0, None, 4, 0) == dg.GEMM_OK
+
+
+def test_noalloc_checks_before_any_hip_call(lib):
+    # Invalid arguments, then shapes whose split-K workspace exceeds the static
+    # scratch, are refused on the host; a shape that fits goes on to the
+    # device check (no GPU here).
+    noalloc = dg.gemm_bf16_ws_noalloc
+    assert noalloc(4, 4, 4, 1.0, A, 3, B, 4, 0.0, C, 4, 0) == dg.GEMM_ERR_INVALID_VALUE
+    assert noalloc(4, 4, 4, 1.0, A + 1, 4, B, 4, 0.0, C, 4, 0) == dg.GEMM_ERR_INVALID_VALUE
+    assert noalloc(0, 4, 4, 1.0, None, 4, None, 4, 0.0, None, 4, 0) == dg.GEMM_OK
+    assert dg.gemm_bf16_workspace_size(512, 8192, 8192) > dg.NOALLOC_SCRATCH_BYTES
+    assert noalloc(512, 8192, 8192, 1.0, A, 8192, B, 8192, 0.0, C, 8192,
+                   0) == dg.GEMM_ERR_SCRATCH_LIMIT
+    import torch
+    if not torch.cuda.is_available():
+        assert dg.gemm_bf16_workspace_size(128, 8192, 8192) <= dg.NOALLOC_SCRATCH_BYTES
+        assert noalloc(128, 8192, 8192, 1.0, A, 8192, B, 8192, 0.0, C, 8192,
+                       0) == dg.GEMM_ERR_UNSUPPORTED_DEVICE
+        assert noalloc(16, 64, 64, 1.0, A, 64, B, 64, 0.0, C, 64,
+                       0) == dg.GEMM_ERR_UNSUPPORTED_DEVICE
 
 
 def test_valid_call_without_gpu_reports_unsupported_device(lib):

@@ -1,0 +1,95 @@
+"""gemm_bf16_ws_noalloc: gemm_bf16_ws with the library's static scratch
+instead of a caller workspace, for callers that cannot allocate. Checked
+through the C ABI against gemm_bf16_ws with a torch-allocated workspace (bit
+for bit: the same kernels and the same split) and against the oracle, on
+consecutive calls that reuse the one scratch, the second with a smaller
+input."""
+import pytest
+import torch
+
+import dense_gemm_04_amd as dg
+import gemm_inputs as gi
+import oracle
+from gpu_util import note, oracle_ref, to_f64, tol
+
+pytestmark = pytest.mark.gpu
+
+
+def _operands(M, N, K, seed, beta):
+    A = gi.random_matrix(M, K, "bf16", seed, dist="n")
+    B = gi.random_matrix(K, N, "bf16", seed + 1)
+    C0 = gi.random_matrix(M, N, "bf16", seed + 2) if beta != 0 else None
+    return A, B, C0
+
+
+def _run(fn_name, A, B, C0, alpha, beta):
+    """One call of gemm_bf16_ws_noalloc or gemm_bf16_ws; returns (C, status)."""
+    M, K = A.shape
+    N = B.shape[1]
+    a, b = A.cuda(), B.cuda()
+    c = C0.cuda() if C0 is not None else torch.full((M, N), float("nan"), dtype=torch.bfloat16,
+                                                    device="cuda")
+    h = int(torch.cuda.current_stream().cuda_stream)
+    if fn_name == "noalloc":
+        st = dg.gemm_bf16_ws_noalloc(M, N, K, alpha, a.data_ptr(), K, b.data_ptr(), N, beta,
+                                     c.data_ptr(), N, h)
+    else:
+        n = dg.gemm_bf16_workspace_size(M, N, K)
+        ws = torch.zeros(max(n, 1), dtype=torch.uint8, device="cuda")
+        st = dg.gemm_bf16_ws(M, N, K, alpha, a.data_ptr(), K, b.data_ptr(), N, beta,
+                             c.data_ptr(), N, ws.data_ptr() if n else None, n, h)
+    torch.cuda.synchronize()
+    return c.cpu(), st
+
+
+# Consecutive calls on the one scratch: the largest streaming split (128
+# rows, 32 MiB), then smaller ones (streaming split, the 64-column split with
+# 64-row tiles, the tiled kernel's split for M > 128, and a shape that does
+# not split).
+SEQUENCE = [((128, 8192, 8192), 1.0, 0.0), ((16, 8192, 8192), 1.0, 0.0), ((16, 4352, 1000), 0.5, 2.0),
+            ((40, 1032, 4104), 1.0, 1.0), ((512, 2048, 4096), 1.0, 0.0),
+            ((16, 16384, 128), 1.0, 0.0)]
+
+
+def test_noalloc_matches_workspace_call_over_consecutive_calls():
+    for n, ((M, N, K), alpha, beta) in enumerate(SEQUENCE):
+        A, B, C0 = _operands(M, N, K, 8100 + 10 * n, beta)
+        note(f"gemm_bf16_ws_noalloc call {n}: M={M} N={N} K={K} alpha={alpha} beta={beta}")
+        C1, st1 = _run("noalloc", A, B, C0, alpha, beta)
+        assert st1 == dg.GEMM_OK, dg.gemm_status_string(st1)
+        C2, st2 = _run("ws", A, B, C0, alpha, beta)
+        assert st2 == dg.GEMM_OK, dg.gemm_status_string(st2)
+        assert torch.equal(C1.view(torch.int16), C2.view(torch.int16)), f"call {n} differs"
+        R, D = oracle_ref("bf16", A, B, C0, alpha, beta)
+        err = oracle.max_rel_err(to_f64(C1), R, D)
+        assert err <= tol("bf16"), f"call {n}: max error ratio {err:.3e}"
+
+
+def test_noalloc_repeat_is_bitwise_stable():
+    # The same call twice on the scratch the previous call left behind.
+    M, N, K = 16, 8192, 8192
+    A, B, _ = _operands(M, N, K, 8200, 0.0)
+    note("gemm_bf16_ws_noalloc repeat 16x8192x8192")
+    first, st = _run("noalloc", A, B, None, 1.0, 0.0)
+    assert st == dg.GEMM_OK
+    again, st = _run("noalloc", A, B, None, 1.0, 0.0)
+    assert st == dg.GEMM_OK
+    assert torch.equal(first.view(torch.int16), again.view(torch.int16))
+
+
+def test_noalloc_rejects_shapes_beyond_the_scratch():
+    # 512 x 8192 x 8192: 64 tiles of 256 x 256, each cut into 4 K ranges of
+    # 256 KB fp32 partials: 64 MiB, past the 32 MiB scratch.
+    M, N, K = 512, 8192, 8192
+    need = dg.gemm_bf16_workspace_size(M, N, K)
+    assert need > dg.NOALLOC_SCRATCH_BYTES
+    a = torch.zeros(M, K, dtype=torch.bfloat16, device="cuda")
+    b = torch.zeros(K, N, dtype=torch.bfloat16, device="cuda")
+    c = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    note("gemm_bf16_ws_noalloc beyond the scratch")
+    st = dg.gemm_bf16_ws_noalloc(M, N, K, 1.0, a.data_ptr(), K, b.data_ptr(), N, 0.0,
+                                 c.data_ptr(), N, 0)
+    torch.cuda.synchronize()
+    assert st == dg.GEMM_ERR_SCRATCH_LIMIT
+    assert "scratch" in dg.gemm_status_string(st)
+    assert bool(torch.isnan(c.float()).all())          # nothing was launched
