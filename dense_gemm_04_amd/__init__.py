@@ -42,7 +42,8 @@ OP_T = 1
 
 EXPORTS = ("gemm_f32", "gemm_bf16", "gemm_f32_ex", "gemm_bf16_ex", "gemm_bf16_ws",
            "gemm_bf16_workspace_size", "gemm_bf16_ws_noalloc", "gemm_f32_ws", "gemm_f32_workspace_size",
-           "gemm_f32_bias_act", "gemm_bf16_bias_act", "gemm_f32_op", "gemm_bf16_op", "gemm_plan",
+           "gemm_f32_bias_act", "gemm_bf16_bias_act", "gemm_f32_op", "gemm_bf16_op",
+           "gemm_f32_scaled", "gemm_bf16_scaled", "gemm_plan",
            "gemm_status_string")
 
 _lib = None
@@ -81,6 +82,10 @@ def load() -> ctypes.CDLL:
     for name in ("gemm_f32_op", "gemm_bf16_op"):
         fn = getattr(lib, name)
         fn.restype, fn.argtypes = ci, [ci, ci] + base[:11] + [vp, ci, vp, ctypes.c_size_t, vp]
+    for name in ("gemm_f32_scaled", "gemm_bf16_scaled"):
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = ci, [ci, ci] + base[:11] + [vp, vp, vp, ci, vp, ctypes.c_size_t,
+                                                              vp]
     for name in ("gemm_bf16_workspace_size", "gemm_f32_workspace_size"):
         fn = getattr(lib, name)
         fn.restype, fn.argtypes = ctypes.c_size_t, [i64, i64, i64]
@@ -154,6 +159,22 @@ def gemm_bf16_op(opa, opb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias=No
                  workspace=None, workspace_bytes=0, stream=0) -> int:
     return load().gemm_bf16_op(opa, opb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, act,
                                workspace, workspace_bytes, stream)
+
+
+def gemm_f32_scaled(opa, opb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, row_scale=None,
+                    col_scale=None, bias=None, act=0, workspace=None, workspace_bytes=0,
+                    stream=0) -> int:
+    return load().gemm_f32_scaled(opa, opb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                                  row_scale, col_scale, bias, act, workspace, workspace_bytes,
+                                  stream)
+
+
+def gemm_bf16_scaled(opa, opb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, row_scale=None,
+                     col_scale=None, bias=None, act=0, workspace=None, workspace_bytes=0,
+                     stream=0) -> int:
+    return load().gemm_bf16_scaled(opa, opb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                                   row_scale, col_scale, bias, act, workspace, workspace_bytes,
+                                   stream)
 
 
 def gemm_plan(elem_bytes, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, variant=0) -> int:

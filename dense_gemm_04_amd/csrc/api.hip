@@ -154,11 +154,13 @@ gemm_status_t run(int64_t M, int64_t N, int64_t K, float alpha, const T* A, int6
                   const T* B, int64_t ldb, float beta, T* C, int64_t ldc, void* stream,
                   int variant, void* ws = nullptr, size_t ws_bytes = 0,
                   const T* bias = nullptr, int act = GEMM_ACT_NONE, bool ta = false,
-                  bool tb = false) {
+                  bool tb = false, const float* row_scale = nullptr,
+                  const float* col_scale = nullptr) {
     constexpr int esz = (int)sizeof(T);
     const int v = plan_impl(esz, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, variant, ta, tb);
     if (v < 0) return GEMM_ERR_INVALID_VALUE;
     if (!valid_epilogue(esz, bias, act)) return GEMM_ERR_INVALID_VALUE;
+    if (!aligned(row_scale, 4) || !aligned(col_scale, 4)) return GEMM_ERR_INVALID_VALUE;
     const Work w = work_of(M, N, K, alpha, beta, bias);
     if (w == Work::kScale && C == nullptr) return GEMM_ERR_INVALID_VALUE;
     if (w == Work::kNone) return GEMM_OK;
@@ -171,7 +173,8 @@ gemm_status_t run(int64_t M, int64_t N, int64_t K, float alpha, const T* A, int6
         if constexpr (esz == 4) e = dg::launch_scale_f32(M, N, beta, C, ldc, bias, act, s);
         else e = dg::launch_scale_bf16(M, N, beta, C, ldc, bias, act, s);
     } else {
-        dg::GemmArgs<T> a{M, N, K, alpha, beta, A, lda, B, ldb, C, ldc, bias, act, ta, tb};
+        dg::GemmArgs<T> a{M, N, K, alpha, beta, A, lda, B, ldb, C, ldc, bias, act, ta, tb,
+                          row_scale, col_scale};
         const bool vec = vector_ok(esz, A, lda, B, ldb, C, ldc);
         if constexpr (esz == 4) {
             e = (v == GEMM_VARIANT_VALU) ? dg::launch_f32_valu(a, vec, s)
@@ -341,6 +344,32 @@ gemm_status_t gemm_bf16_op(int opa, int opb, int64_t M, int64_t N, int64_t K, fl
     return run<uint16_t>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, GEMM_VARIANT_AUTO,
                          workspace, workspace_bytes, bias, act, opa == GEMM_OP_T,
                          opb == GEMM_OP_T);
+}
+
+gemm_status_t gemm_f32_scaled(int opa, int opb, int64_t M, int64_t N, int64_t K, float alpha,
+                              const float* A, int64_t lda, const float* B, int64_t ldb,
+                              float beta, float* C, int64_t ldc, const float* row_scale,
+                              const float* col_scale, const float* bias, int act,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    if (!valid_op(opa) || !valid_op(opb)) return GEMM_ERR_INVALID_VALUE;
+    if (!workspace_ok(workspace, workspace_bytes, gemm_f32_workspace_size(M, N, K)))
+        return GEMM_ERR_INVALID_VALUE;
+    return run<float>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, GEMM_VARIANT_AUTO,
+                      workspace, workspace_bytes, bias, act, opa == GEMM_OP_T, opb == GEMM_OP_T,
+                      row_scale, col_scale);
+}
+
+gemm_status_t gemm_bf16_scaled(int opa, int opb, int64_t M, int64_t N, int64_t K, float alpha,
+                               const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                               float beta, uint16_t* C, int64_t ldc, const float* row_scale,
+                               const float* col_scale, const uint16_t* bias, int act,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+    if (!valid_op(opa) || !valid_op(opb)) return GEMM_ERR_INVALID_VALUE;
+    if (!workspace_ok(workspace, workspace_bytes, gemm_bf16_workspace_size(M, N, K)))
+        return GEMM_ERR_INVALID_VALUE;
+    return run<uint16_t>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, GEMM_VARIANT_AUTO,
+                         workspace, workspace_bytes, bias, act, opa == GEMM_OP_T,
+                         opb == GEMM_OP_T, row_scale, col_scale);
 }
 
 gemm_status_t gemm_f32(int64_t M, int64_t N, int64_t K, float alpha, const float* A,

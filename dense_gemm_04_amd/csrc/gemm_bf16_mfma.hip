@@ -261,11 +261,16 @@ void gemm_bf16_mfma_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
 
     // Epilogue: lane (pl, g) holds rows 4g + i of each 16-row block and the FN
     // consecutive columns wn0 + FN * pl .. + FN - 1.
+    // With EPI, the product is also scaled by the row's and the column's
+    // quantisation scale (row_factor folds the row scale into alpha).
     const float alpha = p.alpha, beta = p.beta;
-    float bv[FN];
+    float bv[FN], cv[FN];
     if constexpr (EPI) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) bv[j] = bias_at(p, n0 + wn0 + FN * pl + j);
+        for (int j = 0; j < FN; ++j) {
+            bv[j] = bias_at(p, n0 + wn0 + FN * pl + j);
+            cv[j] = col_factor(p, n0 + wn0 + FN * pl + j);
+        }
     }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -274,12 +279,13 @@ void gemm_bf16_mfma_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
             const int64_t row = m0 + wm0 + 16 * i + 4 * g + r;
             const int64_t col = n0 + wn0 + FN * pl;
             if (row >= M) continue;
+            const float fr = EPI ? row_factor(p, row) : alpha;
             float v[FN];
 #pragma unroll
-            for (int j = 0; j < FN; ++j) v[j] = alpha * acc[i][j][r];
+            for (int j = 0; j < FN; ++j) v[j] = fr * acc[i][j][r];
             if constexpr (EPI) {
 #pragma unroll
-                for (int j = 0; j < FN; ++j) v[j] = activate(v[j] + bv[j], p.act);
+                for (int j = 0; j < FN; ++j) v[j] = activate(v[j] * cv[j] + bv[j], p.act);
             }
             uint16_t* dst = p.C + row * p.ldc + col;
             if (FN == 8 && col + 8 <= N) {

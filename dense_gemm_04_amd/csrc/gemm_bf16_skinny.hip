@@ -170,7 +170,8 @@ void gemm_bf16_skinny_kernel(GemmArgs<uint16_t> p, int strips) {
 #pragma unroll
         for (int w = 1; w < kNT / 64; ++w) s += part[w][e];
         float v = alpha * s;
-        if constexpr (EPI) v = activate(v + bias_at(p, gc), p.act);
+        if constexpr (EPI)
+            v = activate(row_factor(p, row) * col_factor(p, gc) * s + bias_at(p, gc), p.act);
         uint16_t* dst = p.C + row * p.ldc + gc;
         if (beta != 0.f) v += beta * bf16_to_f32(*dst);
         *dst = f32_to_bf16(v);
@@ -227,8 +228,11 @@ __device__ __forceinline__ void store_row4(const GemmArgs<uint16_t>& p, int64_t 
                                            f32x4 s) {
     if (row >= p.M) return;
     if constexpr (EPI) {
+        // Quantisation scales of the row and the columns, then bias and activation.
+        const float fr = row_factor(p, row);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s[r] = activate(p.alpha * s[r] + bias_at(p, gc + r), p.act);
+        for (int r = 0; r < 4; ++r)
+            s[r] = activate(fr * col_factor(p, gc + r) * s[r] + bias_at(p, gc + r), p.act);
     } else {
         s *= p.alpha;
     }

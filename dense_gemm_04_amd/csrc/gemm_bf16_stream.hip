@@ -265,10 +265,8 @@ void gemm_bf16_stream_kernel(GemmArgs<uint16_t> p, StreamWork wk, unsigned char*
             float v[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                if constexpr (EPI)
-                    v[r] = activate(fr * col_factor(p, col + r) * acc[mb][j][r] + bias_at(p, col + r), p.act);
-                else
-                    v[r] = fr * acc[mb][j][r];
+                v[r] = fr * acc[mb][j][r];
+                if constexpr (EPI) v[r] = activate(v[r] * col_factor(p, col + r) + bias_at(p, col + r), p.act);
             }
             if (col + 4 <= N) {
                 // Four bf16 = 8 bytes, aligned: rows are 16-byte aligned and col % 4 == 0.

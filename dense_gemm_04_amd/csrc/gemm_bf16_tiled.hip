@@ -419,28 +419,34 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, Tail
     }
 
     // Epilogue: acc[j][i] register r holds C(m0 + wm0 + 16 i + pl, n0 + wn0 + 16 j + 4 g + r).
+    // With EPI, the product is also scaled by the row's and the column's
+    // quantisation scale (row_factor folds the row scale into alpha).
     const float alpha = p.alpha, beta = p.beta;
-    float bv[kFN][4];
+    float bv[kFN][4], cv[kFN][4];
     if constexpr (EPI) {
 #pragma unroll
         for (int j = 0; j < kFN; ++j)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) bv[j][r] = bias_at(p, n0 + wn0 + 16 * j + 4 * g + r);
+            for (int r = 0; r < 4; ++r) {
+                bv[j][r] = bias_at(p, n0 + wn0 + 16 * j + 4 * g + r);
+                cv[j][r] = col_factor(p, n0 + wn0 + 16 * j + 4 * g + r);
+            }
     }
 #pragma unroll
     for (int i = 0; i < kFM; ++i) {
         const int64_t row = m0 + wm0 + 16 * i + pl;
         if (row >= M) continue;
         uint16_t* crow = p.C + row * p.ldc;
+        const float fr = EPI ? row_factor(p, row) : alpha;
 #pragma unroll
         for (int j = 0; j < kFN; ++j) {
             const int64_t col = n0 + wn0 + 16 * j + 4 * g;
             float v[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] = alpha * acc[j][i][r];
+            for (int r = 0; r < 4; ++r) v[r] = fr * acc[j][i][r];
             if constexpr (EPI) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) v[r] = activate(v[r] + bv[j][r], p.act);
+                for (int r = 0; r < 4; ++r) v[r] = activate(v[r] * cv[j][r] + bv[j][r], p.act);
             }
             if (col + 4 <= N) {
                 u32x2* dst = reinterpret_cast<u32x2*>(crow + col);

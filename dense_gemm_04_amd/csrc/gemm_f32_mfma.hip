@@ -515,10 +515,15 @@ __device__ __forceinline__ void f32_tile(GemmArgs<float> p, int tiles_m, int til
         // Block j of row block i: lane (pl, g) holds rows 16 i + 4 g + r (or
         // 16 g + 4 r + i with A staged [k][m]) of column wn0 + 16 j + pl; 16
         // lanes store 64 consecutive bytes.
-        float bvk[4];
+        // With EPI, the product is also scaled by the row's and the column's
+        // quantisation scale (row_factor folds the row scale into alpha).
+        float bvk[4], cvk[4];
         if constexpr (EPI) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) bvk[j] = bias_at(p, n0 + wn0 + 16 * j + pl);
+            for (int j = 0; j < 4; ++j) {
+                bvk[j] = bias_at(p, n0 + wn0 + 16 * j + pl);
+                cvk[j] = col_factor(p, n0 + wn0 + 16 * j + pl);
+            }
         }
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
@@ -526,12 +531,13 @@ __device__ __forceinline__ void f32_tile(GemmArgs<float> p, int tiles_m, int til
             for (int r = 0; r < 4; ++r) {
                 const int64_t row = m0 + wm0 + (AMC ? 16 * g + 4 * r + i : 16 * i + 4 * g + r);
                 if (row >= M) continue;
+                const float fr = EPI ? row_factor(p, row) : alpha;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int64_t col = n0 + wn0 + 16 * j + pl;
                     if (col >= N) continue;
-                    float x = alpha * acc[i][0][j][r];
-                    if constexpr (EPI) x = activate(x + bvk[j], p.act);
+                    float x = fr * acc[i][0][j][r];
+                    if constexpr (EPI) x = activate(x * cvk[j] + bvk[j], p.act);
                     float* dst = p.C + row * p.ldc + col;
                     if (beta != 0.f) x += beta * *dst;
                     *dst = x;
@@ -540,12 +546,15 @@ __device__ __forceinline__ void f32_tile(GemmArgs<float> p, int tiles_m, int til
         }
         return;
     }
-    float bv[NG][4];
+    float bv[NG][4], cv[NG][4];
     if constexpr (EPI) {
 #pragma unroll
         for (int gq = 0; gq < NG; ++gq)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) bv[gq][j] = bias_at(p, n0 + wn0 + 64 * gq + 4 * pl + j);
+            for (int j = 0; j < 4; ++j) {
+                bv[gq][j] = bias_at(p, n0 + wn0 + 64 * gq + 4 * pl + j);
+                cv[gq][j] = col_factor(p, n0 + wn0 + 64 * gq + 4 * pl + j);
+            }
     }
     // With beta != 0, a workgroup that computes one tile loads all of its C
     // values before the first store (the stores could alias later loads, so
@@ -578,16 +587,17 @@ __device__ __forceinline__ void f32_tile(GemmArgs<float> p, int tiles_m, int til
             // Block i of an m-contiguous A covers rows 4 x + i.
             const int64_t row = m0 + wm0 + (AMC ? 16 * g + 4 * r + i : 16 * i + 4 * g + r);
             if (row >= M) continue;
+            const float fr = EPI ? row_factor(p, row) : alpha;
 #pragma unroll
             for (int gq = 0; gq < NG; ++gq) {
                 const int64_t col = n0 + wn0 + 64 * gq + 4 * pl;
                 float* dst = p.C + row * p.ldc + col;
                 f32x4 v;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) v[j] = alpha * acc[i][gq][j][r];
+                for (int j = 0; j < 4; ++j) v[j] = fr * acc[i][gq][j][r];
                 if constexpr (EPI) {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) v[j] = activate(v[j] + bv[gq][j], p.act);
+                    for (int j = 0; j < 4; ++j) v[j] = activate(v[j] * cv[gq][j] + bv[gq][j], p.act);
                 }
                 if (col + 4 <= N) {
                     if (beta != 0.f) {

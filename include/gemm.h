@@ -270,6 +270,35 @@ gemm_status_t gemm_bf16_op(int opa, int opb, int64_t M, int64_t N, int64_t K, fl
                            float beta, uint16_t* C, int64_t ldc, const uint16_t* bias, int act,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* Quantisation scales (Blackwell BF16 GEMM notes, section 3.3: quantisation
+ * scaling is epilogue work beside GELU and the residual):
+ *
+ *     C(i,j) <- act(alpha * row_scale[i] * col_scale[j] * sum_k op(A)(i,k) op(B)(k,j)
+ *                   + bias[j]) + beta * C(i,j)
+ *
+ * row_scale: device pointer to M fp32 values (the dequantisation factor of
+ *            each row of op(A), e.g. of a per-token quantised activation), or
+ *            NULL for 1;
+ * col_scale: device pointer to N fp32 values (the factor of each column of
+ *            op(B), e.g. of a per-channel quantised weight), or NULL for 1.
+ * Both 4-byte aligned (GEMM_ERR_INVALID_VALUE otherwise). The factors multiply
+ * the fp32 accumulator in the epilogue, before the bias, the activation and
+ * the beta term, and cost no extra pass over memory; they apply to the same
+ * operand types as the other entry points (fp32 or bf16 operands, fp32
+ * accumulation). opa, opb, bias, act, workspace and every other rule are
+ * those of gemm_*_op; with both scales NULL the two calls are the same. When
+ * K == 0 or alpha == 0 the product term is zero and the scales are not read. */
+gemm_status_t gemm_f32_scaled(int opa, int opb, int64_t M, int64_t N, int64_t K, float alpha,
+                              const float* A, int64_t lda, const float* B, int64_t ldb,
+                              float beta, float* C, int64_t ldc, const float* row_scale,
+                              const float* col_scale, const float* bias, int act,
+                              void* workspace, size_t workspace_bytes, void* stream);
+gemm_status_t gemm_bf16_scaled(int opa, int opb, int64_t M, int64_t N, int64_t K, float alpha,
+                               const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                               float beta, uint16_t* C, int64_t ldc, const float* row_scale,
+                               const float* col_scale, const uint16_t* bias, int act,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* Host-only planning (no HIP call): the variant a call with these arguments
  * would run (a gemm_variant_t value; GEMM_VARIANT_AUTO when the call would
  * launch no GEMM kernel), or -1 when the arguments are invalid. `elem_bytes`
