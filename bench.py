@@ -1,17 +1,26 @@
 """Benchmark: GEMM TFLOPS (2MNK/t) on one MI355X.
 
 Default run: the 4096^3 fp32 SGEMM (the pages' headline shape) is the timed
-step; the 4096^3 bf16 GEMM is timed the same way and reported beside it.
-Inputs are seeded synthetic matrices already resident in HBM. A step is one
-library call (one kernel launch) on torch's current stream, timed with HIP
-events over exactly --steps calls after --warmup untimed calls (each leg first
-runs its call untimed for a quarter second so the GPU clock has settled).
+step; `value` is its rate. Inputs are seeded synthetic matrices already
+resident in HBM. A step is one library call (one kernel launch) on torch's
+current stream, timed with HIP events over exactly --steps calls after
+--warmup untimed calls (each leg first runs its call untimed for a quarter
+second so the GPU clock has settled).
 
 Also reported:
   roofline      the timed kernel against MI355X's published fp32 matrix peak;
-  cpu_baseline  the CPU oracle (fp64, OpenMP over all host threads) timed on a
-                bounded sample of the same workload: full rows of C, scaled to
-                TFLOPS by 2 * rows * N * K / seconds.
+  cpu_baseline  the CPU oracle (fp64, OpenMP over all host threads) on the
+                whole 4096^3 product, as TFLOPS = 2MNK / seconds;
+  workloads     every workload the parity tests cover, each timed as 7
+                repetitions of n back-to-back calls (n >= 20 and a repetition
+                >= 20 ms) after 10 warm-up calls, reported as the median and
+                the minimum time per call; the split-K calls (gemm_*_ws) beside
+                the plain ones for the ragged fp32 shape and small M; the
+                small-M lines rotate 4 operand sets (512 MiB of B, more than
+                the 256 MB Infinity Cache). Each carries its fraction of the
+                bounding roofline, its HBM traffic ratio when a current
+                counter summary exists, and its own oracle timing (config 1
+                also on one thread).
 
 ``--all`` prints one JSON line per workload instead (for the design notes).
 """
@@ -152,6 +161,110 @@ def _device_call(w, sets: int = 1, use_ws: bool = False, act=None, ops=None, var
     return call, stream, inp
 
 
+REPS = 7
+MIN_REP_SECONDS = 0.02
+MIN_REP_CALLS = 20
+
+
+def _time_reps(call, stream, reps: int = REPS, warmup: int = 10):
+    """(median, min) seconds per call and the calls per repetition: after the
+    settling run and `warmup` calls, `reps` repetitions of n back-to-back
+    calls, each bracketed by HIP events on the launch stream, with n chosen so
+    that a repetition lasts at least MIN_REP_SECONDS and has at least
+    MIN_REP_CALLS calls."""
+    import statistics
+    import torch
+    probe = _time_calls(call, 10, warmup, stream)
+    n = max(MIN_REP_CALLS, int(MIN_REP_SECONDS / max(probe, 1e-9)) + 1)
+    per = []
+    for _ in range(reps):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(n):
+            call()
+        end.record(stream)
+        torch.cuda.synchronize()
+        per.append(start.elapsed_time(end) / 1e3 / n)
+    return statistics.median(per), min(per), n
+
+
+# Committed counter summary and kernel source behind each line of the
+# `workloads` report (the traffic ratio is reported only while the summary's
+# source hash matches the kernel built now).
+PROFILE_OF = {
+    "2": ("gemm_f32_mfma_4096.md", "gemm_f32_mfma.hip"),
+    "3": ("gemm_bf16_tiled_4096.md", "gemm_bf16_tiled.hip"),
+    "4": ("gemm_bf16_tiled_proj_8192x12288x4096.md", "gemm_bf16_tiled.hip"),
+    "51": ("gemm_f32_mfma_edge_4095x4097x1023.md", "gemm_f32_mfma.hip"),
+    "51_ws": ("gemm_f32_mfma_edge_splitk_4095x4097x1023.md", "gemm_f32_mfma.hip"),
+    "52": ("gemm_bf16_smallm_16x8192x8192.md", "gemm_bf16_skinny.hip"),
+    "52_ws": ("gemm_bf16_stream_splitk_16x8192x8192.md", "gemm_bf16_stream.hip"),
+}
+
+# The kernel each line runs.
+KERNEL_OF = {
+    "1": "gemm_f32_mfma (copy path, 128x128 tiles)",
+    "2": "gemm_f32_mfma (copy path, 128x128 tiles, tiles walked)",
+    "3": "gemm_bf16_tiled (256x256 tiles)",
+    "4": "gemm_bf16_tiled (256x256 tiles, beta = 1 residual)",
+    "51": "gemm_f32_mfma (unaligned rows, register-staged)",
+    "51_ws": "gemm_f32_mfma (unaligned rows, split-K tail round)",
+    "52": "gemm_bf16_smallm (64-column strips, 128 workgroups)",
+    "52_ws": "gemm_bf16_stream (256-column strips, K interleaved over 8 phases)",
+}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_timing(w, threads: int = 0) -> dict:
+    """The oracle over every entry of the workload's C, timed by wall clock
+    (`threads` = 0: all host threads)."""
+    import oracle
+    import gemm_inputs as gi
+    inp = gi.make(w)
+    A, B = gi.as_numpy(inp["A"]), gi.as_numpy(inp["B"])
+    C0 = gi.as_numpy(inp["C0"]) if inp["C0"] is not None else None
+    t0 = time.perf_counter()
+    oracle.gemm(A, B, C0, w.alpha, w.beta, w.dtype, threads=threads)
+    sec = time.perf_counter() - t0
+    return {"seconds": round(sec, 3), "tflops": tflops(gemm_flops(w.M, w.N, w.K), sec),
+            "gflops_fp64": gemm_flops(w.M, w.N, w.K) / sec / 1e9,
+            "threads": threads if threads > 0 else oracle.max_threads(),
+            "sample": f"all {w.M}x{w.N} entries"}
+
+
+def workload_report(w, key: str, sets: int = 1, use_ws: bool = False) -> dict:
+    """One line of the `workloads` report (see the module docstring)."""
+    call, stream, _ = _device_call(w, sets, use_ws)
+    med, mn, n = _time_reps(call, stream)
+    peak = PEAK_TFLOPS[w.dtype]
+    out = {"workload": w.name, "call": ("gemm_f32_ws" if w.dtype == "f32" else "gemm_bf16_ws")
+           if use_ws else ("gemm_f32" if w.dtype == "f32" else "gemm_bf16"),
+           "kernel": KERNEL_OF.get(key), "dtype": w.dtype, "M": w.M, "N": w.N, "K": w.K,
+           "alpha": w.alpha, "beta": w.beta, "operand_sets": sets,
+           "ms_median": round(med * 1e3, 5), "ms_min": round(mn * 1e3, 5),
+           "reps": REPS, "calls_per_rep": n,
+           "tflops": round(tflops(gemm_flops(w.M, w.N, w.K), med), 3),
+           "peak_tflops": peak, "frac_matrix_peak": round(tflops(gemm_flops(w.M, w.N, w.K), med) / peak, 4),
+           "algorithmic_bytes": w.algorithmic_bytes,
+           "gbs": round(w.algorithmic_bytes / med / 1e9, 1),
+           "frac_hbm": round(w.algorithmic_bytes / med / 1e9 / PEAK_HBM_GBS, 4)}
+    prof = PROFILE_OF.get(key)
+    traffic = measured_traffic(*prof) if prof else None
+    out["traffic_ratio"] = round(traffic / w.algorithmic_bytes, 2) if traffic else None
+    out["bound"] = "hbm" if key.startswith("52") else "mfma"
+    return out
+
+
 def measure(w, steps: int, warmup: int, sets: int = 1, use_ws: bool = False, act=None,
             ops=None, variant=None) -> dict:
     call, stream, _ = _device_call(w, sets, use_ws, act, ops, variant)
@@ -264,32 +377,6 @@ def measured_traffic(summary: str, source: str):
         return None
 
 
-def cpu_baseline(w, target_seconds: float = 12.0) -> dict:
-    """Time the oracle on full rows of C for this workload (bounded sample)."""
-    import oracle
-    import gemm_inputs as gi
-    import numpy as np
-    inp = gi.make(w)
-    A, B = gi.as_numpy(inp["A"]), gi.as_numpy(inp["B"])
-    C0 = gi.as_numpy(inp["C0"]) if inp["C0"] is not None else None
-    threads = oracle.max_threads()
-    rows = max(1, min(w.M, 2 * threads))
-    t0 = time.perf_counter()
-    oracle.gemm(A, B, C0, w.alpha, w.beta, w.dtype, rows=list(range(rows)))
-    t1 = time.perf_counter() - t0
-    # Scale the sample so the timed call takes about target_seconds.
-    rows2 = int(min(w.M, max(rows, rows * target_seconds / max(t1, 1e-3))))
-    rows2 = max(threads, (rows2 // threads) * threads) if rows2 >= threads else rows2
-    sel = list(np.linspace(0, w.M - 1, rows2).astype(np.int64))
-    t0 = time.perf_counter()
-    oracle.gemm(A, B, C0, w.alpha, w.beta, w.dtype, rows=sel)
-    sec = time.perf_counter() - t0
-    return {"value": tflops(gemm_flops(rows2, w.N, w.K), sec), "unit": "TFLOPS",
-            "cores": threads, "kind": "oracle",
-            "sample": f"{rows2} full rows of C ({rows2}x{w.N}x{w.K}, fp64 accumulate) "
-                      f"in {sec:.1f} s"}
-
-
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -387,6 +474,11 @@ def main(argv=None) -> int:
     w = gi.WORKLOADS[2]
     main_r = measure(w, args.steps, args.warmup)
     bf = measure(gi.WORKLOADS[3], args.steps, args.warmup)
+    workloads = {}
+    for key, wid, sets, use_ws in (("1", 1, 1, False), ("2", 2, 1, False), ("3", 3, 1, False),
+                                   ("4", 4, 1, False), ("51", 51, 1, False), ("51_ws", 51, 1, True),
+                                   ("52", 52, 4, False), ("52_ws", 52, 4, True)):
+        workloads[key] = workload_report(gi.WORKLOADS[wid], key, sets, use_ws)
     line = {
         "metric": METRIC,
         "value": round(main_r["tflops"], 3),
@@ -411,8 +503,22 @@ def main(argv=None) -> int:
                       "tflops": round(bf["tflops"], 3), "ms": round(bf["ms"], 4),
                       "peak": PEAK_TFLOPS["bf16"], "frac": round(bf["frac_matrix_peak"], 4)},
     }
+    line["workloads"] = workloads
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(w)
+        # The whole 4096^3 product on all host threads (3-4 s on 16 cores), and
+        # every other workload's oracle beside its line.
+        t = oracle_timing(w)
+        line["cpu_baseline"] = {"value": t["tflops"], "unit": "TFLOPS", "cores": t["threads"],
+                                "kind": "oracle", "cpu_model": cpu_model(),
+                                "sample": f"all 4096x4096 entries of C (fp64 accumulate) in "
+                                          f"{t['seconds']:.1f} s"}
+        for key, rep in workloads.items():
+            wid = int(key.split("_")[0])
+            if key.endswith("_ws"):
+                rep["cpu_oracle"] = workloads[str(wid)].get("cpu_oracle")
+                continue
+            rep["cpu_oracle"] = t if wid == 2 else oracle_timing(gi.WORKLOADS[wid])
+        workloads["1"]["cpu_oracle_1_thread"] = oracle_timing(gi.WORKLOADS[1], threads=1)
     print(json.dumps(line), flush=True)
     return 0
 
