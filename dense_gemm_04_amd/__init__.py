@@ -58,12 +58,25 @@ class GemmError(RuntimeError):
 def load() -> ctypes.CDLL:
     """Load the native library (raises if it has not been built)."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+    if _lib is None:
+        _lib = _bind(LIB_PATH)
+    return _lib
+
+
+def load_check_build(check: str) -> ctypes.CDLL:
+    """One of the LDS-checking builds ("poison" or "sync"; see build.py), as
+    a separate library handle with the same C functions, for the tests that
+    compare it with the normal build."""
+    if check not in ("poison", "sync"):
+        raise ValueError(check)
+    return _bind(os.path.join(PKG, f"libdense_gemm_04_amd_{check}.so"))
+
+
+def _bind(path: str) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
                            "`python -c 'import __graft_entry__ as g; g.build()'`")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     i64, f32, vp, ci = ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_int
     base = [i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64, vp]
     for name in ("gemm_f32", "gemm_bf16"):
@@ -93,7 +106,6 @@ def load() -> ctypes.CDLL:
     lib.gemm_plan.argtypes = [ci, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64, ci]
     lib.gemm_status_string.restype = ctypes.c_char_p
     lib.gemm_status_string.argtypes = [ci]
-    _lib = lib
     return lib
 
 

@@ -182,6 +182,47 @@ __device__ __forceinline__ void lds_barrier() {
     lds_only_barrier();
 }
 
+// ---- checking builds of the LDS pipelines -----------------------------------
+//
+// The library is also built twice more, with DG_LDS_CHECK set, and the tests
+// require both builds to give the normal build's results bit for bit:
+//   1 (poison): right after the barrier that retires an LDS stage (every read
+//     of its previous contents done; the next write into it not yet issued),
+//     the workgroup fills the stage with NaN. A read of a retired stage, or of
+//     a stage whose copy has not landed yet, then sees NaN rather than stale
+//     but plausible data, and the NaN reaches the output.
+//   2 (synchronous copies): every batch of global -> LDS copies is preceded
+//     by a barrier that retires all outstanding LDS reads and followed by a
+//     wait for the copies and a barrier, so no copy is ever in flight while a
+//     wave reads LDS: the order a single staging buffer would impose, with
+//     none of the overlap that the pipelines' own waits have to protect.
+// The normal build (0) compiles every hook to nothing.
+#ifndef DG_LDS_CHECK
+#define DG_LDS_CHECK 0
+#endif
+constexpr int kLdsCheck = DG_LDS_CHECK;
+
+// Poison build: fill `bytes` (a multiple of 16) of LDS at `p` with NaN (all
+// ones is a NaN in fp32 and in bf16), thread t of nt doing every nt-th
+// 16-byte chunk, then a barrier so that no later write into the stage can be
+// overtaken by the fill. Every thread of the workgroup must call it.
+__device__ __forceinline__ void lds_retire(void* p, int bytes, int t, int nt) {
+    if constexpr (kLdsCheck == 1) {
+        for (int i = 16 * t; i < bytes; i += 16 * nt)
+            *reinterpret_cast<u32x4*>(static_cast<char*>(p) + i) = u32x4{~0u, ~0u, ~0u, ~0u};
+        lds_only_barrier();
+    }
+}
+
+// Synchronous-copy build: the hooks around every call that issues copies
+// (reached by every wave of the workgroup, copying or not).
+__device__ __forceinline__ void copy_begin() {
+    if constexpr (kLdsCheck == 2) lds_barrier();
+}
+__device__ __forceinline__ void copy_end() {
+    if constexpr (kLdsCheck == 2) lds_barrier();
+}
+
 // ---- split of the last round of tiles ---------------------------------------
 //
 // The simplest form of stream-K: workgroups 0 .. full - 1 each own a whole

@@ -248,11 +248,16 @@ void gemm_bf16_mfma_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
     };
 
     const int64_t nk = (K + kBK - 1) / kBK;
+    // Poison build: stage 0 starts as NaN; the other stage is refilled with
+    // NaN at the top of each slab, after the barrier that retired it.
+    if constexpr (kLdsCheck == 1) lds_retire(smem, STAGE * 2, threadIdx.x, blockDim.x);
     gload(0);
     sstore(0);
     __syncthreads();
     for (int64_t kt = 0; kt < nk; ++kt) {
         const int cur = (int)(kt & 1);
+        if (kLdsCheck == 1 && kt + 1 < nk)
+            lds_retire(smem + (cur ^ 1) * STAGE, STAGE * 2, threadIdx.x, blockDim.x);
         if (kt + 1 < nk) gload((kt + 1) * kBK);
         compute(cur);
         if (kt + 1 < nk) sstore(cur ^ 1);

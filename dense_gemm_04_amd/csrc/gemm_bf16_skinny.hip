@@ -136,16 +136,24 @@ void gemm_bf16_skinny_kernel(GemmArgs<uint16_t> p, int strips) {
     // One barrier per chunk: stage s is rewritten two chunks after it was
     // read, and the barrier of the chunk in between separates the two.
     const int64_t nc = (K + kKC - 1) / kKC;
+    // Poison build: both stages start as NaN, and each is refilled with NaN
+    // after the barrier that retires it (a no-op in other builds).
+    if constexpr (kLdsCheck == 1) {
+        lds_retire(bt[0], kBN * kKC * 2, t, kNT);
+        lds_retire(bt[1], kBN * kKC * 2, t, kNT);
+    }
     gload(0, 0);
     if (nc > 1) gload(1, kKC);
     for (int64_t c = 0; c < nc; c += 2) {
         sstore(0, 0);
         __syncthreads();
+        if (c > 0 && kLdsCheck == 1) lds_retire(bt[1], kBN * kKC * 2, t, kNT);
         compute(0, 0);
         if (c + 2 < nc) gload(0, (c + 2) * kKC);
         if (c + 1 < nc) {
             sstore(1, 1);
             __syncthreads();
+            if (kLdsCheck == 1) lds_retire(bt[0], kBN * kKC * 2, t, kNT);
             compute(1, 1);
             if (c + 3 < nc) gload(1, (c + 3) * kKC);
         }
@@ -391,8 +399,22 @@ void gemm_bf16_smallm_kernel(GemmArgs<uint16_t> p, SmallMWork wk, unsigned char*
     // order (a rotation measured slower there).
     const int64_t rot = TB ? (int64_t)(strip >> 3) % nc : 0;
     auto rc = [&](int64_t c) { return cb + (c + rot >= nc ? c + rot - nc : c + rot); };
+    // Checking builds (no-ops otherwise): every slot starts as NaN and is
+    // refilled with NaN once retired (poison); copies are bracketed by
+    // barriers (synchronous copies).
+    auto retire = [&](int slot) {
+        if constexpr (kLdsCheck == 1) {
+            lds_retire(lds_b + slot * S::kBStage, S::kBStage * 2, t, kNT);
+            lds_retire(lds_a + slot * S::kAStage, S::kAStage * 2, t, kNT);
+        }
+    };
+    for (int slot = 0; slot < S::kStages; ++slot) retire(slot);
     const int64_t pre = nc < S::kStages - 1 ? nc : S::kStages - 1;
-    for (int64_t c = 0; c < pre; ++c) dma(rc(c), (int)c);
+    for (int64_t c = 0; c < pre; ++c) {
+        copy_begin();
+        dma(rc(c), (int)c);
+        copy_end();
+    }
     int stage = 0;
     for (int64_t c = 0; c < nc; ++c) {
         if (c + S::kStages - 2 <= nc - 1)
@@ -400,7 +422,13 @@ void gemm_bf16_smallm_kernel(GemmArgs<uint16_t> p, SmallMWork wk, unsigned char*
         else
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         lds_only_barrier();
-        if (c + S::kStages - 1 < nc) dma(rc(c + S::kStages - 1), stage == 0 ? S::kStages - 1 : stage - 1);
+        const int prev = stage == 0 ? S::kStages - 1 : stage - 1;   // slot of chunk c - 1, retired
+        if (c > 0) retire(prev);
+        if (c + S::kStages - 1 < nc) {
+            copy_begin();
+            dma(rc(c + S::kStages - 1), prev);
+            copy_end();
+        }
         compute(rc(c), stage);
         stage = stage + 1 == S::kStages ? 0 : stage + 1;
     }

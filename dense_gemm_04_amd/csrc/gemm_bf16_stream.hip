@@ -174,8 +174,22 @@ void gemm_bf16_stream_kernel(GemmArgs<uint16_t> p, StreamWork wk, unsigned char*
     // chunk c each wave waits for its own copies of chunk c (later ones may
     // stay in flight), then the barrier publishes chunk c and retires every
     // read of chunk c - 1, whose slot the copy for chunk c + kStages - 1 reuses.
+    // Checking builds (no-ops otherwise): every slot starts as NaN and is
+    // refilled with NaN once retired (poison); copies are bracketed by
+    // barriers (synchronous copies).
+    auto retire = [&](int slot) {
+        if constexpr (kLdsCheck == 1) {
+            lds_retire(lds_b + slot * S::kBStage, S::kBStage * 2, t, kNT);
+            lds_retire(lds_a + slot * S::kAStage, S::kAStage * 2, t, kNT);
+        }
+    };
+    for (int slot = 0; slot < kStages; ++slot) retire(slot);
     const int64_t pre = nc < kStages - 1 ? nc : kStages - 1;
-    for (int64_t c = 0; c < pre; ++c) dma(c, (int)c);
+    for (int64_t c = 0; c < pre; ++c) {
+        copy_begin();
+        dma(c, (int)c);
+        copy_end();
+    }
     int stage = 0;
     for (int64_t c = 0; c < nc; ++c) {
         if (c + kStages - 2 <= nc - 1)
@@ -183,7 +197,13 @@ void gemm_bf16_stream_kernel(GemmArgs<uint16_t> p, StreamWork wk, unsigned char*
         else
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         lds_only_barrier();
-        if (c + kStages - 1 < nc) dma(c + kStages - 1, stage == 0 ? kStages - 1 : stage - 1);
+        const int prev = stage == 0 ? kStages - 1 : stage - 1;   // slot of chunk c - 1, retired
+        if (c > 0) retire(prev);
+        if (c + kStages - 1 < nc) {
+            copy_begin();
+            dma(c + kStages - 1, prev);
+            copy_end();
+        }
         compute(c, stage);
         stage = stage + 1 == kStages ? 0 : stage + 1;
     }

@@ -337,13 +337,29 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, Tail
     // that ends at nk holds the ragged K tail.
     const int k_tail = (int)(K - (nk - 1) * kBK);   // 1 .. 64
     const bool tail_here = kZeroTail && ke == nk && k_tail < kBK;
+    // Checking builds: both stages start as NaN (poison) and every batch of
+    // copies is bracketed by barriers (synchronous copies); no-ops otherwise.
+    auto retire = [&](int stage) {
+        if constexpr (kLdsCheck == 1) {
+            lds_retire(a_stage(stage), kAStage * 2, t, kNT);
+            lds_retire(b_stage(stage), kBStage * 2, t, kNT);
+        }
+    };
+    retire(0);
+    retire(1);
+    copy_begin();
     dma(kb, 0);
+    copy_end();
     lds_barrier();
     if (tail_here && kb + 1 == ke) {
         zero_a_tail(0, k_tail);
         lds_barrier();
     }
-    if (kb + 1 < ke) dma(kb + 1, 1);
+    if (kb + 1 < ke) {
+        copy_begin();
+        dma(kb + 1, 1);
+        copy_end();
+    }
     read_frags(0, 0, 0);
     // One slab; `cur` is a literal at both call sites (the loop is unrolled by
     // two), so every LDS access names its stage array statically.
@@ -352,11 +368,17 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, Tail
         mfmas(0);
         if (kt + 1 < ke) {
             lds_barrier();
+            // Every read of stage `cur` (slab kt) is retired here.
+            retire(cur);
             if (tail_here && kt + 2 == ke) {
                 zero_a_tail(cur ^ 1, k_tail);
                 lds_barrier();
             }
-            if (kt + 2 < ke) dma(kt + 2, cur);
+            if (kt + 2 < ke) {
+                copy_begin();
+                dma(kt + 2, cur);
+                copy_end();
+            }
             read_frags(cur ^ 1, 0, 0);
         }
         mfmas(1);

@@ -424,7 +424,13 @@ __device__ __forceinline__ void f32_tile(GemmArgs<float> p, int tiles_m, int til
         };
         const int k_tail = (int)(K - (nk - 1) * kBK);   // 1 .. kBK
         const bool tail_here = kZeroLo < kZeroHi && ke == nk && k_tail < kBK;
+        // Checking builds (no-ops otherwise): stage 0 starts as NaN and each
+        // stage is refilled with NaN once retired (poison); copies are
+        // bracketed by barriers (synchronous copies).
+        if constexpr (kLdsCheck == 1) lds_retire(smem, STAGE * 4, t, NT);
+        copy_begin();
         dma(kb, 0);
+        copy_end();
         lds_barrier();
         if (tail_here && kb + 1 == ke) {
             zero_a_tail(0, k_tail);
@@ -434,7 +440,12 @@ __device__ __forceinline__ void f32_tile(GemmArgs<float> p, int tiles_m, int til
             const int cur = (int)((kt - kb) & 1);
             // The other stage was last read in slab kt - 1, before the
             // barrier that ended it.
-            if (kt + 1 < ke) dma(kt + 1, cur ^ 1);
+            if (kt + 1 < ke) {
+                if constexpr (kLdsCheck == 1) lds_retire(smem + (cur ^ 1) * STAGE, STAGE * 4, t, NT);
+                copy_begin();
+                dma(kt + 1, cur ^ 1);
+                copy_end();
+            }
             compute(cur);
             if (kt + 1 < ke) {
                 lds_barrier();
@@ -445,11 +456,15 @@ __device__ __forceinline__ void f32_tile(GemmArgs<float> p, int tiles_m, int til
             }
         }
     } else {
+        // Poison build: stage 0 starts as NaN; the other stage is refilled
+        // with NaN at the top of each slab, after the barrier that retired it.
+        if constexpr (kLdsCheck == 1) lds_retire(smem, STAGE * 4, t, NT);
         gload(kb * kBK);
         sstore(0);
         __syncthreads();
         for (int64_t kt = kb; kt < ke; ++kt) {
             const int cur = (int)((kt - kb) & 1);
+            if (kLdsCheck == 1 && kt + 1 < ke) lds_retire(smem + (cur ^ 1) * STAGE, STAGE * 4, t, NT);
             if (kt + 1 < ke) gload((kt + 1) * kBK);
             compute(cur);
             if (kt + 1 < ke) sstore(cur ^ 1);

@@ -36,6 +36,19 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, name), name
 
 
+@pytest.mark.parametrize("check", ["poison", "sync"])
+def test_checking_builds_load_and_export_every_symbol(check):
+    from dense_gemm_04_amd import build
+    if not os.path.exists(build.lib_path(check)):
+        build.build(check=check)
+    chk = dg.load_check_build(check)
+    for name in header_functions():
+        assert hasattr(chk, name), name
+    # Validation is the same code in every build.
+    assert chk.gemm_f32(-1, 4, 4, 1.0, 0x10000, 4, 0x20000, 4, 0.0, 0x30000, 4,
+                        None) == dg.GEMM_ERR_INVALID_VALUE
+
+
 def test_status_strings(lib):
     assert dg.gemm_status_string(0) == "success"
     assert dg.gemm_status_string(1) == "invalid argument"
