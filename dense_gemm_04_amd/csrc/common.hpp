@@ -241,15 +241,42 @@ struct TailSplit {
 constexpr int kMaxSplitParts = 8;
 
 // Tail split for `tiles` tiles of `nk` K slabs over `slots` resident
-// workgroups: when the last round would be at most half full, its tiles are
-// cut into K ranges (of at least `min_cps` slabs) so that the round fills up.
-inline TailSplit plan_tail_split(int64_t tiles, int64_t nk, int64_t slots, int64_t min_cps = 1) {
+// workgroups, with ranges of at least `min_cps` slabs. Host only.
+//   * A last round at most half full is cut into as many ranges as fill it:
+//     one round of shorter ranges.
+//   * A fuller last round (every tile, when there are fewer tiles than slots)
+//     takes the number of ranges p in 2..8 that minimises its length in slab
+//     times, ceil(tail p / slots) ceil(nk / p) + p fixup: the split units run
+//     in ceil(tail p / slots) rounds, and each tile's last range reads its p
+//     partial tiles back (`fixup` slab times each). Ranges span at least
+//     `min_cps_full` slabs: shorter ones spend more on their own start and
+//     epilogue than the model counts. It splits only when that saves at least
+//     an eighth of the unsplit round's nk slabs. A negative `fixup` leaves
+//     fuller rounds unsplit.
+inline TailSplit plan_tail_split(int64_t tiles, int64_t nk, int64_t slots, int64_t min_cps = 1,
+                                 double fixup = 0.25, int64_t min_cps_full = 16) {
     TailSplit t{(int)tiles, 0, 1, (int)nk};
     const int64_t tail = tiles % slots;
-    if (tail == 0 || 2 * tail > slots || nk < 2 * min_cps) return t;
-    int64_t parts = slots / tail;
-    if (parts > kMaxSplitParts) parts = kMaxSplitParts;
-    if (parts > nk / min_cps) parts = nk / min_cps;
+    if (tail == 0 || nk < 2 * min_cps) return t;
+    int64_t parts = 1;
+    if (2 * tail <= slots) {
+        parts = slots / tail;
+        if (parts > kMaxSplitParts) parts = kMaxSplitParts;
+        if (parts > nk / min_cps) parts = nk / min_cps;
+    } else {
+        if (fixup < 0) return t;
+        const int64_t floor_cps = min_cps > min_cps_full ? min_cps : min_cps_full;
+        double best = (double)nk;
+        for (int64_t p = 2; p <= kMaxSplitParts && p <= nk / floor_cps; ++p) {
+            const int64_t rounds = (tail * p + slots - 1) / slots;
+            const double cost = (double)(rounds * ((nk + p - 1) / p)) + (double)p * fixup;
+            if (cost < best) {
+                best = cost;
+                parts = p;
+            }
+        }
+        if (best > 0.875 * (double)nk) return t;
+    }
     const int64_t cps = (nk + parts - 1) / parts;
     parts = (nk + cps - 1) / cps;                     // every range non-empty
     if (parts < 2) return t;

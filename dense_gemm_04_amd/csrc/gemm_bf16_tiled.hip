@@ -524,10 +524,17 @@ constexpr int kTiledSlotsPerCu = 1;
 // 1.2x and 1.7x).
 constexpr int kTiledMinSlabs = 16;
 
+// A last round more than half full stays unsplit here (the fp32 kernel
+// splits it): cutting 3072^2 x 8192's 144 tiles into 5 K ranges each took it
+// from 168 to 231 us. Each range moves a 256 KB partial tile twice (370 MB for
+// that shape), and 144 busy CUs already run each tile faster than a full chip
+// does under the power limit.
+constexpr double kTiledFixupSlabs = -1.0;
+
 TailSplit plan_tiled(int64_t M, int64_t N, int64_t K, int cus) {
     const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
     return plan_tail_split(tiles, (K + kBK - 1) / kBK, (int64_t)cus * kTiledSlotsPerCu,
-                           kTiledMinSlabs);
+                           kTiledMinSlabs, kTiledFixupSlabs);
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool EPI>

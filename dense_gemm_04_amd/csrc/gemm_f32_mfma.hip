@@ -661,8 +661,17 @@ void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit
     }
 }
 
+// Reading one range's 64 KB partial tile back costs the last range about a
+// quarter of a slab's time (32 k of a 128 x 128 tile, two workgroups per CU).
+// Splitting a last round more than half full measured (same box, with and
+// without a workspace): 2304^2 x 2048 237 -> 204 us, 2048 x 2560 x 4096 467
+// -> 408, 1664 x 2560 x 8192 921 -> 646, 2300 x 2290 x 2050 (unaligned) 332
+// -> 227; 3072 x 2048 x 1024 in ranges of 8 slabs lost (123 -> 144), hence
+// ranges of at least 16 slabs there.
+constexpr double kF32FixupSlabs = 0.25;
+
 TailSplit plan_tail(int64_t tiles, int64_t nk, int cus) {
-    return plan_tail_split(tiles, nk, (int64_t)cus * kSlotsPerCu);
+    return plan_tail_split(tiles, nk, (int64_t)cus * kSlotsPerCu, 1, kF32FixupSlabs);
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool VEC, bool SPLIT, bool EPI>

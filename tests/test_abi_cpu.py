@@ -236,8 +236,9 @@ def test_tiled_workspace_size(lib):
     # 129 x 1000 x 8200: 4 tiles, 129 slabs -> 8 ranges of 17 (the last 10).
     assert dg.gemm_bf16_workspace_size(129, 1000, 8200) == 256 + 4 * 8 * tile
     # No split: a full round (4096^2 = 256 tiles), a last round more than half
-    # full (3000^2 = 144 tiles), fewer than 32 slabs.
+    # full (3072^2 = 144 tiles: splitting it measured slower), fewer than 32 slabs.
     assert dg.gemm_bf16_workspace_size(4096, 4096, 4096) == 0
+    assert dg.gemm_bf16_workspace_size(3072, 3072, 8192) == 0
     assert dg.gemm_bf16_workspace_size(3000, 3000, 3000) == 0
     assert dg.gemm_bf16_workspace_size(1024, 1024, 1024) == 0
     assert dg.gemm_bf16_workspace_size(300, 520, 1984) == 0
@@ -260,12 +261,20 @@ def test_f32_workspace_size(lib):
     # units, 2 workgroups each): 1024 in two full rounds, 32 left, cut into 8
     # K ranges (K = 1023 is 32 slabs of 32, 4 per range).
     assert dg.gemm_f32_workspace_size(4095, 4097, 1023) == 256 + 32 * 8 * 128 * 128 * 4
+    # A last round more than half full: 2304^2 has 18 x 18 = 324 tiles on 512
+    # slots; K = 2048 is 64 slabs, and 3 ranges give 2 rounds of 22 slabs +
+    # 3 x 0.25 = 44.75 against 64 unsplit.
+    assert dg.gemm_f32_workspace_size(2304, 2304, 2048) == 1536 + 324 * 3 * 128 * 128 * 4
     # 300 x 200: 6 tiles, K = 100 is 4 slabs: 4 ranges of one slab.
     assert dg.gemm_f32_workspace_size(300, 200, 100) == 256 + 6 * 4 * 128 * 128 * 4
-    # No split: whole rounds (4096^2 is 1024 tiles), a last round more than half
-    # full, K of one slab, empty or invalid sizes.
+    # 320 tiles (more than half of 512) of 128 slabs: p = 8 gives 5 rounds of
+    # 16 slabs + 8 x 0.25 = 82 against 128 unsplit.
+    assert dg.gemm_f32_workspace_size(128 * 16, 128 * 20, 4096) == 1280 + 320 * 8 * 128 * 128 * 4
+    # No split: whole rounds (4096^2 is 1024 tiles), a fuller last round whose
+    # ranges would be shorter than 16 slabs (3072 x 2048 x 1024: 384 tiles of
+    # 32 slabs), K of one slab, empty or invalid sizes.
     assert dg.gemm_f32_workspace_size(4096, 4096, 4096) == 0
-    assert dg.gemm_f32_workspace_size(128 * 16, 128 * 20, 4096) == 0     # 320 tiles > 256
+    assert dg.gemm_f32_workspace_size(3072, 2048, 1024) == 0
     assert dg.gemm_f32_workspace_size(300, 200, 32) == 0
     assert dg.gemm_f32_workspace_size(0, 200, 100) == 0
     assert dg.gemm_f32_workspace_size(-1, 200, 100) == 0

@@ -96,6 +96,7 @@ CASES = [
     ("f32", (300, 264, 100), (4, 4, 4), (1, 1), False, None),      # copy path, both, padded
     ("f32", (300, 200, 100), (0, 0, 0), (0, 0), True, None),       # copy path, split-K tail
     ("f32", (513, 384, 1000), (4, 8, 12), (0, 0), True, None),     # split-K tail, padded
+    ("f32", (2300, 2290, 2050), (0, 0, 0), (0, 0), True, None),    # fuller last round split: 3 ranges
     ("f32", (257, 130, 65), (1, 3, 5), (0, 0), False, None),       # register-staged (unaligned)
     ("f32", (300, 264, 100), (0, 0, 0), (0, 0), False, 3),         # vector-FMA kernel
 ]

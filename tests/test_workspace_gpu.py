@@ -167,7 +167,10 @@ def run_ws_f32(A, B, C0, alpha, beta, ws, nbytes, ld_pad=(0, 0, 0)):
 # one or several slabs, a single tile split in two.
 F32_SHAPES = [((300, 200, 100), (0, 0, 0)), ((1000, 1032, 136), (0, 0, 0)),
               ((257, 520, 129), (0, 0, 0)), ((130, 70, 64), (0, 0, 0)),
-              ((513, 384, 1000), (4, 8, 12)), ((300, 264, 257), (1, 3, 5))]
+              ((513, 384, 1000), (4, 8, 12)), ((300, 264, 257), (1, 3, 5)),
+              # a last round more than half full: 18 x 18 = 324 tiles on 512
+              # slots, every tile cut into 3 K ranges (two rounds of units)
+              ((2300, 2290, 2050), (0, 0, 0)), ((2300, 2290, 2050), (1, 3, 5))]
 
 
 @pytest.mark.parametrize("case", F32_SHAPES, ids=lambda c: "x".join(map(str, c[0])) + f"_pad{c[1][0]}")
