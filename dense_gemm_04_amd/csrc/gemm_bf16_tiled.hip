@@ -454,6 +454,24 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, Tail
                 cv[j][r] = col_factor(p, n0 + wn0 + 16 * j + 4 * g + r);
             }
     }
+    // With beta != 0 each lane loads all of its C values before its first
+    // store. The stores could alias later loads, so the compiler would
+    // otherwise wait out one memory round trip per 4 columns of a row. The
+    // fragment registers are dead here, which leaves room for the 64 values.
+    u32x2 cpre[kFM][kFN];
+    if (beta != 0.f) {
+#pragma unroll
+        for (int i = 0; i < kFM; ++i) {
+            const int64_t row = m0 + wm0 + 16 * i + pl;
+#pragma unroll
+            for (int j = 0; j < kFN; ++j) {
+                const int64_t col = n0 + wn0 + 16 * j + 4 * g;
+                cpre[i][j] = (row < M && col + 4 <= N)
+                                 ? *reinterpret_cast<const u32x2*>(p.C + row * p.ldc + col)
+                                 : u32x2{0u, 0u};
+            }
+        }
+    }
 #pragma unroll
     for (int i = 0; i < kFM; ++i) {
         const int64_t row = m0 + wm0 + 16 * i + pl;
@@ -473,7 +491,7 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, Tail
             if (col + 4 <= N) {
                 u32x2* dst = reinterpret_cast<u32x2*>(crow + col);
                 if (beta != 0.f) {
-                    const u32x2 c0 = *dst;
+                    const u32x2 c0 = cpre[i][j];
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
                         v[r] += beta * bf16_to_f32((uint16_t)(c0[r >> 1] >> (16 * (r & 1))));
