@@ -209,7 +209,7 @@ PROFILE_OF = {
 
 # The kernel each line runs.
 KERNEL_OF = {
-    "1": "gemm_f32_mfma (copy path, 128x128 tiles)",
+    "1": "gemm_f32_small (16x16 tiles, K over 8 waves)",
     "2": "gemm_f32_mfma (copy path, 128x128 tiles, tiles walked)",
     "3": "gemm_bf16_tiled (256x256 tiles)",
     "4": "gemm_bf16_tiled (256x256 tiles, beta = 1 residual)",

@@ -30,7 +30,8 @@ VARIANT_MFMA = 1
 VARIANT_GENERAL = 2
 VARIANT_VALU = 3
 VARIANT_SKINNY = 4
-VARIANT_NAMES = {0: "auto", 1: "mfma", 2: "general", 3: "valu", 4: "skinny"}
+VARIANT_SMALL = 5
+VARIANT_NAMES = {0: "auto", 1: "mfma", 2: "general", 3: "valu", 4: "skinny", 5: "small"}
 
 ACT_NONE = 0
 ACT_RELU = 1

@@ -80,10 +80,12 @@ bool small_m_ok(int64_t M, bool vec, bool tb) {
 // requested family cannot run it. The small-M kernel reads row-major A and
 // either a row-major B or, with 16-byte rows, a transposed one; other
 // transposed small-M calls go to the tiled kernels.
-int choose(int esz, int64_t M, bool vec, int variant, bool ta = false, bool tb = false) {
+int choose(int esz, int64_t M, int64_t N, int64_t K, bool vec, int variant, bool ta = false,
+           bool tb = false) {
     switch (variant) {
         case GEMM_VARIANT_AUTO:
             if (esz == 2 && !ta && small_m_ok(M, vec, tb)) return GEMM_VARIANT_SKINNY;
+            if (esz == 4 && dg::f32_small_preferred(M, N, K, false)) return GEMM_VARIANT_SMALL;
             return vec ? GEMM_VARIANT_MFMA : GEMM_VARIANT_GENERAL;
         case GEMM_VARIANT_MFMA:
             return vec ? GEMM_VARIANT_MFMA : -1;
@@ -93,6 +95,8 @@ int choose(int esz, int64_t M, bool vec, int variant, bool ta = false, bool tb =
             return esz == 4 ? GEMM_VARIANT_VALU : -1;
         case GEMM_VARIANT_SKINNY:
             return (esz == 2 && small_m_ok(M, vec, false)) ? GEMM_VARIANT_SKINNY : -1;
+        case GEMM_VARIANT_SMALL:
+            return esz == 4 ? GEMM_VARIANT_SMALL : -1;
         default:
             return -1;
     }
@@ -102,10 +106,10 @@ int plan_impl(int esz, int64_t M, int64_t N, int64_t K, float alpha, const void*
               int64_t lda, const void* B, int64_t ldb, float beta, const void* C,
               int64_t ldc, int variant, bool ta = false, bool tb = false) {
     if (esz != 2 && esz != 4) return -1;
-    if (variant < GEMM_VARIANT_AUTO || variant > GEMM_VARIANT_SKINNY) return -1;
+    if (variant < GEMM_VARIANT_AUTO || variant > GEMM_VARIANT_SMALL) return -1;
     if (!valid_args(esz, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, ta, tb)) return -1;
     if (work_of(M, N, K, alpha, beta) != Work::kGemm) return GEMM_VARIANT_AUTO;
-    return choose(esz, M, vector_ok(esz, A, lda, B, ldb, C, ldc), variant, ta, tb);
+    return choose(esz, M, N, K, vector_ok(esz, A, lda, B, ldb, C, ldc), variant, ta, tb);
 }
 
 // Per-device cache of "is this a gfx950" (0 unknown, 1 yes, 2 no) and of its
@@ -157,8 +161,18 @@ gemm_status_t run(int64_t M, int64_t N, int64_t K, float alpha, const T* A, int6
                   bool tb = false, const float* row_scale = nullptr,
                   const float* col_scale = nullptr) {
     constexpr int esz = (int)sizeof(T);
-    const int v = plan_impl(esz, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, variant, ta, tb);
+    int v = plan_impl(esz, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, variant, ta, tb);
     if (v < 0) return GEMM_ERR_INVALID_VALUE;
+    // An fp32 call whose split-K workspace the tiled kernel asks for (the
+    // workspace size query names it) runs the tiled kernel on it.
+    if constexpr (esz == 4) {
+        if (v == GEMM_VARIANT_SMALL && variant == GEMM_VARIANT_AUTO && ws != nullptr &&
+            !dg::f32_small_preferred(M, N, K, true)) {
+            const size_t need = dg::f32_mfma_workspace(M, N, K, kFullCus);
+            if (need > 0 && ws_bytes >= need)
+                v = vector_ok(esz, A, lda, B, ldb, C, ldc) ? GEMM_VARIANT_MFMA : GEMM_VARIANT_GENERAL;
+        }
+    }
     if (!valid_epilogue(esz, bias, act)) return GEMM_ERR_INVALID_VALUE;
     if (!aligned(row_scale, 4) || !aligned(col_scale, 4)) return GEMM_ERR_INVALID_VALUE;
     const Work w = work_of(M, N, K, alpha, beta, bias);
@@ -177,9 +191,9 @@ gemm_status_t run(int64_t M, int64_t N, int64_t K, float alpha, const T* A, int6
                           row_scale, col_scale};
         const bool vec = vector_ok(esz, A, lda, B, ldb, C, ldc);
         if constexpr (esz == 4) {
-            e = (v == GEMM_VARIANT_VALU) ? dg::launch_f32_valu(a, vec, s)
-                                         : dg::launch_f32_mfma(a, v == GEMM_VARIANT_MFMA, ws, ws_bytes,
-                                                               cus, s);
+            if (v == GEMM_VARIANT_VALU) e = dg::launch_f32_valu(a, vec, s);
+            else if (v == GEMM_VARIANT_SMALL) e = dg::launch_f32_small(a, s);
+            else e = dg::launch_f32_mfma(a, v == GEMM_VARIANT_MFMA, ws, ws_bytes, cus, s);
         } else {
             e = (v == GEMM_VARIANT_SKINNY)
                     ? dg::launch_bf16_skinny(a, vec, ws, ws_bytes, cus, s)
@@ -291,6 +305,8 @@ gemm_status_t gemm_bf16_ws(int64_t M, int64_t N, int64_t K, float alpha, const u
 
 size_t gemm_f32_workspace_size(int64_t M, int64_t N, int64_t K) {
     if (M < 0 || N < 0 || K < 0 || M > INT_MAX || N > INT_MAX || K > INT_MAX) return 0;
+    // Shapes that the few-tile kernel takes even with a workspace need none.
+    if (dg::f32_small_preferred(M, N, K, true)) return 0;
     return dg::f32_mfma_workspace(M, N, K, kFullCus);
 }
 

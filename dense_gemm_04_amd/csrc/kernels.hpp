@@ -36,6 +36,18 @@ hipError_t launch_f32_mfma(const GemmArgs<float>& a, bool vec, void* ws, size_t 
                            hipStream_t s);
 size_t f32_mfma_workspace(int64_t M, int64_t N, int64_t K, int cus);
 hipError_t launch_f32_valu(const GemmArgs<float>& a, bool vec, hipStream_t s);
+// fp32 products with few output tiles: T x T tiles with K split over the
+// waves of each workgroup (any layout, rows aligned to 4 bytes).
+struct SmallPlan {
+    int tile;    // 16, 32 or 64
+    int waves;   // waves per workgroup, each one K range: 4, 8 or 16
+};
+// The tile size and wave count this kernel uses for a shape.
+SmallPlan plan_f32_small(int64_t M, int64_t N, int64_t K);
+// Whether the automatic choice runs this kernel rather than the tiled one;
+// `split_ws`: the caller gave the tiled kernel's split-K workspace.
+bool f32_small_preferred(int64_t M, int64_t N, int64_t K, bool split_ws);
+hipError_t launch_f32_small(const GemmArgs<float>& a, hipStream_t s);
 // Small-M bf16 (M <= kSkinnyMaxM; without `vec`, M <= kSkinnyElemMaxM). With
 // `vec` the 64-column copy-ring kernel runs; given a workspace of at least bf16_skinny_workspace(M, N, K) bytes
 // (256-byte aligned, counters zero) it splits K over several workgroups.

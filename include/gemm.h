@@ -92,7 +92,15 @@ typedef enum {
     /* bf16 only, M <= 128 with 16-byte rows (M <= 32 otherwise): small-M
      * kernel that streams B once (Blackwell BF16 GEMM notes, section 5.2:
      * small-batch GEMMs are bandwidth bound). */
-    GEMM_VARIANT_SKINNY = 4
+    GEMM_VARIANT_SKINNY = 4,
+    /* fp32 only, any shape and alignment: few-tile kernel. Each workgroup owns
+     * a 16 x 16, 32 x 32 or 64 x 64 tile of C and its waves split K between
+     * them, adding their partial tiles in a fixed order (RTX 3090 SGEMM
+     * article, section 3: K is walked in slices; here the slices run on
+     * different waves). AUTO picks it when the 128 x 128 tiles of
+     * GEMM_VARIANT_MFMA would leave most compute units idle: up to about 150
+     * such tiles (fp32 256^3 has 4), fewer with a split-K workspace and long K. */
+    GEMM_VARIANT_SMALL = 5
 } gemm_variant_t;
 
 /* fp32 GEMM. A: M x K (lda >= max(1,K)), B: K x N (ldb >= max(1,N)),
@@ -181,12 +189,16 @@ gemm_status_t gemm_bf16_ws_noalloc(int64_t M, int64_t N, int64_t K, float alpha,
  * splitting K to bring more multiprocessors to work). Each range's fp32
  * partial tile goes to the workspace and the last range to finish adds them
  * in a fixed order before the alpha/beta epilogue. Full tiles are computed as
- * in gemm_f32.
+ * in gemm_f32. A fuller last round is split too when a model of its length
+ * says the split ranges finish sooner. Products with few tiles run on the
+ * few-tile kernel (GEMM_VARIANT_SMALL), which splits K inside each workgroup
+ * and needs no workspace, unless they hold at least 2^18 tile-k (128 x 128
+ * tiles times K), where splitting over workgroups wins.
  *
  * gemm_f32_workspace_size: workspace bytes gemm_f32_ws needs for this shape
  * on a full MI355X (256 compute units); 0 when it would not split (no last
- * round, or one more than half full, or K below two 32-deep slabs) or the
- * sizes are invalid. Host only, no HIP call. On a device with fewer compute
+ * round, or one the model leaves whole, or K below two 32-deep slabs), when
+ * the few-tile kernel takes the shape, or when the sizes are invalid. Host only, no HIP call. On a device with fewer compute
  * units the split is planned for that device and uses the workspace only if
  * it is large enough.
  *

@@ -105,7 +105,19 @@ def test_plan_quick_paths(lib):
 
 
 def test_plan_chooses_family(lib):
-    assert plan() == dg.VARIANT_MFMA
+    big = dict(M=4096, N=4096, K=4096)
+    assert plan(**big) == dg.VARIANT_MFMA
+    # fp32 with few 128 x 128 tiles: the few-tile kernel, whatever the alignment.
+    assert plan() == dg.VARIANT_SMALL                          # 64^3
+    assert plan(M=256, N=256, K=256) == dg.VARIANT_SMALL
+    assert plan(M=1536, N=1536, K=1024) == dg.VARIANT_SMALL    # 144 tiles: 32 x 32 tiles win
+    assert plan(M=1792, N=1792, K=1024) == dg.VARIANT_MFMA     # 196 tiles: one tiled round wins
+    assert plan(M=2048, N=2048, K=2048) == dg.VARIANT_MFMA
+    assert plan(a=A + 4) == dg.VARIANT_SMALL
+    assert plan(lda=66) == dg.VARIANT_SMALL
+    assert plan(variant=dg.VARIANT_SMALL, **big) == dg.VARIANT_SMALL
+    assert plan(esz=2, variant=dg.VARIANT_SMALL) == -1
+    assert plan(variant=dg.VARIANT_MFMA) == dg.VARIANT_MFMA
     assert plan(esz=2, M=16) == dg.VARIANT_SKINNY             # bf16, M <= 128 (16-byte rows)
     assert plan(esz=2, M=32) == dg.VARIANT_SKINNY
     assert plan(esz=2, M=33) == dg.VARIANT_SKINNY
@@ -114,9 +126,9 @@ def test_plan_chooses_family(lib):
     assert plan(esz=2, M=32, lda=66) == dg.VARIANT_SKINNY      # unaligned: element-wise, M <= 32
     assert plan(esz=2, M=33, lda=66) == dg.VARIANT_GENERAL
     assert plan(M=4095, N=4097, K=1023) == dg.VARIANT_GENERAL  # ld not a multiple of 4 floats
-    assert plan(a=A + 4) == dg.VARIANT_GENERAL                 # base not 16-byte aligned
-    assert plan(lda=68) == dg.VARIANT_MFMA
-    assert plan(lda=66) == dg.VARIANT_GENERAL
+    assert plan(a=A + 4, **big) == dg.VARIANT_GENERAL          # base not 16-byte aligned
+    assert plan(M=4096, N=4096, K=64, lda=68) == dg.VARIANT_MFMA
+    assert plan(M=4096, N=4096, K=64, lda=66) == dg.VARIANT_GENERAL
     assert plan(variant=dg.VARIANT_VALU) == dg.VARIANT_VALU
     assert plan(esz=2, variant=dg.VARIANT_VALU) == -1
     assert plan(M=16, variant=dg.VARIANT_SKINNY) == -1
@@ -265,8 +277,14 @@ def test_f32_workspace_size(lib):
     # slots; K = 2048 is 64 slabs, and 3 ranges give 2 rounds of 22 slabs +
     # 3 x 0.25 = 44.75 against 64 unsplit.
     assert dg.gemm_f32_workspace_size(2304, 2304, 2048) == 1536 + 324 * 3 * 128 * 128 * 4
-    # 300 x 200: 6 tiles, K = 100 is 4 slabs: 4 ranges of one slab.
-    assert dg.gemm_f32_workspace_size(300, 200, 100) == 256 + 6 * 4 * 128 * 128 * 4
+    # Few tiles with long K: 1024^2 is 64 tiles (64 x 4096 = 2^18 tile-k), cut
+    # into 8 ranges of 16 slabs.
+    assert dg.gemm_f32_workspace_size(1024, 1024, 4096) == 256 + 64 * 8 * 128 * 128 * 4
+    # Few tiles with fewer tile-k go to the few-tile kernel, which needs no
+    # workspace: 300 x 200 (6 tiles), 1024^3 (64 tiles x 1024), 256^3.
+    assert dg.gemm_f32_workspace_size(300, 200, 100) == 0
+    assert dg.gemm_f32_workspace_size(1024, 1024, 1024) == 0
+    assert dg.gemm_f32_workspace_size(256, 256, 256) == 0
     # 320 tiles (more than half of 512) of 128 slabs: p = 8 gives 5 rounds of
     # 16 slabs + 8 x 0.25 = 82 against 128 unsplit.
     assert dg.gemm_f32_workspace_size(128 * 16, 128 * 20, 4096) == 1280 + 320 * 8 * 128 * 128 * 4
@@ -281,8 +299,9 @@ def test_f32_workspace_size(lib):
 
 
 def test_f32_workspace_validation(lib):
-    args = (300, 200, 100, 1.0, A, 100, B, 200, 0.0, C, 200)
-    need = dg.gemm_f32_workspace_size(300, 200, 100)
+    args = (1024, 1024, 4096, 1.0, A, 4096, B, 1024, 0.0, C, 1024)
+    need = dg.gemm_f32_workspace_size(1024, 1024, 4096)
+    assert need > 0
     ws = 0x400000
     assert dg.gemm_f32_ws(*args, None, 64, 0) == dg.GEMM_ERR_INVALID_VALUE
     assert dg.gemm_f32_ws(*args, ws + 64, need, 0) == dg.GEMM_ERR_INVALID_VALUE
@@ -299,8 +318,10 @@ def test_bias_act_validation(lib):
     assert dg.gemm_f32_bias_act(*f32, bias, -1, None, 0, 0) == bad
     assert dg.gemm_f32_bias_act(*f32, bias + 2, dg.ACT_RELU, None, 0, 0) == bad
     assert dg.gemm_bf16_bias_act(*bf, bias + 1, dg.ACT_RELU, None, 0, 0) == bad
-    need = dg.gemm_f32_workspace_size(300, 200, 100)
-    assert dg.gemm_f32_bias_act(*f32, bias, dg.ACT_RELU, 0x400000, need - 1, 0) == bad
+    big = (1024, 1024, 4096, 1.0, A, 4096, B, 1024, 0.0, C, 1024)
+    need = dg.gemm_f32_workspace_size(1024, 1024, 4096)
+    assert need > 0
+    assert dg.gemm_f32_bias_act(*big, bias, dg.ACT_RELU, 0x400000, need - 1, 0) == bad
     assert dg.gemm_f32_bias_act(*f32, bias, dg.ACT_RELU, None, 64, 0) == bad
     # Product-free calls: with no bias and beta == 1 nothing runs; a bias needs C.
     assert dg.gemm_f32_bias_act(4, 4, 0, 1.0, None, 4, None, 4, 1.0, None, 4, None,

@@ -80,10 +80,11 @@ CASES = [
     ("bf16", (16, 4352, 1000), (0, 0, 0), True),     # small-M streaming split (K interleaved)
     ("bf16", (33, 4104, 300), (8, 8, 8), True),      # the same, two row blocks, padded rows
     ("bf16", (5, 100, 77), (1, 1, 1), False),        # small-M element-wise kernel
-    ("f32", (300, 264, 100), (0, 0, 0), False),      # fp32 MFMA, aligned
-    ("f32", (257, 130, 65), (1, 3, 5), False),       # fp32 MFMA, unaligned rows
-    ("f32", (300, 200, 100), (0, 0, 0), True),       # fp32 split-K tail
-    ("f32", (513, 384, 1000), (4, 8, 12), True),     # fp32 split-K tail, padded rows
+    ("f32", (2100, 2000, 100), (0, 0, 0), False),    # fp32 tiled MFMA, aligned
+    ("f32", (2100, 2000, 65), (1, 3, 5), False),     # fp32 tiled MFMA, unaligned rows
+    ("f32", (600, 4100, 300), (4, 8, 12), True),     # fp32 split-K tail, padded rows
+    ("f32", (300, 264, 100), (0, 0, 0), False),      # fp32 few-tile kernel
+    ("f32", (257, 130, 65), (1, 3, 5), False),       # fp32 few-tile kernel, unaligned rows
 ]
 
 
@@ -131,7 +132,9 @@ def test_product_free_epilogue(dtype, act):
                                   ("bf16", (16, 520, 300), (0, 0, 0)),
                                   ("bf16", (5, 100, 77), (1, 1, 1)),
                                   ("f32", (300, 264, 100), (0, 0, 0)),
-                                  ("f32", (257, 130, 65), (1, 3, 5))],
+                                  ("f32", (257, 130, 65), (1, 3, 5)),
+                                  ("f32", (2100, 2000, 100), (0, 0, 0)),
+                                  ("f32", (2100, 2000, 65), (1, 3, 5))],
                          ids=lambda c: f"{c[0]}_{'x'.join(map(str, c[1]))}_pad{c[2][0]}")
 def test_identity_epilogue_is_bit_identical_to_plain(case):
     dtype, (M, N, K), pad = case

@@ -1,5 +1,6 @@
-"""GPU parity of the fp32 kernel's global -> LDS copy path (row-major A and B
-with 16-byte rows) at its edges, against the oracle:
+"""GPU parity of the fp32 kernels at their edges, against the oracle: the
+tiled kernel's global -> LDS copy path (row-major A and B with 16-byte rows)
+and, at the shapes it takes, the few-tile kernel:
 
 * ragged M, N and K, with every padding element of A and B set to NaN, so a
   copy that let a padding element into the product (a row past M, a column of
@@ -26,7 +27,10 @@ from test_transpose_gpu import check as check_op
 pytestmark = pytest.mark.gpu
 
 
-def run_nan_padded(A, B, lda, ldb, ldc, alpha=1.0, beta=0.0, C0=None, ws=False):
+def run_nan_padded(A, B, lda, ldb, ldc, alpha=1.0, beta=0.0, C0=None, ws=False,
+                   variant=dg.VARIANT_MFMA):
+    """One call on NaN-padded operands: gemm_f32_ws with a workspace, else
+    gemm_f32_ex with `variant` (the tiled kernel by default)."""
     M, K = A.shape
     N = B.shape[1]
     _, a = padded(M, K, lda, "f32", fill=float("nan"))
@@ -42,8 +46,8 @@ def run_nan_padded(A, B, lda, ldb, ldc, alpha=1.0, beta=0.0, C0=None, ws=False):
         st = dg.gemm_f32_ws(M, N, K, alpha, a.data_ptr(), lda, b.data_ptr(), ldb, beta,
                             c.data_ptr(), ldc, wbuf.data_ptr() if nbytes else None, nbytes, 0)
     else:
-        st = dg.gemm_f32(M, N, K, alpha, a.data_ptr(), lda, b.data_ptr(), ldb, beta,
-                         c.data_ptr(), ldc, 0)
+        st = dg.gemm_f32_ex(M, N, K, alpha, a.data_ptr(), lda, b.data_ptr(), ldb, beta,
+                            c.data_ptr(), ldc, 0, variant)
     torch.cuda.synchronize()
     return c.cpu(), st, nbytes
 
@@ -62,21 +66,32 @@ SHAPES = [(1, 4, 1), (5, 12, 31), (128, 128, 32), (129, 130, 33), (200, 260, 63)
           (300, 136, 100), (77, 300, 257), (256, 384, 1000)]
 
 
+# The tiled kernel (forced: the copy path, and the register-staged path that
+# element-aligned C rows take) and the few-tile kernel that gemm_f32 runs at
+# these shapes.
+KERNELS = [dg.VARIANT_MFMA, dg.VARIANT_GENERAL, dg.VARIANT_SMALL]
+
+
+@pytest.mark.parametrize("variant", KERNELS, ids=lambda v: dg.VARIANT_NAMES[v])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_nan_padding_never_reaches_c(shape):
+def test_nan_padding_never_reaches_c(shape, variant):
     M, N, K = shape
     A = gi.random_matrix(M, K, "f32", 5100 + M)
     B = gi.random_matrix(K, N, "f32", 5200 + N)
-    # 16-byte rows with at least one padding chunk after each row.
-    lda, ldb, ldc = (K + 3) // 4 * 4 + 4, (N + 3) // 4 * 4 + 8, N + 3
-    note(f"f32 copy path NaN padding M={M} N={N} K={K} lda={lda} ldb={ldb}")
-    C, st, _ = run_nan_padded(A, B, lda, ldb, ldc)
+    # 16-byte rows of A and B with at least one padding chunk after each row;
+    # C rows 16-byte aligned for the copy path, 4-byte aligned otherwise.
+    lda, ldb = (K + 3) // 4 * 4 + 4, (N + 3) // 4 * 4 + 8
+    ldc = (N + 3) // 4 * 4 + 4 if variant == dg.VARIANT_MFMA else N + 3
+    note(f"f32 NaN padding variant={variant} M={M} N={N} K={K} lda={lda} ldb={ldb}")
+    C, st, _ = run_nan_padded(A, B, lda, ldb, ldc, variant=variant)
     assert st == dg.GEMM_OK
     assert torch.isfinite(C).all()
     check(A, B, C)
 
 
-@pytest.mark.parametrize("shape", [(300, 200, 1000), (257, 264, 4100), (1100, 1030, 2100)],
+# Few tiles with enough tile-k that gemm_f32_ws splits them over workgroups:
+# 81 tiles in 6 K ranges, 154 tiles in 3.
+@pytest.mark.parametrize("shape", [(1100, 1030, 4100), (1700, 1300, 2100)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_split_k_with_ragged_tail_and_nan_padding(shape):
     M, N, K = shape
@@ -86,20 +101,23 @@ def test_split_k_with_ragged_tail_and_nan_padding(shape):
     lda, ldb, ldc = (K + 3) // 4 * 4 + 4, (N + 3) // 4 * 4 + 4, N
     note(f"f32 copy path split K M={M} N={N} K={K}")
     C, st, nbytes = run_nan_padded(A, B, lda, ldb, ldc, alpha=0.5, beta=-1.5, C0=C0, ws=True)
+    assert nbytes > 0
     assert st == dg.GEMM_OK
     check(A, B, C, 0.5, -1.5, C0)
 
 
+@pytest.mark.parametrize("variant", [dg.VARIANT_MFMA, dg.VARIANT_SMALL],
+                         ids=lambda v: dg.VARIANT_NAMES[v])
 @pytest.mark.parametrize("lda", [4_000_000, 4_200_000])
-def test_leading_dimension_at_the_copy_offset_limit(lda):
+def test_leading_dimension_at_the_copy_offset_limit(lda, variant):
     """128 rows of A span (128 * lda + 32) * 4 bytes: inside 2^31 at 4.0 M
     (copy path), past it at 4.2 M (register-staged path). Only 3 rows exist,
     so the copies of rows 8 .. 127 fall past the descriptor and read nothing."""
     M, N, K = 3, 40, 50
     A = gi.random_matrix(M, K, "f32", 5600)
     B = gi.random_matrix(K, N, "f32", 5601)
-    note(f"f32 copy path lda={lda}")
-    C, st, _ = run_nan_padded(A, B, lda, N + 4, N)
+    note(f"f32 lda={lda} variant={variant}")
+    C, st, _ = run_nan_padded(A, B, lda, N + 4, N, variant=variant)
     assert st == dg.GEMM_OK
     check(A, B, C)
 
@@ -131,7 +149,10 @@ def run_op_nan_padded(opa, opb, A, B, alpha, beta, C0, ws, pad):
 
 
 @pytest.mark.parametrize("ops", [(0, 1), (1, 0), (1, 1)], ids=["ABt", "AtB", "AtBt"])
-@pytest.mark.parametrize("shape", SHAPES + [(1100, 1030, 2100)], ids=lambda s: "x".join(map(str, s)))
+# SHAPES run on the few-tile kernel; 2100 x 2000 (272 tiles) on the tiled
+# one, and 1100 x 1030 x 4100 on the tiled one split over a workspace.
+@pytest.mark.parametrize("shape", SHAPES + [(1100, 1030, 2100), (2100, 2000, 100), (1100, 1030, 4100)],
+                         ids=lambda s: "x".join(map(str, s)))
 def test_transposed_nan_padding_never_reaches_c(shape, ops):
     M, N, K = shape
     A = gi.random_matrix(M, K, "f32", 5700 + M)

@@ -91,13 +91,13 @@ CASES = [
     ("bf16", (5, 100, 77), (1, 1, 1), (0, 0), False, None),        # small-M element-wise
     ("bf16", (130, 200, 129), (1, 3, 5), (0, 0), False, None),     # unaligned rows
     ("f32", (3000, 2900, 72), (0, 0, 0), (0, 0), False, None),     # copy path, 552 tiles walked
-    ("f32", (300, 264, 100), (0, 0, 0), (1, 0), False, None),      # copy path, A stored K x M
-    ("f32", (300, 264, 100), (0, 0, 0), (0, 1), False, None),      # copy path, B stored N x K
-    ("f32", (300, 264, 100), (4, 4, 4), (1, 1), False, None),      # copy path, both, padded
-    ("f32", (300, 200, 100), (0, 0, 0), (0, 0), True, None),       # copy path, split-K tail
-    ("f32", (513, 384, 1000), (4, 8, 12), (0, 0), True, None),     # split-K tail, padded
+    ("f32", (2100, 2000, 100), (0, 0, 0), (1, 0), False, None),    # copy path, A stored K x M
+    ("f32", (2100, 2000, 100), (0, 0, 0), (0, 1), False, None),    # copy path, B stored N x K
+    ("f32", (2100, 2000, 100), (4, 4, 4), (1, 1), False, None),    # copy path, both, padded
+    ("f32", (1100, 1030, 4100), (0, 0, 0), (0, 0), True, None),    # copy path, few tiles split
+    ("f32", (600, 4100, 300), (4, 8, 12), (0, 0), True, None),     # split-K tail, padded
     ("f32", (2300, 2290, 2050), (0, 0, 0), (0, 0), True, None),    # fuller last round split: 3 ranges
-    ("f32", (257, 130, 65), (1, 3, 5), (0, 0), False, None),       # register-staged (unaligned)
+    ("f32", (2100, 2000, 65), (1, 3, 5), (0, 0), False, None),     # register-staged (unaligned)
     ("f32", (300, 264, 100), (0, 0, 0), (0, 0), False, 3),         # vector-FMA kernel
 ]
 

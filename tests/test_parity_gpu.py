@@ -15,7 +15,8 @@ from gpu_util import note, oracle_ref, run, to_f64, tol
 
 pytestmark = pytest.mark.gpu
 
-F32_VARIANTS = [dg.VARIANT_AUTO, dg.VARIANT_MFMA, dg.VARIANT_GENERAL, dg.VARIANT_VALU]
+F32_VARIANTS = [dg.VARIANT_AUTO, dg.VARIANT_MFMA, dg.VARIANT_GENERAL, dg.VARIANT_VALU,
+                dg.VARIANT_SMALL]
 BF16_VARIANTS = [dg.VARIANT_AUTO, dg.VARIANT_MFMA, dg.VARIANT_GENERAL]
 
 # Shapes that span several tiles in each direction and end in ragged tails
@@ -125,9 +126,11 @@ def test_unaligned_base_pointers(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("variant", [0, 2])
+@pytest.mark.parametrize("variant", [0, 2, 5])
 def test_guard_bands_untouched(dtype, variant):
     """Nothing outside the M x N window of C is written (ldc > N, extra rows)."""
+    if variant == dg.VARIANT_SMALL and dtype != "f32":
+        pytest.skip("variant does not apply")
     M, N, K = 129, 250, 70
     A = gi.random_matrix(M, K, dtype, 900)
     B = gi.random_matrix(K, N, dtype, 901)
@@ -147,9 +150,9 @@ def test_guard_bands_untouched(dtype, variant):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4, 5])
 def test_beta_zero_ignores_nan_in_c(dtype, variant):
-    if (variant == dg.VARIANT_VALU and dtype != "f32") or \
+    if (variant in (dg.VARIANT_VALU, dg.VARIANT_SMALL) and dtype != "f32") or \
        (variant == dg.VARIANT_SKINNY and dtype != "bf16"):
         pytest.skip("variant does not apply")
     M = 16 if variant == dg.VARIANT_SKINNY else 130
@@ -178,9 +181,9 @@ def test_k_zero_and_alpha_zero_scale_c(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("variant", [0, 2, 3, 4])
+@pytest.mark.parametrize("variant", [0, 2, 3, 4, 5])
 def test_identity_gives_b_bitwise(dtype, variant):
-    if (variant == dg.VARIANT_VALU and dtype != "f32") or \
+    if (variant in (dg.VARIANT_VALU, dg.VARIANT_SMALL) and dtype != "f32") or \
        (variant == dg.VARIANT_SKINNY and dtype != "bf16"):
         pytest.skip("variant does not apply")
     K = 32 if variant == dg.VARIANT_SKINNY else 300
@@ -194,10 +197,10 @@ def test_identity_gives_b_bitwise(dtype, variant):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("variant", [0, 2, 3, 4])
+@pytest.mark.parametrize("variant", [0, 2, 3, 4, 5])
 def test_all_ones_exact(dtype, variant):
     """A = B = 1: every entry is K*alpha + beta*c0 exactly (c0 on a quarter grid)."""
-    if (variant == dg.VARIANT_VALU and dtype != "f32") or \
+    if (variant in (dg.VARIANT_VALU, dg.VARIANT_SMALL) and dtype != "f32") or \
        (variant == dg.VARIANT_SKINNY and dtype != "bf16"):
         pytest.skip("variant does not apply")
     M = 20 if variant == dg.VARIANT_SKINNY else 260
@@ -216,11 +219,11 @@ def test_all_ones_exact(dtype, variant):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("variant", [0, 2, 3, 4])
+@pytest.mark.parametrize("variant", [0, 2, 3, 4, 5])
 def test_small_integers_exact(dtype, variant):
     """Integer entries in [-4, 4]: fp32 accumulation is exact in any order, so
     fp32 output equals the oracle and bf16 output equals its rounding."""
-    if (variant == dg.VARIANT_VALU and dtype != "f32") or \
+    if (variant in (dg.VARIANT_VALU, dg.VARIANT_SMALL) and dtype != "f32") or \
        (variant == dg.VARIANT_SKINNY and dtype != "bf16"):
         pytest.skip("variant does not apply")
     M = 31 if variant == dg.VARIANT_SKINNY else 333

@@ -5,8 +5,8 @@ gemm_bf16_scaled) against the oracle's scaled form,
 
 through every kernel family the plain calls use (bf16 tiled, unaligned,
 small-M vector, 64-column and streaming split-K, element-wise small M, the
-tiled split for M > 128, fp32 aligned, unaligned and split-K tail, and
-transposed operands). Two bit-identity checks pin the placement of the
+tiled split for M > 128, fp32 tiled aligned, unaligned and split-K tail, the
+fp32 few-tile kernel, and transposed operands). Two bit-identity checks pin the placement of the
 factors: all-ones scales give exactly the unscaled epilogue, and power-of-two
 scales give exactly the plain product of pre-scaled operands (scaling by a
 power of two commutes with every rounding)."""
@@ -103,12 +103,15 @@ CASES = [
     ("bf16", (300, 264, 200), (0, 0, 0), (1, 0), False),     # tiled, A stored K x M
     ("bf16", (200, 136, 264), (0, 0, 0), (1, 1), False),     # tiled, both transposed
     ("bf16", (16, 520, 300), (0, 0, 0), (0, 1), True),       # small M, B stored N x K, split
-    ("f32", (300, 264, 100), (0, 0, 0), (0, 0), False),      # fp32 copy path
-    ("f32", (257, 130, 65), (1, 3, 5), (0, 0), False),       # fp32 unaligned rows
-    ("f32", (300, 200, 100), (0, 0, 0), (0, 0), True),       # fp32 split-K tail
-    ("f32", (513, 384, 1000), (4, 8, 12), (0, 0), True),     # fp32 split-K tail, padded
-    ("f32", (200, 136, 264), (0, 0, 0), (0, 1), False),      # fp32, B stored N x K
-    ("f32", (136, 200, 264), (0, 0, 0), (1, 0), False),      # fp32, A stored K x M
+    ("f32", (2100, 2000, 100), (0, 0, 0), (0, 0), False),    # fp32 tiled copy path
+    ("f32", (2100, 2000, 65), (1, 3, 5), (0, 0), False),     # fp32 tiled, unaligned rows
+    ("f32", (600, 4100, 300), (4, 8, 12), (0, 0), True),     # fp32 tiled split-K tail, padded
+    ("f32", (2100, 2000, 100), (0, 0, 0), (1, 1), False),    # fp32 tiled, both transposed
+    ("f32", (300, 264, 100), (0, 0, 0), (0, 0), False),      # fp32 few-tile kernel
+    ("f32", (257, 130, 65), (1, 3, 5), (0, 0), False),       # few-tile, unaligned rows
+    ("f32", (513, 384, 1000), (4, 8, 12), (0, 0), True),     # few-tile (needs no workspace)
+    ("f32", (200, 136, 264), (0, 0, 0), (0, 1), False),      # few-tile, B stored N x K
+    ("f32", (136, 200, 264), (0, 0, 0), (1, 0), False),      # few-tile, A stored K x M
 ]
 
 

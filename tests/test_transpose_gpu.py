@@ -111,9 +111,11 @@ def test_op_with_epilogue(dtype, ops):
 
 @pytest.mark.parametrize("ops", OPS[1:], ids=lambda o: OP_ID[o[0]] + OP_ID[o[1]])
 def test_f32_op_split_k(ops):
-    nbytes = check("f32", ops[0], ops[1], 300, 200, 100, 4500, 0.5, 2.0, ws=True)
+    # 165 tiles in 3 K ranges; 256 unaligned tiles in 2.
+    nbytes = check("f32", ops[0], ops[1], 600, 4100, 300, 4500, 0.5, 2.0, ws=True)
     assert nbytes > 0
-    check("f32", ops[0], ops[1], 300, 264, 257, 4510, 1.0, 0.0, (1, 3, 5), ws=True)
+    nbytes = check("f32", ops[0], ops[1], 4095, 1000, 1000, 4510, 1.0, 0.0, (1, 3, 5), ws=True)
+    assert nbytes > 0
 
 
 @pytest.mark.parametrize("ops", OPS, ids=lambda o: OP_ID[o[0]] + OP_ID[o[1]])

@@ -164,10 +164,12 @@ def run_ws_f32(A, B, C0, alpha, beta, ws, nbytes, ld_pad=(0, 0, 0)):
 
 
 # Aligned (vector) and unaligned (element-wise) rows, ragged tiles, K ranges of
-# one or several slabs, a single tile split in two.
-F32_SHAPES = [((300, 200, 100), (0, 0, 0)), ((1000, 1032, 136), (0, 0, 0)),
-              ((257, 520, 129), (0, 0, 0)), ((130, 70, 64), (0, 0, 0)),
-              ((513, 384, 1000), (4, 8, 12)), ((300, 264, 257), (1, 3, 5)),
+# one or several slabs. Shapes with few tiles split only with at least 2^18
+# tile-k (fewer go to the few-tile kernel, which needs no workspace).
+F32_SHAPES = [((1100, 1030, 4100), (0, 0, 0)),     # 81 tiles, 6 ranges of 22 slabs
+              ((1700, 1300, 2100), (4, 8, 12)),    # 154 tiles, 3 ranges
+              ((600, 4100, 300), (0, 0, 0)),       # 165 tiles, 3 ranges of 3-4 slabs
+              ((4095, 1000, 1000), (1, 3, 5)),     # 256 tiles, unaligned, 2 ranges
               # a last round more than half full: 18 x 18 = 324 tiles on 512
               # slots, every tile cut into 3 K ranges (two rounds of units)
               ((2300, 2290, 2050), (0, 0, 0)), ((2300, 2290, 2050), (1, 3, 5))]
@@ -195,8 +197,9 @@ def test_f32_split_k_parity(case):
 
 
 def test_f32_split_k_deterministic():
-    M, N, K = 1000, 1032, 136
+    M, N, K = 600, 4100, 300
     nbytes = dg.gemm_f32_workspace_size(M, N, K)
+    assert nbytes > 0
     ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     A = gi.random_matrix(M, K, "f32", 1790)
     B = gi.random_matrix(K, N, "f32", 1791)
