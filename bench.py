@@ -20,7 +20,11 @@ Also reported:
                 the 256 MB Infinity Cache). Each carries its fraction of the
                 bounding roofline, its HBM traffic ratio when a current
                 counter summary exists, and its own oracle timing (config 1
-                also on one thread).
+                also on one thread). The 256^3 line, whose kernel takes less
+                time than a caller needs to issue a call, also carries
+                `graph`: 200 of the same calls captured in one HIP graph and
+                replayed, each replay checked bit for bit against the eager
+                result.
 
 ``--all`` prints one JSON line per workload instead (for the design notes).
 """
@@ -100,15 +104,23 @@ def _time_calls(call, steps: int, warmup: int, stream, settle: float = SETTLE_SE
     return start.elapsed_time(end) / 1e3 / steps     # seconds per call
 
 
-def _device_call(w, sets: int = 1, use_ws: bool = False, act=None, ops=None, variant=None):
+def _device_call(w, sets: int = 1, use_ws: bool = False, act=None, ops=None, variant=None,
+                 stream=None):
     """Allocate `sets` independent operand sets on the GPU and return a callable
     that runs the library on the next set each time (through gemm_*_ws with a
     zeroed workspace when `use_ws`; through gemm_*_bias_act with a seeded bias
     vector and activation `act` when `act` is given; through gemm_*_op with A
-    stored K x M and/or B stored N x K when `ops` = (opa, opb) is given)."""
+    stored K x M and/or B stored N x K when `ops` = (opa, opb) is given; through
+    gemm_*_ex with `variant` when given), launching on `stream` (default: the
+    current one). Each set's argument tuple is built once, and the call goes
+    straight to the ctypes function, so that a call costs the caller as little
+    as the binding allows (about 3 us, of which the HIP launch is 2.4)."""
+    import itertools
     import torch
     import dense_gemm_04_amd as dg
     import gemm_inputs as gi
+    lib = dg.load()
+    f32 = w.dtype == "f32"
     inp = gi.make(w)
     bufs = []
     opa, opb = ops if ops is not None else (0, 0)
@@ -118,51 +130,42 @@ def _device_call(w, sets: int = 1, use_ws: bool = False, act=None, ops=None, var
         C = inp["C0"].cuda() if inp["C0"] is not None else torch.zeros(
             w.M, w.N, dtype=A.dtype, device="cuda")
         bufs.append((A, B, C))
-    stream = torch.cuda.current_stream()
+    stream = stream if stream is not None else torch.cuda.current_stream()
     h = int(stream.cuda_stream)
-    fn = dg.gemm_f32 if w.dtype == "f32" else dg.gemm_bf16
-    state = {"i": 0}
-    if use_ws:
-        size_fn, ws_fn = ((dg.gemm_f32_workspace_size, dg.gemm_f32_ws) if w.dtype == "f32"
-                          else (dg.gemm_bf16_workspace_size, dg.gemm_bf16_ws))
-        nbytes = size_fn(w.M, w.N, w.K)
-        ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device="cuda")
-
-        def fn(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream):
-            return ws_fn(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
-                         ws.data_ptr() if nbytes else None, nbytes, stream)
-    if act is not None:
-        bias = gi.random_matrix(1, w.N, w.dtype, 1000 * w.wid + 4)[0].cuda()
-        epi_fn = dg.gemm_f32_bias_act if w.dtype == "f32" else dg.gemm_bf16_bias_act
-        code = {v: k for k, v in dg.ACT_NAMES.items()}[act]
-
-        def fn(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream):
-            return epi_fn(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias.data_ptr(), code,
-                          None, 0, stream)
-
-    if variant is not None:
-        ex_fn = dg.gemm_f32_ex if w.dtype == "f32" else dg.gemm_bf16_ex
-
-        def fn(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream):
-            return ex_fn(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, variant)
     lda, ldb = (w.M if opa else w.K), (w.K if opb else w.N)
+    size_fn = dg.gemm_f32_workspace_size if f32 else dg.gemm_bf16_workspace_size
+    nbytes = size_fn(w.M, w.N, w.K) if use_ws else 0
+    ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    wsp = ws.data_ptr() if nbytes else None
+    # arguments: pre + (M, N, K, alpha, A, lda, B, ldb, beta, C, ldc) + mid + (stream,) + post
+    pre, mid, post = (), (), ()
     if ops is not None:
-        op_fn = dg.gemm_f32_op if w.dtype == "f32" else dg.gemm_bf16_op
-        op_size = dg.gemm_f32_workspace_size if w.dtype == "f32" else dg.gemm_bf16_workspace_size
-        op_bytes = op_size(w.M, w.N, w.K) if use_ws else 0
-        op_ws = torch.zeros(max(op_bytes, 1), dtype=torch.uint8, device="cuda")
-
-        def fn(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream):
-            return op_fn(opa, opb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, None, 0,
-                         op_ws.data_ptr() if op_bytes else None, op_bytes, stream)
+        raw = lib.gemm_f32_op if f32 else lib.gemm_bf16_op
+        pre, mid = (opa, opb), (None, 0, wsp, nbytes)
+    elif act is not None:
+        bias = gi.random_matrix(1, w.N, w.dtype, 1000 * w.wid + 4)[0].cuda()
+        bufs.append(bias)
+        raw = lib.gemm_f32_bias_act if f32 else lib.gemm_bf16_bias_act
+        code = {v: k for k, v in dg.ACT_NAMES.items()}[act]
+        mid = (bias.data_ptr(), code, wsp, nbytes)
+    elif variant is not None:
+        raw = lib.gemm_f32_ex if f32 else lib.gemm_bf16_ex
+        post = (variant,)
+    elif use_ws:
+        raw = lib.gemm_f32_ws if f32 else lib.gemm_bf16_ws
+        mid = (wsp, nbytes)
+    else:
+        raw = lib.gemm_f32 if f32 else lib.gemm_bf16
+    argsets = [pre + (w.M, w.N, w.K, w.alpha, A.data_ptr(), lda, B.data_ptr(), ldb, w.beta,
+                      C.data_ptr(), w.N) + mid + (h,) + post for A, B, C in bufs[:sets]]
+    nxt = itertools.cycle(argsets).__next__
 
     def call():
-        A, B, C = bufs[state["i"] % sets]
-        state["i"] += 1
-        st = fn(w.M, w.N, w.K, w.alpha, A.data_ptr(), lda, B.data_ptr(), ldb, w.beta,
-                C.data_ptr(), w.N, h)
-        if st != dg.GEMM_OK:
+        st = raw(*nxt())
+        if st:
             raise RuntimeError(f"gemm returned {st}: {dg.gemm_status_string(st)}")
+    call.keep = (bufs, ws)          # the buffers the argument tuples point into
+    call.outputs = [b[2] for b in bufs[:sets]]
     return call, stream, inp
 
 
@@ -198,6 +201,7 @@ def _time_reps(call, stream, reps: int = REPS, warmup: int = 10):
 # `workloads` report (the traffic ratio is reported only while the summary's
 # source hash matches the kernel built now).
 PROFILE_OF = {
+    "1": ("gemm_f32_small_256.md", "gemm_f32_small.hip"),
     "2": ("gemm_f32_mfma_4096.md", "gemm_f32_mfma.hip"),
     "3": ("gemm_bf16_tiled_4096.md", "gemm_bf16_tiled.hip"),
     "4": ("gemm_bf16_tiled_proj_8192x12288x4096.md", "gemm_bf16_tiled.hip"),
@@ -267,7 +271,59 @@ def workload_report(w, key: str, sets: int = 1, use_ws: bool = False) -> dict:
     traffic = measured_traffic(*prof) if prof else None
     out["traffic_ratio"] = round(traffic / w.algorithmic_bytes, 2) if traffic else None
     out["bound"] = "hbm" if key.startswith("52") else "mfma"
+    if key in GRAPH_KEYS:
+        out["graph"] = graph_report(w, sets, use_ws)
     return out
+
+
+# Workloads whose kernel runs in less time than a caller needs to issue one
+# call: also timed as calls replayed from a captured HIP graph.
+GRAPH_KEYS = ("1",)
+GRAPH_CALLS = 200
+
+
+def graph_report(w, sets: int = 1, use_ws: bool = False) -> dict:
+    """GRAPH_CALLS calls captured once into a HIP graph (torch.cuda.CUDAGraph)
+    on a stream of their own, then replayed: the GPU's own rate for
+    back-to-back calls, without the per-call launch cost on the host. Each
+    replay must leave C bit-identical to the eager call's result."""
+    import statistics
+    import torch
+    s = torch.cuda.Stream()
+    call, _, _ = _device_call(w, sets, use_ws, stream=s)
+    with torch.cuda.stream(s):
+        for _ in range(20):
+            call()
+    torch.cuda.synchronize()
+    eager = [c.clone() for c in call.outputs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for _ in range(GRAPH_CALLS):
+            call()
+    torch.cuda.synchronize()
+    per = []
+    same = True
+    with torch.cuda.stream(s):
+        t_end = time.perf_counter() + SETTLE_SECONDS
+        while time.perf_counter() < t_end:
+            g.replay()
+            torch.cuda.synchronize()
+        for _ in range(REPS):
+            for c in call.outputs:
+                c.fill_(float("nan"))
+            start = torch.cuda.Event(enable_timing=True)
+            end = torch.cuda.Event(enable_timing=True)
+            start.record(s)
+            g.replay()
+            end.record(s)
+            torch.cuda.synchronize()
+            per.append(start.elapsed_time(end) / 1e3 / GRAPH_CALLS)
+            same = same and all(torch.equal(c, e) for c, e in zip(call.outputs, eager))
+    med = statistics.median(per)
+    return {"calls_per_graph": GRAPH_CALLS, "replays": REPS,
+            "ms_median": round(med * 1e3, 5), "ms_min": round(min(per) * 1e3, 5),
+            "tflops": round(tflops(gemm_flops(w.M, w.N, w.K), med), 3),
+            "matches_eager": bool(same)}
 
 
 def measure(w, steps: int, warmup: int, sets: int = 1, use_ws: bool = False, act=None,
@@ -303,7 +359,7 @@ def vendor_lines(steps: int, warmup: int):
     import torch
     import gemm_inputs as gi
     torch.backends.cuda.matmul.allow_tf32 = False
-    for wid, opb in ((2, 0), (3, 0), (4, 0), (51, 0), (52, 0), (52, 1)):
+    for wid, opb in ((1, 0), (2, 0), (3, 0), (4, 0), (51, 0), (52, 0), (52, 1)):
         w = gi.WORKLOADS[wid]
         inp = gi.make(w)
         # As for this library's small-M lines, 4 operand sets (512 MiB of B)
