@@ -14,9 +14,10 @@ Also reported:
   workloads     every workload the parity tests cover, each timed as 7
                 repetitions of n back-to-back calls (n >= 20 and a repetition
                 >= 20 ms) after 10 warm-up calls, reported as the median and
-                the minimum time per call; the split-K calls (gemm_*_ws) beside
-                the plain ones for the ragged fp32 shape and small M; the
-                small-M lines rotate 4 operand sets (512 MiB of B, more than
+                the minimum time per call; the split-K call (gemm_bf16_ws)
+                beside the plain one for small M (the ragged fp32 shape needs no
+                workspace: its partly full last round runs as a strip on the
+                few-tile kernel); the small-M lines rotate 4 operand sets (512 MiB of B, more than
                 the 256 MB Infinity Cache). Each carries its fraction of the
                 bounding roofline, its HBM traffic ratio when a current
                 counter summary exists, and its own oracle timing (config 1
@@ -205,8 +206,8 @@ PROFILE_OF = {
     "2": ("gemm_f32_mfma_4096.md", "gemm_f32_mfma.hip"),
     "3": ("gemm_bf16_tiled_4096.md", "gemm_bf16_tiled.hip"),
     "4": ("gemm_bf16_tiled_proj_8192x12288x4096.md", "gemm_bf16_tiled.hip"),
-    "51": ("gemm_f32_mfma_edge_4095x4097x1023.md", "gemm_f32_mfma.hip"),
-    "51_ws": ("gemm_f32_mfma_edge_splitk_4095x4097x1023.md", "gemm_f32_mfma.hip"),
+    "51": (("gemm_f32_mfma_edge_4095x4097x1023.md", "gemm_f32_mfma.hip"),
+           ("gemm_f32_small_edge_strip_4095x1x1023.md", "gemm_f32_small.hip")),
     "52": ("gemm_bf16_smallm_16x8192x8192.md", "gemm_bf16_skinny.hip"),
     "52_ws": ("gemm_bf16_stream_splitk_16x8192x8192.md", "gemm_bf16_stream.hip"),
 }
@@ -217,8 +218,8 @@ KERNEL_OF = {
     "2": "gemm_f32_mfma (copy path, 128x128 tiles, tiles walked)",
     "3": "gemm_bf16_tiled (256x256 tiles)",
     "4": "gemm_bf16_tiled (256x256 tiles, beta = 1 residual)",
-    "51": "gemm_f32_mfma (unaligned rows, register-staged)",
-    "51_ws": "gemm_f32_mfma (unaligned rows, split-K tail round)",
+    "51": ("gemm_f32_mfma on C columns 0-4095 (two whole rounds, unaligned rows), then "
+           "gemm_f32_small on column 4096"),
     "52": "gemm_bf16_smallm (64-column strips, 128 workgroups)",
     "52_ws": "gemm_bf16_stream (256-column strips, K interleaved over 8 phases)",
 }
@@ -267,8 +268,7 @@ def workload_report(w, key: str, sets: int = 1, use_ws: bool = False) -> dict:
            "algorithmic_bytes": w.algorithmic_bytes,
            "gbs": round(w.algorithmic_bytes / med / 1e9, 1),
            "frac_hbm": round(w.algorithmic_bytes / med / 1e9 / PEAK_HBM_GBS, 4)}
-    prof = PROFILE_OF.get(key)
-    traffic = measured_traffic(*prof) if prof else None
+    traffic = workload_traffic(key)
     out["traffic_ratio"] = round(traffic / w.algorithmic_bytes, 2) if traffic else None
     out["bound"] = "hbm" if key.startswith("52") else "mfma"
     if key in GRAPH_KEYS:
@@ -413,6 +413,18 @@ def kernel_source_sha(path: str) -> str:
     return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
+def workload_traffic(key: str):
+    """HBM bytes per call of a `workloads` line: the sum over the kernels the
+    call launches (PROFILE_OF holds one (summary, source) pair, or one pair
+    per kernel), or None when any summary is missing or stale."""
+    prof = PROFILE_OF.get(key)
+    if not prof:
+        return None
+    pairs = (prof,) if isinstance(prof[0], str) else prof
+    parts = [measured_traffic(*p) for p in pairs]
+    return None if any(x is None for x in parts) else sum(parts)
+
+
 def measured_traffic(summary: str, source: str):
     """HBM bytes per launch from a committed rocprofv3 counter summary.
 
@@ -447,7 +459,7 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", type=int, default=None,
                     help="time one workload id (1, 2, 3, 4, 51, 52; 61-65 mid-size) and print its line "
-                         "(with the split-K line for 51 and 52, the bias + GELU line for 2 and 4, "
+                         "(with the split-K line for 52, the bias + GELU line for 2 and 4, "
                          "the transposed-layout lines for 2, 3 and 52)")
     ap.add_argument("--vendor", action="store_true",
                     help="time torch's own GEMM (torch.mm / torch.addmm, the platform BLAS) on the "
@@ -492,7 +504,7 @@ def main(argv=None) -> int:
             return 0
         r = measure(w, args.steps, args.warmup, 4 if args.only == 52 else 1)
         print(json.dumps(r), flush=True)
-        if args.only in (51, 52):
+        if args.only == 52:
             print(json.dumps(measure(w, args.steps, args.warmup, 4 if args.only == 52 else 1,
                                      use_ws=True)), flush=True)
         if args.only in EPILOGUE_WORKLOADS:
@@ -537,7 +549,7 @@ def main(argv=None) -> int:
     bf = measure(gi.WORKLOADS[3], args.steps, args.warmup)
     workloads = {}
     for key, wid, sets, use_ws in (("1", 1, 1, False), ("2", 2, 1, False), ("3", 3, 1, False),
-                                   ("4", 4, 1, False), ("51", 51, 1, False), ("51_ws", 51, 1, True),
+                                   ("4", 4, 1, False), ("51", 51, 1, False),
                                    ("52", 52, 4, False), ("52_ws", 52, 4, True)):
         workloads[key] = workload_report(gi.WORKLOADS[wid], key, sets, use_ws)
     line = {

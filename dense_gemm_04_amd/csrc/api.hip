@@ -153,6 +153,38 @@ bool valid_epilogue(int esz, const void* bias, int act) {
     return act >= GEMM_ACT_NONE && act <= GEMM_ACT_GELU_TANH && aligned(bias, esz);
 }
 
+// The tiled fp32 kernel as the automatic choice runs it: when its last round
+// of tiles would be partly full, the trailing columns (or rows) of C that
+// hold those tiles go to the few-tile kernel and the tiled kernel runs whole
+// rounds on the rest (plan_f32_partition); otherwise the tiled kernel alone,
+// splitting its last round over the workspace if one is given.
+hipError_t launch_f32_auto(const dg::GemmArgs<float>& a, bool vec, void* ws, size_t ws_bytes,
+                           int cus, hipStream_t s) {
+    const size_t need = dg::f32_mfma_workspace(a.M, a.N, a.K, kFullCus);
+    const bool split_ws = ws != nullptr && need > 0 && ws_bytes >= need;
+    const dg::F32Partition pt = dg::plan_f32_partition(a.M, a.N, a.K, split_ws);
+    if (pt.by == 0) return dg::launch_f32_mfma(a, vec, ws, ws_bytes, cus, s);
+    dg::GemmArgs<float> head = a, strip = a;
+    const int64_t k0 = pt.split;
+    if (pt.by == 1) {                      // columns [k0, N) of C
+        head.N = k0;
+        strip.N = a.N - k0;
+        strip.B = a.tb ? a.B + k0 * a.ldb : a.B + k0;
+        strip.C = a.C + k0;
+        if (a.bias != nullptr) strip.bias = a.bias + k0;
+        if (a.col_scale != nullptr) strip.col_scale = a.col_scale + k0;
+    } else {                               // rows [k0, M) of C
+        head.M = k0;
+        strip.M = a.M - k0;
+        strip.A = a.ta ? a.A + k0 : a.A + k0 * a.lda;
+        strip.C = a.C + k0 * a.ldc;
+        if (a.row_scale != nullptr) strip.row_scale = a.row_scale + k0;
+    }
+    const hipError_t e = dg::launch_f32_mfma(head, vec, nullptr, 0, cus, s);
+    if (e != hipSuccess) return e;
+    return dg::launch_f32_small(strip, s);
+}
+
 template <typename T>
 gemm_status_t run(int64_t M, int64_t N, int64_t K, float alpha, const T* A, int64_t lda,
                   const T* B, int64_t ldb, float beta, T* C, int64_t ldc, void* stream,
@@ -193,6 +225,8 @@ gemm_status_t run(int64_t M, int64_t N, int64_t K, float alpha, const T* A, int6
         if constexpr (esz == 4) {
             if (v == GEMM_VARIANT_VALU) e = dg::launch_f32_valu(a, vec, s);
             else if (v == GEMM_VARIANT_SMALL) e = dg::launch_f32_small(a, s);
+            else if (variant == GEMM_VARIANT_AUTO)
+                e = launch_f32_auto(a, v == GEMM_VARIANT_MFMA, ws, ws_bytes, cus, s);
             else e = dg::launch_f32_mfma(a, v == GEMM_VARIANT_MFMA, ws, ws_bytes, cus, s);
         } else {
             e = (v == GEMM_VARIANT_SKINNY)
@@ -305,8 +339,10 @@ gemm_status_t gemm_bf16_ws(int64_t M, int64_t N, int64_t K, float alpha, const u
 
 size_t gemm_f32_workspace_size(int64_t M, int64_t N, int64_t K) {
     if (M < 0 || N < 0 || K < 0 || M > INT_MAX || N > INT_MAX || K > INT_MAX) return 0;
-    // Shapes that the few-tile kernel takes even with a workspace need none.
+    // Shapes that the few-tile kernel takes even with a workspace need none,
+    // nor do those whose partly full last round is cheaper as a strip on it.
     if (dg::f32_small_preferred(M, N, K, true)) return 0;
+    if (dg::plan_f32_partition(M, N, K, true).by != 0) return 0;
     return dg::f32_mfma_workspace(M, N, K, kFullCus);
 }
 

@@ -256,15 +256,25 @@ SmallPlan plan_f32_small(int64_t M, int64_t N, int64_t K) {
     return SmallPlan{best, waves};
 }
 
+// A round of the tiled kernel in the same units: at most one 128 x 128 tile
+// per CU takes 128^2 over its efficiency relative to a 64 x 64 few-tile tile,
+// 1.45 (1536^2 x 1024: 72.2 us tiled, 61.2 with 32 x 32 tiles; 2048^3: 140.6
+// tiled, 180.6 with 64 x 64 tiles at four per CU); two per CU take 1.63 times
+// that (4096^3: 943 us for two such rounds of K = 4096).
+constexpr double kTiledRound1 = 128.0 * 128.0 / 1.45;
+constexpr double kTiledRound2 = 1.63 * kTiledRound1;
+
+static double best_small_cost(int64_t M, int64_t N) {
+    double best = small_cost(M, N, 64);
+    for (int T : {32, 16}) best = small_cost(M, N, T) < best ? small_cost(M, N, T) : best;
+    return best;
+}
+
 bool f32_small_preferred(int64_t M, int64_t N, int64_t K, bool split_ws) {
     const int64_t tiles128 = ((M + 127) / 128) * ((N + 127) / 128);
     if (tiles128 > kPlanCus) return false;
-    // The tiled kernel with at most one 128 x 128 tile per CU takes 128^2
-    // over its efficiency relative to a 64 x 64 few-tile tile, 1.45 (1536^2 x
-    // 1024: 72.2 us tiled, 61.2 with 32 x 32 tiles; 2048^3: 140.6 tiled, 180.6
-    // with 64 x 64 tiles at four per CU).
     const SmallPlan sp = plan_f32_small(M, N, K);
-    if (small_cost(M, N, sp.tile) >= 128.0 * 128.0 / 1.45) return false;
+    if (small_cost(M, N, sp.tile) >= kTiledRound1) return false;
     // Given its split-K workspace the tiled kernel shares K between
     // workgroups too, and wins once there are enough tile-k to share:
     // 1024^2 x 4096 86.3 us against 89.6, 1408^2 x 4096 150.4 against 175.4,
@@ -272,6 +282,33 @@ bool f32_small_preferred(int64_t M, int64_t N, int64_t K, bool split_ws) {
     // against 26.3, 64 x 4096 x 4096 55.4 against 30.1).
     if (split_ws && tiles128 * K >= ((int64_t)1 << 18)) return false;
     return true;
+}
+
+F32Partition plan_f32_partition(int64_t M, int64_t N, int64_t K, bool split_ws) {
+    (void)K;
+    F32Partition none{0, 0};
+    const int64_t tm = (M + 127) / 128, tn = (N + 127) / 128;
+    const int64_t slots = 2 * kPlanCus;       // the tiled kernel's resident workgroups
+    const int64_t tiles = tm * tn, tail = tiles % slots;
+    if (tiles < slots || tail == 0) return none;
+    // The last round's cost, and the strip that takes its tiles off the
+    // tiled kernel: trailing tile columns (or rows) covering at least `tail`
+    // tiles, so that the tiled kernel is left whole rounds.
+    const double round = tail <= kPlanCus ? kTiledRound1 : kTiledRound2;
+    const int64_t rn = (tail + tm - 1) / tm, rm = (tail + tn - 1) / tn;
+    const int64_t nsplit = (tn - rn) * 128, msplit = (tm - rm) * 128;
+    const double cost_n = rn < tn ? best_small_cost(M, N - nsplit) : 1e300;
+    const double cost_m = rm < tm ? best_small_cost(M - msplit, N) : 1e300;
+    const bool by_cols = cost_n <= cost_m;
+    const double cost = by_cols ? cost_n : cost_m;
+    // Worth it when the strip clearly beats the round it removes. It also
+    // beat splitting that round over a workspace wherever both applied (same
+    // box: 4095 x 4097 x 1023 313 us against 329, 4096 x 4352 x 2048 531
+    // against 603, 2560 x 4096 x 2048 338 against 360), so `split_ws` does not
+    // change the choice.
+    (void)split_ws;
+    if (cost > 0.8 * round) return none;
+    return by_cols ? F32Partition{1, nsplit} : F32Partition{2, msplit};
 }
 
 hipError_t launch_f32_small(const GemmArgs<float>& a, hipStream_t s) {

@@ -48,6 +48,16 @@ SmallPlan plan_f32_small(int64_t M, int64_t N, int64_t K);
 // `split_ws`: the caller gave the tiled kernel's split-K workspace.
 bool f32_small_preferred(int64_t M, int64_t N, int64_t K, bool split_ws);
 hipError_t launch_f32_small(const GemmArgs<float>& a, hipStream_t s);
+// Products whose 128 x 128 tiles fill whole rounds of the tiled kernel and
+// leave a last round partly full: `by` 1 puts columns [split, N) of C, 2 rows
+// [split, M), on the few-tile kernel, so that the tiled kernel runs whole
+// rounds on the rest; 0: no partition. `split_ws`: the caller gave the tiled
+// kernel's split-K workspace, which the partition must then clearly beat.
+struct F32Partition {
+    int by;
+    int64_t split;
+};
+F32Partition plan_f32_partition(int64_t M, int64_t N, int64_t K, bool split_ws);
 // Small-M bf16 (M <= kSkinnyMaxM; without `vec`, M <= kSkinnyElemMaxM). With
 // `vec` the 64-column copy-ring kernel runs; given a workspace of at least bf16_skinny_workspace(M, N, K) bytes
 // (256-byte aligned, counters zero) it splits K over several workgroups.

@@ -76,7 +76,12 @@ typedef enum {
 } gemm_status_t;
 
 /* Kernel family selection for the *_ex entry points. AUTO is what gemm_f32 and
- * gemm_bf16 use; the others force one family (for measurements and tests). */
+ * gemm_bf16 use; the others force one family (for measurements and tests).
+ * An fp32 AUTO call whose 128 x 128 tiles fill whole rounds of the MFMA
+ * kernel and leave a last round partly full runs two kernels on one stream:
+ * the MFMA kernel on whole rounds and GEMM_VARIANT_SMALL on the strip of
+ * trailing columns (or rows) that held the last round's tiles (4095 x 4097:
+ * C's last column). gemm_plan reports the MFMA family for such calls. */
 typedef enum {
     GEMM_VARIANT_AUTO = 0,
     /* LDS-tiled MFMA kernel with 128-bit global loads; needs every pointer

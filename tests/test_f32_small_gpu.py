@@ -149,3 +149,75 @@ def test_small_exact_integers():
     assert st == dg.GEMM_OK
     R, _ = oracle_ref("f32", A, B, C0, 1.0, -1.0)
     assert np.array_equal(to_f64(C), R)
+
+
+# ---- partly full last rounds: a strip of C on the few-tile kernel ----------
+#
+# (M, N, K): 4096 x 2176 has 32 x 17 = 544 tiles of 128 x 128 on 512 slots;
+# the 32 left over are tile column 16, so columns 2048 .. 2175 go to the
+# few-tile kernel. 2176 x 4096 leaves tile row 16 (rows 2048 .. 2175). 4095 x
+# 2177 x 129 leaves 64 tiles: its last two tile columns (129 columns of C,
+# the last one ragged).
+PARTITIONED = [(4096, 2176, 200), (2176, 4096, 200), (4095, 2177, 129)]
+
+
+@pytest.mark.parametrize("shape", PARTITIONED, ids=_sid)
+def test_partition_needs_no_workspace(shape):
+    # The split-K tail would need a workspace here; the strip does not.
+    assert dg.gemm_f32_workspace_size(*shape) == 0
+
+
+@pytest.mark.parametrize("variant", range(4))
+@pytest.mark.parametrize("shape", PARTITIONED, ids=_sid)
+def test_partition_parity_full(shape, variant):
+    """Every entry against the oracle, through gemm_f32_scaled, with the
+    strip's pointers offset in each operand: (0) plain, alpha and beta;
+    (1) both operands stored transposed, rows padded to odd lengths;
+    (2) row and column scales with bias and GELU; (3) B stored N x K with
+    column scales and ReLU, workspace given (and unused)."""
+    from test_scale_gpu import oracle_scaled, run_scaled, scales
+    M, N, K = shape
+    ops, pad, ws = [((0, 0), (0, 0, 0), False), ((1, 1), (1, 3, 5), False),
+                    ((0, 0), (4, 4, 4), False), ((0, 1), (0, 0, 0), True)][variant]
+    alpha, beta = [(0.5, 2.0), (1.0, -1.0), (1.0, 0.5), (-0.75, 0.0)][variant]
+    seed = 7900 + M + variant
+    A = gi.random_matrix(M, K, "f32", seed)
+    B = gi.random_matrix(K, N, "f32", seed + 1)
+    C0 = gi.random_matrix(M, N, "f32", seed + 2) if beta != 0 else None
+    u = scales(M, seed + 3) if variant == 2 else None
+    v = scales(N, seed + 4) if variant in (2, 3) else None
+    bias = gi.random_matrix(1, N, "f32", seed + 5)[0].contiguous() if variant == 2 else None
+    act = {2: "gelu_tanh", 3: "relu"}.get(variant, "none")
+    note(f"partition f32 M={M} N={N} K={K} ops={ops} pad={pad} ws={ws} variant={variant}")
+    C, st = run_scaled("f32", A, B, C0, u, v, bias, act, alpha, beta, ops, pad, ws)
+    assert st == dg.GEMM_OK, dg.gemm_status_string(st)
+    assert torch.isfinite(C).all()
+    R, D = oracle_scaled("f32", A, B, C0, u, v, bias, act if (bias is not None or act != "none") else None,
+                         alpha, beta)
+    err = oracle.max_rel_err(to_f64(C), R, D)
+    assert err <= tol("f32"), f"max error ratio {err:.3e}"
+
+
+@pytest.mark.parametrize("shape", PARTITIONED, ids=_sid)
+def test_partition_against_tiled_kernel_alone(shape):
+    """The tiled kernel alone (forced) gives the same outputs outside the
+    strip bit for bit: the partition leaves the tiled part's arithmetic as it
+    was."""
+    M, N, K = shape
+    A = gi.random_matrix(M, K, "f32", 8000 + M)
+    B = gi.random_matrix(K, N, "f32", 8001 + N)
+    note(f"partition vs tiled alone M={M} N={N} K={K}")
+    Ca, st, _ = run("f32", A, B, None, 1.0, 0.0, dg.VARIANT_AUTO)
+    assert st == dg.GEMM_OK
+    forced = dg.VARIANT_MFMA if K % 4 == 0 and N % 4 == 0 else dg.VARIANT_GENERAL
+    Ct, st, _ = run("f32", A, B, None, 1.0, 0.0, forced)
+    assert st == dg.GEMM_OK
+    tm, tn = (M + 127) // 128, (N + 127) // 128
+    tail = (tm * tn) % 512
+    if M == 2176:            # row strip: tile rows from 16 on
+        same = (slice(0, (tm - -(-tail // tn)) * 128), slice(None))
+    else:                    # column strip
+        same = (slice(None), slice(0, (tn - -(-tail // tm)) * 128))
+    assert torch.equal(Ca[same].view(torch.int32), Ct[same].view(torch.int32))
+    R, D = oracle_ref("f32", A, B, None, 1.0, 0.0)
+    assert oracle.max_rel_err(to_f64(Ca), R, D) <= tol("f32")

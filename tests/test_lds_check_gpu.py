@@ -133,7 +133,7 @@ def test_checking_builds_match_normal_build(case):
 # Split-K paths: repeated calls on one workspace must give identical bits
 # every time (fixed-order sums; counters left at zero by every call).
 REPEAT = [("bf16", (16, 8192, 8192)), ("bf16", (16, 1032, 4104)), ("bf16", (512, 512, 4096)),
-          ("f32", (4095, 4097, 1023))]
+          ("f32", (2300, 2290, 2050)), ("f32", (1024, 1024, 4096))]
 
 
 @pytest.mark.parametrize("case", REPEAT, ids=lambda c: f"{c[0]}_{'x'.join(map(str, c[1]))}")

@@ -65,21 +65,39 @@ def test_workload_small_m_split_k():
         assert err <= tol(w.dtype)
 
 
-def test_workload_edge_split_k():
-    # 4095 x 4097 x 1023 through gemm_f32_ws: 1024 whole tiles, then the last
-    # 32 tiles (the ragged ones among them) split into 8 K ranges each.
+def test_workload_edge_tiled_kernel_alone():
+    # 4095 x 4097 x 1023 on the tiled kernel alone (gemm_f32_ex, forced
+    # element-wise variant): 1056 tiles in three rounds, the ragged last tile
+    # column (one column of C) included. The automatic choice puts that
+    # column on the few-tile kernel instead (test_workload_full_size[51]).
     w = gi.WORKLOADS[51]
-    note(f"workload {w.name} via gemm_f32_ws")
+    note(f"workload {w.name} on the tiled kernel alone")
     A, B, C = _operands(w)
-    nbytes = dg.gemm_f32_workspace_size(w.M, w.N, w.K)
-    assert nbytes > 0
-    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
-    st = dg.gemm_f32_ws(w.M, w.N, w.K, w.alpha, A.data_ptr(), w.K, B.data_ptr(), w.N, w.beta,
-                        C.data_ptr(), w.N, ws.data_ptr(), nbytes,
-                        int(torch.cuda.current_stream().cuda_stream))
+    st = dg.gemm_f32_ex(w.M, w.N, w.K, w.alpha, A.data_ptr(), w.K, B.data_ptr(), w.N, w.beta,
+                        C.data_ptr(), w.N, int(torch.cuda.current_stream().cuda_stream),
+                        dg.VARIANT_GENERAL)
     torch.cuda.synchronize()
     assert st == dg.GEMM_OK, dg.gemm_status_string(st)
     R, D = workload_reference(51)
     err = full_max_err(C, R, D)
     note(f"all {w.M}x{w.N} entries, max error ratio {err:.3e}")
     assert err <= tol(w.dtype)
+
+
+def test_workload_edge_workspace_call_is_the_plain_call():
+    # gemm_f32_ws needs no workspace for 4095 x 4097 x 1023 (the partly full
+    # last round goes to the few-tile kernel as a strip, which beats splitting
+    # it) and gives the plain call's bits.
+    w = gi.WORKLOADS[51]
+    assert dg.gemm_f32_workspace_size(w.M, w.N, w.K) == 0
+    A, B, C = _operands(w)
+    C2 = C.clone()
+    h = int(torch.cuda.current_stream().cuda_stream)
+    note(f"workload {w.name} via gemm_f32 and gemm_f32_ws")
+    st = dg.gemm_f32(w.M, w.N, w.K, w.alpha, A.data_ptr(), w.K, B.data_ptr(), w.N, w.beta,
+                     C.data_ptr(), w.N, h)
+    st2 = dg.gemm_f32_ws(w.M, w.N, w.K, w.alpha, A.data_ptr(), w.K, B.data_ptr(), w.N, w.beta,
+                         C2.data_ptr(), w.N, None, 0, h)
+    torch.cuda.synchronize()
+    assert st == st2 == dg.GEMM_OK
+    assert torch.equal(C.view(torch.int32), C2.view(torch.int32))
