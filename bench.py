@@ -218,8 +218,8 @@ KERNEL_OF = {
     "2": "gemm_f32_mfma (copy path, 128x128 tiles, tiles walked)",
     "3": "gemm_bf16_tiled (256x256 tiles)",
     "4": "gemm_bf16_tiled (256x256 tiles, beta = 1 residual)",
-    "51": ("gemm_f32_mfma on C columns 0-4095 (two whole rounds, unaligned rows), then "
-           "gemm_f32_small on column 4096"),
+    "51": ("gemm_f32_mfma on C columns 0-4095 (two whole rounds, unaligned rows: 4-byte "
+           "copies), then gemm_f32_small on column 4096"),
     "52": "gemm_bf16_smallm (64-column strips, 128 workgroups)",
     "52_ws": "gemm_bf16_stream (256-column strips, K interleaved over 8 phases)",
 }

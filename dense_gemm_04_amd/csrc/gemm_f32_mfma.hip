@@ -25,9 +25,11 @@
 //     beta term) follows the block layout: 128-bit loads and stores when a
 //     lane holds 4 consecutive columns, element-wise ones otherwise.
 //
-// Rows that are not 16-byte aligned (VEC = false) are register-staged: the
-// same 128-bit global accesses at 4-byte alignment (element-wise only at the
-// edges), then LDS stores. Transposed operands on that path are loaded as
+// Rows aligned only to 4 bytes (VEC = false, DW = true) take the same copy
+// path with 4-byte LDS-destined loads, four per 1 KB copy, into the same
+// layouts. Past the copies' 31-bit offset range operands are register-staged:
+// 128-bit global accesses at 4-byte alignment (element-wise only at the
+// edges), then LDS stores; transposed operands on that path are loaded as
 // 4 x 4 blocks and transposed in registers, so the LDS layout is that of
 // row-major operands.
 //
@@ -98,16 +100,16 @@ __device__ __forceinline__ void transpose4x4(const f32x4 (&x)[4], f32x4 (&y)[4])
     for (int j = 0; j < 4; ++j) y[j] = f32x4{x[0][j], x[1][j], x[2][j], x[3][j]};
 }
 
-// Whether a workgroup walks several tiles: on the copy path without split-K,
+// Whether a workgroup walks several tiles: on the copy paths without split-K,
 // workgroup w takes tiles w, w + gridDim.x, ... (the same XCD slot each time).
 // The register-staged path keeps one tile per workgroup: in a tile loop its
 // registers no longer fit two waves per SIMD. With split-K every workgroup is
 // one work item.
-constexpr bool walks_tiles(bool vec, bool split) { return vec && !split; }
+constexpr bool walks_tiles(bool copies, bool split) { return copies && !split; }
 
 // One tile (or, with SPLIT, one K range of a tile) for work item bidx of nbid.
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool VEC, bool SPLIT, bool EPI, bool TA,
-          bool TB>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool VEC, bool DW, bool SPLIT, bool EPI,
+          bool TA, bool TB>
 __device__ __forceinline__ void f32_tile(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit ts,
                                          unsigned char* ws, const int bidx, const int nbid) {
     constexpr int NT = WAVES_M * WAVES_N * 64;
@@ -131,7 +133,11 @@ __device__ __forceinline__ void f32_tile(GemmArgs<float> p, int tiles_m, int til
     // 4 consecutive n or m per lane). A k-contiguous operand's MFMA blocks
     // cover 16 consecutive rows (columns); an m/n-contiguous operand's blocks
     // are 4-way interleaved.
-    constexpr bool DMA = VEC;
+    // DW: rows aligned to 4 bytes only, copied by 4-byte LDS-destined loads
+    // into the same layouts (256 bytes per wave instruction, four per 1 KB
+    // copy of the 16-byte schedule).
+    static_assert(!(VEC && DW), "one copy width");
+    constexpr bool DMA = VEC || DW;
     constexpr bool AMC = DMA && TA;      // A^T staged [k][m]
     constexpr bool BKC = DMA && TB;      // B^T staged [n][k]
     static_assert(!DMA || (BM == 128 && BN == 128 && NT == 256 && NG == 1),
@@ -359,6 +365,28 @@ __device__ __forceinline__ void f32_tile(GemmArgs<float> p, int tiles_m, int til
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             bt_voff[i] = (uint32_t)((ar * p.ldb + 4 * (ap ^ s_ar ^ (2 * i))) * 4);
+        // 4-byte copies: sub-copy s (0..3) of copy I fills 256 bytes at
+        // I * 1024 + s * 256. In a k-contiguous tile that is rows 8 I + 2 s
+        // + h (h = lane / 32) at physical position lane % 32: chunk pc =
+        // (lane % 32) / 4, element e = lane % 4. Its logical chunk is pc ^
+        // ((r ^ r / 4) mod 8) ^ 2 I mod 8 with r = 2 s + h, and since the row
+        // swizzle of 2 s + 1 is that of 2 s with bit 0 flipped, that is
+        // (pc ^ h) ^ c(s, I) with c(s, I) = ((2 s) ^ (2 s) / 4 ^ 2 I) mod 8, a
+        // compile-time value. dw_koff[c] holds the lane's byte offset for each
+        // c (row h, logical chunk (pc ^ h) ^ c, element e); the row offset
+        // 8 I + 2 s goes into the scalar offset. In an m/n-contiguous tile a
+        // sub-copy is half of one k row: lane l takes element 64 (s & 1) + l
+        // of row 2 I + s / 2.
+        uint32_t dw_akoff[8], dw_bkoff[8];
+        if constexpr (DW) {
+            const int h = lane >> 5, pc = (lane & 31) >> 2, e = lane & 3;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                dw_akoff[c] = (uint32_t)((h * p.lda + 4 * ((pc ^ h) ^ c) + e) * 4);
+                dw_bkoff[c] = (uint32_t)((h * p.ldb + 4 * ((pc ^ h) ^ c) + e) * 4);
+            }
+        }
+        auto dw_c = [](int s, int I) { return ((2 * s) ^ ((2 * s) >> 2) ^ (2 * I)) & 7; };
         const int64_t rows_a = M - m0 < BM ? M - m0 : BM;
         const int64_t cols_b = N - n0 < BN ? N - n0 : BN;   // also B^T's valid rows
         auto dma = [&](int64_t kt, int stage) {
@@ -374,7 +402,15 @@ __device__ __forceinline__ void f32_tile(GemmArgs<float> p, int tiles_m, int til
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int I = 4 * wv + i;
-                    dma16(ad, at_voff, (uint32_t)(2 * I * p.lda * 4), As + I * 1024);
+                    if constexpr (DW) {
+#pragma unroll
+                        for (int s = 0; s < 4; ++s)
+                            dma4(ad, (uint32_t)(4 * lane),
+                                 (uint32_t)(((2 * I + (s >> 1)) * p.lda + 64 * (s & 1)) * 4),
+                                 As + I * 1024 + s * 256);
+                    } else {
+                        dma16(ad, at_voff, (uint32_t)(2 * I * p.lda * 4), As + I * 1024);
+                    }
                 }
             } else {
                 const rsrc_t ad = make_rsrc(p.A + m0 * p.lda + k0,
@@ -382,7 +418,14 @@ __device__ __forceinline__ void f32_tile(GemmArgs<float> p, int tiles_m, int til
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int I = 4 * wv + i;
-                    dma16(ad, a_voff[i], (uint32_t)(8 * I * p.lda * 4), As + I * 1024);
+                    if constexpr (DW) {
+#pragma unroll
+                        for (int s = 0; s < 4; ++s)
+                            dma4(ad, dw_akoff[dw_c(s, i)], (uint32_t)((8 * I + 2 * s) * p.lda * 4),
+                                 As + I * 1024 + s * 256);
+                    } else {
+                        dma16(ad, a_voff[i], (uint32_t)(8 * I * p.lda * 4), As + I * 1024);
+                    }
                 }
             }
             if constexpr (BKC) {
@@ -391,7 +434,14 @@ __device__ __forceinline__ void f32_tile(GemmArgs<float> p, int tiles_m, int til
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int J = 4 * wv + j;
-                    dma16(bd, bt_voff[j], (uint32_t)(8 * J * p.ldb * 4), Bs + J * 1024);
+                    if constexpr (DW) {
+#pragma unroll
+                        for (int s = 0; s < 4; ++s)
+                            dma4(bd, dw_bkoff[dw_c(s, j)], (uint32_t)((8 * J + 2 * s) * p.ldb * 4),
+                                 Bs + J * 1024 + s * 256);
+                    } else {
+                        dma16(bd, bt_voff[j], (uint32_t)(8 * J * p.ldb * 4), Bs + J * 1024);
+                    }
                 }
             } else {
                 const rsrc_t bd = make_rsrc(p.B + k0 * p.ldb + n0,
@@ -399,7 +449,15 @@ __device__ __forceinline__ void f32_tile(GemmArgs<float> p, int tiles_m, int til
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int J = 4 * wv + j;
-                    dma16(bd, b_voff, (uint32_t)(2 * J * p.ldb * 4), Bs + J * 1024);
+                    if constexpr (DW) {
+#pragma unroll
+                        for (int s = 0; s < 4; ++s)
+                            dma4(bd, (uint32_t)(4 * lane),
+                                 (uint32_t)(((2 * J + (s >> 1)) * p.ldb + 64 * (s & 1)) * 4),
+                                 Bs + J * 1024 + s * 256);
+                    } else {
+                        dma16(bd, b_voff, (uint32_t)(2 * J * p.ldb * 4), Bs + J * 1024);
+                    }
                 }
             }
         };
@@ -576,7 +634,7 @@ __device__ __forceinline__ void f32_tile(GemmArgs<float> p, int tiles_m, int til
     // the compiler would otherwise wait for each load in turn). A workgroup
     // that walks tiles skips this: the extra registers would leave room for
     // only one wave per SIMD.
-    constexpr bool kPreloadC = !walks_tiles(VEC, SPLIT);
+    constexpr bool kPreloadC = !walks_tiles(DMA, SPLIT);
     f32x4 cpre[kPreloadC ? FM : 1][4][NG];
     if (kPreloadC && beta != 0.f) {
 #pragma unroll
@@ -642,21 +700,21 @@ __device__ __forceinline__ void f32_tile(GemmArgs<float> p, int tiles_m, int til
 
 constexpr int kSlotsPerCu = 2;   // resident workgroups per compute unit (64 KB LDS each)
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool VEC, bool SPLIT, bool EPI, bool TA,
-          bool TB>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool VEC, bool DW, bool SPLIT, bool EPI,
+          bool TA, bool TB>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64)
 void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit ts,
                           unsigned char* ws) {
-    if constexpr (!walks_tiles(VEC, SPLIT)) {
-        f32_tile<BM, BN, WAVES_M, WAVES_N, VEC, SPLIT, EPI, TA, TB>(p, tiles_m, tiles_n, ts, ws,
-                                                                  (int)blockIdx.x, (int)gridDim.x);
+    if constexpr (!walks_tiles(VEC || DW, SPLIT)) {
+        f32_tile<BM, BN, WAVES_M, WAVES_N, VEC, DW, SPLIT, EPI, TA, TB>(p, tiles_m, tiles_n, ts, ws,
+                                                                      (int)blockIdx.x, (int)gridDim.x);
     } else {
         const int64_t total = (int64_t)tiles_m * tiles_n;
         for (int64_t b = blockIdx.x; b < total; b += gridDim.x) {
             // The previous tile's last slab may have been read from stage 0.
             if (b != (int64_t)blockIdx.x) __syncthreads();
-            f32_tile<BM, BN, WAVES_M, WAVES_N, VEC, SPLIT, EPI, TA, TB>(p, tiles_m, tiles_n, ts, ws,
-                                                                      (int)b, (int)total);
+            f32_tile<BM, BN, WAVES_M, WAVES_N, VEC, DW, SPLIT, EPI, TA, TB>(p, tiles_m, tiles_n, ts,
+                                                                          ws, (int)b, (int)total);
         }
     }
 }
@@ -674,25 +732,31 @@ TailSplit plan_tail(int64_t tiles, int64_t nk, int cus) {
     return plan_tail_split(tiles, nk, (int64_t)cus * kSlotsPerCu, 1, kF32FixupSlabs);
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool VEC, bool SPLIT, bool EPI>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool VEC, bool DW, bool SPLIT, bool EPI>
 const void* pick_layout(bool ta, bool tb) {
 #define DG_F32_KERNEL(TA, TB) \
-    (const void*)&gemm_f32_mfma_kernel<BM, BN, WAVES_M, WAVES_N, VEC, SPLIT, EPI, TA, TB>
+    (const void*)&gemm_f32_mfma_kernel<BM, BN, WAVES_M, WAVES_N, VEC, DW, SPLIT, EPI, TA, TB>
     return ta ? (tb ? DG_F32_KERNEL(true, true) : DG_F32_KERNEL(true, false))
               : (tb ? DG_F32_KERNEL(false, true) : DG_F32_KERNEL(false, false));
 #undef DG_F32_KERNEL
 }
 
+// Copy mode: 0 register-staged, 1 16-byte copies (VEC), 2 4-byte copies (DW).
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool EPI, bool SPLIT>
+const void* pick_mode(int mode, bool ta, bool tb) {
+    return mode == 1 ? pick_layout<BM, BN, WAVES_M, WAVES_N, true, false, SPLIT, EPI>(ta, tb)
+         : mode == 2 ? pick_layout<BM, BN, WAVES_M, WAVES_N, false, true, SPLIT, EPI>(ta, tb)
+                     : pick_layout<BM, BN, WAVES_M, WAVES_N, false, false, SPLIT, EPI>(ta, tb);
+}
+
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool EPI>
-const void* pick_kernel(bool vec, bool split, bool ta, bool tb) {
-    return split ? (vec ? pick_layout<BM, BN, WAVES_M, WAVES_N, true, true, EPI>(ta, tb)
-                        : pick_layout<BM, BN, WAVES_M, WAVES_N, false, true, EPI>(ta, tb))
-                 : (vec ? pick_layout<BM, BN, WAVES_M, WAVES_N, true, false, EPI>(ta, tb)
-                        : pick_layout<BM, BN, WAVES_M, WAVES_N, false, false, EPI>(ta, tb));
+const void* pick_kernel(int mode, bool split, bool ta, bool tb) {
+    return split ? pick_mode<BM, BN, WAVES_M, WAVES_N, EPI, true>(mode, ta, tb)
+                 : pick_mode<BM, BN, WAVES_M, WAVES_N, EPI, false>(mode, ta, tb);
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N>
-hipError_t launch_tiles(const GemmArgs<float>& a, bool vec, void* ws, size_t ws_bytes, int cus,
+hipError_t launch_tiles(const GemmArgs<float>& a, int mode, void* ws, size_t ws_bytes, int cus,
                         hipStream_t s) {
     const int64_t tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
     int tm = (int)tiles_m, tn = (int)tiles_n;
@@ -703,12 +767,12 @@ hipError_t launch_tiles(const GemmArgs<float>& a, bool vec, void* ws, size_t ws_
     unsigned char* wsp = split ? static_cast<unsigned char*>(ws) : nullptr;
     void* kargs[] = {&args, &tm, &tn, &ts, &wsp};
     const void* fn = has_epilogue(a)
-                         ? pick_kernel<BM, BN, WAVES_M, WAVES_N, true>(vec, split, a.ta, a.tb)
-                         : pick_kernel<BM, BN, WAVES_M, WAVES_N, false>(vec, split, a.ta, a.tb);
+                         ? pick_kernel<BM, BN, WAVES_M, WAVES_N, true>(mode, split, a.ta, a.tb)
+                         : pick_kernel<BM, BN, WAVES_M, WAVES_N, false>(mode, split, a.ta, a.tb);
     const int64_t items = split ? (int64_t)ts.full + (int64_t)ts.tail * ts.parts : tiles_m * tiles_n;
     if (items > kMaxGrid) return hipErrorInvalidConfiguration;
     const int64_t slots = (int64_t)kSlotsPerCu * cus;
-    const int64_t grid = walks_tiles(vec, split) && items > slots ? slots : items;
+    const int64_t grid = walks_tiles(mode != 0, split) && items > slots ? slots : items;
     return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(WAVES_M * WAVES_N * 64), kargs, 0, s);
 }
 
@@ -725,10 +789,11 @@ static bool f32_copies_fit(const GemmArgs<float>& a) {
 
 hipError_t launch_f32_mfma(const GemmArgs<float>& a, bool vec, void* ws, size_t ws_bytes, int cus,
                            hipStream_t s) {
-    // Operands with 16-byte rows take the copy path; past its offset range
-    // they take the register-staged path at element alignment.
-    if (vec && !f32_copies_fit(a)) vec = false;
-    return launch_tiles<128, 128, 2, 2>(a, vec, ws, ws_bytes, cus, s);
+    // Operands with 16-byte rows take the 16-byte copy path, others the
+    // 4-byte one; past the copies' offset range both take the register-staged
+    // path at element alignment.
+    const int mode = !f32_copies_fit(a) ? 0 : (vec ? 1 : 2);
+    return launch_tiles<128, 128, 2, 2>(a, mode, ws, ws_bytes, cus, s);
 }
 
 size_t f32_mfma_workspace(int64_t M, int64_t N, int64_t K, int cus) {

@@ -13,8 +13,8 @@ normal build's results bit for bit, through the C ABI, on every pipeline:
 Cases cover the bf16 tiled kernel (several rounds of tiles, split-K tail,
 transposed layouts), the small-M copy rings (64-column and streaming, split
 and not), the element-wise and unaligned kernels, and the fp32 copy path
-(tiles walked, transposed layouts, split-K tail), its register-staged path
-and the vector-FMA kernel, at ragged shapes. A second test repeats each
+(16-byte and 4-byte copies: tiles walked, transposed layouts, split-K
+tail), its register-staged path and the vector-FMA kernel, at ragged shapes. A second test repeats each
 split-K path 100 times and requires identical bits every time.
 """
 import pytest
@@ -97,14 +97,18 @@ CASES = [
     ("f32", (1100, 1030, 4100), (0, 0, 0), (0, 0), True, None),    # copy path, few tiles split
     ("f32", (600, 4100, 300), (4, 8, 12), (0, 0), True, None),     # split-K tail, padded
     ("f32", (2300, 2290, 2050), (0, 0, 0), (0, 0), True, None),    # fuller last round split: 3 ranges
-    ("f32", (2100, 2000, 65), (1, 3, 5), (0, 0), False, None),     # register-staged (unaligned)
+    ("f32", (2100, 2000, 65), (1, 3, 5), (0, 0), False, None),     # 4-byte copies (unaligned rows)
+    ("f32", (2100, 2000, 100), (1, 3, 5), (1, 1), False, None),    # 4-byte copies, both transposed
+    ("f32", (2100, 2000, 100), (3, 1, 5), (0, 1), False, None),    # 4-byte copies, B stored N x K
+    ("f32", (1100, 1030, 4100), (1, 3, 5), (0, 0), True, None),    # 4-byte copies, split K
+    ("f32", (3, 40, 50), (4_199_950, 0, 0), (0, 0), False, 2),     # register-staged (lda past the copy range)
     ("f32", (300, 264, 100), (0, 0, 0), (0, 0), False, 3),         # vector-FMA kernel
 ]
 
 
 def _case_id(c):
     return (f"{c[0]}_{'x'.join(map(str, c[1]))}_pad{c[2][0]}_{'NT'[c[3][0]]}{'NT'[c[3][1]]}"
-            + ("_ws" if c[4] else "") + ("_valu" if c[5] == 3 else ""))
+            + ("_ws" if c[4] else "") + {None: "", 2: "_general", 3: "_valu"}[c[5]])
 
 
 @pytest.mark.parametrize("case", CASES, ids=_case_id)
