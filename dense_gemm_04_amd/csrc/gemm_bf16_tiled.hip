@@ -444,6 +444,71 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, Tail
     // With EPI, the product is also scaled by the row's and the column's
     // quantisation scale (row_factor folds the row scale into alpha).
     const float alpha = p.alpha, beta = p.beta;
+    static_assert(kWTN == 64 && kFM * 16 == kWTM, "the row-order epilogue covers 64-column wave tiles");
+    if (m0 + kBM <= M && n0 + kBN <= N) {
+        // Whole tiles: C is read and written 16 bytes (8 columns) per lane
+        // and instruction, 8 rows of 128 bytes per wave instruction, instead
+        // of the 4 columns a lane holds after the MFMAs (16 rows of 32 bytes
+        // per instruction): the projection with beta = 1 ran 685 against
+        // 646 us in a copy with this access pattern. Each 16-row block of a
+        // wave's results goes through a wave-private LDS scratch (rows padded
+        // to 68 floats: the 128-bit writes and reads are conflict-free) into
+        // row order. Lane l takes columns 8 (l mod 8) .. + 7 of rows l / 8 and
+        // l / 8 + 8 of each block. The arithmetic is the same as below.
+        const int cc = lane & 7, rr = lane >> 3;
+        const int64_t gcol = n0 + wn0 + 8 * cc;
+        float cf8[8], bv8[8];
+        if constexpr (EPI) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                cf8[e] = col_factor(p, gcol + e);
+                bv8[e] = bias_at(p, gcol + e);
+            }
+        }
+        u32x4 c0q[kFM][2];
+        if (beta != 0.f) {
+#pragma unroll
+            for (int i = 0; i < kFM; ++i)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    c0q[i][h] = *reinterpret_cast<const u32x4*>(
+                        p.C + (m0 + wm0 + 16 * i + rr + 8 * h) * p.ldc + gcol);
+        }
+        // Every wave has read its last fragments: the stages are free.
+        lds_only_barrier();
+        constexpr int kScrLd = 68;
+        static_assert(4 * 16 * kScrLd * 4 <= kAStage * 2, "four wave scratches per A stage");
+        float* scr = reinterpret_cast<float*>(wave < 4 ? a_st0 : a_st1) + (wave & 3) * 16 * kScrLd;
+#pragma unroll
+        for (int i = 0; i < kFM; ++i) {
+#pragma unroll
+            for (int j = 0; j < kFN; ++j)
+                *reinterpret_cast<f32x4*>(scr + pl * kScrLd + 16 * j + 4 * g) = acc[j][i];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int row = rr + 8 * h;
+                const f32x4 lo = *reinterpret_cast<const f32x4*>(scr + row * kScrLd + 8 * cc);
+                const f32x4 hi = *reinterpret_cast<const f32x4*>(scr + row * kScrLd + 8 * cc + 4);
+                const int64_t grow = m0 + wm0 + 16 * i + row;
+                const float fr = EPI ? row_factor(p, grow) : alpha;
+                float v[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    v[e] = fr * (e < 4 ? lo[e] : hi[e - 4]);
+                    if constexpr (EPI) v[e] = activate(v[e] * cf8[e] + bv8[e], p.act);
+                }
+                if (beta != 0.f) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        v[e] += beta * bf16_to_f32((uint16_t)(c0q[i][h][e >> 1] >> (16 * (e & 1))));
+                }
+                *reinterpret_cast<u32x4*>(p.C + grow * p.ldc + gcol) =
+                    u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                          pack_bf16x2(v[6], v[7])};
+            }
+        }
+        return;
+    }
     float bv[kFN][4], cv[kFN][4];
     if constexpr (EPI) {
 #pragma unroll
