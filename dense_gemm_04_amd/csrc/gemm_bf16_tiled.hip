@@ -69,15 +69,21 @@ __device__ __forceinline__ int a_off(int row, int c) {
     return row * kBK + ((c ^ (row & 7)) << 3);
 }
 
-// B tile [64][256]: chunk c (8 bf16, c in 0..31) of row k. The XOR term is
-// even and depends on k mod 4 and k / 8 mod 4, the two indices that vary
-// across the 16-lane groups of a transposing read.
+// B tile [64][BN]: chunk c (8 bf16) of row k. The XOR term is even, so a
+// 16-lane group's two neighbouring chunks stay neighbours, and depends on
+// k mod 4 (the rows within a 16-lane group of a transposing read) and on k / 8
+// (the rows of the other groups). 256-wide rows (32 chunks, 512 bytes, twice
+// the LDS banks) take k / 8 mod 4; 128-wide rows (16 chunks, 256 bytes, once
+// the banks) take k / 8 mod 2, so the term stays below 16 and every chunk in
+// its own row, and puts the odd groups of 8 rows on the other half of the banks.
+template <int BN>
 __device__ __forceinline__ int b_swz(int k) {
-    return ((k & 3) | (((k >> 3) & 3) << 2)) << 1;
+    if constexpr (BN == 256) return ((k & 3) | (((k >> 3) & 3) << 2)) << 1;
+    return ((k & 3) << 1) | (((k >> 3) & 1) << 3);
 }
 template <int BN>
 __device__ __forceinline__ int b_off(int k, int c) {
-    return k * BN + ((c ^ b_swz(k)) << 3);
+    return k * BN + ((c ^ b_swz<BN>(k)) << 3);
 }
 
 
@@ -104,7 +110,7 @@ __device__ __forceinline__ int opaque_lane() {
 // padded to 256 bytes][slots: tail x parts partial tiles of BM x BN fp32,
 // value c of thread t at byte (c * threads + t) * 16 of its slot].
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool EPI, bool TA, bool TB, bool SPLIT>
-__global__ __launch_bounds__(WAVES_M * WAVES_N * 64, 1)
+__global__ __launch_bounds__(WAVES_M * WAVES_N * 64, BM == 128 ? 2 : 1)
 void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, TailSplit ts,
                             unsigned char* ws) {
     constexpr int kNT = WAVES_M * WAVES_N * 64;
@@ -125,7 +131,7 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, Tail
     static_assert(kACopies * kDmaWaves * 1024 == kAStage * 2, "A slab must split evenly");
     static_assert(kBCopies * kDmaWaves * 1024 == kBStage * 2, "B slab must split evenly");
     static_assert(BN == 256 || BN == 128, "B row length");
-    static_assert(BM == 256 && (!TA || BM == BN), "operand tile sizes");
+    static_assert((BM == 256 || BM == 128) && (!TA || BM == BN), "operand tile sizes");
     static_assert(kWTM % 16 == 0 && kWTN % 16 == 0, "wave tile");
     // One array per operand and pipeline stage, so the compiler can tell which
     // stage an LDS-destined load writes and does not make reads of the other
@@ -210,7 +216,7 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, Tail
             for (int i = 0; i < kACopies; ++i) {
                 const int I = wave * kACopies + i;
                 const int row = kBRowsPerCopy * I + lrow;
-                const int c = pos ^ b_swz(row);
+                const int c = pos ^ b_swz<BM>(row);
                 dma16(desc, (uint32_t)(lrow * lda * 2 + c * 16),
                       (uint32_t)((kBRowsPerCopy * I) * lda * 2), As + I * 1024);
             }
@@ -230,7 +236,7 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, Tail
                 for (int i = 0; i < kBCopies; ++i) {
                     const int I = wave * kBCopies + i;
                     const int row = kBRowsPerCopy * I + lrow;
-                    const int c = pos ^ b_swz(row);
+                    const int c = pos ^ b_swz<BN>(row);
                     dma16(b_desc, (uint32_t)(lrow * ldb * 2 + c * 16),
                           (uint32_t)((kBRowsPerCopy * I) * ldb * 2), Bs + I * 1024);
                 }
@@ -239,7 +245,7 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, Tail
                 for (int i = 0; i < kBCopies; ++i) {
                     const int I = wave * kBCopies + i;
                     const int row = kBRowsPerCopy * I + b_lrow;
-                    const int c = b_pos ^ b_swz(row);
+                    const int c = b_pos ^ b_swz<BN>(row);
                     dma16(b_desc, (uint32_t)(b_lrow * ldb * 2 + c * 16),
                           (uint32_t)((kBRowsPerCopy * I) * ldb * 2), Bs + I * 1024);
                 }
@@ -476,9 +482,10 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, Tail
         }
         // Every wave has read its last fragments: the stages are free.
         lds_only_barrier();
-        constexpr int kScrLd = 68;
-        static_assert(4 * 16 * kScrLd * 4 <= kAStage * 2, "four wave scratches per A stage");
-        float* scr = reinterpret_cast<float*>(wave < 4 ? a_st0 : a_st1) + (wave & 3) * 16 * kScrLd;
+        constexpr int kScrLd = 68, kScrPerStage = kWaves / 2;
+        static_assert(kScrPerStage * 16 * kScrLd * 4 <= kAStage * 2, "half the wave scratches per A stage");
+        float* scr = reinterpret_cast<float*>(wave < kScrPerStage ? a_st0 : a_st1) +
+                     (wave % kScrPerStage) * 16 * kScrLd;
 #pragma unroll
         for (int i = 0; i < kFM; ++i) {
 #pragma unroll
@@ -597,43 +604,70 @@ const void* pick_tiled(bool ta, bool tb) {
 #undef DG_TILED
 }
 
-// One workgroup per compute unit (8 waves of 256 registers, 128 KB of LDS).
-constexpr int kTiledSlotsPerCu = 1;
-// Each K range spans at least 16 slabs (1024 k). Every range stores a 256 KB
-// fp32 partial tile and the tile's last range reads them all back, which
-// costs a CU 10-30 us whatever the tile count; only ranges with that much
-// MFMA work to save pay for it (1024^3 and 2048^3 measured slower split into
-// ranges of 4 and 8 slabs; 1024 x 4096 x 4096 and 512 x 8192 x 8192 gain
-// 1.2x and 1.7x).
-constexpr int kTiledMinSlabs = 16;
+// Two tile sizes: 256 x 256 (8 waves of 128 x 64, 128 KB of LDS, one
+// workgroup per CU) and 128 x 128 (4 waves of 64 x 64, 64 KB, two per CU).
+// The smaller tile multiplies less per byte it stages (79% of the larger
+// one's rate at full occupancy: 4096^3 138.8 against 109.3 us) but gives four
+// times the workgroups, which products with few 256 x 256 tiles need
+// (512 x 8192 x 8192: 64 such tiles, 161.7 us; 256 of 128 x 128, 86.7 us).
+//
+// The model, in units of one 256 x 256 tile's K loop on a CU: 256 x 256 tiles
+// cost ceil(tiles / 256); a round of 128 x 128 tiles costs 0.635 with two per
+// CU and 0.536 with at most one (the measured ratios above), so 4096^3 costs
+// 1 against 1.27, 4352 x 4096 x 4096 (272 large tiles, two rounds) 2 against
+// 1.81 (184.1 against 163.2 us), 3072^3 1 against 1.17 (66.9 against 76.3).
+// 128 x 128 tiles run when they cost under 0.95 of the larger ones. Planned
+// for a full MI355X (256 CUs) whatever the device, so the choice, and the
+// rounding that follows from it, does not depend on partitioning.
+constexpr int64_t kTilePlanCus = 256;
 
-// A last round more than half full stays unsplit here (the fp32 kernel
-// splits it): cutting 3072^2 x 8192's 144 tiles into 5 K ranges each took it
-// from 168 to 231 us. Each range moves a 256 KB partial tile twice (370 MB for
-// that shape), and 144 busy CUs already run each tile faster than a full chip
-// does under the power limit.
+int tiled_tile(int64_t M, int64_t N) {
+    const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+    const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+    const double cost256 = (double)((t256 + kTilePlanCus - 1) / kTilePlanCus);
+    const int64_t full = t128 / (2 * kTilePlanCus), rem = t128 % (2 * kTilePlanCus);
+    const double cost128 = 0.635 * (double)full + (rem == 0 ? 0.0 : rem > kTilePlanCus ? 0.635 : 0.536);
+    return cost128 < 0.95 * cost256 ? 128 : 256;
+}
+
+// Split K (with a workspace) for 128 x 128 tiles only, when they leave most
+// CUs idle (fewer than half as many tiles as CUs, planned at one workgroup per
+// CU: a second workgroup on a CU only shares its matrix cores). The model
+// gives 256 x 256 tiles only to products with more than 128 of them, whose
+// last round is more than half full, where a split measured slower (3072^2 x
+// 8192's 144 tiles cut into 5 K ranges: 168 -> 231 us).
+// Each K range spans at least 16 slabs (1024 k): every range stores an fp32
+// partial tile and the tile's last range reads them all back, which only
+// ranges with that much MFMA work to save pay for.
+constexpr int kTiledMinSlabs = 16;
 constexpr double kTiledFixupSlabs = -1.0;
 
-TailSplit plan_tiled(int64_t M, int64_t N, int64_t K, int cus) {
-    const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
-    return plan_tail_split(tiles, (K + kBK - 1) / kBK, (int64_t)cus * kTiledSlotsPerCu,
-                           kTiledMinSlabs, kTiledFixupSlabs);
+TailSplit plan_tiled128(int64_t M, int64_t N, int64_t K, int cus) {
+    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    return plan_tail_split(tiles, (K + kBK - 1) / kBK, (int64_t)cus, kTiledMinSlabs, kTiledFixupSlabs);
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool EPI>
 hipError_t launch_cfg(const GemmArgs<uint16_t>& a, void* ws, size_t ws_bytes, int cus,
                       hipStream_t s) {
-    static_assert(BM == 256 && BN == 256, "plan_tiled assumes 256 x 256 tiles");
     const int64_t tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
     int tm = (int)tiles_m, tn = (int)tiles_n;
     GemmArgs<uint16_t> args = a;
-    TailSplit ts = plan_tiled(a.M, a.N, a.K, cus);
-    const bool split = ws != nullptr && ts.tail > 0 && ws_bytes >= tail_workspace(ts, BM, BN);
-    if (!split) ts = TailSplit{(int)(tiles_m * tiles_n), 0, 1, 0};
+    TailSplit ts = TailSplit{(int)(tiles_m * tiles_n), 0, 1, 0};
+    bool split = false;
+    if constexpr (BM == 128) {
+        const TailSplit plan = plan_tiled128(a.M, a.N, a.K, cus);
+        split = ws != nullptr && plan.tail > 0 && ws_bytes >= tail_workspace(plan, BM, BN);
+        if (split) ts = plan;
+    }
     unsigned char* wsp = split ? static_cast<unsigned char*>(ws) : nullptr;
     void* kargs[] = {&args, &tm, &tn, &ts, &wsp};
-    const void* fn = split ? pick_tiled<BM, BN, WAVES_M, WAVES_N, EPI, true>(a.ta, a.tb)
-                           : pick_tiled<BM, BN, WAVES_M, WAVES_N, EPI, false>(a.ta, a.tb);
+    const void* fn;
+    if constexpr (BM == 128)
+        fn = split ? pick_tiled<BM, BN, WAVES_M, WAVES_N, EPI, true>(a.ta, a.tb)
+                   : pick_tiled<BM, BN, WAVES_M, WAVES_N, EPI, false>(a.ta, a.tb);
+    else
+        fn = pick_tiled<BM, BN, WAVES_M, WAVES_N, EPI, false>(a.ta, a.tb);
     const int64_t grid = split ? (int64_t)ts.full + (int64_t)ts.tail * ts.parts : tiles_m * tiles_n;
     if (grid > kMaxGrid) return hipErrorInvalidConfiguration;
     return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(WAVES_M * WAVES_N * 64), kargs, 0, s);
@@ -641,13 +675,17 @@ hipError_t launch_cfg(const GemmArgs<uint16_t>& a, void* ws, size_t ws_bytes, in
 
 hipError_t launch_bf16_tiled(const GemmArgs<uint16_t>& a, void* ws, size_t ws_bytes, int cus,
                              hipStream_t s) {
+    if (tiled_tile(a.M, a.N) == 128) {
+        if (has_epilogue(a)) return launch_cfg<128, 128, 2, 2, true>(a, ws, ws_bytes, cus, s);
+        return launch_cfg<128, 128, 2, 2, false>(a, ws, ws_bytes, cus, s);
+    }
     if (has_epilogue(a)) return launch_cfg<256, 256, 2, 4, true>(a, ws, ws_bytes, cus, s);
     return launch_cfg<256, 256, 2, 4, false>(a, ws, ws_bytes, cus, s);
 }
 
 size_t bf16_tiled_workspace(int64_t M, int64_t N, int64_t K, int cus) {
-    if (M < 1 || N < 1 || K < 1) return 0;
-    return tail_workspace(plan_tiled(M, N, K, cus), 256, 256);
+    if (M < 1 || N < 1 || K < 1 || tiled_tile(M, N) != 128) return 0;
+    return tail_workspace(plan_tiled128(M, N, K, cus), 128, 128);
 }
 
 }  // namespace dg

@@ -157,8 +157,9 @@ def test_noalloc_checks_before_any_hip_call(lib):
     assert noalloc(4, 4, 4, 1.0, A, 3, B, 4, 0.0, C, 4, 0) == dg.GEMM_ERR_INVALID_VALUE
     assert noalloc(4, 4, 4, 1.0, A + 1, 4, B, 4, 0.0, C, 4, 0) == dg.GEMM_ERR_INVALID_VALUE
     assert noalloc(0, 4, 4, 1.0, None, 4, None, 4, 0.0, None, 4, 0) == dg.GEMM_OK
-    assert dg.gemm_bf16_workspace_size(512, 8192, 8192) > dg.NOALLOC_SCRATCH_BYTES
-    assert noalloc(512, 8192, 8192, 1.0, A, 8192, B, 8192, 0.0, C, 8192,
+    # 128 x 4352 x 8192: 17 strips x 16 phases of 128 x 256 fp32 partials.
+    assert dg.gemm_bf16_workspace_size(128, 4352, 8192) > dg.NOALLOC_SCRATCH_BYTES
+    assert noalloc(128, 4352, 8192, 1.0, A, 8192, B, 4352, 0.0, C, 4352,
                    0) == dg.GEMM_ERR_SCRATCH_LIMIT
     import torch
     if not torch.cuda.is_available():
@@ -219,7 +220,7 @@ def test_workspace_size(lib):
     # M > 128 is sized for the tiled kernel instead (see the next test); no
     # small-M split when strips already fill the GPU, one K chunk, empty or
     # invalid sizes.
-    assert dg.gemm_bf16_workspace_size(129, 8192, 8192) == 256 + 32 * 8 * 256 * 256 * 4
+    assert dg.gemm_bf16_workspace_size(129, 8192, 8192) == 512 + 128 * 2 * 128 * 128 * 4
     assert dg.gemm_bf16_workspace_size(16, 2048, 8192) > 0
     assert dg.gemm_bf16_workspace_size(16, 16384, 128) == 0
     assert dg.gemm_bf16_workspace_size(16, 64, 128) == 0
@@ -236,19 +237,22 @@ def test_workspace_size(lib):
 
 
 def test_tiled_workspace_size(lib):
-    # M > 128: the bf16 tiled kernel's split. 256 x 256 tiles, one workgroup
-    # per compute unit: a last round at most half full (of 256) is cut into
-    # up to 8 K ranges of at least 16 slabs of 64, each with a 256 KB fp32
-    # partial tile.
-    tile = 256 * 256 * 4
-    # 512 x 8192 x 8192: 64 tiles, 128 slabs -> 4 ranges each.
-    assert dg.gemm_bf16_workspace_size(512, 8192, 8192) == 256 + 64 * 4 * tile
-    # 2048^3: 64 tiles, 32 slabs -> 2 ranges.
-    assert dg.gemm_bf16_workspace_size(2048, 2048, 2048) == 256 + 64 * 2 * tile
-    # 129 x 1000 x 8200: 4 tiles, 129 slabs -> 8 ranges of 17 (the last 10).
-    assert dg.gemm_bf16_workspace_size(129, 1000, 8200) == 256 + 4 * 8 * tile
-    # No split: a full round (4096^2 = 256 tiles), a last round more than half
-    # full (3072^2 = 144 tiles: splitting it measured slower), fewer than 32 slabs.
+    # M > 128: the bf16 tiled kernel's split, for 128 x 128 tiles that leave
+    # most CUs idle: fewer than half as many tiles as CUs (256), cut into up to
+    # 8 K ranges of at least 16 slabs of 64, each with a 64 KB fp32 partial.
+    tile = 128 * 128 * 4
+    # 129 x 8192 x 8192: 128 tiles, 128 slabs -> 2 ranges.
+    assert dg.gemm_bf16_workspace_size(129, 8192, 8192) == 512 + 128 * 2 * tile
+    # 1024^2 x 4096: 64 tiles, 64 slabs -> 4 ranges; 512^2 x 4096: 16 tiles -> 4.
+    assert dg.gemm_bf16_workspace_size(1024, 1024, 4096) == 256 + 64 * 4 * tile
+    assert dg.gemm_bf16_workspace_size(512, 512, 4096) == 256 + 16 * 4 * tile
+    # 129 x 1000 x 8200: 16 tiles, 129 slabs -> 8 ranges of 17 (the last 10).
+    assert dg.gemm_bf16_workspace_size(129, 1000, 8200) == 256 + 16 * 8 * tile
+    # No split: one tile per CU already (512 x 8192 and 2048^2: 256 small
+    # tiles), products on 256 x 256 tiles (4096^2; 3072^2 and 3000^2, whose
+    # 144 large tiles beat 576 small ones), fewer than 32 slabs.
+    assert dg.gemm_bf16_workspace_size(512, 8192, 8192) == 0
+    assert dg.gemm_bf16_workspace_size(2048, 2048, 2048) == 0
     assert dg.gemm_bf16_workspace_size(4096, 4096, 4096) == 0
     assert dg.gemm_bf16_workspace_size(3072, 3072, 8192) == 0
     assert dg.gemm_bf16_workspace_size(3000, 3000, 3000) == 0

@@ -1,0 +1,99 @@
+"""The bf16 tiled kernel's two tile sizes, 256 x 256 (products with many
+tiles) and 128 x 128 (products with few), through the C ABI.
+
+* Both accumulate each output over K in the same order, so the first 512 rows
+  of a 4096-row product (256 x 256 tiles) must equal a 512-row product of the
+  same rows (128 x 128 tiles) bit for bit, in all four operand layouts, with
+  ragged N and K.
+* Ragged 256 x 256 tiles against the oracle in every layout, with the fused
+  bias + GELU epilogue and with quantisation scales (the smaller test shapes
+  elsewhere run on 128 x 128 tiles).
+* 128 x 128 tiles split over a workspace against the oracle.
+"""
+import pytest
+import torch
+
+import dense_gemm_04_amd as dg
+import gemm_inputs as gi
+import oracle
+from gpu_util import note, padded, to_f64, tol
+from test_transpose_gpu import check as check_op
+
+pytestmark = pytest.mark.gpu
+
+OPS = [(0, 0), (0, 1), (1, 0), (1, 1)]
+OP_IDS = ["NN", "NT", "TN", "TT"]
+
+
+def _store(X, trans):
+    S = X.t().contiguous() if trans else X
+    buf, view = padded(S.shape[0], S.shape[1], S.shape[1], "bf16", fill=float("nan"))
+    view.copy_(S.cuda())
+    return buf, view, S.shape[1]
+
+
+def _op(opa, opb, A, B):
+    M, K = A.shape
+    N = B.shape[1]
+    _, a, lda = _store(A, opa)
+    _, b, ldb = _store(B, opb)
+    c = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    st = dg.gemm_bf16_op(opa, opb, M, N, K, 1.0, a.data_ptr(), lda, b.data_ptr(), ldb, 0.0,
+                         c.data_ptr(), N, None, 0, None, 0, 0)
+    torch.cuda.synchronize()
+    assert st == dg.GEMM_OK, dg.gemm_status_string(st)
+    return c.cpu()
+
+
+@pytest.mark.parametrize("ops", OPS, ids=OP_IDS)
+def test_tile_sizes_give_the_same_bits(ops):
+    # 512 x 4000: 4 x 32 = 128 small tiles, one per CU (cost 0.536 against a
+    # round of 32 large ones); 4096 x 4000: 256 large tiles (cost 1 against
+    # 1.27 for 1024 small ones).
+    M_small, M_big, N, K = 512, 4096, 4000, 1000
+    A = gi.random_matrix(M_small, K, "bf16", 8300, dist="n")
+    B = gi.random_matrix(K, N, "bf16", 8301)
+    A_big = torch.zeros(M_big, K, dtype=A.dtype)
+    A_big[:M_small] = A
+    note(f"bf16 tile sizes {ops}: {M_small} and {M_big} rows, N={N} K={K}")
+    small = _op(ops[0], ops[1], A, B)
+    big = _op(ops[0], ops[1], A_big, B)
+    assert torch.equal(small.view(torch.int16), big[:M_small].view(torch.int16))
+    assert bool((big[M_small:].float() == 0).all())
+
+
+@pytest.mark.parametrize("ops", OPS, ids=OP_IDS)
+def test_large_tiles_ragged(ops):
+    # 4000 x 4000 x 136: 16 x 16 tiles of 256 x 256, the last row and column
+    # of tiles ragged, K of two slabs plus a tail.
+    check_op("bf16", ops[0], ops[1], 4000, 4000, 136, 8400 + 7 * ops[0] + ops[1], alpha=0.75,
+             beta=0.5, pad=(8, 8, 8))
+
+
+def test_large_tiles_ragged_bias_gelu():
+    check_op("bf16", 0, 0, 4000, 4000, 136, 8500, alpha=1.25, beta=1.0, bias=True, act="gelu_tanh")
+
+
+def test_large_tiles_ragged_scaled():
+    from test_scale_gpu import oracle_scaled, run_scaled, scales
+    M, N, K = 4000, 4000, 136
+    A = gi.random_matrix(M, K, "bf16", 8600, dist="n")
+    B = gi.random_matrix(K, N, "bf16", 8601)
+    C0 = gi.random_matrix(M, N, "bf16", 8602)
+    u, v = scales(M, 8603), scales(N, 8604)
+    bias = gi.random_matrix(1, N, "bf16", 8605)[0].contiguous()
+    note("bf16 large tiles, scaled with bias and ReLU")
+    C, st = run_scaled("bf16", A, B, C0, u, v, bias, "relu", 0.5, 1.0)
+    assert st == dg.GEMM_OK
+    R, D = oracle_scaled("bf16", A, B, C0, u, v, bias, "relu", 0.5, 1.0)
+    assert oracle.max_rel_err(to_f64(C), R, D) <= tol("bf16")
+
+
+# Small tiles split over a workspace: 64 tiles in 4 K ranges, 16 tiles of a
+# ragged product in 8.
+@pytest.mark.parametrize("shape", [(1024, 1024, 4096), (129, 1000, 8200)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_small_tiles_split(shape):
+    M, N, K = shape
+    assert dg.gemm_bf16_workspace_size(M, N, K) > 0
+    check_op("bf16", 0, 0, M, N, K, 8700 + M, alpha=1.0, beta=1.0, ws=True)

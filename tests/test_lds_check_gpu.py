@@ -10,8 +10,8 @@ normal build's results bit for bit, through the C ABI, on every pipeline:
     not landed, turns into NaN in C;
   * sync: every batch of copies completes before any wave reads LDS again,
     the order one staging buffer would impose.
-Cases cover the bf16 tiled kernel (several rounds of tiles, split-K tail,
-transposed layouts), the small-M copy rings (64-column and streaming, split
+Cases cover the bf16 tiled kernel (both tile sizes, several rounds of tiles,
+split-K tail, transposed layouts), the small-M copy rings (64-column and streaming, split
 and not), the element-wise and unaligned kernels, and the fp32 copy path
 (16-byte and 4-byte copies: tiles walked, transposed layouts, split-K
 tail), its register-staged path and the vector-FMA kernel, at ragged shapes. A second test repeats each
@@ -77,7 +77,9 @@ def run(lib, dtype, A, B, C0, alpha, beta, ops=(0, 0), pad=(0, 0, 0), ws=False, 
 
 # (dtype, (M, N, K), ld_pad, ops, workspace, forced variant)
 CASES = [
-    ("bf16", (4360, 4104, 200), (0, 0, 0), (0, 0), False, None),   # tiled, 306 tiles: two rounds
+    ("bf16", (4360, 4104, 200), (0, 0, 0), (0, 0), False, None),   # tiled, 1155 small tiles: three rounds
+    ("bf16", (4000, 4000, 200), (0, 0, 0), (0, 0), False, None),   # tiled, 256 large tiles, ragged
+    ("bf16", (4000, 4000, 136), (8, 8, 8), (1, 1), False, None),   # large tiles, both transposed, padded
     ("bf16", (520, 520, 4100), (0, 0, 0), (0, 0), True, None),     # tiled split-K tail, ragged K
     ("bf16", (300, 264, 200), (0, 0, 0), (1, 0), False, None),     # tiled, A stored K x M
     ("bf16", (300, 264, 200), (0, 0, 0), (0, 1), False, None),     # tiled, B stored N x K (M > 128)

@@ -44,8 +44,8 @@ def _run(fn_name, A, B, C0, alpha, beta):
 
 # Consecutive calls on the one scratch: the largest streaming split (128
 # rows, 32 MiB), then smaller ones (streaming split, the 64-column split with
-# 64-row tiles, the tiled kernel's split for M > 128, and a shape that does
-# not split).
+# 64-row tiles, the tiled kernel's split for M > 128 on 128 x 128 tiles, and a
+# shape that does not split).
 SEQUENCE = [((128, 8192, 8192), 1.0, 0.0), ((16, 8192, 8192), 1.0, 0.0), ((16, 4352, 1000), 0.5, 2.0),
             ((40, 1032, 4104), 1.0, 1.0), ((512, 2048, 4096), 1.0, 0.0),
             ((16, 16384, 128), 1.0, 0.0)]
@@ -78,9 +78,9 @@ def test_noalloc_repeat_is_bitwise_stable():
 
 
 def test_noalloc_rejects_shapes_beyond_the_scratch():
-    # 512 x 8192 x 8192: 64 tiles of 256 x 256, each cut into 4 K ranges of
-    # 256 KB fp32 partials: 64 MiB, past the 32 MiB scratch.
-    M, N, K = 512, 8192, 8192
+    # 128 x 4352 x 8192: 17 strips of 256 columns, K interleaved over 16
+    # phases, each phase a 128 x 256 fp32 partial: 34 MiB, past the scratch.
+    M, N, K = 128, 4352, 8192
     need = dg.gemm_bf16_workspace_size(M, N, K)
     assert need > dg.NOALLOC_SCRATCH_BYTES
     a = torch.zeros(M, K, dtype=torch.bfloat16, device="cuda")
