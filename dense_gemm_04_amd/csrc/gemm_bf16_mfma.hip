@@ -351,9 +351,19 @@ hipError_t launch_bf16_general(const GemmArgs<uint16_t>& a, bool vec, hipStream_
     return launch_tiles<256, 256, 2, 2>(a, vec, s);
 }
 
+// Rows (and bases) of A, B and C aligned to 4 bytes: even leading dimensions.
+static bool rows_4byte(const GemmArgs<uint16_t>& a) {
+    auto al = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 3) == 0; };
+    return al(a.A) && al(a.B) && al(a.C) && a.lda % 2 == 0 && a.ldb % 2 == 0 && a.ldc % 2 == 0;
+}
+
 hipError_t launch_bf16_mfma(const GemmArgs<uint16_t>& a, bool vec, void* ws, size_t ws_bytes,
                             int cus, hipStream_t s) {
-    if (vec && bf16_tiled_fits(a)) return launch_bf16_tiled(a, ws, ws_bytes, cus, s);
+    // 16-byte rows take the tiled kernel's 1 KB copies, 4-byte rows its
+    // 4-byte ones; other rows, and offsets past its 31-bit range, the
+    // element-wise kernel.
+    if (bf16_tiled_fits(a) && (vec || rows_4byte(a)))
+        return launch_bf16_tiled(a, !vec, ws, ws_bytes, cus, s);
     return launch_bf16_general(a, vec, s);
 }
 

@@ -1,9 +1,11 @@
 // bf16 GEMM on gfx950 matrix cores, vector path: C = alpha * A * B + beta * C,
 // row-major, fp32 accumulation, one rounding to bf16 at the end.
 //
-// Used when A, B and C rows are 16-byte aligned (the common case, and every
-// workload shape of interest). The element-wise kernel in gemm_bf16_mfma.hip
-// covers everything else.
+// Used when A, B and C rows are 4-byte aligned: with 16-byte rows (the
+// common case, and every workload shape of interest) slabs move in 1 KB
+// copies, with rows aligned to 4 bytes only (DW: even leading dimensions) in
+// 256-byte ones, into the same LDS layouts. The element-wise kernel in
+// gemm_bf16_mfma.hip covers everything else.
 //
 // Tiling (the shared-memory tiling, float4 loads, register blocking and
 // double buffering of the RTX 3090 SGEMM article, sections 3-5, and the
@@ -52,6 +54,8 @@
 // X(row p, k = 8g .. 8g+7) as its first operand and Y(k = 8g .. 8g+7, col p)
 // as its second, and receives D(row 4g + r, col p) in register r. A and B use
 // the same k assignment, so the hardware's internal pairing does not matter.
+
+#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -109,7 +113,8 @@ __device__ __forceinline__ int opaque_lane() {
 // ws (only with SPLIT and ts.tail > 0): [counters: one int per split tile,
 // padded to 256 bytes][slots: tail x parts partial tiles of BM x BN fp32,
 // value c of thread t at byte (c * threads + t) * 16 of its slot].
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool EPI, bool TA, bool TB, bool SPLIT>
+// DW: A, B and C rows (and bases) are aligned to 4 bytes, not 16.
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool EPI, bool TA, bool TB, bool SPLIT, bool DW>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64, BM == 128 ? 2 : 1)
 void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, TailSplit ts,
                             unsigned char* ws) {
@@ -121,10 +126,13 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, Tail
     constexpr int kAStage = BM * kBK;                         // bf16 elements
     constexpr int kBStage = kBK * BN;
     // Only the first wave of each SIMD (waves 0 .. kWaves / 2 - 1 with two
-    // waves per SIMD) issues the slab copies: a burst of copies fills the
-    // texture unit's queue and stalls the issuing wave, and the other wave on
-    // the SIMD keeps the matrix core busy meanwhile.
-    constexpr int kDmaWaves = kWaves / 2;
+    // waves per SIMD) issues the 1 KB slab copies: a burst of copies fills
+    // the texture unit's queue and stalls the issuing wave, and the other wave
+    // on the SIMD keeps the matrix core busy meanwhile. The 4-byte copies are
+    // four times as many instructions, and every wave shares them (4096^3
+    // with 4100-element rows: 140 against 130 us; 512 x 8192 x 8192: 190
+    // against 131 us).
+    constexpr int kDmaWaves = DW ? kWaves : kWaves / 2;
     constexpr int kACopies = kAStage * 2 / 1024 / kDmaWaves;  // 1 KB LDS copies per issuing wave
     constexpr int kBCopies = kBStage * 2 / 1024 / kDmaWaves;
     constexpr int kBRowsPerCopy = 1024 / (BN * 2);            // rows of a [64][BN] slab per copy
@@ -170,12 +178,15 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, Tail
     // stays in its page). Rows past M therefore arrive in LDS as zeros. The
     // same for a transposed B (rows n0 .. of the N x K storage). Each is dead
     // code when its operand is not k-contiguous.
+    // With 4-byte copies the end is rounded up to a 4-byte word instead
+    // (the base is only 4-byte aligned).
+    constexpr int64_t kRnd = DW ? 3 : 15;
     const int64_t rows_a = (M - m0 < kBM) ? M - m0 : kBM;
     (void)kNT;
-    const uint32_t a_bytes = (uint32_t)((((rows_a - 1) * lda + K) * 2 + 15) & ~(int64_t)15);
+    const uint32_t a_bytes = (uint32_t)((((rows_a - 1) * lda + K) * 2 + kRnd) & ~kRnd);
     const rsrc_t a_desc = make_rsrc(p.A + m0 * lda, a_bytes);
     const int64_t rows_bt = (N - n0 < kBN) ? N - n0 : kBN;
-    const uint32_t bt_bytes = (uint32_t)((((rows_bt - 1) * ldb + K) * 2 + 15) & ~(int64_t)15);
+    const uint32_t bt_bytes = (uint32_t)((((rows_bt - 1) * ldb + K) * 2 + kRnd) & ~kRnd);
     const rsrc_t bt_desc = make_rsrc(p.B + n0 * ldb, bt_bytes);
 
     // Global -> LDS copies. One buffer_load_dwordx4 ... lds moves 1 KB: lane l
@@ -186,13 +197,80 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, Tail
     //   m/n-contiguous slab ([64][R], row-major B or transposed A): copy I
     //      fills rows Q I .. Q I + Q - 1 (Q = 1024 / row bytes); lane -> row
     //      Q I + l / (64 / Q).
+    //
+    // 4-byte copies (DW): sub-copy s (0 .. 3) of 1 KB copy I fills LDS bytes
+    // 1024 I + 256 s .. + 255, lane l the 4 bytes at 4 l of them, in the same
+    // swizzled layouts.
+    //   k-contiguous tile: rows 8 I + 2 s + h (h = l / 32), physical chunk
+    //      (l / 4) mod 8, which holds logical chunk (l / 4) mod 8 ^ (2 s + h)
+    //      of the row (its row mod 8 is 2 s + h): in-row byte
+    //      ((4 l) mod 128 ^ 16 h) ^ 32 s.
+    //   m/n-contiguous slab (rows of BN elements; a transposed A has BM == BN):
+    //      slab byte b = 1024 I + 256 s lies in row b / 2BN at in-row byte
+    //      b mod 2BN + 4 l, whose chunk index is XOR-ed with the row's swizzle:
+    //      in-row byte 4 l ^ x with x = b mod 2BN ^ 16 b_swz(row), the same
+    //      for every lane.
+    // The lane offsets come from an opaque copy of the lane index (see the
+    // transposed copies below), and the row stride and LDS base pass through
+    // an empty asm statement, so that the per-copy scalar offsets are formed
+    // at each slab instead of being hoisted out of the K loop, where they
+    // would not fit in scalar registers.
+    auto dw_kc = [&](int ln, rsrc_t desc, int64_t ld, int I, int64_t k0, uint32_t dst) __attribute__((always_inline)) {
+        const int h = ln >> 5;
+        uint32_t ld2 = (uint32_t)(ld * 2), base = dst + I * 1024;
+        asm volatile("" : "+s"(ld2), "+s"(base));
+        const uint32_t rowb = (uint32_t)h * ld2;
+        const uint32_t in0 = (uint32_t)(((4 * ln) & 127) ^ (h << 4));
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            dma4(desc, rowb + (in0 ^ (uint32_t)(32 * s)),
+                 (uint32_t)(8 * I + 2 * s) * ld2 + (uint32_t)(k0 * 2), base + s * 256);
+    };
+    auto dw_mn = [&](int ln, rsrc_t desc, int64_t ld, int I, uint32_t dst) __attribute__((always_inline)) {
+        const uint32_t l4 = (uint32_t)(4 * ln);
+        uint32_t ld2 = (uint32_t)(ld * 2), base = dst;
+        asm volatile("" : "+s"(ld2), "+s"(base));
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int b = 1024 * I + 256 * s;
+            const int row = b / (2 * kBN);
+            const uint32_t x = (uint32_t)((b % (2 * kBN)) ^ (b_swz<kBN>(row) << 4));
+            dma4(desc, l4 ^ x, (uint32_t)row * ld2, base + b);
+        }
+    };
     const int a_lrow = lane >> 3, a_pos = lane & 7;
     const int b_lrow = lane / (64 / kBRowsPerCopy), b_pos = lane % (64 / kBRowsPerCopy);
-    auto dma = [&](int64_t kt, int stage) {
+    // Inlined at each call site: an out-of-line copy routine would read its
+    // captured descriptors and offsets back from per-lane stack memory.
+    auto dma = [&](int64_t kt, int stage) __attribute__((always_inline)) {
         if (wave >= kDmaWaves) return;
         const int64_t k0 = kt * kBK;
         const uint32_t As = lds_addr(a_stage(stage));
         const uint32_t Bs = lds_addr(b_stage(stage));
+        if constexpr (DW) {
+            const int ln = opaque_lane();
+            if constexpr (!TA) {
+#pragma unroll
+                for (int i = 0; i < kACopies; ++i) dw_kc(ln, a_desc, lda, wave * kACopies + i, k0, As);
+            } else {
+                const int64_t rem = (((K - k0 - 1) * lda + (M - m0)) * 2 + kRnd) & ~kRnd;
+                const uint32_t bytes = rem < ((int64_t)1 << 31) ? (uint32_t)rem : 0x80000000u;
+                const rsrc_t desc = make_rsrc(p.A + k0 * lda + m0, bytes);
+#pragma unroll
+                for (int i = 0; i < kACopies; ++i) dw_mn(ln, desc, lda, wave * kACopies + i, As);
+            }
+            if constexpr (!TB) {
+                const int64_t rem = (((K - k0 - 1) * ldb + (N - n0)) * 2 + kRnd) & ~kRnd;
+                const uint32_t bytes = rem < ((int64_t)1 << 31) ? (uint32_t)rem : 0x80000000u;
+                const rsrc_t desc = make_rsrc(p.B + k0 * ldb + n0, bytes);
+#pragma unroll
+                for (int i = 0; i < kBCopies; ++i) dw_mn(ln, desc, ldb, wave * kBCopies + i, Bs);
+            } else {
+#pragma unroll
+                for (int i = 0; i < kBCopies; ++i) dw_kc(ln, bt_desc, ldb, wave * kBCopies + i, k0, Bs);
+            }
+            return;
+        }
         if constexpr (!TA) {
 #pragma unroll
             for (int i = 0; i < kACopies; ++i) {
@@ -471,13 +549,16 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, Tail
                 bv8[e] = bias_at(p, gcol + e);
             }
         }
+        // C rows aligned to 4 bytes only (DW): the same 128-bit accesses at
+        // 4-byte alignment.
+        using cvec = std::conditional_t<DW, u32x4_a4, u32x4>;
         u32x4 c0q[kFM][2];
         if (beta != 0.f) {
 #pragma unroll
             for (int i = 0; i < kFM; ++i)
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
-                    c0q[i][h] = *reinterpret_cast<const u32x4*>(
+                    c0q[i][h] = *reinterpret_cast<const cvec*>(
                         p.C + (m0 + wm0 + 16 * i + rr + 8 * h) * p.ldc + gcol);
         }
         // Every wave has read its last fragments: the stages are free.
@@ -509,7 +590,7 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, Tail
                     for (int e = 0; e < 8; ++e)
                         v[e] += beta * bf16_to_f32((uint16_t)(c0q[i][h][e >> 1] >> (16 * (e & 1))));
                 }
-                *reinterpret_cast<u32x4*>(p.C + grow * p.ldc + gcol) =
+                *reinterpret_cast<cvec*>(p.C + grow * p.ldc + gcol) =
                     u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
                           pack_bf16x2(v[6], v[7])};
             }
@@ -530,6 +611,7 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, Tail
     // store. The stores could alias later loads, so the compiler would
     // otherwise wait out one memory round trip per 4 columns of a row. The
     // fragment registers are dead here, which leaves room for the 64 values.
+    using cvec2 = std::conditional_t<DW, u32x2_a4, u32x2>;
     u32x2 cpre[kFM][kFN];
     if (beta != 0.f) {
 #pragma unroll
@@ -539,7 +621,7 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, Tail
             for (int j = 0; j < kFN; ++j) {
                 const int64_t col = n0 + wn0 + 16 * j + 4 * g;
                 cpre[i][j] = (row < M && col + 4 <= N)
-                                 ? *reinterpret_cast<const u32x2*>(p.C + row * p.ldc + col)
+                                 ? *reinterpret_cast<const cvec2*>(p.C + row * p.ldc + col)
                                  : u32x2{0u, 0u};
             }
         }
@@ -561,7 +643,7 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, Tail
                 for (int r = 0; r < 4; ++r) v[r] = activate(v[r] * cv[j][r] + bv[j][r], p.act);
             }
             if (col + 4 <= N) {
-                u32x2* dst = reinterpret_cast<u32x2*>(crow + col);
+                cvec2* dst = reinterpret_cast<cvec2*>(crow + col);
                 if (beta != 0.f) {
                     const u32x2 c0 = cpre[i][j];
 #pragma unroll
@@ -595,13 +677,19 @@ bool bf16_tiled_fits(const GemmArgs<uint16_t>& a) {
     return (a.ta ? mc(a.lda, a.M) : kc(a.lda)) && (a.tb ? kc(a.ldb) : mc(a.ldb, a.N));
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool EPI, bool SPLIT>
-const void* pick_tiled(bool ta, bool tb) {
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool EPI, bool SPLIT, bool DW>
+const void* pick_layout(bool ta, bool tb) {
 #define DG_TILED(TA, TB) \
-    (const void*)&gemm_bf16_tiled_kernel<BM, BN, WAVES_M, WAVES_N, EPI, TA, TB, SPLIT>
+    (const void*)&gemm_bf16_tiled_kernel<BM, BN, WAVES_M, WAVES_N, EPI, TA, TB, SPLIT, DW>
     return ta ? (tb ? DG_TILED(true, true) : DG_TILED(true, false))
               : (tb ? DG_TILED(false, true) : DG_TILED(false, false));
 #undef DG_TILED
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool EPI, bool SPLIT>
+const void* pick_tiled(bool ta, bool tb, bool dw) {
+    return dw ? pick_layout<BM, BN, WAVES_M, WAVES_N, EPI, SPLIT, true>(ta, tb)
+              : pick_layout<BM, BN, WAVES_M, WAVES_N, EPI, SPLIT, false>(ta, tb);
 }
 
 // Two tile sizes: 256 x 256 (8 waves of 128 x 64, 128 KB of LDS, one
@@ -648,7 +736,7 @@ TailSplit plan_tiled128(int64_t M, int64_t N, int64_t K, int cus) {
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool EPI>
-hipError_t launch_cfg(const GemmArgs<uint16_t>& a, void* ws, size_t ws_bytes, int cus,
+hipError_t launch_cfg(const GemmArgs<uint16_t>& a, bool dw, void* ws, size_t ws_bytes, int cus,
                       hipStream_t s) {
     const int64_t tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
     int tm = (int)tiles_m, tn = (int)tiles_n;
@@ -664,23 +752,23 @@ hipError_t launch_cfg(const GemmArgs<uint16_t>& a, void* ws, size_t ws_bytes, in
     void* kargs[] = {&args, &tm, &tn, &ts, &wsp};
     const void* fn;
     if constexpr (BM == 128)
-        fn = split ? pick_tiled<BM, BN, WAVES_M, WAVES_N, EPI, true>(a.ta, a.tb)
-                   : pick_tiled<BM, BN, WAVES_M, WAVES_N, EPI, false>(a.ta, a.tb);
+        fn = split ? pick_tiled<BM, BN, WAVES_M, WAVES_N, EPI, true>(a.ta, a.tb, dw)
+                   : pick_tiled<BM, BN, WAVES_M, WAVES_N, EPI, false>(a.ta, a.tb, dw);
     else
-        fn = pick_tiled<BM, BN, WAVES_M, WAVES_N, EPI, false>(a.ta, a.tb);
+        fn = pick_tiled<BM, BN, WAVES_M, WAVES_N, EPI, false>(a.ta, a.tb, dw);
     const int64_t grid = split ? (int64_t)ts.full + (int64_t)ts.tail * ts.parts : tiles_m * tiles_n;
     if (grid > kMaxGrid) return hipErrorInvalidConfiguration;
     return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(WAVES_M * WAVES_N * 64), kargs, 0, s);
 }
 
-hipError_t launch_bf16_tiled(const GemmArgs<uint16_t>& a, void* ws, size_t ws_bytes, int cus,
-                             hipStream_t s) {
+hipError_t launch_bf16_tiled(const GemmArgs<uint16_t>& a, bool dw, void* ws, size_t ws_bytes,
+                             int cus, hipStream_t s) {
     if (tiled_tile(a.M, a.N) == 128) {
-        if (has_epilogue(a)) return launch_cfg<128, 128, 2, 2, true>(a, ws, ws_bytes, cus, s);
-        return launch_cfg<128, 128, 2, 2, false>(a, ws, ws_bytes, cus, s);
+        if (has_epilogue(a)) return launch_cfg<128, 128, 2, 2, true>(a, dw, ws, ws_bytes, cus, s);
+        return launch_cfg<128, 128, 2, 2, false>(a, dw, ws, ws_bytes, cus, s);
     }
-    if (has_epilogue(a)) return launch_cfg<256, 256, 2, 4, true>(a, ws, ws_bytes, cus, s);
-    return launch_cfg<256, 256, 2, 4, false>(a, ws, ws_bytes, cus, s);
+    if (has_epilogue(a)) return launch_cfg<256, 256, 2, 4, true>(a, dw, ws, ws_bytes, cus, s);
+    return launch_cfg<256, 256, 2, 4, false>(a, dw, ws, ws_bytes, cus, s);
 }
 
 size_t bf16_tiled_workspace(int64_t M, int64_t N, int64_t K, int cus) {

@@ -11,9 +11,10 @@ namespace dg {
 // Every launcher runs the epilogue instantiation of its kernel when the
 // arguments carry a bias or an activation (has_epilogue).
 //
-// `vec` selects 128-bit global loads/stores; the caller guarantees 16-byte
-// aligned base pointers and leading dimensions that keep every row 16-byte
-// aligned. Without it every global access is element-wise.
+// `vec` tells a launcher that every base pointer and row is 16-byte aligned
+// (128-bit copies and accesses). Without it each launcher takes the widest
+// accesses the actual alignment allows: 4-byte copies for rows aligned to 4
+// bytes, unaligned 128-bit or element-wise accesses otherwise.
 //
 // Workspace arguments (ws may be null): given at least the bytes the matching
 // *_workspace function returns for the shape (256-byte aligned, counters
@@ -21,11 +22,12 @@ namespace dg {
 // most of the `cus` compute units idle; otherwise it runs unsplit.
 hipError_t launch_bf16_mfma(const GemmArgs<uint16_t>& a, bool vec, void* ws, size_t ws_bytes,
                             int cus, hipStream_t s);
-// The two bf16 MFMA kernels behind launch_bf16_mfma: the tiled vector kernel
-// (needs `vec` and offsets that fit its 31-bit buffer offsets; splits K with
-// a workspace) and the element-wise one that takes any alignment.
-hipError_t launch_bf16_tiled(const GemmArgs<uint16_t>& a, void* ws, size_t ws_bytes, int cus,
-                             hipStream_t s);
+// The two bf16 MFMA kernels behind launch_bf16_mfma: the tiled kernel (needs
+// rows aligned to 16 bytes, or to 4 with `dw`, and offsets that fit its 31-bit
+// buffer offsets; splits K with a workspace) and the element-wise one that
+// takes any alignment.
+hipError_t launch_bf16_tiled(const GemmArgs<uint16_t>& a, bool dw, void* ws, size_t ws_bytes,
+                             int cus, hipStream_t s);
 size_t bf16_tiled_workspace(int64_t M, int64_t N, int64_t K, int cus);
 bool bf16_tiled_fits(const GemmArgs<uint16_t>& a);
 hipError_t launch_bf16_general(const GemmArgs<uint16_t>& a, bool vec, hipStream_t s);

@@ -87,9 +87,15 @@ typedef enum {
     /* LDS-tiled MFMA kernel with 128-bit global loads; needs every pointer
      * 16-byte aligned and lda, ldb, ldc multiples of 16 bytes / element size. */
     GEMM_VARIANT_MFMA = 1,
-    /* The same MFMA tiling with element-wise global loads and stores: any
-     * alignment and leading dimension (RTX 3090 SGEMM article, section 6.2:
-     * a scalar fallback when float4 alignment does not hold). */
+    /* The MFMA kernels for rows that are not 16-byte aligned (RTX 3090 SGEMM
+     * article, section 6.2: a fallback when float4 alignment does not hold);
+     * any alignment and leading dimension. Where every base and row is
+     * 4-byte aligned (always for fp32; bf16 with even lda, ldb, ldc) the
+     * tiles of GEMM_VARIANT_MFMA are filled by 4-byte copies; otherwise (bf16
+     * with an odd leading dimension or base) a kernel with unaligned 128-bit
+     * and element-wise loads runs. Leading dimensions past the copies' 31-bit
+     * offset range load through registers. AUTO picks this family whenever
+     * the rows are not 16-byte aligned. */
     GEMM_VARIANT_GENERAL = 2,
     /* fp32 only: vector-FMA (non-matrix-core) kernel with per-thread register
      * micro-tiles, kept as a measured comparison (same article, sections 5.1-5.3). */

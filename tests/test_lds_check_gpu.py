@@ -11,7 +11,7 @@ normal build's results bit for bit, through the C ABI, on every pipeline:
   * sync: every batch of copies completes before any wave reads LDS again,
     the order one staging buffer would impose.
 Cases cover the bf16 tiled kernel (both tile sizes, several rounds of tiles,
-split-K tail, transposed layouts), the small-M copy rings (64-column and streaming, split
+split-K tail, transposed layouts, 16-byte and 4-byte copies), the small-M copy rings (64-column and streaming, split
 and not), the element-wise and unaligned kernels, and the fp32 copy path
 (16-byte and 4-byte copies: tiles walked, transposed layouts, split-K
 tail), its register-staged path and the vector-FMA kernel, at ragged shapes. A second test repeats each
@@ -92,6 +92,11 @@ CASES = [
     ("bf16", (33, 4104, 300), (8, 8, 8), (0, 0), True, None),      # streaming split, padded
     ("bf16", (5, 100, 77), (1, 1, 1), (0, 0), False, None),        # small-M element-wise
     ("bf16", (130, 200, 129), (1, 3, 5), (0, 0), False, None),     # unaligned rows
+    ("bf16", (4000, 4000, 200), (2, 2, 2), (0, 0), False, None),   # 4-byte copies, large tiles
+    ("bf16", (300, 264, 200), (2, 2, 2), (1, 1), False, None),     # 4-byte copies, both transposed
+    ("bf16", (300, 264, 129), (2, 2, 2), (1, 0), False, None),     # 4-byte copies, A stored K x M
+    ("bf16", (300, 264, 129), (1, 3, 2), (0, 1), False, None),     # 4-byte copies, B stored N x K
+    ("bf16", (520, 522, 4100), (2, 0, 0), (0, 0), True, None),     # 4-byte copies, split K
     ("f32", (3000, 2900, 72), (0, 0, 0), (0, 0), False, None),     # copy path, 552 tiles walked
     ("f32", (2100, 2000, 100), (0, 0, 0), (1, 0), False, None),    # copy path, A stored K x M
     ("f32", (2100, 2000, 100), (0, 0, 0), (0, 1), False, None),    # copy path, B stored N x K

@@ -94,7 +94,8 @@ def test_bf16_small_m_up_to_128(M, NK):
 @pytest.mark.parametrize("M", [33, 64, 128])
 def test_bf16_small_m_wide_unaligned_falls_back(M):
     # Rows that are not 16-byte aligned: the element-wise small-M kernel stops
-    # at 32 rows, so these run on the unaligned tiled kernel.
+    # at 32 rows, so these run on the tiled kernels (4-byte copies for even
+    # leading dimensions, the unaligned kernel for odd ones).
     assert dg.gemm_plan(2, M, 200, 1100, 1.0, 4096, 1100, 8192, 200, 0.0, 16384, 200,
                         dg.VARIANT_AUTO) == dg.VARIANT_GENERAL
     check("bf16", M, 200, 1100, 1.0, 1.0, dg.VARIANT_AUTO, 950 + M)
