@@ -12,8 +12,9 @@
 // asynchronous load/compute pipelining of the Blackwell BF16 GEMM notes,
 // section 2.3, re-planned for CDNA4):
 //   * one workgroup of 8 waves (2 x 4, each a 128 x 64 block of C) per
-//     256 x 256 tile, tiles renumbered per XCD and rastered in groups of 4
-//     tile rows for L2 reuse;
+//     256 x 256 tile (or of 8 waves of 64 x 32 per 128 x 128 tile, for
+//     products with few large tiles), tiles renumbered per XCD and rastered
+//     in groups of 4 tile rows for L2 reuse;
 //   * K in slabs of 64 held in two LDS stages. Slabs move from global memory
 //     straight into LDS with LDS-destined 128-bit buffer loads (no register
 //     round trip), two slabs ahead of the MFMAs; one barrier per slab
@@ -114,8 +115,11 @@ __device__ __forceinline__ int opaque_lane() {
 // padded to 256 bytes][slots: tail x parts partial tiles of BM x BN fp32,
 // value c of thread t at byte (c * threads + t) * 16 of its slot].
 // DW: A, B and C rows (and bases) are aligned to 4 bytes, not 16.
+// The second bound is waves per SIMD: 128 x 128 tiles run two workgroups of
+// 8 waves per CU (at most 128 VGPRs) unless split over a workspace, which
+// only happens when the split workgroups fit one per CU.
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool EPI, bool TA, bool TB, bool SPLIT, bool DW>
-__global__ __launch_bounds__(WAVES_M * WAVES_N * 64, BM == 128 ? 2 : 1)
+__global__ __launch_bounds__(WAVES_M * WAVES_N * 64, BM == 128 && !SPLIT ? 4 : 2)
 void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, TailSplit ts,
                             unsigned char* ws) {
     constexpr int kNT = WAVES_M * WAVES_N * 64;
@@ -528,18 +532,24 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, Tail
     // With EPI, the product is also scaled by the row's and the column's
     // quantisation scale (row_factor folds the row scale into alpha).
     const float alpha = p.alpha, beta = p.beta;
-    static_assert(kWTN == 64 && kFM * 16 == kWTM, "the row-order epilogue covers 64-column wave tiles");
+    if constexpr (kWTN == 64 || kWTN == 32) {
     if (m0 + kBM <= M && n0 + kBN <= N) {
         // Whole tiles: C is read and written 16 bytes (8 columns) per lane
-        // and instruction, 8 rows of 128 bytes per wave instruction, instead
-        // of the 4 columns a lane holds after the MFMAs (16 rows of 32 bytes
+        // and instruction, 8 rows of 128 bytes (64-column wave tiles) or 16
+        // rows of 64 bytes (32-column ones) per wave instruction, instead of
+        // the 4 columns a lane holds after the MFMAs (16 rows of 32 bytes
         // per instruction): the projection with beta = 1 ran 685 against
-        // 646 us in a copy with this access pattern. Each 16-row block of a
-        // wave's results goes through a wave-private LDS scratch (rows padded
-        // to 68 floats: the 128-bit writes and reads are conflict-free) into
-        // row order. Lane l takes columns 8 (l mod 8) .. + 7 of rows l / 8 and
-        // l / 8 + 8 of each block. The arithmetic is the same as below.
-        const int cc = lane & 7, rr = lane >> 3;
+        // 646 us in a copy with this access pattern, 2560^3 with beta = 1 on
+        // 128 x 128 tiles 40.8 against 36.4 us. Each 16-row block of a wave's
+        // results goes through a wave-private LDS scratch (rows padded by 4
+        // floats: with 64-column tiles the 128-bit writes and reads measure
+        // conflict-free) into row order. Lane l takes columns
+        // 8 (l mod kLpr) .. + 7 of rows l / kLpr + kRpp h of each block. The
+        // arithmetic is the same as below.
+        constexpr int kLpr = kWTN / 8;             // lanes per row (8 columns each)
+        constexpr int kRpp = 64 / kLpr;            // rows per pass
+        constexpr int kPasses = 16 / kRpp;
+        const int cc = lane % kLpr, rr = lane / kLpr;
         const int64_t gcol = n0 + wn0 + 8 * cc;
         float cf8[8], bv8[8];
         if constexpr (EPI) {
@@ -552,18 +562,18 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, Tail
         // C rows aligned to 4 bytes only (DW): the same 128-bit accesses at
         // 4-byte alignment.
         using cvec = std::conditional_t<DW, u32x4_a4, u32x4>;
-        u32x4 c0q[kFM][2];
+        u32x4 c0q[kFM][kPasses];
         if (beta != 0.f) {
 #pragma unroll
             for (int i = 0; i < kFM; ++i)
 #pragma unroll
-                for (int h = 0; h < 2; ++h)
+                for (int h = 0; h < kPasses; ++h)
                     c0q[i][h] = *reinterpret_cast<const cvec*>(
-                        p.C + (m0 + wm0 + 16 * i + rr + 8 * h) * p.ldc + gcol);
+                        p.C + (m0 + wm0 + 16 * i + rr + kRpp * h) * p.ldc + gcol);
         }
         // Every wave has read its last fragments: the stages are free.
         lds_only_barrier();
-        constexpr int kScrLd = 68, kScrPerStage = kWaves / 2;
+        constexpr int kScrLd = kWTN + 4, kScrPerStage = kWaves / 2;
         static_assert(kScrPerStage * 16 * kScrLd * 4 <= kAStage * 2, "half the wave scratches per A stage");
         float* scr = reinterpret_cast<float*>(wave < kScrPerStage ? a_st0 : a_st1) +
                      (wave % kScrPerStage) * 16 * kScrLd;
@@ -573,8 +583,8 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, Tail
             for (int j = 0; j < kFN; ++j)
                 *reinterpret_cast<f32x4*>(scr + pl * kScrLd + 16 * j + 4 * g) = acc[j][i];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int row = rr + 8 * h;
+            for (int h = 0; h < kPasses; ++h) {
+                const int row = rr + kRpp * h;
                 const f32x4 lo = *reinterpret_cast<const f32x4*>(scr + row * kScrLd + 8 * cc);
                 const f32x4 hi = *reinterpret_cast<const f32x4*>(scr + row * kScrLd + 8 * cc + 4);
                 const int64_t grow = m0 + wm0 + 16 * i + row;
@@ -596,6 +606,7 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, Tail
             }
         }
         return;
+    }
     }
     float bv[kFN][4], cv[kFN][4];
     if constexpr (EPI) {
@@ -693,17 +704,20 @@ const void* pick_tiled(bool ta, bool tb, bool dw) {
 }
 
 // Two tile sizes: 256 x 256 (8 waves of 128 x 64, 128 KB of LDS, one
-// workgroup per CU) and 128 x 128 (4 waves of 64 x 64, 64 KB, two per CU).
-// The smaller tile multiplies less per byte it stages (79% of the larger
-// one's rate at full occupancy: 4096^3 138.8 against 109.3 us) but gives four
-// times the workgroups, which products with few 256 x 256 tiles need
-// (512 x 8192 x 8192: 64 such tiles, 161.7 us; 256 of 128 x 128, 86.7 us).
+// workgroup per CU) and 128 x 128 (8 waves of 64 x 32, 64 KB, two per CU).
+// The smaller tile multiplies less per byte it stages (4096^3: 127.5 against
+// 103.3 us) but gives four times the workgroups, which products with few
+// 256 x 256 tiles need (512 x 8192 x 8192: 64 such tiles, 162.2 us; 256 of
+// 128 x 128, 79.7 us). Its 8 waves read 50% more LDS per MFMA than 4 waves of
+// 64 x 64 would, but keep two waves on every SIMD even when a tile has its CU
+// to itself: 512 x 8192 x 8192 ran 87.5 us with 4 waves, 2560^3 42.1 us
+// against 40.1.
 //
 // The model, in units of one 256 x 256 tile's K loop on a CU: 256 x 256 tiles
-// cost ceil(tiles / 256); a round of 128 x 128 tiles costs 0.635 with two per
-// CU and 0.536 with at most one (the measured ratios above), so 4096^3 costs
-// 1 against 1.27, 4352 x 4096 x 4096 (272 large tiles, two rounds) 2 against
-// 1.81 (184.1 against 163.2 us), 3072^3 1 against 1.17 (66.9 against 76.3).
+// cost ceil(tiles / 256); a round of 128 x 128 tiles costs 0.61 with two per
+// CU and 0.49 with at most one (the measured ratios above), so 4096^3 costs
+// 1 against 1.22, 4352 x 4096 x 4096 (272 large tiles, two rounds) 2 against
+// 1.71 (182.2 against 152.5 us), 3072^3 1 against 1.10 (67.3 against 76.5).
 // 128 x 128 tiles run when they cost under 0.95 of the larger ones. Planned
 // for a full MI355X (256 CUs) whatever the device, so the choice, and the
 // rounding that follows from it, does not depend on partitioning.
@@ -714,7 +728,7 @@ int tiled_tile(int64_t M, int64_t N) {
     const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
     const double cost256 = (double)((t256 + kTilePlanCus - 1) / kTilePlanCus);
     const int64_t full = t128 / (2 * kTilePlanCus), rem = t128 % (2 * kTilePlanCus);
-    const double cost128 = 0.635 * (double)full + (rem == 0 ? 0.0 : rem > kTilePlanCus ? 0.635 : 0.536);
+    const double cost128 = 0.61 * (double)full + (rem == 0 ? 0.0 : rem > kTilePlanCus ? 0.61 : 0.49);
     return cost128 < 0.95 * cost256 ? 128 : 256;
 }
 
@@ -764,8 +778,8 @@ hipError_t launch_cfg(const GemmArgs<uint16_t>& a, bool dw, void* ws, size_t ws_
 hipError_t launch_bf16_tiled(const GemmArgs<uint16_t>& a, bool dw, void* ws, size_t ws_bytes,
                              int cus, hipStream_t s) {
     if (tiled_tile(a.M, a.N) == 128) {
-        if (has_epilogue(a)) return launch_cfg<128, 128, 2, 2, true>(a, dw, ws, ws_bytes, cus, s);
-        return launch_cfg<128, 128, 2, 2, false>(a, dw, ws, ws_bytes, cus, s);
+        if (has_epilogue(a)) return launch_cfg<128, 128, 2, 4, true>(a, dw, ws, ws_bytes, cus, s);
+        return launch_cfg<128, 128, 2, 4, false>(a, dw, ws, ws_bytes, cus, s);
     }
     if (has_epilogue(a)) return launch_cfg<256, 256, 2, 4, true>(a, dw, ws, ws_bytes, cus, s);
     return launch_cfg<256, 256, 2, 4, false>(a, dw, ws, ws_bytes, cus, s);

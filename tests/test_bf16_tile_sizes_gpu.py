@@ -1,5 +1,6 @@
 """The bf16 tiled kernel's two tile sizes, 256 x 256 (products with many
-tiles) and 128 x 128 (products with few), through the C ABI.
+tiles, 8 waves of 128 x 64) and 128 x 128 (products with few, 8 waves of
+64 x 32), through the C ABI.
 
 * Both accumulate each output over K in the same order, so the first 512 rows
   of a 4096-row product (256 x 256 tiles) must equal a 512-row product of the
@@ -47,9 +48,10 @@ def _op(opa, opb, A, B):
 
 @pytest.mark.parametrize("ops", OPS, ids=OP_IDS)
 def test_tile_sizes_give_the_same_bits(ops):
-    # 512 x 4000: 4 x 32 = 128 small tiles, one per CU (cost 0.536 against a
+    # 512 x 4000: 4 x 32 = 128 small tiles, one per CU (cost 0.49 against a
     # round of 32 large ones); 4096 x 4000: 256 large tiles (cost 1 against
-    # 1.27 for 1024 small ones).
+    # 1.22 for 1024 small ones). The two tile sizes also run different wave
+    # shapes (8 waves of 64 x 32 against 8 of 128 x 64).
     M_small, M_big, N, K = 512, 4096, 4000, 1000
     A = gi.random_matrix(M_small, K, "bf16", 8300, dist="n")
     B = gi.random_matrix(K, N, "bf16", 8301)
