@@ -81,9 +81,14 @@ __device__ __forceinline__ int a_off(int row, int c) {
 // the LDS banks) take k / 8 mod 4; 128-wide rows (16 chunks, 256 bytes, once
 // the banks) take k / 8 mod 2, so the term stays below 16 and every chunk in
 // its own row, and puts the odd groups of 8 rows on the other half of the banks.
+// 64-wide rows (8 chunks, 128 bytes, half the banks) alternate bank halves by
+// themselves, so the term separates the rows of each parity that a 32-lane
+// read phase touches (k0 .. k0 + 3 and k0 + 8 .. k0 + 11): (k / 2 mod 2) and
+// (k / 8 mod 2), values 0 .. 6, and rows 2m and 2m + 1 share it.
 template <int BN>
 __device__ __forceinline__ int b_swz(int k) {
     if constexpr (BN == 256) return ((k & 3) | (((k >> 3) & 3) << 2)) << 1;
+    if constexpr (BN == 64) return (((k >> 1) & 1) << 1) | (((k >> 3) & 1) << 2);
     return ((k & 3) << 1) | (((k >> 3) & 1) << 3);
 }
 template <int BN>
@@ -117,9 +122,10 @@ __device__ __forceinline__ int opaque_lane() {
 // DW: A, B and C rows (and bases) are aligned to 4 bytes, not 16.
 // The second bound is waves per SIMD: 128 x 128 tiles run two workgroups of
 // 8 waves per CU (at most 128 VGPRs) unless split over a workspace, which
-// only happens when the split workgroups fit one per CU.
+// only happens when the split workgroups fit one per CU; 64 x 64 tiles (4
+// waves) run up to four.
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool EPI, bool TA, bool TB, bool SPLIT, bool DW>
-__global__ __launch_bounds__(WAVES_M * WAVES_N * 64, BM == 128 && !SPLIT ? 4 : 2)
+__global__ __launch_bounds__(WAVES_M * WAVES_N * 64, (BM == 128 && !SPLIT) || BM == 64 ? 4 : 2)
 void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, TailSplit ts,
                             unsigned char* ws) {
     constexpr int kNT = WAVES_M * WAVES_N * 64;
@@ -142,8 +148,8 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, Tail
     constexpr int kBRowsPerCopy = 1024 / (BN * 2);            // rows of a [64][BN] slab per copy
     static_assert(kACopies * kDmaWaves * 1024 == kAStage * 2, "A slab must split evenly");
     static_assert(kBCopies * kDmaWaves * 1024 == kBStage * 2, "B slab must split evenly");
-    static_assert(BN == 256 || BN == 128, "B row length");
-    static_assert((BM == 256 || BM == 128) && (!TA || BM == BN), "operand tile sizes");
+    static_assert(BN == 256 || BN == 128 || BN == 64, "B row length");
+    static_assert((BM == 256 || BM == 128 || BM == 64) && (!TA || BM == BN), "operand tile sizes");
     static_assert(kWTM % 16 == 0 && kWTN % 16 == 0, "wave tile");
     // One array per operand and pipeline stage, so the compiler can tell which
     // stage an LDS-destined load writes and does not make reads of the other
@@ -231,15 +237,29 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, Tail
                  (uint32_t)(8 * I + 2 * s) * ld2 + (uint32_t)(k0 * 2), base + s * 256);
     };
     auto dw_mn = [&](int ln, rsrc_t desc, int64_t ld, int I, uint32_t dst) __attribute__((always_inline)) {
-        const uint32_t l4 = (uint32_t)(4 * ln);
         uint32_t ld2 = (uint32_t)(ld * 2), base = dst;
         asm volatile("" : "+s"(ld2), "+s"(base));
+        if constexpr (2 * kBN >= 256) {
+            const uint32_t l4 = (uint32_t)(4 * ln);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int b = 1024 * I + 256 * s;
-            const int row = b / (2 * kBN);
-            const uint32_t x = (uint32_t)((b % (2 * kBN)) ^ (b_swz<kBN>(row) << 4));
-            dma4(desc, l4 ^ x, (uint32_t)row * ld2, base + b);
+            for (int s = 0; s < 4; ++s) {
+                const int b = 1024 * I + 256 * s;
+                const int row = b / (2 * kBN);
+                const uint32_t x = (uint32_t)((b % (2 * kBN)) ^ (b_swz<kBN>(row) << 4));
+                dma4(desc, l4 ^ x, (uint32_t)row * ld2, base + b);
+            }
+        } else {
+            // 128-byte rows: sub-copy s holds rows 8 I + 2 s + h (h = l / 32),
+            // which share one swizzle.
+            const int h = ln >> 5;
+            const uint32_t rowb = (uint32_t)h * ld2;
+            const uint32_t in0 = (uint32_t)((4 * ln) & 127);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int row = 8 * I + 2 * s;
+                const uint32_t x = (uint32_t)(b_swz<kBN>(row) << 4);
+                dma4(desc, rowb + (in0 ^ x), (uint32_t)row * ld2, base + 1024 * I + 256 * s);
+            }
         }
     };
     const int a_lrow = lane >> 3, a_pos = lane & 7;
@@ -541,9 +561,8 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, Tail
         // per instruction): the projection with beta = 1 ran 685 against
         // 646 us in a copy with this access pattern, 2560^3 with beta = 1 on
         // 128 x 128 tiles 40.8 against 36.4 us. Each 16-row block of a wave's
-        // results goes through a wave-private LDS scratch (rows padded by 4
-        // floats: with 64-column tiles the 128-bit writes and reads measure
-        // conflict-free) into row order. Lane l takes columns
+        // results goes through a wave-private LDS scratch into row order.
+        // Lane l takes columns
         // 8 (l mod kLpr) .. + 7 of rows l / kLpr + kRpp h of each block. The
         // arithmetic is the same as below.
         constexpr int kLpr = kWTN / 8;             // lanes per row (8 columns each)
@@ -573,7 +592,12 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, Tail
         }
         // Every wave has read its last fragments: the stages are free.
         lds_only_barrier();
-        constexpr int kScrLd = kWTN + 4, kScrPerStage = kWaves / 2;
+        // Scratch rows: 64 floats with 16-byte chunk c of row r at chunk
+        // c ^ (r mod 16) for 64-column wave tiles (measured conflict-free);
+        // kWTN + 4 floats, unswizzled, for 32-column ones (about 2 conflict
+        // cycles per access measured; two XOR layouts measured 4).
+        constexpr int kScrLd = kWTN == 64 ? 64 : kWTN + 4, kScrPerStage = kWaves / 2;
+        auto scr_at = [](int r, int c) { return r * kScrLd + 4 * (kWTN == 64 ? (c ^ (r & 15)) : c); };
         static_assert(kScrPerStage * 16 * kScrLd * 4 <= kAStage * 2, "half the wave scratches per A stage");
         float* scr = reinterpret_cast<float*>(wave < kScrPerStage ? a_st0 : a_st1) +
                      (wave % kScrPerStage) * 16 * kScrLd;
@@ -581,12 +605,12 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, Tail
         for (int i = 0; i < kFM; ++i) {
 #pragma unroll
             for (int j = 0; j < kFN; ++j)
-                *reinterpret_cast<f32x4*>(scr + pl * kScrLd + 16 * j + 4 * g) = acc[j][i];
+                *reinterpret_cast<f32x4*>(scr + scr_at(pl, 4 * j + g)) = acc[j][i];
 #pragma unroll
             for (int h = 0; h < kPasses; ++h) {
                 const int row = rr + kRpp * h;
-                const f32x4 lo = *reinterpret_cast<const f32x4*>(scr + row * kScrLd + 8 * cc);
-                const f32x4 hi = *reinterpret_cast<const f32x4*>(scr + row * kScrLd + 8 * cc + 4);
+                const f32x4 lo = *reinterpret_cast<const f32x4*>(scr + scr_at(row, 2 * cc));
+                const f32x4 hi = *reinterpret_cast<const f32x4*>(scr + scr_at(row, 2 * cc + 1));
                 const int64_t grow = m0 + wm0 + 16 * i + row;
                 const float fr = EPI ? row_factor(p, grow) : alpha;
                 float v[8];
@@ -703,8 +727,9 @@ const void* pick_tiled(bool ta, bool tb, bool dw) {
               : pick_layout<BM, BN, WAVES_M, WAVES_N, EPI, SPLIT, false>(ta, tb);
 }
 
-// Two tile sizes: 256 x 256 (8 waves of 128 x 64, 128 KB of LDS, one
-// workgroup per CU) and 128 x 128 (8 waves of 64 x 32, 64 KB, two per CU).
+// Three tile sizes: 256 x 256 (8 waves of 128 x 64, 128 KB of LDS, one
+// workgroup per CU), 128 x 128 (8 waves of 64 x 32, 64 KB, two per CU) and
+// 64 x 64 (4 waves of 32 x 32, 32 KB, up to four per CU).
 // The smaller tile multiplies less per byte it stages (4096^3: 127.5 against
 // 103.3 us) but gives four times the workgroups, which products with few
 // 256 x 256 tiles need (512 x 8192 x 8192: 64 such tiles, 162.2 us; 256 of
@@ -721,6 +746,15 @@ const void* pick_tiled(bool ta, bool tb, bool dw) {
 // 128 x 128 tiles run when they cost under 0.95 of the larger ones. Planned
 // for a full MI355X (256 CUs) whatever the device, so the choice, and the
 // rounding that follows from it, does not depend on partitioning.
+//
+// Among products that take 128 x 128 tiles, those with at most 160 of them
+// (and no split over a workspace) run 64 x 64 tiles instead: four times the
+// workgroups for four times the LDS reads per MFMA. Measured against 128 x
+// 128 tiles: 1024^2 x 4096 (64 small tiles) 32.2 against 41.0 us, 1280^2 x
+// 4096 (100) 33.1 against 44.1, 1536^2 x 4096 (144) 41.1 against 43.2,
+// 1536 x 2048 x 4096 (192) 43.5 against 42.7, 2048^3 (256) 29.9 against 25.7.
+// A round of 64 x 64 tiles costs about 0.385 + 0.07 (q - 1) at q tiles per CU,
+// under the 0.49 of a lone round of 128 x 128 ones while q < 2.5.
 constexpr int64_t kTilePlanCus = 256;
 
 int tiled_tile(int64_t M, int64_t N) {
@@ -778,6 +812,15 @@ hipError_t launch_cfg(const GemmArgs<uint16_t>& a, bool dw, void* ws, size_t ws_
 hipError_t launch_bf16_tiled(const GemmArgs<uint16_t>& a, bool dw, void* ws, size_t ws_bytes,
                              int cus, hipStream_t s) {
     if (tiled_tile(a.M, a.N) == 128) {
+        // At most 160 small tiles (on a full MI355X) and no split over a
+        // workspace: 64 x 64 tiles.
+        const int64_t t128 = ((a.M + 127) / 128) * ((a.N + 127) / 128);
+        const TailSplit plan = plan_tiled128(a.M, a.N, a.K, cus);
+        const bool split = ws != nullptr && plan.tail > 0 && ws_bytes >= tail_workspace(plan, 128, 128);
+        if (8 * t128 <= 5 * kTilePlanCus && !split) {
+            if (has_epilogue(a)) return launch_cfg<64, 64, 2, 2, true>(a, dw, ws, ws_bytes, cus, s);
+            return launch_cfg<64, 64, 2, 2, false>(a, dw, ws, ws_bytes, cus, s);
+        }
         if (has_epilogue(a)) return launch_cfg<128, 128, 2, 4, true>(a, dw, ws, ws_bytes, cus, s);
         return launch_cfg<128, 128, 2, 4, false>(a, dw, ws, ws_bytes, cus, s);
     }

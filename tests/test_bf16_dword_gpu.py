@@ -5,7 +5,7 @@ leading dimensions that are not multiples of 8, or bases 4 bytes past a
 * Those copies fill the same LDS layouts as the 1 KB copies of 16-byte rows,
   and the arithmetic is the same, so a product stored with 4-byte rows must
   equal the same product stored with 16-byte rows bit for bit: every operand
-  layout, both tile sizes, ragged M, N and K, beta = 0 and beta != 0.
+  layout, every tile size, ragged M, N and K, beta = 0 and beta != 0.
 * Against the oracle: ragged edges in every layout, bases offset by 2
   elements, the fused bias + GELU epilogue, quantisation scales, and a
   split-K workspace.
@@ -87,10 +87,11 @@ def inputs(M, N, K, seed, beta):
     return A, B, C0
 
 
-# 512 x 1000: 32 tiles of 128 x 128; 3000 x 2998: 144 tiles of 256 x 256
-# (576 small ones would cost more); ragged in M, N and K.
+# 512 x 1000: 32 tiles of 128 x 128, so 128 tiles of 64 x 64; 2048 x 1500:
+# 192 tiles of 128 x 128; 3000 x 2998: 144 tiles of 256 x 256 (576 small
+# ones would cost more); ragged in M, N and K.
 @pytest.mark.parametrize("ops", OPS, ids=OP_IDS)
-@pytest.mark.parametrize("shape", [(512, 1000, 1001), (3000, 2998, 200)],
+@pytest.mark.parametrize("shape", [(512, 1000, 1001), (2048, 1500, 300), (3000, 2998, 200)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_same_bits_as_16_byte_rows(shape, ops):
     M, N, K = shape
@@ -156,6 +157,6 @@ def test_oracle_split_k(ops):
     C = run(ops, A, B, C0, 1.0, 1.0, ws=True)
     R, D = oracle_op("bf16", A, B, C0, 1.0, 1.0)
     assert oracle.max_rel_err(to_f64(C), R, D) <= tol("bf16")
-    plain = run(ops, A, B, C0, 1.0, 1.0, ws=False)
+    plain = run(ops, A, B, C0, 1.0, 1.0, ws=False)      # 288 tiles of 64 x 64
     R2 = oracle.max_rel_err(to_f64(plain), R, D)
     assert R2 <= tol("bf16")

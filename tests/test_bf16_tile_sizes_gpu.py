@@ -1,15 +1,18 @@
-"""The bf16 tiled kernel's two tile sizes, 256 x 256 (products with many
-tiles, 8 waves of 128 x 64) and 128 x 128 (products with few, 8 waves of
-64 x 32), through the C ABI.
+"""The bf16 tiled kernel's three tile sizes, 256 x 256 (products with many
+tiles, 8 waves of 128 x 64), 128 x 128 (fewer, 8 waves of 64 x 32) and 64 x 64
+(at most 160 tiles of 128 x 128 and no split, 4 waves of 32 x 32), through the
+C ABI.
 
-* Both accumulate each output over K in the same order, so the first 512 rows
-  of a 4096-row product (256 x 256 tiles) must equal a 512-row product of the
-  same rows (128 x 128 tiles) bit for bit, in all four operand layouts, with
-  ragged N and K.
+* All accumulate each output over K in the same order, so the first 512 rows
+  of a 4096-row product (256 x 256 tiles) and of a 2048-row one (128 x 128
+  tiles) must equal a 512-row product of the same rows (64 x 64 tiles) bit
+  for bit, in all four operand layouts, with ragged N and K.
 * Ragged 256 x 256 tiles against the oracle in every layout, with the fused
   bias + GELU epilogue and with quantisation scales (the smaller test shapes
   elsewhere run on 128 x 128 tiles).
-* 128 x 128 tiles split over a workspace against the oracle.
+* 128 x 128 tiles split over a workspace against the oracle, and the same
+  shapes without a workspace (64 x 64 tiles).
+* Ragged 128 x 128 tiles alone on their CUs and 64 x 64 tiles in every layout.
 """
 import pytest
 import torch
@@ -48,20 +51,21 @@ def _op(opa, opb, A, B):
 
 @pytest.mark.parametrize("ops", OPS, ids=OP_IDS)
 def test_tile_sizes_give_the_same_bits(ops):
-    # 512 x 4000: 4 x 32 = 128 small tiles, one per CU (cost 0.49 against a
-    # round of 32 large ones); 4096 x 4000: 256 large tiles (cost 1 against
-    # 1.22 for 1024 small ones). The two tile sizes also run different wave
-    # shapes (8 waves of 64 x 32 against 8 of 128 x 64).
-    M_small, M_big, N, K = 512, 4096, 4000, 1000
+    # 512 x 4000: 4 x 32 = 128 tiles of 128 x 128, so 64 x 64 tiles;
+    # 2048 x 4000: 512 tiles of 128 x 128 (cost 0.61 against a round of 128
+    # large ones); 4096 x 4000: 256 large tiles (cost 1 against 1.22 for 1024
+    # small ones). The sizes also run different wave shapes.
+    M_small, N, K = 512, 4000, 1000
     A = gi.random_matrix(M_small, K, "bf16", 8300, dist="n")
     B = gi.random_matrix(K, N, "bf16", 8301)
-    A_big = torch.zeros(M_big, K, dtype=A.dtype)
-    A_big[:M_small] = A
-    note(f"bf16 tile sizes {ops}: {M_small} and {M_big} rows, N={N} K={K}")
+    note(f"bf16 tile sizes {ops}: 512, 2048 and 4096 rows, N={N} K={K}")
     small = _op(ops[0], ops[1], A, B)
-    big = _op(ops[0], ops[1], A_big, B)
-    assert torch.equal(small.view(torch.int16), big[:M_small].view(torch.int16))
-    assert bool((big[M_small:].float() == 0).all())
+    for M_big in (2048, 4096):
+        A_big = torch.zeros(M_big, K, dtype=A.dtype)
+        A_big[:M_small] = A
+        big = _op(ops[0], ops[1], A_big, B)
+        assert torch.equal(small.view(torch.int16), big[:M_small].view(torch.int16)), M_big
+        assert bool((big[M_small:].float() == 0).all())
 
 
 @pytest.mark.parametrize("ops", OPS, ids=OP_IDS)
@@ -99,3 +103,21 @@ def test_small_tiles_split(shape):
     M, N, K = shape
     assert dg.gemm_bf16_workspace_size(M, N, K) > 0
     check_op("bf16", 0, 0, M, N, K, 8700 + M, alpha=1.0, beta=1.0, ws=True)
+
+
+# 2048 x 1500: 192 tiles of 128 x 128, each alone on its CU; 300 x 520: 15
+# of them, so 40 tiles of 64 x 64. Ragged M, N and K in every layout.
+@pytest.mark.parametrize("ops", OPS, ids=OP_IDS)
+@pytest.mark.parametrize("shape", [(2048, 1500, 300), (300, 520, 129)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_small_tiles_ragged(shape, ops):
+    M, N, K = shape
+    check_op("bf16", ops[0], ops[1], M, N, K, 8800 + 7 * ops[0] + ops[1] + M, alpha=0.75,
+             beta=0.5, pad=(8, 8, 8))
+
+
+@pytest.mark.parametrize("shape", [(2048, 1500, 300), (300, 520, 129)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_small_tiles_bias_gelu(shape):
+    M, N, K = shape
+    check_op("bf16", 1, 0, M, N, K, 8900 + M, alpha=1.25, beta=1.0, bias=True, act="gelu_tanh")

@@ -10,7 +10,7 @@ normal build's results bit for bit, through the C ABI, on every pipeline:
     not landed, turns into NaN in C;
   * sync: every batch of copies completes before any wave reads LDS again,
     the order one staging buffer would impose.
-Cases cover the bf16 tiled kernel (both tile sizes, several rounds of tiles,
+Cases cover the bf16 tiled kernel (all three tile sizes, several rounds of tiles,
 split-K tail, transposed layouts, 16-byte and 4-byte copies), the small-M copy rings (64-column and streaming, split
 and not), the element-wise and unaligned kernels, and the fp32 copy path
 (16-byte and 4-byte copies: tiles walked, transposed layouts, split-K
@@ -81,6 +81,10 @@ CASES = [
     ("bf16", (4000, 4000, 200), (0, 0, 0), (0, 0), False, None),   # tiled, 256 large tiles, ragged
     ("bf16", (4000, 4000, 136), (8, 8, 8), (1, 1), False, None),   # large tiles, both transposed, padded
     ("bf16", (520, 520, 4100), (0, 0, 0), (0, 0), True, None),     # tiled split-K tail, ragged K
+    ("bf16", (520, 520, 4100), (0, 0, 0), (0, 0), False, None),    # same without a workspace: 64 x 64 tiles
+    ("bf16", (2048, 1500, 300), (0, 0, 0), (0, 0), False, None),   # 192 small tiles, one per CU
+    ("bf16", (2048, 1500, 300), (8, 8, 8), (1, 1), False, None),   # the same, both transposed
+    ("bf16", (2048, 1500, 300), (2, 2, 2), (0, 1), False, None),   # the same, 4-byte copies, B stored N x K
     ("bf16", (300, 264, 200), (0, 0, 0), (1, 0), False, None),     # tiled, A stored K x M
     ("bf16", (300, 264, 200), (0, 0, 0), (0, 1), False, None),     # tiled, B stored N x K (M > 128)
     ("bf16", (300, 264, 200), (8, 8, 8), (1, 1), False, None),     # tiled, both, padded rows
