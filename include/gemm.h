@@ -138,16 +138,20 @@ gemm_status_t gemm_bf16_ex(int64_t M, int64_t N, int64_t K, float alpha,
 /* Split-K for small M (RTX 3090 SGEMM article, section 7.2: cutting K into
  * pieces that run in parallel and summing their partial results brings more
  * multiprocessors to work). With M <= 128 one workgroup per 64-column strip of
- * C leaves most of the GPU idle when N is small; a workspace lets the bf16
- * small-M kernel give each strip several workgroups, each over a range of K.
- * Each stores its fp32 partial tile in the workspace, and the strip's last
- * workgroup to finish adds the partials in a fixed order (so results do not
- * depend on timing) and forms alpha * sum + beta * C.
+ * C leaves half the GPU idle at N = 8192; a workspace gives each strip several
+ * workgroups, each over a part of K: with row-major 16-byte rows and at least
+ * 16 strips of 256 columns, a streaming kernel whose workgroups take
+ * interleaved 32-row blocks of K (16 x 8192 x 8192: 32 strips x 8), otherwise
+ * the small-M kernel over contiguous K segments. Each workgroup stores its
+ * fp32 partial tile in the workspace, and the strip's last workgroup to
+ * finish adds the partials in a fixed order (so results do not depend on
+ * timing) and forms alpha * sum + beta * C.
  *
  * For M > 128 the tiled bf16 kernel splits the same way as the fp32 one (see
- * gemm_f32_ws): when fewer 256 x 256 tiles than compute units, or a last
- * round at most half full, would leave CUs idle, each such tile is cut into up
- * to 8 K ranges of at least 1024 k, with 256 KB fp32 partial tiles.
+ * gemm_f32_ws), on 128 x 128 tiles: when fewer than half as many such tiles
+ * as compute units, or a last round at most half full, would leave CUs idle,
+ * each tile of that round is cut into up to 8 K ranges of at least 1024 k,
+ * with 64 KB fp32 partial tiles.
  *
  * gemm_bf16_workspace_size: workspace bytes gemm_bf16_ws needs to split this
  * shape; 0 when it would not split (small M: N already fills the GPU or K is
@@ -182,7 +186,7 @@ gemm_status_t gemm_bf16_ws(int64_t M, int64_t N, int64_t K, float alpha,
  * gemm_bf16_workspace_size(M, N, K) bytes (bit for bit). Shapes whose
  * workspace would exceed the scratch return GEMM_ERR_SCRATCH_LIMIT and
  * launch nothing (16 x 8192 x 8192 needs 4 MiB and 128 x 8192 x 8192 32 MiB,
- * which fit; 512 x 8192 x 8192 needs 64 MiB, which does not; shapes that
+ * which fit; 128 x 4352 x 8192 needs 34 MiB, which does not; shapes that
  * would not split need none and run as gemm_bf16). All calls on one GPU share its scratch: calls that overlap
  * in time on one GPU (different streams, or threads without ordering) race
  * and give undefined results; calls ordered on one stream are safe. Other
