@@ -7,8 +7,9 @@ leading dimensions that are not multiples of 8, or bases 4 bytes past a
   equal the same product stored with 16-byte rows bit for bit: every operand
   layout, every tile size, ragged M, N and K, beta = 0 and beta != 0.
 * Against the oracle: ragged edges in every layout, bases offset by 2
-  elements, the fused bias + GELU epilogue, quantisation scales, and a
-  split-K workspace.
+  elements, the fused bias + GELU epilogue, quantisation scales, a split-K
+  workspace, and a leading dimension just inside and just past the copies'
+  31-bit offset range (16-byte and 4-byte rows).
 """
 import pytest
 import torch
@@ -160,3 +161,28 @@ def test_oracle_split_k(ops):
     plain = run(ops, A, B, C0, 1.0, 1.0, ws=False)      # 288 tiles of 64 x 64
     R2 = oracle.max_rel_err(to_f64(plain), R, D)
     assert R2 <= tol("bf16")
+
+
+# B stored N x K is copied k-contiguous: 256 rows of its storage span
+# (256 ldb + K) * 2 bytes, inside 2^31 at 4.0 M elements and past it at
+# 4.2 M, where the call takes the element-wise kernel. 16-byte rows
+# (multiples of 8) and 4-byte rows (even, not multiples of 8); the padding
+# between rows holds NaN.
+@pytest.mark.parametrize("ldb", [4_000_000, 4_200_000, 4_000_002, 4_200_002])
+def test_leading_dimension_at_the_copy_offset_limit(ldb):
+    M, N, K = 200, 40, 50
+    A, B, C0 = inputs(M, N, K, 9995, 0.5)
+    note(f"bf16 A B^T with ldb={ldb} M={M} N={N} K={K}")
+    _, a = padded(M, K, 56, "bf16", fill=float("nan"))
+    a.copy_(A.cuda())
+    bbuf, b = padded(N, K, ldb, "bf16", fill=float("nan"))
+    b.copy_(B.t().contiguous().cuda())
+    _, c = padded(M, N, 48, "bf16", fill=float("nan"))
+    c.copy_(C0.cuda())
+    st = dg.gemm_bf16_op(0, 1, M, N, K, 0.75, a.data_ptr(), 56, b.data_ptr(), ldb, 0.5,
+                         c.data_ptr(), 48, None, dg.ACT_NONE, None, 0, 0)
+    torch.cuda.synchronize()
+    assert st == dg.GEMM_OK, dg.gemm_status_string(st)
+    del bbuf, b
+    R, D = oracle_op("bf16", A, B, C0, 0.75, 0.5)
+    assert oracle.max_rel_err(to_f64(c.cpu()), R, D) <= tol("bf16")
