@@ -58,63 +58,15 @@
 
 #include <type_traits>
 
+#include "bf16_lds.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace dg {
 namespace {
 
-constexpr int kBK = 64;
 constexpr int kGroupM = 4;
-
-// A tile [256][64]: chunk c (8 bf16) of row `row`. XOR with row mod 8 keeps
-// the eight 16-byte reads of 8 consecutive rows on distinct banks, and keeps
-// every address affine in the 16-row block index (one address register).
-__device__ __forceinline__ int a_off(int row, int c) {
-    return row * kBK + ((c ^ (row & 7)) << 3);
-}
-
-// B tile [64][BN]: chunk c (8 bf16) of row k. The XOR term is even, so a
-// 16-lane group's two neighbouring chunks stay neighbours, and depends on
-// k mod 4 (the rows within a 16-lane group of a transposing read) and on k / 8
-// (the rows of the other groups). 256-wide rows (32 chunks, 512 bytes, twice
-// the LDS banks) take k / 8 mod 4; 128-wide rows (16 chunks, 256 bytes, once
-// the banks) take k / 8 mod 2, so the term stays below 16 and every chunk in
-// its own row, and puts the odd groups of 8 rows on the other half of the banks.
-// 64-wide rows (8 chunks, 128 bytes, half the banks) alternate bank halves by
-// themselves, so the term separates the rows of each parity that a 32-lane
-// read phase touches (k0 .. k0 + 3 and k0 + 8 .. k0 + 11): (k / 2 mod 2) and
-// (k / 8 mod 2), values 0 .. 6, and rows 2m and 2m + 1 share it.
-template <int BN>
-__device__ __forceinline__ int b_swz(int k) {
-    if constexpr (BN == 256) return ((k & 3) | (((k >> 3) & 3) << 2)) << 1;
-    if constexpr (BN == 64) return (((k >> 1) & 1) << 1) | (((k >> 3) & 1) << 2);
-    return ((k & 3) << 1) | (((k >> 3) & 1) << 3);
-}
-template <int BN>
-__device__ __forceinline__ int b_off(int k, int c) {
-    return k * BN + ((c ^ b_swz<BN>(k)) << 3);
-}
-
-
-template <int BN>
-__device__ __forceinline__ bf16x8 read_b_frag(const uint16_t* Bs, int k0, int col) {
-    // Lane 4r + q of each 16-lane group addresses row k0 + r (+4), columns col .. col+3.
-    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_i16x4*)(Bs + b_off<BN>(k0, col >> 3) + (col & 7)));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_i16x4*)(Bs + b_off<BN>(k0 + 4, col >> 3) + (col & 7)));
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-// The lane index, computed afresh (mbcnt) from an operand the compiler cannot
-// see through, so that it is not kept live in a register across the main loop.
-__device__ __forceinline__ int opaque_lane() {
-    unsigned m = ~0u;
-    asm volatile("" : "+s"(m));
-    return (int)__builtin_amdgcn_mbcnt_hi(m, __builtin_amdgcn_mbcnt_lo(m, 0u));
-}
+using namespace bf16lds;
 
 // ws (only with SPLIT and ts.tail > 0): [counters: one int per split tile,
 // padded to 256 bytes][slots: tail x parts partial tiles of BM x BN fp32,
@@ -748,7 +700,8 @@ const void* pick_tiled(bool ta, bool tb, bool dw) {
 // rounding that follows from it, does not depend on partitioning.
 //
 // Among products that take 128 x 128 tiles, those with at most 160 of them
-// (and no split over a workspace) run 64 x 64 tiles instead: four times the
+// (and no split over a workspace) run 64 x 64 tiles instead, unless the
+// few-tile kernel takes them (below; 16-byte rows): four times the
 // workgroups for four times the LDS reads per MFMA. Measured against 128 x
 // 128 tiles: 1024^2 x 4096 (64 small tiles) 32.2 against 41.0 us, 1280^2 x
 // 4096 (100) 33.1 against 44.1, 1536^2 x 4096 (144) 41.1 against 43.2,
@@ -781,6 +734,22 @@ constexpr double kTiledFixupSlabs = -1.0;
 TailSplit plan_tiled128(int64_t M, int64_t N, int64_t K, int cus) {
     const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
     return plan_tail_split(tiles, (K + kBK - 1) / kBK, (int64_t)cus, kTiledMinSlabs, kTiledFixupSlabs);
+}
+
+// The few-tile kernel (gemm_bf16_few.hip: one 64 x 64 tile per workgroup, K
+// split over its 4 waves, one workgroup per CU), for 16-byte rows:
+//   * without a split over a workspace, for up to two rounds of its tiles
+//     (512 on a full MI355X), where the tiled kernel's 64 x 64 or 128 x 128
+//     tiles would run (1024^2 x 4096: 18 against 32 us; 1280^2 x 4096, 400
+//     tiles: 31.8 against 33.3; 1536^2 x 4096, 576 tiles: 45.8 against 40.5);
+//   * with one, when its tiles fit one round and are at least as many as the
+//     split's workgroups (1024^2 x 4096: 256 tiles against 64 x 4 ranges,
+//     18.3 against 24.1 us; 129 x 1000 x 8200: 48 against 16 x 8, 33.1
+//     against 23.2 us; 384 x 1024 x 8192: 96 against 24 x 8, 27.5 against 24.0).
+static bool few_preferred(int64_t M, int64_t N, const TailSplit* split) {
+    const int64_t t64 = ((M + 63) / 64) * ((N + 63) / 64);
+    if (split != nullptr) return t64 <= kTilePlanCus && t64 >= (int64_t)split->tail * split->parts;
+    return t64 <= 2 * kTilePlanCus;
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool EPI>
@@ -817,6 +786,7 @@ hipError_t launch_bf16_tiled(const GemmArgs<uint16_t>& a, bool dw, void* ws, siz
         const int64_t t128 = ((a.M + 127) / 128) * ((a.N + 127) / 128);
         const TailSplit plan = plan_tiled128(a.M, a.N, a.K, cus);
         const bool split = ws != nullptr && plan.tail > 0 && ws_bytes >= tail_workspace(plan, 128, 128);
+        if (!dw && few_preferred(a.M, a.N, split ? &plan : nullptr)) return launch_bf16_few(a, s);
         if (8 * t128 <= 5 * kTilePlanCus && !split) {
             if (has_epilogue(a)) return launch_cfg<64, 64, 2, 2, true>(a, dw, ws, ws_bytes, cus, s);
             return launch_cfg<64, 64, 2, 2, false>(a, dw, ws, ws_bytes, cus, s);
@@ -830,7 +800,11 @@ hipError_t launch_bf16_tiled(const GemmArgs<uint16_t>& a, bool dw, void* ws, siz
 
 size_t bf16_tiled_workspace(int64_t M, int64_t N, int64_t K, int cus) {
     if (M < 1 || N < 1 || K < 1 || tiled_tile(M, N) != 128) return 0;
-    return tail_workspace(plan_tiled128(M, N, K, cus), 128, 128);
+    const TailSplit plan = plan_tiled128(M, N, K, cus);
+    // Products the few-tile kernel takes in preference to the split (rows
+    // aligned to 16 bytes) need no workspace.
+    if (plan.tail > 0 && few_preferred(M, N, &plan)) return 0;
+    return tail_workspace(plan, 128, 128);
 }
 
 }  // namespace dg

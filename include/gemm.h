@@ -151,7 +151,10 @@ gemm_status_t gemm_bf16_ex(int64_t M, int64_t N, int64_t K, float alpha,
  * gemm_f32_ws), on 128 x 128 tiles: when fewer than half as many such tiles
  * as compute units, or a last round at most half full, would leave CUs idle,
  * each tile of that round is cut into up to 8 K ranges of at least 1024 k,
- * with 64 KB fp32 partial tiles.
+ * with 64 KB fp32 partial tiles. Products whose 64 x 64 tiles fit one round
+ * of compute units and are at least as many as the split's workgroups run
+ * on the few-tile kernel instead (K split over the waves of a workgroup, no
+ * workspace): 1024 x 1024 x 4096 needs none.
  *
  * gemm_bf16_workspace_size: workspace bytes gemm_bf16_ws needs to split this
  * shape; 0 when it would not split (small M: N already fills the GPU or K is

@@ -243,9 +243,16 @@ def test_tiled_workspace_size(lib):
     tile = 128 * 128 * 4
     # 129 x 8192 x 8192: 128 tiles, 128 slabs -> 2 ranges.
     assert dg.gemm_bf16_workspace_size(129, 8192, 8192) == 512 + 128 * 2 * tile
-    # 1024^2 x 4096: 64 tiles, 64 slabs -> 4 ranges; 512^2 x 4096: 16 tiles -> 4.
-    assert dg.gemm_bf16_workspace_size(1024, 1024, 4096) == 256 + 64 * 4 * tile
-    assert dg.gemm_bf16_workspace_size(512, 512, 4096) == 256 + 16 * 4 * tile
+    # 512^2 x 16384: 16 tiles, 256 slabs -> 8 ranges; 640 x 1000 x 8192: 40
+    # tiles -> 6 ranges (240 workgroups, more than its 160 tiles of 64 x 64).
+    assert dg.gemm_bf16_workspace_size(512, 512, 16384) == 256 + 16 * 8 * tile
+    assert dg.gemm_bf16_workspace_size(640, 1000, 8192) == 256 + 40 * 6 * tile
+    # The few-tile kernel instead, when its 64 x 64 tiles fit one round and
+    # are at least as many as the split's workgroups: 1024^2 x 4096 (256
+    # against 64 x 4), 512^2 x 4096 (64 against 16 x 4), 1024^2 x 2048.
+    assert dg.gemm_bf16_workspace_size(1024, 1024, 4096) == 0
+    assert dg.gemm_bf16_workspace_size(512, 512, 4096) == 0
+    assert dg.gemm_bf16_workspace_size(1024, 1024, 2048) == 0
     # 129 x 1000 x 8200: 16 tiles, 129 slabs -> 8 ranges of 17 (the last 10).
     assert dg.gemm_bf16_workspace_size(129, 1000, 8200) == 256 + 16 * 8 * tile
     # No split: one tile per CU already (512 x 8192 and 2048^2: 256 small

@@ -1,18 +1,19 @@
 """The bf16 tiled kernel's three tile sizes, 256 x 256 (products with many
 tiles, 8 waves of 128 x 64), 128 x 128 (fewer, 8 waves of 64 x 32) and 64 x 64
-(at most 160 tiles of 128 x 128 and no split, 4 waves of 32 x 32), through the
-C ABI.
+(at most 160 tiles of 128 x 128 and no split, 4 waves of 32 x 32; products
+with at most 512 of them and 16-byte rows go to the few-tile kernel instead),
+through the C ABI.
 
-* All accumulate each output over K in the same order, so the first 512 rows
+* All accumulate each output over K in the same order, so the first 640 rows
   of a 4096-row product (256 x 256 tiles) and of a 2048-row one (128 x 128
-  tiles) must equal a 512-row product of the same rows (64 x 64 tiles) bit
+  tiles) must equal a 640-row product of the same rows (64 x 64 tiles) bit
   for bit, in all four operand layouts, with ragged N and K.
 * Ragged 256 x 256 tiles against the oracle in every layout, with the fused
   bias + GELU epilogue and with quantisation scales (the smaller test shapes
   elsewhere run on 128 x 128 tiles).
-* 128 x 128 tiles split over a workspace against the oracle, and the same
-  shapes without a workspace (64 x 64 tiles).
-* Ragged 128 x 128 tiles alone on their CUs and 64 x 64 tiles in every layout.
+* 128 x 128 tiles split over a workspace against the oracle.
+* Ragged 128 x 128 tiles alone on their CUs and 64 x 64 tiles in every layout,
+  with 16-byte rows.
 """
 import pytest
 import torch
@@ -51,14 +52,15 @@ def _op(opa, opb, A, B):
 
 @pytest.mark.parametrize("ops", OPS, ids=OP_IDS)
 def test_tile_sizes_give_the_same_bits(ops):
-    # 512 x 4000: 4 x 32 = 128 tiles of 128 x 128, so 64 x 64 tiles;
-    # 2048 x 4000: 512 tiles of 128 x 128 (cost 0.61 against a round of 128
-    # large ones); 4096 x 4000: 256 large tiles (cost 1 against 1.22 for 1024
-    # small ones). The sizes also run different wave shapes.
-    M_small, N, K = 512, 4000, 1000
+    # 640 x 4000: 5 x 32 = 160 tiles of 128 x 128 and 630 of 64 x 64 (more
+    # than two rounds of the few-tile kernel), so 64 x 64 tiles; 2048 x 4000:
+    # 512 tiles of 128 x 128 (cost 0.61 against a round of 128 large ones);
+    # 4096 x 4000: 256 large tiles (cost 1 against 1.22 for 1024 small ones).
+    # The sizes also run different wave shapes.
+    M_small, N, K = 640, 4000, 1000
     A = gi.random_matrix(M_small, K, "bf16", 8300, dist="n")
     B = gi.random_matrix(K, N, "bf16", 8301)
-    note(f"bf16 tile sizes {ops}: 512, 2048 and 4096 rows, N={N} K={K}")
+    note(f"bf16 tile sizes {ops}: 640, 2048 and 4096 rows, N={N} K={K}")
     small = _op(ops[0], ops[1], A, B)
     for M_big in (2048, 4096):
         A_big = torch.zeros(M_big, K, dtype=A.dtype)
@@ -95,9 +97,9 @@ def test_large_tiles_ragged_scaled():
     assert oracle.max_rel_err(to_f64(C), R, D) <= tol("bf16")
 
 
-# Small tiles split over a workspace: 64 tiles in 4 K ranges, 16 tiles of a
-# ragged product in 8.
-@pytest.mark.parametrize("shape", [(1024, 1024, 4096), (129, 1000, 8200)],
+# Small tiles split over a workspace: 40 tiles in 6 K ranges, 16 tiles of a
+# ragged product in 8 (more workgroups than the few-tile kernel would run).
+@pytest.mark.parametrize("shape", [(640, 1000, 8192), (129, 1000, 8200)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_small_tiles_split(shape):
     M, N, K = shape
@@ -105,19 +107,33 @@ def test_small_tiles_split(shape):
     check_op("bf16", 0, 0, M, N, K, 8700 + M, alpha=1.0, beta=1.0, ws=True)
 
 
-# 2048 x 1500: 192 tiles of 128 x 128, each alone on its CU; 300 x 520: 15
-# of them, so 40 tiles of 64 x 64. Ragged M, N and K in every layout.
+# 2048 x 1500: 192 tiles of 128 x 128, each alone on its CU; 1500 x 1530:
+# 144 of them and 576 of 64 x 64, so 64 x 64 tiles. Ragged M, N and K in
+# every layout, 16-byte rows (leading dimensions rounded up to multiples of 8).
+SMALL_TILE_SHAPES = [(2048, 1500, 300), (1500, 1530, 136)]
+
+
 @pytest.mark.parametrize("ops", OPS, ids=OP_IDS)
-@pytest.mark.parametrize("shape", [(2048, 1500, 300), (300, 520, 129)],
-                         ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("shape", SMALL_TILE_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_small_tiles_ragged(shape, ops):
+    from test_bf16_dword_gpu import inputs, run
+    from test_transpose_gpu import oracle_op
     M, N, K = shape
-    check_op("bf16", ops[0], ops[1], M, N, K, 8800 + 7 * ops[0] + ops[1] + M, alpha=0.75,
-             beta=0.5, pad=(8, 8, 8))
+    A, B, C0 = inputs(M, N, K, 8800 + 7 * ops[0] + ops[1] + M, 0.5)
+    note(f"bf16 small tiles {ops} M={M} N={N} K={K}")
+    C = run(ops, A, B, C0, 0.75, 0.5, four=False)
+    R, D = oracle_op("bf16", A, B, C0, 0.75, 0.5)
+    assert oracle.max_rel_err(to_f64(C), R, D) <= tol("bf16")
 
 
-@pytest.mark.parametrize("shape", [(2048, 1500, 300), (300, 520, 129)],
-                         ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("shape", SMALL_TILE_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_small_tiles_bias_gelu(shape):
+    from test_bf16_dword_gpu import inputs, run
+    from test_transpose_gpu import oracle_op
     M, N, K = shape
-    check_op("bf16", 1, 0, M, N, K, 8900 + M, alpha=1.25, beta=1.0, bias=True, act="gelu_tanh")
+    A, B, C0 = inputs(M, N, K, 8900 + M, 1.0)
+    bias = gi.random_matrix(1, N, "bf16", 8903)[0].contiguous()
+    note(f"bf16 small tiles, bias + GELU, M={M} N={N} K={K}")
+    C = run((1, 0), A, B, C0, 1.25, 1.0, four=False, bias=bias, act="gelu_tanh")
+    R, D = oracle_op("bf16", A, B, C0, 1.25, 1.0, bias, "gelu_tanh")
+    assert oracle.max_rel_err(to_f64(C), R, D) <= tol("bf16")

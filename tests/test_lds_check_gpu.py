@@ -81,7 +81,9 @@ CASES = [
     ("bf16", (4000, 4000, 200), (0, 0, 0), (0, 0), False, None),   # tiled, 256 large tiles, ragged
     ("bf16", (4000, 4000, 136), (8, 8, 8), (1, 1), False, None),   # large tiles, both transposed, padded
     ("bf16", (520, 520, 4100), (0, 0, 0), (0, 0), True, None),     # tiled split-K tail, ragged K
-    ("bf16", (520, 520, 4100), (0, 0, 0), (0, 0), False, None),    # same without a workspace: 64 x 64 tiles
+    ("bf16", (520, 520, 4100), (0, 0, 0), (0, 0), False, None),    # same without a workspace: few-tile kernel
+    ("bf16", (256, 264, 200), (0, 0, 0), (1, 1), False, None),     # few-tile kernel, both transposed
+    ("bf16", (1500, 1528, 136), (8, 0, 0), (0, 0), False, None),   # 64 x 64 tiles (576), 16-byte rows
     ("bf16", (2048, 1500, 300), (0, 0, 0), (0, 0), False, None),   # 192 small tiles, one per CU
     ("bf16", (2048, 1500, 300), (8, 8, 8), (1, 1), False, None),   # the same, both transposed
     ("bf16", (2048, 1500, 300), (2, 2, 2), (0, 1), False, None),   # the same, 4-byte copies, B stored N x K
@@ -147,7 +149,7 @@ def test_checking_builds_match_normal_build(case):
 
 # Split-K paths: repeated calls on one workspace must give identical bits
 # every time (fixed-order sums; counters left at zero by every call).
-REPEAT = [("bf16", (16, 8192, 8192)), ("bf16", (16, 1032, 4104)), ("bf16", (512, 512, 4096)),
+REPEAT = [("bf16", (16, 8192, 8192)), ("bf16", (16, 1032, 4104)), ("bf16", (512, 512, 16384)),
           ("f32", (2300, 2290, 2050)), ("f32", (1024, 1024, 4096))]
 
 

@@ -99,7 +99,8 @@ CASES = [
     ("bf16", (16, 4352, 1000), (0, 0, 0), (0, 0), True),     # small-M streaming split
     ("bf16", (100, 4160, 1500), (8, 8, 8), (0, 0), True),    # streaming split, 7 row blocks, padded
     ("bf16", (5, 100, 77), (1, 1, 1), (0, 0), False),        # small-M element-wise
-    ("bf16", (512, 512, 4096), (0, 0, 0), (0, 0), True),     # tiled split-K (M > 128)
+    ("bf16", (512, 512, 16384), (0, 0, 0), (0, 0), True),    # tiled split-K (M > 128)
+    ("bf16", (512, 512, 4096), (0, 0, 0), (0, 0), True),     # few-tile kernel (the workspace unused)
     ("bf16", (300, 264, 200), (0, 0, 0), (1, 0), False),     # tiled, A stored K x M
     ("bf16", (200, 136, 264), (0, 0, 0), (1, 1), False),     # tiled, both transposed
     ("bf16", (16, 520, 300), (0, 0, 0), (0, 1), True),       # small M, B stored N x K, split

@@ -216,8 +216,9 @@ def test_f32_split_k_deterministic():
 
 # (shape, ld padding): ragged M, N and K, K ranges of one or several slabs,
 # the ragged K tail in the last range, padded 16-byte rows.
-TILED_SHAPES = [((300, 520, 2100), (0, 0, 0)), ((257, 264, 4100), (0, 0, 0)),
-                ((512, 512, 4096), (0, 0, 0)), ((1024, 1024, 2048), (8, 16, 24)),
+# Long K against few tiles, so that the split beats the few-tile kernel.
+TILED_SHAPES = [((300, 520, 8200), (0, 0, 0)), ((257, 264, 4100), (0, 0, 0)),
+                ((512, 512, 16384), (0, 0, 0)), ((640, 1000, 8192), (8, 16, 24)),
                 ((129, 1000, 8200), (0, 0, 0))]
 
 
@@ -236,7 +237,7 @@ def test_bf16_tiled_split_k_parity(case, ops):
 
 def test_bf16_tiled_split_k_deterministic_and_counters_reset():
     from test_transpose_gpu import run_op
-    M, N, K = 512, 512, 4096
+    M, N, K = 512, 512, 16384
     A = gi.random_matrix(M, K, "bf16", 5200, dist="n")
     B = gi.random_matrix(K, N, "bf16", 5201)
     nbytes = dg.gemm_bf16_workspace_size(M, N, K)
@@ -253,7 +254,7 @@ def test_bf16_tiled_split_k_deterministic_and_counters_reset():
         outs.append(c.cpu())
     assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
     assert torch.equal(outs[0].view(torch.int16), outs[2].view(torch.int16))
-    assert int(ws[:4 * 4].view(torch.int32).abs().sum()) == 0          # 4 tiles' counters
+    assert int(ws[:16 * 4].view(torch.int32).abs().sum()) == 0         # 16 tiles' counters
     R, D = oracle_ref("bf16", A, B, None, 1.0, 0.0)
     assert oracle.max_rel_err(to_f64(outs[0]), R, D) <= tol("bf16")
 
