@@ -1,4 +1,4 @@
-// bf16 GEMM for products with few output tiles, 16-byte rows:
+// bf16 GEMM for products with few output tiles:
 // C = alpha * op(A) * op(B) + beta * C, fp32 accumulation, one rounding to bf16.
 //
 // With at most a few hundred 64 x 64 tiles each CU holds one workgroup of the
@@ -24,6 +24,12 @@
 // Edges as in the tiled kernel: descriptors end where the matrices end (rows
 // past M, N and K arrive as zeros), k >= K inside a k-contiguous slab is
 // zeroed in LDS, columns past N are never stored.
+//
+// Rows aligned to 4 bytes only (DW) fill the same LDS layouts with 4-byte
+// copies, four times as many instructions for the same bytes; the arithmetic,
+// and so every bit of the result, is that of 16-byte rows.
+
+#include <type_traits>
 
 #include "bf16_lds.hpp"
 #include "common.hpp"
@@ -40,7 +46,7 @@ constexpr int kSlab = kT * kBK;              // bf16 elements of one operand sla
 constexpr int kCopies = kSlab * 2 / 1024;    // 1 KB copies per operand slab
 constexpr int kGroupM = 4;
 
-template <bool EPI, bool TA, bool TB>
+template <bool EPI, bool TA, bool TB, bool DW>
 __global__ __launch_bounds__(kW * 64, 1)
 void gemm_bf16_few_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
     // [wave][stage][A slab | B slab]: 32 KB per wave.
@@ -66,11 +72,14 @@ void gemm_bf16_few_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
     auto b_stage = [&](int st) { return mine + st * 2 * kSlab + kSlab; };
 
     // Descriptors of the k-contiguous operands (row-major A, transposed B):
-    // rows m0 .. (or n0 ..) of the tile, ending after element K of the last one.
+    // rows m0 .. (or n0 ..) of the tile, ending after element K of the last
+    // one, rounded up to the copy width (16 bytes, or 4 with DW).
+    constexpr int64_t kRnd = DW ? 3 : 15;
+    constexpr int kSlabCopies = (DW ? 4 : 1) * 2 * kCopies;   // copy instructions per slab
     const int64_t rows_a = M - m0 < kT ? M - m0 : kT;
-    const rsrc_t a_desc = make_rsrc(p.A + m0 * lda, (uint32_t)((((rows_a - 1) * lda + K) * 2 + 15) & ~(int64_t)15));
+    const rsrc_t a_desc = make_rsrc(p.A + m0 * lda, (uint32_t)((((rows_a - 1) * lda + K) * 2 + kRnd) & ~kRnd));
     const int64_t rows_bt = N - n0 < kT ? N - n0 : kT;
-    const rsrc_t bt_desc = make_rsrc(p.B + n0 * ldb, (uint32_t)((((rows_bt - 1) * ldb + K) * 2 + 15) & ~(int64_t)15));
+    const rsrc_t bt_desc = make_rsrc(p.B + n0 * ldb, (uint32_t)((((rows_bt - 1) * ldb + K) * 2 + kRnd) & ~kRnd));
 
     // One slab of both operands into stage `st`: 8 copies of 1 KB each, lane l
     // of copy I filling bytes 16 l .. of rows 8 I + l / 8 at physical chunk
@@ -93,13 +102,62 @@ void gemm_bf16_few_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
                   (uint32_t)((8 * I) * ld * 2), dst + I * 1024);
         }
     };
-    auto issue = [&](int64_t kt, int st) {
+    // 4-byte copies: sub-copy s (0 .. 3) of 1 KB copy I fills LDS bytes
+    // 1024 I + 256 s .. + 255, lane l the 4 bytes at 4 l of them, which lie
+    // in rows 8 I + 2 s + h (h = l / 32) at in-row byte (4 l) mod 128 of the
+    // layout. A k-contiguous row r keeps its logical chunk c at physical
+    // chunk c ^ (r mod 8), here (l / 4) mod 8 ^ (2 s + h): the lane reads
+    // in-row byte (4 l) mod 128 ^ 16 h ^ 32 s. An m/n-contiguous row r uses
+    // the chunk swizzle b_swz(r), the same for both rows of a sub-copy: in-row
+    // byte (4 l) mod 128 ^ 16 b_swz(8 I + 2 s).
+    // The row stride and the LDS base pass through an empty asm statement, so
+    // that the 32 per-copy scalar offsets of an operand are formed at each
+    // slab instead of being hoisted out of the K loop, where they would not
+    // fit in scalar registers.
+    auto dw_kc = [&](rsrc_t desc, int64_t ld, int64_t k0, uint32_t dst) __attribute__((always_inline)) {
+        const int ln = opaque_lane(), h = ln >> 5;
+        uint32_t ld2 = (uint32_t)(ld * 2), base = dst;
+        asm volatile("" : "+s"(ld2), "+s"(base));
+        const uint32_t rowb = (uint32_t)h * ld2;
+        const uint32_t in0 = (uint32_t)(((4 * ln) & 127) ^ (h << 4));
+#pragma unroll
+        for (int I = 0; I < kCopies; ++I)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                dma4(desc, rowb + (in0 ^ (uint32_t)(32 * s)),
+                     (uint32_t)(8 * I + 2 * s) * ld2 + (uint32_t)(k0 * 2), base + 1024 * I + 256 * s);
+    };
+    auto dw_mn = [&](const uint16_t* bp, int64_t ld, int64_t k0, int64_t extent, uint32_t dst) __attribute__((always_inline)) {
+        const int64_t rem = (((K - k0 - 1) * ld + extent) * 2 + 3) & ~(int64_t)3;
+        const rsrc_t desc = make_rsrc(bp + k0 * ld, rem < ((int64_t)1 << 31) ? (uint32_t)rem : 0x80000000u);
+        const int ln = opaque_lane(), h = ln >> 5;
+        uint32_t ld2 = (uint32_t)(ld * 2), base = dst;
+        asm volatile("" : "+s"(ld2), "+s"(base));
+        const uint32_t rowb = (uint32_t)h * ld2;
+        const uint32_t in0 = (uint32_t)((4 * ln) & 127);
+#pragma unroll
+        for (int I = 0; I < kCopies; ++I)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int row = 8 * I + 2 * s;
+                dma4(desc, rowb + (in0 ^ (uint32_t)(b_swz<kT>(row) << 4)), (uint32_t)row * ld2,
+                     base + 1024 * I + 256 * s);
+            }
+    };
+    auto issue = [&](int64_t kt, int st) __attribute__((always_inline)) {
         const int64_t k0 = kt * kBK;
         const uint32_t As = lds_addr(a_stage(st)), Bs = lds_addr(b_stage(st));
-        if constexpr (TA) copy_mn(p.A + m0, lda, k0, M - m0, As);
-        else copy_kc(a_desc, lda, k0, As);
-        if constexpr (TB) copy_kc(bt_desc, ldb, k0, Bs);
-        else copy_mn(p.B + n0, ldb, k0, N - n0, Bs);
+        if constexpr (DW) {
+            if constexpr (TA) dw_mn(p.A + m0, lda, k0, M - m0, As);
+            else dw_kc(a_desc, lda, k0, As);
+            if constexpr (TB) dw_kc(bt_desc, ldb, k0, Bs);
+            else dw_mn(p.B + n0, ldb, k0, N - n0, Bs);
+        } else {
+            if constexpr (TA) copy_mn(p.A + m0, lda, k0, M - m0, As);
+            else copy_kc(a_desc, lda, k0, As);
+            if constexpr (TB) copy_kc(bt_desc, ldb, k0, Bs);
+            else copy_mn(p.B + n0, ldb, k0, N - n0, Bs);
+        }
         // Synchronous-copy build: the copies complete before anything else.
         if constexpr (kLdsCheck == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     };
@@ -165,7 +223,10 @@ void gemm_bf16_few_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
         if constexpr (kLdsCheck == 1) { poison(0); poison(1); }
         issue(kb, 0);
         if (kb + 1 < ke) issue(kb + 1, 1);
-        if (kb + 1 < ke) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kCopies));
+        // Wait for slab kb with slab kb + 1 still in flight (with 4-byte
+        // copies 64 instructions, one more than vmcnt counts: one of them is
+        // waited for too).
+        if (kb + 1 < ke) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kSlabCopies < 63 ? kSlabCopies : 63));
         else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         if (tail_here && kb + 1 == ke) zero_tail(0);
         read_frags(0, 0, 0);
@@ -220,12 +281,14 @@ void gemm_bf16_few_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
     if (row >= M) return;
     uint16_t* crow = p.C + row * p.ldc;
     const float fr = EPI ? row_factor(p, row) : alpha;
+    // With DW, C's rows too may be aligned to 4 bytes only.
+    using cvec = std::conditional_t<DW, u32x2_a4, u32x2>;
     u32x2 c0[4];
     if (beta != 0.f) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int64_t col = n0 + 16 * j + 4 * g;
-            c0[j] = col + 4 <= N ? *reinterpret_cast<const u32x2*>(crow + col) : u32x2{0u, 0u};
+            c0[j] = col + 4 <= N ? (u32x2)*reinterpret_cast<const cvec*>(crow + col) : u32x2{0u, 0u};
         }
     }
 #pragma unroll
@@ -243,7 +306,7 @@ void gemm_bf16_few_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
                 for (int r = 0; r < 4; ++r)
                     v[r] += beta * bf16_to_f32((uint16_t)(c0[j][r >> 1] >> (16 * (r & 1))));
             }
-            *reinterpret_cast<u32x2*>(crow + col) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            *reinterpret_cast<cvec*>(crow + col) = cvec{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
         } else {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -257,22 +320,24 @@ void gemm_bf16_few_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n) {
     }
 }
 
-template <bool EPI>
+template <bool EPI, bool DW>
 const void* pick_few(bool ta, bool tb) {
-    return ta ? (tb ? (const void*)&gemm_bf16_few_kernel<EPI, true, true>
-                    : (const void*)&gemm_bf16_few_kernel<EPI, true, false>)
-              : (tb ? (const void*)&gemm_bf16_few_kernel<EPI, false, true>
-                    : (const void*)&gemm_bf16_few_kernel<EPI, false, false>);
+    return ta ? (tb ? (const void*)&gemm_bf16_few_kernel<EPI, true, true, DW>
+                    : (const void*)&gemm_bf16_few_kernel<EPI, true, false, DW>)
+              : (tb ? (const void*)&gemm_bf16_few_kernel<EPI, false, true, DW>
+                    : (const void*)&gemm_bf16_few_kernel<EPI, false, false, DW>);
 }
 
 }  // namespace
 
-hipError_t launch_bf16_few(const GemmArgs<uint16_t>& a, hipStream_t s) {
+hipError_t launch_bf16_few(const GemmArgs<uint16_t>& a, bool dw, hipStream_t s) {
     const int64_t tiles_m = (a.M + kT - 1) / kT, tiles_n = (a.N + kT - 1) / kT;
     int tm = (int)tiles_m, tn = (int)tiles_n;
     GemmArgs<uint16_t> args = a;
     void* kargs[] = {&args, &tm, &tn};
-    const void* fn = has_epilogue(a) ? pick_few<true>(a.ta, a.tb) : pick_few<false>(a.ta, a.tb);
+    const bool epi = has_epilogue(a);
+    const void* fn = dw ? (epi ? pick_few<true, true>(a.ta, a.tb) : pick_few<false, true>(a.ta, a.tb))
+                        : (epi ? pick_few<true, false>(a.ta, a.tb) : pick_few<false, false>(a.ta, a.tb));
     if (tiles_m * tiles_n > kMaxGrid) return hipErrorInvalidConfiguration;
     return hipLaunchKernel(fn, dim3((unsigned)(tiles_m * tiles_n)), dim3(kW * 64), kargs, 0, s);
 }

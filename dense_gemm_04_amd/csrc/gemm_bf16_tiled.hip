@@ -701,7 +701,7 @@ const void* pick_tiled(bool ta, bool tb, bool dw) {
 //
 // Among products that take 128 x 128 tiles, those with at most 160 of them
 // (and no split over a workspace) run 64 x 64 tiles instead, unless the
-// few-tile kernel takes them (below; 16-byte rows): four times the
+// few-tile kernel takes them (below): four times the
 // workgroups for four times the LDS reads per MFMA. Measured against 128 x
 // 128 tiles: 1024^2 x 4096 (64 small tiles) 32.2 against 41.0 us, 1280^2 x
 // 4096 (100) 33.1 against 44.1, 1536^2 x 4096 (144) 41.1 against 43.2,
@@ -737,19 +737,25 @@ TailSplit plan_tiled128(int64_t M, int64_t N, int64_t K, int cus) {
 }
 
 // The few-tile kernel (gemm_bf16_few.hip: one 64 x 64 tile per workgroup, K
-// split over its 4 waves, one workgroup per CU), for 16-byte rows:
+// split over its 4 waves, one workgroup per CU):
 //   * without a split over a workspace, for up to two rounds of its tiles
 //     (512 on a full MI355X), where the tiled kernel's 64 x 64 or 128 x 128
 //     tiles would run (1024^2 x 4096: 18 against 32 us; 1280^2 x 4096, 400
 //     tiles: 31.8 against 33.3; 1536^2 x 4096, 576 tiles: 45.8 against 40.5);
+//     with 4-byte copies (dw) for one round only, as its four times as many
+//     copy instructions make a second round cost more than the tiled
+//     kernel's (1024^2 x 4096: 27.7 against 44.8 us; 1024 x 1536 x 4096,
+//     384 tiles: 52.0 against 49.0);
 //   * with one, when its tiles fit one round and are at least as many as the
 //     split's workgroups (1024^2 x 4096: 256 tiles against 64 x 4 ranges,
 //     18.3 against 24.1 us; 129 x 1000 x 8200: 48 against 16 x 8, 33.1
-//     against 23.2 us; 384 x 1024 x 8192: 96 against 24 x 8, 27.5 against 24.0).
-static bool few_preferred(int64_t M, int64_t N, const TailSplit* split) {
+//     against 23.2 us; 384 x 1024 x 8192: 96 against 24 x 8, 27.5 against 24.0;
+//     with 4-byte copies 1024^2 x 2048: 15.9 against 25.0 us, 1024^2 x 4096:
+//     28.6 against 29.4, 1024^2 x 8192: 49.6 against 41.3).
+static bool few_preferred(int64_t M, int64_t N, const TailSplit* split, bool dw) {
     const int64_t t64 = ((M + 63) / 64) * ((N + 63) / 64);
     if (split != nullptr) return t64 <= kTilePlanCus && t64 >= (int64_t)split->tail * split->parts;
-    return t64 <= 2 * kTilePlanCus;
+    return t64 <= (dw ? 1 : 2) * kTilePlanCus;
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool EPI>
@@ -786,7 +792,7 @@ hipError_t launch_bf16_tiled(const GemmArgs<uint16_t>& a, bool dw, void* ws, siz
         const int64_t t128 = ((a.M + 127) / 128) * ((a.N + 127) / 128);
         const TailSplit plan = plan_tiled128(a.M, a.N, a.K, cus);
         const bool split = ws != nullptr && plan.tail > 0 && ws_bytes >= tail_workspace(plan, 128, 128);
-        if (!dw && few_preferred(a.M, a.N, split ? &plan : nullptr)) return launch_bf16_few(a, s);
+        if (few_preferred(a.M, a.N, split ? &plan : nullptr, dw)) return launch_bf16_few(a, dw, s);
         if (8 * t128 <= 5 * kTilePlanCus && !split) {
             if (has_epilogue(a)) return launch_cfg<64, 64, 2, 2, true>(a, dw, ws, ws_bytes, cus, s);
             return launch_cfg<64, 64, 2, 2, false>(a, dw, ws, ws_bytes, cus, s);
@@ -801,9 +807,9 @@ hipError_t launch_bf16_tiled(const GemmArgs<uint16_t>& a, bool dw, void* ws, siz
 size_t bf16_tiled_workspace(int64_t M, int64_t N, int64_t K, int cus) {
     if (M < 1 || N < 1 || K < 1 || tiled_tile(M, N) != 128) return 0;
     const TailSplit plan = plan_tiled128(M, N, K, cus);
-    // Products the few-tile kernel takes in preference to the split (rows
-    // aligned to 16 bytes) need no workspace.
-    if (plan.tail > 0 && few_preferred(M, N, &plan)) return 0;
+    // Products the few-tile kernel takes in preference to the split need no
+    // workspace.
+    if (plan.tail > 0 && few_preferred(M, N, &plan, false)) return 0;
     return tail_workspace(plan, 128, 128);
 }
 

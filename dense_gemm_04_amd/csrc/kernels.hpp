@@ -29,9 +29,9 @@ hipError_t launch_bf16_mfma(const GemmArgs<uint16_t>& a, bool vec, void* ws, siz
 hipError_t launch_bf16_tiled(const GemmArgs<uint16_t>& a, bool dw, void* ws, size_t ws_bytes,
                              int cus, hipStream_t s);
 size_t bf16_tiled_workspace(int64_t M, int64_t N, int64_t K, int cus);
-// bf16 products with few 64 x 64 tiles and 16-byte rows: K split over the 4
-// waves of each workgroup (no workspace).
-hipError_t launch_bf16_few(const GemmArgs<uint16_t>& a, hipStream_t s);
+// bf16 products with few 64 x 64 tiles: K split over the 4 waves of each
+// workgroup (no workspace). `dw`: rows aligned to 4 bytes only (4-byte copies).
+hipError_t launch_bf16_few(const GemmArgs<uint16_t>& a, bool dw, hipStream_t s);
 bool bf16_tiled_fits(const GemmArgs<uint16_t>& a);
 hipError_t launch_bf16_general(const GemmArgs<uint16_t>& a, bool vec, hipStream_t s);
 // fp32 MFMA kernel. Given a workspace of at least f32_mfma_workspace(M, N, K,

@@ -1,6 +1,7 @@
 """bf16 operands whose rows are aligned to 4 bytes but not to 16 (even
 leading dimensions that are not multiples of 8, or bases 4 bytes past a
-16-byte boundary), through the C ABI: the tiled kernel's 4-byte copies.
+16-byte boundary), through the C ABI: the 4-byte copies of the tiled and
+few-tile kernels.
 
 * Those copies fill the same LDS layouts as the 1 KB copies of 16-byte rows,
   and the arithmetic is the same, so a product stored with 4-byte rows must
@@ -9,7 +10,8 @@ leading dimensions that are not multiples of 8, or bases 4 bytes past a
 * Against the oracle: ragged edges in every layout, bases offset by 2
   elements, the fused bias + GELU epilogue, quantisation scales, a split-K
   workspace, and a leading dimension just inside and just past the copies'
-  31-bit offset range (16-byte and 4-byte rows).
+  31-bit offset range (16-byte and 4-byte rows). Products with at most 256
+  tiles of 64 x 64 run on the few-tile kernel, the rest on the tiled one.
 """
 import pytest
 import torch
@@ -159,7 +161,7 @@ def test_oracle_split_k(ops):
     C = run(ops, A, B, C0, 1.0, 1.0, ws=True)
     R, D = oracle_op("bf16", A, B, C0, 1.0, 1.0)
     assert oracle.max_rel_err(to_f64(C), R, D) <= tol("bf16")
-    plain = run(ops, A, B, C0, 1.0, 1.0, ws=False)      # 288 tiles of 64 x 64
+    plain = run(ops, A, B, C0, 1.0, 1.0, ws=False)      # tiled kernel, 272 tiles of 64 x 64
     R2 = oracle.max_rel_err(to_f64(plain), R, D)
     assert R2 <= tol("bf16")
 

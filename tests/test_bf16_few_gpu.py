@@ -1,14 +1,18 @@
 """The bf16 few-tile kernel (one 64 x 64 tile per workgroup, K split over its
 4 waves, partials added in wave order), through the C ABI. It takes products
-with 16-byte rows whose 64 x 64 tiles fit two rounds of workgroups (512 on a
-full MI355X), or one round when a workspace split would run fewer workgroups.
+whose 64 x 64 tiles fit two rounds of workgroups (512 on a full MI355X), or
+one round when a workspace split would run fewer workgroups.
 
 * Against the oracle in every operand layout: ragged M, N and K, the ragged K
   tail in the last wave's last slab, K shorter than four slabs (idle waves),
   a single tile, two rounds of tiles, alpha / beta, bias + GELU, quantisation
   scales.
 * Exact small-integer products equal the exact result bit for bit (every
-  partial sum is exact, so a lost or doubled partial would show).
+  partial sum is exact, so a lost or doubled partial would show), with 16-byte
+  and with 4-byte rows.
+* Rows aligned to 4 bytes only (4-byte copies into the same LDS layouts) give
+  the bits of 16-byte rows in every layout, on the shapes above whose tiles
+  fit one round (the kernel takes no more with 4-byte rows).
 * Repeated calls give the same bits; a call with a workspace on a shape the
   kernel takes gives the plain call's bits (the workspace is not used).
 """
@@ -47,6 +51,22 @@ def test_parity(shape, ops):
         assert oracle.max_rel_err(to_f64(C), R, D) <= tol("bf16"), f"call {rep}"
 
 
+# With 4-byte rows the kernel takes one round of tiles (256), not two.
+ONE_ROUND = [s for s in SHAPES if ((s[0] + 63) // 64) * ((s[1] + 63) // 64) <= 256]
+
+
+@pytest.mark.parametrize("ops", OPS, ids=OP_IDS)
+@pytest.mark.parametrize("shape", ONE_ROUND, ids=lambda s: "x".join(map(str, s)))
+def test_four_byte_rows_same_bits(shape, ops):
+    M, N, K = shape
+    for rep, (alpha, beta) in enumerate(((1.0, 0.0), (0.75, -1.5))):
+        A, B, C0 = inputs(M, N, K, 9720 + 3 * M + rep, beta)
+        note(f"bf16 few-tile, 4-byte rows {ops} M={M} N={N} K={K} alpha={alpha} beta={beta}")
+        four = run(ops, A, B, C0, alpha, beta, four=True)
+        wide = run(ops, A, B, C0, alpha, beta, four=False)
+        assert torch.equal(four.view(torch.int16), wide.view(torch.int16)), f"call {rep}"
+
+
 @pytest.mark.parametrize("ops", [(0, 0), (1, 1)], ids=["NN", "TT"])
 def test_bias_gelu(ops):
     M, N, K = 300, 520, 1000
@@ -70,7 +90,8 @@ def test_scaled():
     assert oracle.max_rel_err(to_f64(C), R, D) <= tol("bf16")
 
 
-def test_exact_integers():
+@pytest.mark.parametrize("four", [False, True], ids=["16-byte", "4-byte"])
+def test_exact_integers(four):
     # Entries in -2 .. 2: every partial sum is an integer of magnitude at
     # most 4 K = 16000, exact in fp32, and so is alpha times it (alpha = 1/64):
     # the kernel's one rounding to bf16 must equal round-to-nearest-even of
@@ -79,8 +100,8 @@ def test_exact_integers():
     g = torch.Generator().manual_seed(9770)
     A = torch.randint(-2, 3, (M, K), generator=g).to(torch.bfloat16)
     B = torch.randint(-2, 3, (K, N), generator=g).to(torch.bfloat16)
-    note(f"bf16 few-tile, exact integers M={M} N={N} K={K}")
-    C = run((0, 0), A, B, None, 1.0 / 64, 0.0, four=False)
+    note(f"bf16 few-tile, exact integers M={M} N={N} K={K} four={four}")
+    C = run((0, 0), A, B, None, 1.0 / 64, 0.0, four=four)
     exact = (A.double() @ B.double()) / 64
     assert torch.equal(C, exact.to(torch.bfloat16))
 

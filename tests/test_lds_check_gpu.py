@@ -99,9 +99,12 @@ CASES = [
     ("bf16", (5, 100, 77), (1, 1, 1), (0, 0), False, None),        # small-M element-wise
     ("bf16", (130, 200, 129), (1, 3, 5), (0, 0), False, None),     # unaligned rows
     ("bf16", (4000, 4000, 200), (2, 2, 2), (0, 0), False, None),   # 4-byte copies, large tiles
-    ("bf16", (300, 264, 200), (2, 2, 2), (1, 1), False, None),     # 4-byte copies, both transposed
-    ("bf16", (300, 264, 129), (2, 2, 2), (1, 0), False, None),     # 4-byte copies, A stored K x M
-    ("bf16", (300, 264, 129), (1, 3, 2), (0, 1), False, None),     # 4-byte copies, B stored N x K
+    ("bf16", (300, 264, 200), (2, 2, 2), (1, 1), False, None),     # few-tile, 4-byte copies, both transposed
+    ("bf16", (300, 264, 129), (2, 2, 2), (1, 0), False, None),     # few-tile, 4-byte copies, A stored K x M
+    ("bf16", (300, 264, 129), (1, 3, 2), (0, 1), False, None),     # few-tile, 4-byte copies, B stored N x K
+    ("bf16", (520, 520, 4100), (2, 2, 2), (0, 0), False, None),    # few-tile, 4-byte copies, ragged K
+    ("bf16", (1500, 1530, 136), (2, 2, 2), (0, 0), False, None),   # 64 x 64 tiles (576), 4-byte copies
+    ("bf16", (1500, 1530, 136), (2, 2, 2), (1, 1), False, None),   # the same, both transposed
     ("bf16", (520, 522, 4100), (2, 0, 0), (0, 0), True, None),     # 4-byte copies, split K
     ("f32", (3000, 2900, 72), (0, 0, 0), (0, 0), False, None),     # copy path, 552 tiles walked
     ("f32", (2100, 2000, 100), (0, 0, 0), (1, 0), False, None),    # copy path, A stored K x M
