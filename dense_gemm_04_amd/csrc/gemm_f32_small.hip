@@ -290,6 +290,30 @@ F32Partition plan_f32_partition(int64_t M, int64_t N, int64_t K, bool split_ws) 
     const int64_t tm = (M + 127) / 128, tn = (N + 127) / 128;
     const int64_t slots = 2 * kPlanCus;       // the tiled kernel's resident workgroups
     const int64_t tiles = tm * tn, tail = tiles % slots;
+    if (tiles > kPlanCus && tiles < slots) {
+        // 257 .. 511 tiles: one round with two tiles on some CUs, which lasts
+        // about as long as a full round (kTiledRound2). The trailing columns
+        // (or rows) holding the tiles past one per CU can go to the few-tile
+        // kernel instead, leaving the tiled kernel one tile per CU
+        // (kTiledRound1). The model overstates the cost of the pair by about
+        // a tenth; measured (same box, plain calls, model ratio of the pair
+        // to the round in brackets): 2048 x 2304 x 4096 467 -> 328 us (0.74),
+        // 2048 x 2560 x 4096 467 -> 363 (0.84), 2304^2 x 4096 467 -> 403
+        // (0.94), 3072 x 2048 x 4096 471 -> 451 (1.06), but 2304 x 2816 x
+        // 4096 471 -> 503 (1.20) and 2560^2 x 4096 470 -> 528 (1.26). Hence
+        // the pair below 1.1. Given a workspace, splitting the round over K
+        // beat the pair from 0.94 up (2304^2 x 2048 204 against 207 us,
+        // 3072 x 2048 x 4096 432 against 451) and lost below (2048 x 2560 x
+        // 4096 408 against 363): the pair only below 0.9 then.
+        const int64_t extra = tiles - kPlanCus;
+        const int64_t rn = (extra + tm - 1) / tm, rm = (extra + tn - 1) / tn;
+        const double cost_n = rn < tn ? best_small_cost(M, N - (tn - rn) * 128) : 1e300;
+        const double cost_m = rm < tm ? best_small_cost(M - (tm - rm) * 128, N) : 1e300;
+        const bool by_cols = cost_n <= cost_m;
+        const double cost = by_cols ? cost_n : cost_m;
+        if (kTiledRound1 + cost > (split_ws ? 0.9 : 1.1) * kTiledRound2) return none;
+        return by_cols ? F32Partition{1, (tn - rn) * 128} : F32Partition{2, (tm - rm) * 128};
+    }
     if (tiles < slots || tail == 0) return none;
     // The last round's cost, and the strip that takes its tiles off the
     // tiled kernel: trailing tile columns (or rows) covering at least `tail`

@@ -81,7 +81,11 @@ typedef enum {
  * kernel and leave a last round partly full runs two kernels on one stream:
  * the MFMA kernel on whole rounds and GEMM_VARIANT_SMALL on the strip of
  * trailing columns (or rows) that held the last round's tiles (4095 x 4097:
- * C's last column). gemm_plan reports the MFMA family for such calls. */
+ * C's last column). So does one whose 257 .. 511 tiles would put two tiles
+ * on some compute units, when a model says the pair is faster: the MFMA
+ * kernel then runs at most one tile per compute unit and the strip holds the
+ * rest (2048 x 2560: columns 2048 .. 2559). gemm_plan reports the MFMA
+ * family for such calls. */
 typedef enum {
     GEMM_VARIANT_AUTO = 0,
     /* LDS-tiled MFMA kernel with 128-bit global loads; needs every pointer
@@ -216,7 +220,8 @@ gemm_status_t gemm_bf16_ws_noalloc(int64_t M, int64_t N, int64_t K, float alpha,
  * gemm_f32_workspace_size: workspace bytes gemm_f32_ws needs for this shape
  * on a full MI355X (256 compute units); 0 when it would not split (no last
  * round, or one the model leaves whole, or K below two 32-deep slabs), when
- * the few-tile kernel takes the shape, or when the sizes are invalid. Host only, no HIP call. On a device with fewer compute
+ * the few-tile kernel takes the shape or a strip of it (see
+ * GEMM_VARIANT_AUTO), or when the sizes are invalid. Host only, no HIP call. On a device with fewer compute
  * units the split is planned for that device and uses the workspace only if
  * it is large enough.
  *

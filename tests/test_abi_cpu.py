@@ -296,9 +296,13 @@ def test_f32_workspace_size(lib):
     assert dg.gemm_f32_workspace_size(300, 200, 100) == 0
     assert dg.gemm_f32_workspace_size(1024, 1024, 1024) == 0
     assert dg.gemm_f32_workspace_size(256, 256, 256) == 0
-    # 320 tiles (more than half of 512) of 128 slabs: p = 8 gives 5 rounds of
-    # 16 slabs + 8 x 0.25 = 82 against 128 unsplit.
-    assert dg.gemm_f32_workspace_size(128 * 16, 128 * 20, 4096) == 1280 + 320 * 8 * 128 * 128 * 4
+    # 257 .. 511 tiles: one round, two tiles on some CUs. 2048 x 2560 (320
+    # tiles) puts its last 4 tile columns (64 tiles) on the few-tile kernel and
+    # runs one tile per CU on the rest, which beats the split given a
+    # workspace too, so it needs none; so does 2048 x 2304 (288 tiles). For
+    # 2304^2 (above) the split wins when a workspace is given.
+    assert dg.gemm_f32_workspace_size(128 * 16, 128 * 20, 4096) == 0
+    assert dg.gemm_f32_workspace_size(2048, 2304, 4096) == 0
     # No split: whole rounds (4096^2 is 1024 tiles), a fuller last round whose
     # ranges would be shorter than 16 slabs (3072 x 2048 x 1024: 384 tiles of
     # 32 slabs), K of one slab, empty or invalid sizes.

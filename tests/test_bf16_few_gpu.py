@@ -22,7 +22,7 @@ import torch
 import dense_gemm_04_amd as dg
 import gemm_inputs as gi
 import oracle
-from gpu_util import note, to_f64, tol
+from gpu_util import note, padded, to_f64, tol
 from test_bf16_dword_gpu import inputs, run
 from test_transpose_gpu import oracle_op
 
@@ -67,13 +67,14 @@ def test_four_byte_rows_same_bits(shape, ops):
         assert torch.equal(four.view(torch.int16), wide.view(torch.int16)), f"call {rep}"
 
 
+@pytest.mark.parametrize("four", [False, True], ids=["16-byte", "4-byte"])
 @pytest.mark.parametrize("ops", [(0, 0), (1, 1)], ids=["NN", "TT"])
-def test_bias_gelu(ops):
+def test_bias_gelu(ops, four):
     M, N, K = 300, 520, 1000
     A, B, C0 = inputs(M, N, K, 9750 + ops[0], 1.0)
     bias = gi.random_matrix(1, N, "bf16", 9753)[0].contiguous()
-    note(f"bf16 few-tile, bias + GELU {ops} M={M} N={N} K={K}")
-    C = run(ops, A, B, C0, 1.25, 1.0, four=False, bias=bias, act="gelu_tanh")
+    note(f"bf16 few-tile, bias + GELU {ops} M={M} N={N} K={K} four={four}")
+    C = run(ops, A, B, C0, 1.25, 1.0, four=four, bias=bias, act="gelu_tanh")
     R, D = oracle_op("bf16", A, B, C0, 1.25, 1.0, bias, "gelu_tanh")
     assert oracle.max_rel_err(to_f64(C), R, D) <= tol("bf16")
 
@@ -106,22 +107,30 @@ def test_exact_integers(four):
     assert torch.equal(C, exact.to(torch.bfloat16))
 
 
-def test_repeatable_and_workspace_unused():
+@pytest.mark.parametrize("four", [False, True], ids=["16-byte", "4-byte"])
+def test_repeatable_and_workspace_unused(four):
     # 1024^2 x 4096: the split would cut its 64 tiles of 128 x 128 into 4 K
     # ranges (16 MiB of workspace); the few-tile kernel's 256 tiles take it.
     M, N, K = 1024, 1024, 4096
     assert dg.gemm_bf16_workspace_size(M, N, K) == 0
     A, B, C0 = inputs(M, N, K, 9780, 0.5)
-    note(f"bf16 few-tile, repeats and a workspace call, M={M} N={N} K={K}")
-    first = run((0, 0), A, B, C0, 1.0, 0.5, four=False)
-    again = run((0, 0), A, B, C0, 1.0, 0.5, four=False)
+    note(f"bf16 few-tile, repeats and a workspace call, M={M} N={N} K={K} four={four}")
+    first = run((0, 0), A, B, C0, 1.0, 0.5, four=four)
+    again = run((0, 0), A, B, C0, 1.0, 0.5, four=four)
     assert torch.equal(first.view(torch.int16), again.view(torch.int16))
-    a, b = A.cuda(), B.cuda()
-    c = C0.cuda()
+    # The same call through gemm_bf16_ws with a workspace, rows of
+    # K + 4 and N + 4 elements for 4-byte rows.
+    pad = 4 if four else 0
+    _, a = padded(M, K, K + pad, "bf16", fill=float("nan"))
+    a.copy_(A.cuda())
+    _, b = padded(K, N, N + pad, "bf16", fill=float("nan"))
+    b.copy_(B.cuda())
+    _, c = padded(M, N, N + pad, "bf16", fill=float("nan"))
+    c.copy_(C0.cuda())
     nbytes = (16 << 20) + 256
     ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
-    st = dg.gemm_bf16_ws(M, N, K, 1.0, a.data_ptr(), K, b.data_ptr(), N, 0.5, c.data_ptr(), N,
-                         ws.data_ptr(), nbytes, 0)
+    st = dg.gemm_bf16_ws(M, N, K, 1.0, a.data_ptr(), K + pad, b.data_ptr(), N + pad, 0.5,
+                         c.data_ptr(), N + pad, ws.data_ptr(), nbytes, 0)
     torch.cuda.synchronize()
     assert st == dg.GEMM_OK
     assert torch.equal(first.view(torch.int16), c.cpu().view(torch.int16))

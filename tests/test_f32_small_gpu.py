@@ -175,6 +175,10 @@ def test_partition_parity_full(shape, variant):
     (1) both operands stored transposed, rows padded to odd lengths;
     (2) row and column scales with bias and GELU; (3) B stored N x K with
     column scales and ReLU, workspace given (and unused)."""
+    _partition_parity(shape, variant)
+
+
+def _partition_parity(shape, variant):
     from test_scale_gpu import oracle_scaled, run_scaled, scales
     M, N, K = shape
     ops, pad, ws = [((0, 0), (0, 0, 0), False), ((1, 1), (1, 3, 5), False),
@@ -218,6 +222,45 @@ def test_partition_against_tiled_kernel_alone(shape):
         same = (slice(0, (tm - -(-tail // tn)) * 128), slice(None))
     else:                    # column strip
         same = (slice(None), slice(0, (tn - -(-tail // tm)) * 128))
+    assert torch.equal(Ca[same].view(torch.int32), Ct[same].view(torch.int32))
+    R, D = oracle_ref("f32", A, B, None, 1.0, 0.0)
+    assert oracle.max_rel_err(to_f64(Ca), R, D) <= tol("f32")
+
+
+# ---- one round with two tiles on some CUs: the tiles past one per CU ------
+#
+# With 257 .. 511 tiles of 128 x 128 the tiled kernel would run a single
+# round with two tiles on some CUs. The trailing tile columns (or rows) that
+# hold the tiles past one per CU go to the few-tile kernel instead, and the
+# tiled kernel runs one tile per CU on the rest. (M, N, K, strip): 2048 x 2560
+# (320 tiles): columns 2048 .. 2559; 2177 x 2300 (324 tiles, both edges
+# ragged): rows 1792 .. 2176 (385 rows); 3072 x 2048 (384 tiles): rows
+# 2048 .. 3071; 2304^2 (324 tiles): columns 1792 .. 2303.
+ONE_ROUND = [((2048, 2560, 200), ("cols", 2048)), ((2177, 2300, 129), ("rows", 1792)),
+             ((3072, 2048, 100), ("rows", 2048)), ((2304, 2304, 136), ("cols", 1792))]
+
+
+@pytest.mark.parametrize("variant", range(4))
+@pytest.mark.parametrize("case", ONE_ROUND, ids=lambda c: _sid(c[0]))
+def test_one_round_partition_parity_full(case, variant):
+    """As test_partition_parity_full, for the one-round partition."""
+    _partition_parity(case[0], variant)
+
+
+@pytest.mark.parametrize("case", ONE_ROUND, ids=lambda c: _sid(c[0]))
+def test_one_round_partition_against_tiled_kernel_alone(case):
+    """Outside the strip the outputs are the tiled kernel's alone (forced),
+    bit for bit; inside, they match the oracle."""
+    (M, N, K), (by, start) = case
+    A = gi.random_matrix(M, K, "f32", 8100 + M)
+    B = gi.random_matrix(K, N, "f32", 8101 + N)
+    note(f"one-round partition vs tiled alone M={M} N={N} K={K}")
+    Ca, st, _ = run("f32", A, B, None, 1.0, 0.0, dg.VARIANT_AUTO)
+    assert st == dg.GEMM_OK
+    forced = dg.VARIANT_MFMA if K % 4 == 0 and N % 4 == 0 else dg.VARIANT_GENERAL
+    Ct, st, _ = run("f32", A, B, None, 1.0, 0.0, forced)
+    assert st == dg.GEMM_OK
+    same = (slice(0, start), slice(None)) if by == "rows" else (slice(None), slice(0, start))
     assert torch.equal(Ca[same].view(torch.int32), Ct[same].view(torch.int32))
     R, D = oracle_ref("f32", A, B, None, 1.0, 0.0)
     assert oracle.max_rel_err(to_f64(Ca), R, D) <= tol("f32")
