@@ -784,8 +784,90 @@ hipError_t launch_cfg(const GemmArgs<uint16_t>& a, bool dw, void* ws, size_t ws_
     return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(WAVES_M * WAVES_N * 64), kargs, 0, s);
 }
 
+// Modelled time of what launch_tiles (below) runs for an M x N product
+// without a split, in rounds of 256 x 256 tiles at equal K: the few-tile
+// kernel about 0.17 of such a round per round of its tiles (0.28 with 4-byte
+// copies; 1024^2 x 4096: 17-18 and 27.7 us against about 100 for a round of
+// 256 x 256 tiles), 64 x 64 tiles 0.385 + 0.07 (q - 1) at q per CU, 128 x 128
+// tiles as in tiled_tile.
+static double tiled_cost(int64_t M, int64_t N, bool dw) {
+    const int64_t t64 = ((M + 63) / 64) * ((N + 63) / 64);
+    if (tiled_tile(M, N) == 128) {
+        if (few_preferred(M, N, nullptr, dw))
+            return (dw ? 0.28 : 0.17) * (double)((t64 + kTilePlanCus - 1) / kTilePlanCus);
+        const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+        if (8 * t128 <= 5 * kTilePlanCus)
+            return 0.385 + 0.07 * (double)((t64 + kTilePlanCus - 1) / kTilePlanCus - 1);
+        const int64_t full = t128 / (2 * kTilePlanCus), rem = t128 % (2 * kTilePlanCus);
+        return 0.61 * (double)full + (rem == 0 ? 0.0 : rem > kTilePlanCus ? 0.61 : 0.49);
+    }
+    const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+    return (double)((t256 + kTilePlanCus - 1) / kTilePlanCus);
+}
+
+struct Bf16Partition {
+    int by;            // 0: none; 1: columns [split, N) of C; 2: rows [split, M)
+    int64_t split;
+};
+
+// Products with at least one whole round of 256 x 256 tiles and a partly full
+// last one: the fewest trailing tile columns (or rows) that hold the last
+// round's tiles run as a separate product (on the few-tile kernel when it is
+// thin), leaving the tiled kernel whole rounds of 256 x 256 tiles, when the
+// model puts the pair below 0.95 of the whole product as planned. Measured
+// (same box, medians of 7; model ratio in brackets): 4352 x 4096 x 4096
+// 159.2 -> 128.6 us (0.68, a 256-row strip on the few-tile kernel),
+// 4224 x 4096 x 4096 159.4 -> 119.2 (0.68), 4096 x 4608 x 4096 149.6 -> 131.8
+// (0.78), 4500 x 4100 x 4096 218.3 -> 191.3 (0.87), 8448 x 8192 x 4096
+// 469.1 -> 441.9 (0.87), 8192 x 12544 x 4096 671.5 -> 649.1 (0.91); with
+// 4-byte rows 4352 x 4096 x 4096 219.5 -> 158.1 (0.75); but 5120^2 x 4096
+// 186.0 -> 183.7 and 6144 x 4352 x 4096 185.2 -> 187.1 (both 1.0).
+static Bf16Partition plan_bf16_partition(int64_t M, int64_t N, bool dw) {
+    const Bf16Partition none{0, 0};
+    const int64_t tm = (M + 255) / 256, tn = (N + 255) / 256, tiles = tm * tn;
+    const int64_t left = tiles % kTilePlanCus;
+    if (tiles <= kTilePlanCus || left == 0) return none;
+    const int64_t rn = (left + tm - 1) / tm, rm = (left + tn - 1) / tn;
+    auto rounds = [](int64_t t) { return (double)((t + kTilePlanCus - 1) / kTilePlanCus); };
+    const double cost_n = rn < tn ? rounds(tm * (tn - rn)) + tiled_cost(M, N - (tn - rn) * 256, dw) : 1e300;
+    const double cost_m = rm < tm ? rounds((tm - rm) * tn) + tiled_cost(M - (tm - rm) * 256, N, dw) : 1e300;
+    const bool by_cols = cost_n <= cost_m;
+    if ((by_cols ? cost_n : cost_m) >= 0.95 * tiled_cost(M, N, dw)) return none;
+    return by_cols ? Bf16Partition{1, (tn - rn) * 256} : Bf16Partition{2, (tm - rm) * 256};
+}
+
+static hipError_t launch_tiles(const GemmArgs<uint16_t>& a, bool dw, void* ws, size_t ws_bytes,
+                               int cus, hipStream_t s);
+
 hipError_t launch_bf16_tiled(const GemmArgs<uint16_t>& a, bool dw, void* ws, size_t ws_bytes,
                              int cus, hipStream_t s) {
+    const Bf16Partition pt = plan_bf16_partition(a.M, a.N, dw);
+    if (pt.by == 0) return launch_tiles(a, dw, ws, ws_bytes, cus, s);
+    GemmArgs<uint16_t> head = a, strip = a;
+    const int64_t k0 = pt.split;
+    if (pt.by == 1) {                      // columns [k0, N) of C
+        head.N = k0;
+        strip.N = a.N - k0;
+        strip.B = a.tb ? a.B + k0 * a.ldb : a.B + k0;
+        strip.C = a.C + k0;
+        if (a.bias != nullptr) strip.bias = a.bias + k0;
+        if (a.col_scale != nullptr) strip.col_scale = a.col_scale + k0;
+    } else {                               // rows [k0, M) of C
+        head.M = k0;
+        strip.M = a.M - k0;
+        strip.A = a.ta ? a.A + k0 : a.A + k0 * a.lda;
+        strip.C = a.C + k0 * a.ldc;
+        if (a.row_scale != nullptr) strip.row_scale = a.row_scale + k0;
+    }
+    // Whole rounds: the head takes 256 x 256 tiles (tiled_tile picks them for
+    // any product of whole rounds) and no split.
+    const hipError_t e = launch_tiles(head, dw, nullptr, 0, cus, s);
+    if (e != hipSuccess) return e;
+    return launch_tiles(strip, dw, nullptr, 0, cus, s);
+}
+
+static hipError_t launch_tiles(const GemmArgs<uint16_t>& a, bool dw, void* ws, size_t ws_bytes,
+                               int cus, hipStream_t s) {
     if (tiled_tile(a.M, a.N) == 128) {
         // At most 160 small tiles (on a full MI355X) and no split over a
         // workspace: 64 x 64 tiles.
@@ -806,6 +888,8 @@ hipError_t launch_bf16_tiled(const GemmArgs<uint16_t>& a, bool dw, void* ws, siz
 
 size_t bf16_tiled_workspace(int64_t M, int64_t N, int64_t K, int cus) {
     if (M < 1 || N < 1 || K < 1 || tiled_tile(M, N) != 128) return 0;
+    // A partitioned product (16-byte rows) runs no split.
+    if (plan_bf16_partition(M, N, false).by != 0) return 0;
     const TailSplit plan = plan_tiled128(M, N, K, cus);
     // Products the few-tile kernel takes in preference to the split need no
     // workspace.

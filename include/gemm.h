@@ -84,8 +84,12 @@ typedef enum {
  * C's last column). So does one whose 257 .. 511 tiles would put two tiles
  * on some compute units, when a model says the pair is faster: the MFMA
  * kernel then runs at most one tile per compute unit and the strip holds the
- * rest (2048 x 2560: columns 2048 .. 2559). gemm_plan reports the MFMA
- * family for such calls. */
+ * rest (2048 x 2560: columns 2048 .. 2559). A bf16 AUTO call with at least
+ * one whole round of 256 x 256 tiles and a partly full last one likewise runs
+ * the trailing columns (or rows) that hold the last round's tiles as a second
+ * product when a model says the pair is faster (4352 x 4096: rows 4096 ..
+ * 4351, on the few-tile kernel). gemm_plan reports the MFMA family for such
+ * calls. */
 typedef enum {
     GEMM_VARIANT_AUTO = 0,
     /* LDS-tiled MFMA kernel with 128-bit global loads; needs every pointer

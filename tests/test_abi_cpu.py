@@ -221,6 +221,10 @@ def test_workspace_size(lib):
     # small-M split when strips already fill the GPU, one K chunk, empty or
     # invalid sizes.
     assert dg.gemm_bf16_workspace_size(129, 8192, 8192) == 512 + 128 * 2 * 128 * 128 * 4
+    # 4352 x 4096 would take 128 x 128 tiles whose last round (64 of 1088) a
+    # workspace could split; it runs one round of 256 x 256 tiles and a
+    # 256-row strip on the few-tile kernel instead, with no workspace.
+    assert dg.gemm_bf16_workspace_size(4352, 4096, 4096) == 0
     assert dg.gemm_bf16_workspace_size(16, 2048, 8192) > 0
     assert dg.gemm_bf16_workspace_size(16, 16384, 128) == 0
     assert dg.gemm_bf16_workspace_size(16, 64, 128) == 0
