@@ -24,8 +24,10 @@ hipError_t launch_bf16_mfma(const GemmArgs<uint16_t>& a, bool vec, void* ws, siz
                             int cus, hipStream_t s);
 // The two bf16 MFMA kernels behind launch_bf16_mfma: the tiled kernel (needs
 // rows aligned to 16 bytes, or to 4 with `dw`, and offsets that fit its 31-bit
-// buffer offsets; splits K with a workspace) and the element-wise one that
-// takes any alignment.
+// buffer offsets; splits K with a workspace; products with few tiles go to
+// the few-tile kernel, and a partly full last round of 256 x 256 tiles may
+// run as a second product, a strip of trailing columns or rows) and the
+// element-wise one that takes any alignment.
 hipError_t launch_bf16_tiled(const GemmArgs<uint16_t>& a, bool dw, void* ws, size_t ws_bytes,
                              int cus, hipStream_t s);
 size_t bf16_tiled_workspace(int64_t M, int64_t N, int64_t K, int cus);
