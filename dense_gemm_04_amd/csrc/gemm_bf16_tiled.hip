@@ -76,11 +76,19 @@ using namespace bf16lds;
 // 8 waves per CU (at most 128 VGPRs) unless split over a workspace, which
 // only happens when the split workgroups fit one per CU; 64 x 64 tiles (4
 // waves) run up to four.
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool EPI, bool TA, bool TB, bool SPLIT, bool DW>
-__global__ __launch_bounds__(WAVES_M * WAVES_N * 64, (BM == 128 && !SPLIT) || BM == 64 ? 4 : 2)
+// KS = 2: two groups of WAVES_M x WAVES_N waves in one workgroup share each
+// tile, each over its own half of K with its own LDS stages (the host
+// launches it only with an even number of K slabs and no split); group 1
+// hands its accumulators to group 0 through LDS after the loop. Both groups
+// take every barrier in the same order: the loop's barriers depend only on
+// the number of slabs, which the groups share.
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool EPI, bool TA, bool TB, bool SPLIT, bool DW,
+          int KS = 1>
+__global__ __launch_bounds__(KS * WAVES_M * WAVES_N * 64, (BM == 128 && !SPLIT) || BM == 64 ? 4 : 2)
 void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, TailSplit ts,
                             unsigned char* ws) {
-    constexpr int kNT = WAVES_M * WAVES_N * 64;
+    static_assert(KS == 1 || (KS == 2 && !SPLIT && BM == 128 && BN == 128), "K split in the workgroup");
+    constexpr int kNT = WAVES_M * WAVES_N * 64;                // threads of one group
     constexpr int kWaves = WAVES_M * WAVES_N;
     constexpr int kBM = BM, kBN = BN;
     constexpr int kWTM = BM / WAVES_M, kWTN = BN / WAVES_N;   // wave tile
@@ -107,10 +115,11 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, Tail
     // stage an LDS-destined load writes and does not make reads of the other
     // stage wait for it. Laid out [A0 | A1 | B0 | B1]: stage 1 is 32 KB past
     // stage 0, within reach of the LDS instructions' immediate offset.
-    __shared__ __attribute__((aligned(16))) uint16_t a_st0[kAStage];
-    __shared__ __attribute__((aligned(16))) uint16_t a_st1[kAStage];
-    __shared__ __attribute__((aligned(16))) uint16_t b_st0[kBStage];
-    __shared__ __attribute__((aligned(16))) uint16_t b_st1[kBStage];
+    // With KS = 2 each array holds both groups' stages, group g at g x stage.
+    __shared__ __attribute__((aligned(16))) uint16_t a_st0[KS * kAStage];
+    __shared__ __attribute__((aligned(16))) uint16_t a_st1[KS * kAStage];
+    __shared__ __attribute__((aligned(16))) uint16_t b_st0[KS * kBStage];
+    __shared__ __attribute__((aligned(16))) uint16_t b_st1[KS * kBStage];
 
     const int64_t M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb;
     const int64_t nk = (K + kBK - 1) / kBK;
@@ -130,10 +139,17 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, Tail
         split_tile = true;
     }
     const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
-    const int t = threadIdx.x, lane = t & 63;
+    // wave / t: index within this thread's group (the whole workgroup when
+    // KS = 1); grp: the group, which owns slabs grp x nk / 2 .. with KS = 2.
+    const int grp = KS == 1 ? 0 : __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) / kWaves;
+    const int t = (int)threadIdx.x - grp * kNT, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    auto a_stage = [&](int stage) -> uint16_t* { return stage == 0 ? a_st0 : a_st1; };
-    auto b_stage = [&](int stage) -> uint16_t* { return stage == 0 ? b_st0 : b_st1; };
+    if constexpr (KS == 2) {
+        kb = grp * (nk / 2);
+        ke = kb + nk / 2;
+    }
+    auto a_stage = [&](int stage) -> uint16_t* { return (stage == 0 ? a_st0 : a_st1) + grp * kAStage; };
+    auto b_stage = [&](int stage) -> uint16_t* { return (stage == 0 ? b_st0 : b_st1) + grp * kBStage; };
 
     // A descriptor (row-major A): rows m0 .. min(M, m0 + 256) - 1, ending
     // after element K of the last row (rounded up to its 16-byte chunk, which
@@ -397,6 +413,9 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, Tail
     // that ends at nk holds the ragged K tail.
     const int k_tail = (int)(K - (nk - 1) * kBK);   // 1 .. 64
     const bool tail_here = kZeroTail && ke == nk && k_tail < kBK;
+    // The barrier after the zeroing: taken by both groups of a KS = 2
+    // workgroup at the same slab index (their ranges have equal lengths).
+    const bool tail_bar = kZeroTail && k_tail < kBK && (KS == 2 || ke == nk);
     // Checking builds: both stages start as NaN (poison) and every batch of
     // copies is bracketed by barriers (synchronous copies); no-ops otherwise.
     auto retire = [&](int stage) {
@@ -411,8 +430,8 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, Tail
     dma(kb, 0);
     copy_end();
     lds_barrier();
-    if (tail_here && kb + 1 == ke) {
-        zero_a_tail(0, k_tail);
+    if (tail_bar && kb + 1 == ke) {
+        if (tail_here) zero_a_tail(0, k_tail);
         lds_barrier();
     }
     if (kb + 1 < ke) {
@@ -430,8 +449,8 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, Tail
             lds_barrier();
             // Every read of stage `cur` (slab kt) is retired here.
             retire(cur);
-            if (tail_here && kt + 2 == ke) {
-                zero_a_tail(cur ^ 1, k_tail);
+            if (tail_bar && kt + 2 == ke) {
+                if (tail_here) zero_a_tail(cur ^ 1, k_tail);
                 lds_barrier();
             }
             if (kt + 2 < ke) {
@@ -446,6 +465,38 @@ void gemm_bf16_tiled_kernel(GemmArgs<uint16_t> p, int tiles_m, int tiles_n, Tail
     for (int64_t kt = kb; kt < ke; kt += 2) {
         slab(kt, 0);
         if (kt + 1 < ke) slab(kt + 1, 1);
+    }
+
+    if constexpr (KS == 2) {
+        // Group 1 hands its partial tile to group 0 through LDS (value c of
+        // lane l of wave w at f32x4 (c x waves + w) x 64 + l, across a_st0 and
+        // a_st1), and group 0 adds it to its own: acc = first half of K +
+        // second half, the same bits on every call.
+        constexpr int E4 = kFN * kFM;
+        constexpr int kPerArr = KS * kAStage * 2 / 16;                // f32x4 per A array
+        static_assert(E4 * kWaves * 64 <= 2 * kPerArr, "partial tile fits the A stages");
+        auto slot = [&](int c) -> f32x4* {
+            const int q = (c * kWaves + wave) * 64 + lane;
+            return reinterpret_cast<f32x4*>(q < kPerArr ? a_st0 : a_st1) + (q < kPerArr ? q : q - kPerArr);
+        };
+        lds_only_barrier();                            // every stage read is done
+        if (grp == 1) {
+#pragma unroll
+            for (int j = 0; j < kFN; ++j)
+#pragma unroll
+                for (int i = 0; i < kFM; ++i) *slot(j * kFM + i) = acc[j][i];
+        }
+        lds_only_barrier();
+        if (grp == 1) {
+            // The epilogue below takes one barrier for whole tiles (before
+            // its scratch use) and none otherwise: match it, then leave.
+            if ((kWTN == 64 || kWTN == 32) && m0 + kBM <= M && n0 + kBN <= N) lds_only_barrier();
+            return;
+        }
+#pragma unroll
+        for (int j = 0; j < kFN; ++j)
+#pragma unroll
+            for (int i = 0; i < kFM; ++i) acc[j][i] += *slot(j * kFM + i);
     }
 
     if constexpr (SPLIT) {
@@ -664,23 +715,24 @@ bool bf16_tiled_fits(const GemmArgs<uint16_t>& a) {
     return (a.ta ? mc(a.lda, a.M) : kc(a.lda)) && (a.tb ? kc(a.ldb) : mc(a.ldb, a.N));
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool EPI, bool SPLIT, bool DW>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool EPI, bool SPLIT, bool DW, int KS = 1>
 const void* pick_layout(bool ta, bool tb) {
 #define DG_TILED(TA, TB) \
-    (const void*)&gemm_bf16_tiled_kernel<BM, BN, WAVES_M, WAVES_N, EPI, TA, TB, SPLIT, DW>
+    (const void*)&gemm_bf16_tiled_kernel<BM, BN, WAVES_M, WAVES_N, EPI, TA, TB, SPLIT, DW, KS>
     return ta ? (tb ? DG_TILED(true, true) : DG_TILED(true, false))
               : (tb ? DG_TILED(false, true) : DG_TILED(false, false));
 #undef DG_TILED
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool EPI, bool SPLIT>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool EPI, bool SPLIT, int KS = 1>
 const void* pick_tiled(bool ta, bool tb, bool dw) {
-    return dw ? pick_layout<BM, BN, WAVES_M, WAVES_N, EPI, SPLIT, true>(ta, tb)
-              : pick_layout<BM, BN, WAVES_M, WAVES_N, EPI, SPLIT, false>(ta, tb);
+    return dw ? pick_layout<BM, BN, WAVES_M, WAVES_N, EPI, SPLIT, true, KS>(ta, tb)
+              : pick_layout<BM, BN, WAVES_M, WAVES_N, EPI, SPLIT, false, KS>(ta, tb);
 }
 
 // Three tile sizes: 256 x 256 (8 waves of 128 x 64, 128 KB of LDS, one
-// workgroup per CU), 128 x 128 (8 waves of 64 x 32, 64 KB, two per CU) and
+// workgroup per CU), 128 x 128 (8 waves of 64 x 32, 64 KB, two per CU; or,
+// one per CU, 16 waves in two groups that split K, 128 KB: ks_preferred) and
 // 64 x 64 (4 waves of 32 x 32, 32 KB, up to four per CU).
 // The smaller tile multiplies less per byte it stages (4096^3: 127.5 against
 // 103.3 us) but gives four times the workgroups, which products with few
@@ -758,6 +810,23 @@ static bool few_preferred(int64_t M, int64_t N, const TailSplit* split, bool dw)
     return t64 <= (dw ? 1 : 2) * kTilePlanCus;
 }
 
+// 128 x 128 tiles with K split between two groups of 8 waves in each
+// workgroup (KS = 2, 16 waves and 128 KB of LDS per CU): for products with at
+// most one such tile per CU and an even number of at least 32 K slabs. A CU
+// holding one tile of the plain kernel runs 8 waves, 2 per SIMD; two groups
+// give it 4 per SIMD, as two workgroups per CU would, and the tile finishes in
+// about half the slab steps. Measured (same box, medians of 7): 512 x 8192 x
+// 8192 87.0 -> 72.5 us, 2048^2 x 8192 86.7 -> 77.4, 1024 x 4096 x 4096 43.5
+// -> 37.6, 1792 x 2048 x 8192 77.9 -> 66.7, 2048^2 x 2048 24.9 -> 23.2, but
+// 2048^2 x 1024 (16 slabs) 12.5 -> 13.6. It also replaces 64 x 64 tiles for
+// 129 .. 160 tiles of 128 x 128 (1536^2 x 4096 41.8 -> 36.6 us, 1536^2 x 8192
+// 77.2 -> 64.0, with 4-byte rows 66.5 -> 53.2), not for fewer (with 4-byte
+// rows 1280^2 x 4096, 100 tiles: 49.8 -> 53.1).
+static bool ks_preferred(int64_t tiles128, int64_t K) {
+    const int64_t nk = (K + kBK - 1) / kBK;
+    return tiles128 <= kTilePlanCus && nk % 2 == 0 && nk >= 32;
+}
+
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool EPI>
 hipError_t launch_cfg(const GemmArgs<uint16_t>& a, bool dw, void* ws, size_t ws_bytes, int cus,
                       hipStream_t s) {
@@ -773,15 +842,21 @@ hipError_t launch_cfg(const GemmArgs<uint16_t>& a, bool dw, void* ws, size_t ws_
     }
     unsigned char* wsp = split ? static_cast<unsigned char*>(ws) : nullptr;
     void* kargs[] = {&args, &tm, &tn, &ts, &wsp};
+    // At most one 128 x 128 tile per CU and no split: two groups of 8 waves
+    // share each tile's K (ks_preferred).
+    int ks = 1;
+    if constexpr (BM == 128)
+        if (!split && ks_preferred(tiles_m * tiles_n, a.K)) ks = 2;
     const void* fn;
     if constexpr (BM == 128)
         fn = split ? pick_tiled<BM, BN, WAVES_M, WAVES_N, EPI, true>(a.ta, a.tb, dw)
-                   : pick_tiled<BM, BN, WAVES_M, WAVES_N, EPI, false>(a.ta, a.tb, dw);
+             : ks == 2 ? pick_tiled<BM, BN, WAVES_M, WAVES_N, EPI, false, 2>(a.ta, a.tb, dw)
+                       : pick_tiled<BM, BN, WAVES_M, WAVES_N, EPI, false>(a.ta, a.tb, dw);
     else
         fn = pick_tiled<BM, BN, WAVES_M, WAVES_N, EPI, false>(a.ta, a.tb, dw);
     const int64_t grid = split ? (int64_t)ts.full + (int64_t)ts.tail * ts.parts : tiles_m * tiles_n;
     if (grid > kMaxGrid) return hipErrorInvalidConfiguration;
-    return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(WAVES_M * WAVES_N * 64), kargs, 0, s);
+    return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(ks * WAVES_M * WAVES_N * 64), kargs, 0, s);
 }
 
 // Modelled time of what launch_tiles (below) runs for an M x N product
@@ -875,7 +950,7 @@ static hipError_t launch_tiles(const GemmArgs<uint16_t>& a, bool dw, void* ws, s
         const TailSplit plan = plan_tiled128(a.M, a.N, a.K, cus);
         const bool split = ws != nullptr && plan.tail > 0 && ws_bytes >= tail_workspace(plan, 128, 128);
         if (few_preferred(a.M, a.N, split ? &plan : nullptr, dw)) return launch_bf16_few(a, dw, s);
-        if (8 * t128 <= 5 * kTilePlanCus && !split) {
+        if (8 * t128 <= 5 * kTilePlanCus && !split && !(2 * t128 > kTilePlanCus && ks_preferred(t128, a.K))) {
             if (has_epilogue(a)) return launch_cfg<64, 64, 2, 2, true>(a, dw, ws, ws_bytes, cus, s);
             return launch_cfg<64, 64, 2, 2, false>(a, dw, ws, ws_bytes, cus, s);
         }

@@ -85,6 +85,8 @@ CASES = [
     ("bf16", (256, 264, 200), (0, 0, 0), (1, 1), False, None),     # few-tile kernel, both transposed
     ("bf16", (1500, 1528, 136), (8, 0, 0), (0, 0), False, None),   # 64 x 64 tiles (576), 16-byte rows
     ("bf16", (2048, 1500, 300), (0, 0, 0), (0, 0), False, None),   # 192 small tiles, one per CU
+    ("bf16", (2048, 2048, 2048), (0, 0, 0), (0, 0), False, None),  # 128 x 128 tiles, K split in the workgroup
+    ("bf16", (2000, 2000, 2150), (2, 2, 2), (1, 1), False, None),  # the same, ragged, K tail, 4-byte copies, both transposed
     ("bf16", (2048, 1500, 300), (8, 8, 8), (1, 1), False, None),   # the same, both transposed
     ("bf16", (2048, 1500, 300), (2, 2, 2), (0, 1), False, None),   # the same, 4-byte copies, B stored N x K
     ("bf16", (300, 264, 200), (0, 0, 0), (1, 0), False, None),     # tiled, A stored K x M
