@@ -2,15 +2,16 @@
 sizes and in the launch configuration it times (default kernel choice, packed
 leading dimensions): the plain call, and the split-K call through a workspace
 when the size query asks for one. Between them they run the bf16 tiled kernel
-on 128 x 128 tiles with and without a tail split, the small-M kernel at 128
-rows, the fp32 kernel with a last round more than half full (plain and split)
-and the bf16 few-tile kernel.
+on 128 x 128 tiles (K split between two groups of waves) and on a round of
+256 x 256 tiles beside a strip, the small-M kernel at 128 rows, the fp32
+kernel with a last round more than half full (one tile per CU beside a strip,
+or split over K) and the bf16 few-tile kernel.
 
 Compared with the oracle on sampled rows and columns of C that touch every
 64-row and every 64-column band (the first, the last and one random row of
 each band, over all N columns; the same for columns, over all M rows): every
 output tile of every kernel is checked, while the oracle does a few percent
-of the full product (the full oracle for the six shapes takes minutes).
+of the full product (the full oracle for these shapes takes minutes).
 """
 import numpy as np
 import pytest
