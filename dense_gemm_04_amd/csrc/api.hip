@@ -76,6 +76,22 @@ bool small_m_ok(int64_t M, bool vec, bool tb) {
     return vec ? M <= dg::kSkinnyMaxM : (!tb && M <= dg::kSkinnyElemMaxM);
 }
 
+// 65 .. 128 rows run faster on the tiled kernels (their few-tile kernel,
+// 64 x 64 tiles with K split over each workgroup's waves) whenever those
+// tiles fit one round of compute units: the small-M kernel then holds 8 row
+// blocks of A per strip and streams B at about half the rate. Same box, B
+// from HBM (4 rotating operand sets), small-M kernel plain / with its split
+// over a workspace / few-tile kernel: 96 x 8192 x 8192 77.9 / 43.2 / 43.7 us,
+// 128 x 8192 x 8192 79.2 / 45.8 / 48.4, 128 x 4096 x 8192 73.3 / 45.7 /
+// 37.0, 96 x 4096 x 4096 33.1 / 36.8 / 16.7, 96 x 8192 x 2048 18.0 / 27.1 /
+// 12.6. With two rounds of those tiles the small-M kernel stays (128 x 12288
+// x 4096: 43.6 against 52.3 us). Only 16-byte rows take the small-M kernel
+// above 32 rows, so the rule needs no alignment (the workspace size query
+// applies it too).
+bool small_m_to_tiles(int64_t M, int64_t N) {
+    return M > 64 && ((M + 63) / 64) * ((N + 63) / 64) <= 256;
+}
+
 // The kernel family for a valid call that has GEMM work, or -1 if the
 // requested family cannot run it. The small-M kernel reads row-major A and
 // either a row-major B or, with 16-byte rows, a transposed one; other
@@ -84,7 +100,8 @@ int choose(int esz, int64_t M, int64_t N, int64_t K, bool vec, int variant, bool
            bool tb = false) {
     switch (variant) {
         case GEMM_VARIANT_AUTO:
-            if (esz == 2 && !ta && small_m_ok(M, vec, tb)) return GEMM_VARIANT_SKINNY;
+            if (esz == 2 && !ta && small_m_ok(M, vec, tb) && !small_m_to_tiles(M, N))
+                return GEMM_VARIANT_SKINNY;
             if (esz == 4 && dg::f32_small_preferred(M, N, K, false)) return GEMM_VARIANT_SMALL;
             return vec ? GEMM_VARIANT_MFMA : GEMM_VARIANT_GENERAL;
         case GEMM_VARIANT_MFMA:
@@ -324,7 +341,7 @@ gemm_status_t gemm_bf16_ex(int64_t M, int64_t N, int64_t K, float alpha, const u
 
 size_t gemm_bf16_workspace_size(int64_t M, int64_t N, int64_t K) {
     if (M < 0 || N < 0 || K < 0 || M > INT_MAX || N > INT_MAX || K > INT_MAX) return 0;
-    if (M <= dg::kSkinnyMaxM) return dg::bf16_skinny_workspace(M, N, K);
+    if (M <= dg::kSkinnyMaxM && !small_m_to_tiles(M, N)) return dg::bf16_skinny_workspace(M, N, K);
     return dg::bf16_tiled_workspace(M, N, K, kFullCus);
 }
 

@@ -110,7 +110,10 @@ typedef enum {
     GEMM_VARIANT_VALU = 3,
     /* bf16 only, M <= 128 with 16-byte rows (M <= 32 otherwise): small-M
      * kernel that streams B once (Blackwell BF16 GEMM notes, section 5.2:
-     * small-batch GEMMs are bandwidth bound). */
+     * small-batch GEMMs are bandwidth bound). AUTO takes it for such calls
+     * except 65 .. 128 rows whose 64 x 64 tiles fit one round of compute
+     * units (N <= 8192), which run faster on the MFMA family's few-tile
+     * kernel, with or without a workspace. */
     GEMM_VARIANT_SKINNY = 4,
     /* fp32 only, any shape and alignment: few-tile kernel. Each workgroup owns
      * a 16 x 16, 32 x 32 or 64 x 64 tile of C and its waves split K between
@@ -196,8 +199,8 @@ gemm_status_t gemm_bf16_ws(int64_t M, int64_t N, int64_t K, float alpha,
  * Results are those of gemm_bf16_ws with a workspace of
  * gemm_bf16_workspace_size(M, N, K) bytes (bit for bit). Shapes whose
  * workspace would exceed the scratch return GEMM_ERR_SCRATCH_LIMIT and
- * launch nothing (16 x 8192 x 8192 needs 4 MiB and 128 x 8192 x 8192 32 MiB,
- * which fit; 128 x 4352 x 8192 needs 34 MiB, which does not; shapes that
+ * launch nothing (16 x 8192 x 8192 needs 4 MiB and 128 x 16384 x 8192 32 MiB,
+ * which fit; 128 x 8256 x 8192 needs 33 MiB, which does not; shapes that
  * would not split need none and run as gemm_bf16). All calls on one GPU share its scratch: calls that overlap
  * in time on one GPU (different streams, or threads without ordering) race
  * and give undefined results; calls ordered on one stream are safe. Other
@@ -296,8 +299,9 @@ gemm_status_t gemm_bf16_bias_act(int64_t M, int64_t N, int64_t K, float alpha,
  * gemm_*_bias_act (with opa == opb == GEMM_OP_N the two calls are the same);
  * an opa or opb other than the two codes is GEMM_ERR_INVALID_VALUE. The
  * small-M kernel (bf16, M <= 128) reads a row-major A and a row-major or,
- * with 16-byte rows, transposed B; other transposed small-M calls run on the
- * tiled kernels. */
+ * with 16-byte rows, transposed B; other transposed small-M calls, like the
+ * 65 .. 128-row calls that GEMM_VARIANT_SKINNY describes, run on the tiled
+ * kernels. */
 typedef enum { GEMM_OP_N = 0, GEMM_OP_T = 1 } gemm_op_t;
 
 gemm_status_t gemm_f32_op(int opa, int opb, int64_t M, int64_t N, int64_t K, float alpha,

@@ -121,7 +121,12 @@ def test_plan_chooses_family(lib):
     assert plan(esz=2, M=16) == dg.VARIANT_SKINNY             # bf16, M <= 128 (16-byte rows)
     assert plan(esz=2, M=32) == dg.VARIANT_SKINNY
     assert plan(esz=2, M=33) == dg.VARIANT_SKINNY
-    assert plan(esz=2, M=128) == dg.VARIANT_SKINNY
+    assert plan(esz=2, M=64) == dg.VARIANT_SKINNY
+    # 65 .. 128 rows: the tiled kernels when their 64 x 64 tiles fit one round
+    # (at most 256; here 2), else the small-M kernel (2 x 129 tiles).
+    assert plan(esz=2, M=128) == dg.VARIANT_MFMA
+    assert plan(esz=2, M=65, N=8192) == dg.VARIANT_MFMA
+    assert plan(esz=2, M=128, N=8256) == dg.VARIANT_SKINNY
     assert plan(esz=2, M=129) == dg.VARIANT_MFMA
     assert plan(esz=2, M=32, lda=66) == dg.VARIANT_SKINNY      # unaligned: element-wise, M <= 32
     assert plan(esz=2, M=33, lda=66) == dg.VARIANT_GENERAL
@@ -157,9 +162,9 @@ def test_noalloc_checks_before_any_hip_call(lib):
     assert noalloc(4, 4, 4, 1.0, A, 3, B, 4, 0.0, C, 4, 0) == dg.GEMM_ERR_INVALID_VALUE
     assert noalloc(4, 4, 4, 1.0, A + 1, 4, B, 4, 0.0, C, 4, 0) == dg.GEMM_ERR_INVALID_VALUE
     assert noalloc(0, 4, 4, 1.0, None, 4, None, 4, 0.0, None, 4, 0) == dg.GEMM_OK
-    # 128 x 4352 x 8192: 17 strips x 16 phases of 128 x 256 fp32 partials.
-    assert dg.gemm_bf16_workspace_size(128, 4352, 8192) > dg.NOALLOC_SCRATCH_BYTES
-    assert noalloc(128, 4352, 8192, 1.0, A, 8192, B, 4352, 0.0, C, 4352,
+    # 128 x 8256 x 8192: 33 strips x 8 phases of 128 x 256 fp32 partials.
+    assert dg.gemm_bf16_workspace_size(128, 8256, 8192) > dg.NOALLOC_SCRATCH_BYTES
+    assert noalloc(128, 8256, 8192, 1.0, A, 8192, B, 8256, 0.0, C, 8256,
                    0) == dg.GEMM_ERR_SCRATCH_LIMIT
     import torch
     if not torch.cuda.is_available():
@@ -200,7 +205,12 @@ def test_workspace_size(lib):
     # 17..32 rows use 32-row tiles, 33..64 64-row and 65..128 128-row tiles.
     assert dg.gemm_bf16_workspace_size(32, 8192, 8192) == 256 + 32 * 8 * 32 * 256 * 4
     assert dg.gemm_bf16_workspace_size(33, 8192, 8192) == 256 + 32 * 8 * 64 * 256 * 4
-    assert dg.gemm_bf16_workspace_size(128, 8192, 8192) == 256 + 32 * 8 * 128 * 256 * 4
+    assert dg.gemm_bf16_workspace_size(128, 16384, 8192) == 256 + 64 * 4 * 128 * 256 * 4
+    # 65 .. 128 rows whose 64 x 64 tiles fit one round run on the tiled
+    # kernels (the few-tile kernel here: no workspace; 128 x 4352: the split
+    # of 34 tiles of 128 x 128 into 7 K ranges).
+    assert dg.gemm_bf16_workspace_size(128, 8192, 8192) == 0
+    assert dg.gemm_bf16_workspace_size(128, 4352, 8192) == 256 + 34 * 7 * 128 * 128 * 4
     # 64 strips of 256 columns: 4 phases fill the chip.
     assert dg.gemm_bf16_workspace_size(16, 16384, 8192) == 256 + 64 * 4 * 16 * 256 * 4
     # 16 strips (N = 3841) would take 16 phases, the most; K = 4104 has 129

@@ -135,3 +135,28 @@ def test_repeatable_and_workspace_unused(four):
     assert st == dg.GEMM_OK
     assert torch.equal(first.view(torch.int16), c.cpu().view(torch.int16))
     assert int(ws.count_nonzero()) == 0
+
+
+# 65 .. 128 rows whose 64 x 64 tiles fit one round: without a workspace the
+# automatic choice runs them on this kernel instead of the small-M one (with
+# a workspace the small-M split still runs, and must agree with the oracle
+# too). Ragged M, N and K; B row-major or stored N x K.
+SMALL_M_SHAPES = [(65, 520, 1000), (100, 8192, 300), (128, 1000, 4100)]
+
+
+@pytest.mark.parametrize("ops", [(0, 0), (0, 1)], ids=["NN", "NT"])
+@pytest.mark.parametrize("shape", SMALL_M_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_small_m_rows_plain_and_with_workspace(shape, ops):
+    M, N, K = shape
+    if ops == (0, 0):
+        # gemm_plan describes the row-major call.
+        from test_bf16_dword_gpu import _ld
+        plan = dg.gemm_plan(2, M, N, K, 1.0, 16, _ld(K, False), 16, _ld(N, False), 0.0, 16,
+                            _ld(N, False), dg.VARIANT_AUTO)
+        assert plan == dg.VARIANT_MFMA
+    A, B, C0 = inputs(M, N, K, 9790 + M + ops[1], 0.5)
+    R, D = oracle_op("bf16", A, B, C0, 0.75, 0.5)
+    for ws in (False, True):
+        note(f"bf16 {M} rows {ops} N={N} K={K} workspace={ws}")
+        C = run(ops, A, B, C0, 0.75, 0.5, four=False, ws=ws)
+        assert oracle.max_rel_err(to_f64(C), R, D) <= tol("bf16"), f"workspace={ws}"
