@@ -79,9 +79,9 @@ def test_noalloc_repeat_is_bitwise_stable():
 
 
 def test_noalloc_rejects_shapes_beyond_the_scratch():
-    # 128 x 4352 x 8192: 17 strips of 256 columns, K interleaved over 16
-    # phases, each phase a 128 x 256 fp32 partial: 34 MiB, past the scratch.
-    M, N, K = 128, 4352, 8192
+    # 128 x 8256 x 8192: 33 strips of 256 columns, K interleaved over 8
+    # phases, each phase a 128 x 256 fp32 partial: 33 MiB, past the scratch.
+    M, N, K = 128, 8256, 8192
     need = dg.gemm_bf16_workspace_size(M, N, K)
     assert need > dg.NOALLOC_SCRATCH_BYTES
     a = torch.zeros(M, K, dtype=torch.bfloat16, device="cuda")
