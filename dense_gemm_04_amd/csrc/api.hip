@@ -92,15 +92,26 @@ bool small_m_to_tiles(int64_t M, int64_t N) {
     return M > 64 && ((M + 63) / 64) * ((N + 63) / 64) <= 256;
 }
 
+// 33 .. 64 rows (4 row blocks in the small-M kernel) without a workspace: the
+// few-tile kernel too, while N x K stays within 2^25 (same box and method:
+// 48 x 4096 x 8192 39.7 -> 33.3 us, 64 x 4096 x 8192 40.4 -> 35.3, 64 x 2048
+// x 8192 39.1 -> 29.5, 64 x 8192 x 4096 22.2 -> 20.1, 64 x 4096 x 4096 21.2
+// -> 17.6; but 48 x 8192 x 8192 43.1 against 46.9). Given a workspace the
+// small-M split mostly wins there (64 x 4096 x 8192: 30.5 us) and runs.
+bool small_m_plain_to_tiles(int64_t M, int64_t N, int64_t K, bool split_ws) {
+    return !split_ws && M > 32 && M <= 64 && N <= 16384 && N * K <= ((int64_t)1 << 25);
+}
+
 // The kernel family for a valid call that has GEMM work, or -1 if the
 // requested family cannot run it. The small-M kernel reads row-major A and
 // either a row-major B or, with 16-byte rows, a transposed one; other
 // transposed small-M calls go to the tiled kernels.
 int choose(int esz, int64_t M, int64_t N, int64_t K, bool vec, int variant, bool ta = false,
-           bool tb = false) {
+           bool tb = false, bool split_ws = false) {
     switch (variant) {
         case GEMM_VARIANT_AUTO:
-            if (esz == 2 && !ta && small_m_ok(M, vec, tb) && !small_m_to_tiles(M, N))
+            if (esz == 2 && !ta && small_m_ok(M, vec, tb) && !small_m_to_tiles(M, N) &&
+                !(vec && small_m_plain_to_tiles(M, N, K, split_ws)))
                 return GEMM_VARIANT_SKINNY;
             if (esz == 4 && dg::f32_small_preferred(M, N, K, false)) return GEMM_VARIANT_SMALL;
             return vec ? GEMM_VARIANT_MFMA : GEMM_VARIANT_GENERAL;
@@ -121,12 +132,12 @@ int choose(int esz, int64_t M, int64_t N, int64_t K, bool vec, int variant, bool
 
 int plan_impl(int esz, int64_t M, int64_t N, int64_t K, float alpha, const void* A,
               int64_t lda, const void* B, int64_t ldb, float beta, const void* C,
-              int64_t ldc, int variant, bool ta = false, bool tb = false) {
+              int64_t ldc, int variant, bool ta = false, bool tb = false, bool split_ws = false) {
     if (esz != 2 && esz != 4) return -1;
     if (variant < GEMM_VARIANT_AUTO || variant > GEMM_VARIANT_SMALL) return -1;
     if (!valid_args(esz, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, ta, tb)) return -1;
     if (work_of(M, N, K, alpha, beta) != Work::kGemm) return GEMM_VARIANT_AUTO;
-    return choose(esz, M, N, K, vector_ok(esz, A, lda, B, ldb, C, ldc), variant, ta, tb);
+    return choose(esz, M, N, K, vector_ok(esz, A, lda, B, ldb, C, ldc), variant, ta, tb, split_ws);
 }
 
 // Per-device cache of "is this a gfx950" (0 unknown, 1 yes, 2 no) and of its
@@ -210,7 +221,11 @@ gemm_status_t run(int64_t M, int64_t N, int64_t K, float alpha, const T* A, int6
                   bool tb = false, const float* row_scale = nullptr,
                   const float* col_scale = nullptr) {
     constexpr int esz = (int)sizeof(T);
-    int v = plan_impl(esz, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, variant, ta, tb);
+    // A workspace the small-M split can use (the size query names it).
+    const bool split_ws = esz == 2 && ws != nullptr && ws_bytes > 0 &&
+                          ws_bytes >= gemm_bf16_workspace_size(M, N, K) &&
+                          gemm_bf16_workspace_size(M, N, K) > 0;
+    int v = plan_impl(esz, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, variant, ta, tb, split_ws);
     if (v < 0) return GEMM_ERR_INVALID_VALUE;
     // An fp32 call whose split-K workspace the tiled kernel asks for (the
     // workspace size query names it) runs the tiled kernel on it.

@@ -112,8 +112,9 @@ typedef enum {
      * kernel that streams B once (Blackwell BF16 GEMM notes, section 5.2:
      * small-batch GEMMs are bandwidth bound). AUTO takes it for such calls
      * except 65 .. 128 rows whose 64 x 64 tiles fit one round of compute
-     * units (N <= 8192), which run faster on the MFMA family's few-tile
-     * kernel, with or without a workspace. */
+     * units (N <= 8192), with or without a workspace, and 33 .. 64 rows with
+     * N x K <= 2^25 without one: those run faster on the MFMA family's
+     * few-tile kernel. */
     GEMM_VARIANT_SKINNY = 4,
     /* fp32 only, any shape and alignment: few-tile kernel. Each workgroup owns
      * a 16 x 16, 32 x 32 or 64 x 64 tile of C and its waves split K between

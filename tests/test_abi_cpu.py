@@ -120,8 +120,11 @@ def test_plan_chooses_family(lib):
     assert plan(variant=dg.VARIANT_MFMA) == dg.VARIANT_MFMA
     assert plan(esz=2, M=16) == dg.VARIANT_SKINNY             # bf16, M <= 128 (16-byte rows)
     assert plan(esz=2, M=32) == dg.VARIANT_SKINNY
-    assert plan(esz=2, M=33) == dg.VARIANT_SKINNY
-    assert plan(esz=2, M=64) == dg.VARIANT_SKINNY
+    # 33 .. 64 rows: the tiled kernels when N x K <= 2^25 (plain calls), else
+    # the small-M kernel.
+    assert plan(esz=2, M=33) == dg.VARIANT_MFMA
+    assert plan(esz=2, M=33, N=8192, K=8192) == dg.VARIANT_SKINNY
+    assert plan(esz=2, M=64, N=8192, K=8192) == dg.VARIANT_SKINNY
     # 65 .. 128 rows: the tiled kernels when their 64 x 64 tiles fit one round
     # (at most 256; here 2), else the small-M kernel (2 x 129 tiles).
     assert plan(esz=2, M=128) == dg.VARIANT_MFMA

@@ -137,11 +137,13 @@ def test_repeatable_and_workspace_unused(four):
     assert int(ws.count_nonzero()) == 0
 
 
-# 65 .. 128 rows whose 64 x 64 tiles fit one round: without a workspace the
-# automatic choice runs them on this kernel instead of the small-M one (with
-# a workspace the small-M split still runs, and must agree with the oracle
-# too). Ragged M, N and K; B row-major or stored N x K.
-SMALL_M_SHAPES = [(65, 520, 1000), (100, 8192, 300), (128, 1000, 4100)]
+# Small M that the automatic choice gives this kernel rather than the small-M
+# one: 65 .. 128 rows whose 64 x 64 tiles fit one round (with or without a
+# workspace), and 33 .. 64 rows with N x K <= 2^25 (plain calls; with a
+# workspace the small-M split runs, and must agree with the oracle too).
+# Ragged M, N and K; B row-major or stored N x K.
+SMALL_M_SHAPES = [(65, 520, 1000), (100, 8192, 300), (128, 1000, 4100), (48, 1000, 4100),
+                  (33, 4096, 8192)]
 
 
 @pytest.mark.parametrize("ops", [(0, 0), (0, 1)], ids=["NN", "NT"])
