@@ -88,16 +88,20 @@ bool small_m_ok(int64_t M, bool vec, bool tb) {
 // x 4096: 43.6 against 52.3 us). Only 16-byte rows take the small-M kernel
 // above 32 rows, so the rule needs no alignment (the workspace size query
 // applies it too).
-bool small_m_to_tiles(int64_t M, int64_t N) {
-    return M > 64 && ((M + 63) / 64) * ((N + 63) / 64) <= 256;
+//
+// 33 .. 64 rows (4 row blocks in the small-M kernel): the few-tile kernel too,
+// while N x K stays within 2^25 (same box and method, plain small-M / its
+// split / few-tile: 48 x 4096 x 8192 39.7 / 28.9 / 33.3 us, 64 x 4096 x 8192
+// 40.4 / 30.5 / 35.3, 64 x 2048 x 8192 39.1 / 26.5 / 29.5, 64 x 8192 x 4096
+// 22.2 / 24.8 / 20.1, 64 x 4096 x 4096 21.2 / 23.8 / 17.6, 64 x 4096 x 2048
+// 11.2 / 21.5 / 11.2, 48 x 8192 x 4096 19.9 / 23.2 / 19.8; but 48 x 8192 x
+// 8192 43.1 / 35.4 / 46.9). With K <= 4096 the split never won, so those
+// run there with or without a workspace; with longer K only plain calls do
+// (small_m_plain_to_tiles).
+bool small_m_to_tiles(int64_t M, int64_t N, int64_t K) {
+    if (M > 64) return ((M + 63) / 64) * ((N + 63) / 64) <= 256;
+    return M > 32 && K <= 4096 && N <= 16384 && N * K <= ((int64_t)1 << 25);
 }
-
-// 33 .. 64 rows (4 row blocks in the small-M kernel) without a workspace: the
-// few-tile kernel too, while N x K stays within 2^25 (same box and method:
-// 48 x 4096 x 8192 39.7 -> 33.3 us, 64 x 4096 x 8192 40.4 -> 35.3, 64 x 2048
-// x 8192 39.1 -> 29.5, 64 x 8192 x 4096 22.2 -> 20.1, 64 x 4096 x 4096 21.2
-// -> 17.6; but 48 x 8192 x 8192 43.1 against 46.9). Given a workspace the
-// small-M split mostly wins there (64 x 4096 x 8192: 30.5 us) and runs.
 bool small_m_plain_to_tiles(int64_t M, int64_t N, int64_t K, bool split_ws) {
     return !split_ws && M > 32 && M <= 64 && N <= 16384 && N * K <= ((int64_t)1 << 25);
 }
@@ -110,7 +114,7 @@ int choose(int esz, int64_t M, int64_t N, int64_t K, bool vec, int variant, bool
            bool tb = false, bool split_ws = false) {
     switch (variant) {
         case GEMM_VARIANT_AUTO:
-            if (esz == 2 && !ta && small_m_ok(M, vec, tb) && !small_m_to_tiles(M, N) &&
+            if (esz == 2 && !ta && small_m_ok(M, vec, tb) && !small_m_to_tiles(M, N, K) &&
                 !(vec && small_m_plain_to_tiles(M, N, K, split_ws)))
                 return GEMM_VARIANT_SKINNY;
             if (esz == 4 && dg::f32_small_preferred(M, N, K, false)) return GEMM_VARIANT_SMALL;
@@ -356,7 +360,7 @@ gemm_status_t gemm_bf16_ex(int64_t M, int64_t N, int64_t K, float alpha, const u
 
 size_t gemm_bf16_workspace_size(int64_t M, int64_t N, int64_t K) {
     if (M < 0 || N < 0 || K < 0 || M > INT_MAX || N > INT_MAX || K > INT_MAX) return 0;
-    if (M <= dg::kSkinnyMaxM && !small_m_to_tiles(M, N)) return dg::bf16_skinny_workspace(M, N, K);
+    if (M <= dg::kSkinnyMaxM && !small_m_to_tiles(M, N, K)) return dg::bf16_skinny_workspace(M, N, K);
     return dg::bf16_tiled_workspace(M, N, K, kFullCus);
 }
 

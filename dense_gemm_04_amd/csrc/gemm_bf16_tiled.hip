@@ -803,10 +803,16 @@ TailSplit plan_tiled128(int64_t M, int64_t N, int64_t K, int cus) {
 //     18.3 against 24.1 us; 129 x 1000 x 8200: 48 against 16 x 8, 33.1
 //     against 23.2 us; 384 x 1024 x 8192: 96 against 24 x 8, 27.5 against 24.0;
 //     with 4-byte copies 1024^2 x 2048: 15.9 against 25.0 us, 1024^2 x 4096:
-//     28.6 against 29.4, 1024^2 x 8192: 49.6 against 41.3).
-static bool few_preferred(int64_t M, int64_t N, const TailSplit* split, bool dw) {
+//     28.6 against 29.4, 1024^2 x 8192: 49.6 against 41.3); with K up to 4096
+//     also when they are at least half as many (64 x 8192 x 4096: 128 tiles
+//     against 64 x 4 ranges, 20.7 against 25.4 us; 48 x 8192 x 4096 20.0
+//     against 25.0), where the split's ranges are short.
+static bool few_preferred(int64_t M, int64_t N, int64_t K, const TailSplit* split, bool dw) {
     const int64_t t64 = ((M + 63) / 64) * ((N + 63) / 64);
-    if (split != nullptr) return t64 <= kTilePlanCus && t64 >= (int64_t)split->tail * split->parts;
+    if (split != nullptr) {
+        const int64_t wgs = (int64_t)split->tail * split->parts;
+        return t64 <= kTilePlanCus && (t64 >= wgs || (K <= 4096 && 2 * t64 >= wgs));
+    }
     return t64 <= (dw ? 1 : 2) * kTilePlanCus;
 }
 
@@ -868,7 +874,7 @@ hipError_t launch_cfg(const GemmArgs<uint16_t>& a, bool dw, void* ws, size_t ws_
 static double tiled_cost(int64_t M, int64_t N, bool dw) {
     const int64_t t64 = ((M + 63) / 64) * ((N + 63) / 64);
     if (tiled_tile(M, N) == 128) {
-        if (few_preferred(M, N, nullptr, dw))
+        if (few_preferred(M, N, 0, nullptr, dw))
             return (dw ? 0.28 : 0.17) * (double)((t64 + kTilePlanCus - 1) / kTilePlanCus);
         const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
         if (8 * t128 <= 5 * kTilePlanCus)
@@ -949,7 +955,7 @@ static hipError_t launch_tiles(const GemmArgs<uint16_t>& a, bool dw, void* ws, s
         const int64_t t128 = ((a.M + 127) / 128) * ((a.N + 127) / 128);
         const TailSplit plan = plan_tiled128(a.M, a.N, a.K, cus);
         const bool split = ws != nullptr && plan.tail > 0 && ws_bytes >= tail_workspace(plan, 128, 128);
-        if (few_preferred(a.M, a.N, split ? &plan : nullptr, dw)) return launch_bf16_few(a, dw, s);
+        if (few_preferred(a.M, a.N, a.K, split ? &plan : nullptr, dw)) return launch_bf16_few(a, dw, s);
         if (8 * t128 <= 5 * kTilePlanCus && !split && !(2 * t128 > kTilePlanCus && ks_preferred(t128, a.K))) {
             if (has_epilogue(a)) return launch_cfg<64, 64, 2, 2, true>(a, dw, ws, ws_bytes, cus, s);
             return launch_cfg<64, 64, 2, 2, false>(a, dw, ws, ws_bytes, cus, s);
@@ -968,7 +974,7 @@ size_t bf16_tiled_workspace(int64_t M, int64_t N, int64_t K, int cus) {
     const TailSplit plan = plan_tiled128(M, N, K, cus);
     // Products the few-tile kernel takes in preference to the split need no
     // workspace.
-    if (plan.tail > 0 && few_preferred(M, N, &plan, false)) return 0;
+    if (plan.tail > 0 && few_preferred(M, N, K, &plan, false)) return 0;
     return tail_workspace(plan, 128, 128);
 }
 

@@ -78,7 +78,7 @@ CASES = [
     ("bf16", (32, 72, 130), (0, 0, 0), False),       # small-M vector kernel, two row blocks
     ("bf16", (16, 1032, 2000), (0, 0, 0), True),     # small-M split-K
     ("bf16", (16, 4352, 1000), (0, 0, 0), True),     # small-M streaming split (K interleaved)
-    ("bf16", (33, 4104, 300), (8, 8, 8), True),      # the same, two row blocks, padded rows
+    ("bf16", (33, 4104, 4200), (8, 8, 8), True),     # the same, two row blocks, padded rows
     ("bf16", (5, 100, 77), (1, 1, 1), False),        # small-M element-wise kernel
     ("f32", (2100, 2000, 100), (0, 0, 0), False),    # fp32 tiled MFMA, aligned
     ("f32", (2100, 2000, 65), (1, 3, 5), False),     # fp32 tiled MFMA, unaligned rows
