@@ -79,7 +79,7 @@ bool small_m_ok(int64_t M, bool vec, bool tb) {
 // 65 .. 128 rows run faster on the tiled kernels (their few-tile kernel,
 // 64 x 64 tiles with K split over each workgroup's waves) whenever those
 // tiles fit one round of compute units: the small-M kernel then holds 8 row
-// blocks of A per strip and streams B at about half the rate. Same box, B
+// blocks of A per strip and streams B at about half the rate. One MI355X, B
 // from HBM (4 rotating operand sets), small-M kernel plain / with its split
 // over a workspace / few-tile kernel: 96 x 8192 x 8192 77.9 / 43.2 / 43.7 us,
 // 128 x 8192 x 8192 79.2 / 45.8 / 48.4, 128 x 4096 x 8192 73.3 / 45.7 /
@@ -90,7 +90,7 @@ bool small_m_ok(int64_t M, bool vec, bool tb) {
 // applies it too).
 //
 // 33 .. 64 rows (4 row blocks in the small-M kernel): the few-tile kernel too,
-// while N x K stays within 2^25 (same box and method, plain small-M / its
+// while N x K stays within 2^25 (one MI355X, same method, plain small-M / its
 // split / few-tile: 48 x 4096 x 8192 39.7 / 28.9 / 33.3 us, 64 x 4096 x 8192
 // 40.4 / 30.5 / 35.3, 64 x 2048 x 8192 39.1 / 26.5 / 29.5, 64 x 8192 x 4096
 // 22.2 / 24.8 / 20.1, 64 x 4096 x 4096 21.2 / 23.8 / 17.6, 64 x 4096 x 2048

@@ -821,7 +821,7 @@ static bool few_preferred(int64_t M, int64_t N, int64_t K, const TailSplit* spli
 // most one such tile per CU and an even number of at least 32 K slabs. A CU
 // holding one tile of the plain kernel runs 8 waves, 2 per SIMD; two groups
 // give it 4 per SIMD, as two workgroups per CU would, and the tile finishes in
-// about half the slab steps. Measured (same box, medians of 7): 512 x 8192 x
+// about half the slab steps. Measured (one MI355X, medians of 7): 512 x 8192 x
 // 8192 87.0 -> 72.5 us, 2048^2 x 8192 86.7 -> 77.4, 1024 x 4096 x 4096 43.5
 // -> 37.6, 1792 x 2048 x 8192 77.9 -> 66.7, 2048^2 x 2048 24.9 -> 23.2, but
 // 2048^2 x 1024 (16 slabs) 12.5 -> 13.6. It also replaces 64 x 64 tiles for
@@ -896,7 +896,7 @@ struct Bf16Partition {
 // round's tiles run as a separate product (on the few-tile kernel when it is
 // thin), leaving the tiled kernel whole rounds of 256 x 256 tiles, when the
 // model puts the pair below 0.95 of the whole product as planned. Measured
-// (same box, medians of 7; model ratio in brackets): 4352 x 4096 x 4096
+// (one MI355X, medians of 7; model ratio in brackets): 4352 x 4096 x 4096
 // 159.2 -> 128.6 us (0.68, a 256-row strip on the few-tile kernel),
 // 4224 x 4096 x 4096 159.4 -> 119.2 (0.68), 4096 x 4608 x 4096 149.6 -> 131.8
 // (0.78), 4500 x 4100 x 4096 218.3 -> 191.3 (0.87), 8448 x 8192 x 4096

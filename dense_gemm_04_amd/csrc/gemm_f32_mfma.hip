@@ -721,7 +721,7 @@ void gemm_f32_mfma_kernel(GemmArgs<float> p, int tiles_m, int tiles_n, TailSplit
 
 // Reading one range's 64 KB partial tile back costs the last range about a
 // quarter of a slab's time (32 k of a 128 x 128 tile, two workgroups per CU).
-// Splitting a last round more than half full measured (same box, with and
+// Splitting a last round more than half full measured (one MI355X, with and
 // without a workspace): 2304^2 x 2048 237 -> 204 us, 2048 x 2560 x 4096 467
 // -> 408, 1664 x 2560 x 8192 921 -> 646, 2300 x 2290 x 2050 (unaligned) 332
 // -> 227; 3072 x 2048 x 1024 in ranges of 8 slabs lost (123 -> 144), hence

@@ -67,7 +67,7 @@ __device__ __forceinline__ f32x4 load_k4(const float* __restrict__ X, int64_t ld
 // rows, so the tiles of one XCD share A rows and B columns in its L2; without
 // it, workgroup b takes tile (b / tiles_n, b mod tiles_n). The renumbering's
 // divisions delay a workgroup's first loads by about 0.2 us, which only a
-// long enough K loop repays (same box, plain order against renumbered: 256^3
+// long enough K loop repays (one MI355X, plain order against renumbered: 256^3
 // 2.83 against 3.13 us, 512^3 5.80 against 5.97; 1024^3 26.26 against 25.38,
 // 256^2 x 4096 14.62 against 13.27).
 constexpr int kGroupM = 4;
@@ -296,7 +296,7 @@ F32Partition plan_f32_partition(int64_t M, int64_t N, int64_t K, bool split_ws) 
         // (or rows) holding the tiles past one per CU can go to the few-tile
         // kernel instead, leaving the tiled kernel one tile per CU
         // (kTiledRound1). The model overstates the cost of the pair by about
-        // a tenth; measured (same box, plain calls, model ratio of the pair
+        // a tenth; measured (one MI355X, plain calls, model ratio of the pair
         // to the round in brackets): 2048 x 2304 x 4096 467 -> 328 us (0.74),
         // 2048 x 2560 x 4096 467 -> 363 (0.84), 2304^2 x 4096 467 -> 403
         // (0.94), 3072 x 2048 x 4096 471 -> 451 (1.06), but 2304 x 2816 x
@@ -326,8 +326,8 @@ F32Partition plan_f32_partition(int64_t M, int64_t N, int64_t K, bool split_ws) 
     const bool by_cols = cost_n <= cost_m;
     const double cost = by_cols ? cost_n : cost_m;
     // Worth it when the strip clearly beats the round it removes. It also
-    // beat splitting that round over a workspace wherever both applied (same
-    // box: 4095 x 4097 x 1023 313 us against 329, 4096 x 4352 x 2048 531
+    // beat splitting that round over a workspace wherever both applied (one
+    // MI355X: 4095 x 4097 x 1023 313 us against 329, 4096 x 4352 x 2048 531
     // against 603, 2560 x 4096 x 2048 338 against 360), so `split_ws` does not
     // change the choice.
     (void)split_ws;

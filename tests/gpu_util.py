@@ -14,7 +14,7 @@ TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 
 def note(msg: str) -> None:
-    """Name the case on the real stderr before a GPU step (survives a lost box)."""
+    """Name the case on the real stderr before a GPU step (it survives a lost process)."""
     sys.__stderr__.write(f"[gpu-case] {msg}\n")
     sys.__stderr__.flush()
 
