@@ -106,6 +106,15 @@ bool small_m_plain_to_tiles(int64_t M, int64_t N, int64_t K, bool split_ws) {
     return !split_ws && M > 32 && M <= 64 && N <= 16384 && N * K <= ((int64_t)1 << 25);
 }
 
+// The small-M kernels split K over a workspace only from K = 4096 on: with
+// shorter K the split's second phase (partial tiles, counters, the fixed-order
+// sum) costs more than the extra workgroups save, however few strips there
+// are (one MI355X, B from HBM, plain / split: 16 x 8192 x 1024 6.0 / 8.8 us,
+// 32 x 8192 x 2048 9.8 / 13.0, 16 x 8192 x 3072 11.8 / 12.6, 16 x 1024 x
+// 2048 8.2 / 13.9, 17 x 64 x 1000 5.8 / 11.8; at K = 4096 level or ahead:
+// 16 x 8192 x 4096 15.5 / 15.3, 16 x 4096 x 4096 14.3 / 13.0).
+constexpr int64_t kSmallMSplitMinK = 4096;
+
 // The kernel family for a valid call that has GEMM work, or -1 if the
 // requested family cannot run it. The small-M kernel reads row-major A and
 // either a row-major B or, with 16-byte rows, a transposed one; other
@@ -265,8 +274,10 @@ gemm_status_t run(int64_t M, int64_t N, int64_t K, float alpha, const T* A, int6
                 e = launch_f32_auto(a, v == GEMM_VARIANT_MFMA, ws, ws_bytes, cus, s);
             else e = dg::launch_f32_mfma(a, v == GEMM_VARIANT_MFMA, ws, ws_bytes, cus, s);
         } else {
+            // The small-M kernels get the workspace only where the size
+            // query asks for one (a split that pays).
             e = (v == GEMM_VARIANT_SKINNY)
-                    ? dg::launch_bf16_skinny(a, vec, ws, ws_bytes, cus, s)
+                    ? dg::launch_bf16_skinny(a, vec, split_ws ? ws : nullptr, split_ws ? ws_bytes : 0, cus, s)
                     : dg::launch_bf16_mfma(a, v == GEMM_VARIANT_MFMA, ws, ws_bytes, cus, s);
         }
     }
@@ -360,7 +371,8 @@ gemm_status_t gemm_bf16_ex(int64_t M, int64_t N, int64_t K, float alpha, const u
 
 size_t gemm_bf16_workspace_size(int64_t M, int64_t N, int64_t K) {
     if (M < 0 || N < 0 || K < 0 || M > INT_MAX || N > INT_MAX || K > INT_MAX) return 0;
-    if (M <= dg::kSkinnyMaxM && !small_m_to_tiles(M, N, K)) return dg::bf16_skinny_workspace(M, N, K);
+    if (M <= dg::kSkinnyMaxM && !small_m_to_tiles(M, N, K))
+        return K >= kSmallMSplitMinK ? dg::bf16_skinny_workspace(M, N, K) : 0;
     return dg::bf16_tiled_workspace(M, N, K, kFullCus);
 }
 

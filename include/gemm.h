@@ -154,7 +154,8 @@ gemm_status_t gemm_bf16_ex(int64_t M, int64_t N, int64_t K, float alpha,
  * workgroups, each over a part of K: with row-major 16-byte rows and at least
  * 16 strips of 256 columns, a streaming kernel whose workgroups take
  * interleaved 32-row blocks of K (16 x 8192 x 8192: 32 strips x 8), otherwise
- * the small-M kernel over contiguous K segments. Each workgroup stores its
+ * the small-M kernel over contiguous K segments. Only K >= 4096 splits:
+ * shorter K runs unsplit, which is faster there. Each workgroup stores its
  * fp32 partial tile in the workspace, and the strip's last workgroup to
  * finish adds the partials in a fixed order (so results do not depend on
  * timing) and forms alpha * sum + beta * C.
@@ -169,9 +170,9 @@ gemm_status_t gemm_bf16_ex(int64_t M, int64_t N, int64_t K, float alpha,
  * workspace): 1024 x 1024 x 4096 needs none.
  *
  * gemm_bf16_workspace_size: workspace bytes gemm_bf16_ws needs to split this
- * shape; 0 when it would not split (small M: N already fills the GPU or K is
- * a single 128-row chunk; M > 128: no idle CUs, or K below 2048) or the sizes
- * are invalid. Host only, no HIP call. Sized for a full MI355X (256 compute
+ * shape; 0 when it would not split (small M: K below 4096, where the
+ * unsplit kernels are at least as fast, or N already fills the GPU; M > 128:
+ * no idle CUs, or K below 2048) or the sizes are invalid. Host only, no HIP call. Sized for a full MI355X (256 compute
  * units). */
 size_t gemm_bf16_workspace_size(int64_t M, int64_t N, int64_t K);
 

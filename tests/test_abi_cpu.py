@@ -217,15 +217,13 @@ def test_workspace_size(lib):
     # 64 strips of 256 columns: 4 phases fill the chip.
     assert dg.gemm_bf16_workspace_size(16, 16384, 8192) == 256 + 64 * 4 * 16 * 256 * 4
     # 16 strips (N = 3841) would take 16 phases, the most; K = 4104 has 129
-    # blocks of 32 rows, K = 700 only 22, enough for 5 phases of 4 blocks.
+    # blocks of 32 rows.
     assert dg.gemm_bf16_workspace_size(16, 3841, 4104) == 256 + 16 * 16 * 16 * 256 * 4
-    assert dg.gemm_bf16_workspace_size(16, 3841, 700) == 256 + 16 * 5 * 16 * 256 * 4
-    # K = 260 has 9 blocks: 2 phases. The size is the larger of the two
-    # small-M splits (the 64-column kernel, which a transposed B uses, would
-    # cut 65 strips into 3 segments here). K = 40 (2 blocks) does not split
-    # here, nor in the 64-column kernel (one 128-row chunk).
-    assert dg.gemm_bf16_workspace_size(7, 4104, 260) == max(256 + 17 * 2 * 16 * 256 * 4,
-                                                            512 + 3 * 65 * 16 * 64 * 4)
+    # The small-M splits need K >= 4096: shorter K runs unsplit, faster.
+    assert dg.gemm_bf16_workspace_size(16, 3841, 700) == 0
+    assert dg.gemm_bf16_workspace_size(7, 4104, 260) == 0
+    assert dg.gemm_bf16_workspace_size(16, 8192, 4095) == 0
+    assert dg.gemm_bf16_workspace_size(16, 8192, 4096) > 0
     assert dg.gemm_bf16_workspace_size(7, 4104, 40) == 0
     # N = 3840 is 15 strips: the 64-column kernel's split (60 strips of 64
     # columns; K = 8192 has 64 chunks of 128: 5 segments of 13 chunks).
@@ -247,8 +245,8 @@ def test_workspace_size(lib):
     assert dg.gemm_bf16_workspace_size(-1, 64, 1024) == 0
     # Segments are capped at 64 (N = 64, K = 2^20: 64 segments of 128 chunks).
     assert dg.gemm_bf16_workspace_size(16, 64, 1 << 20) == 256 + 64 * 1 * 16 * 64 * 4
-    # Every segment is non-empty: K = 300 is 3 chunks, so 3 segments.
-    assert dg.gemm_bf16_workspace_size(16, 64, 300) == 256 + 3 * 16 * 64 * 4
+    # K = 300 (3 chunks) would give 3 segments, but below K = 4096 nothing splits.
+    assert dg.gemm_bf16_workspace_size(16, 64, 300) == 0
     # 17 strips want 16 segments; K = 4104 has 33 chunks: 11 segments of 3.
     assert dg.gemm_bf16_workspace_size(16, 1032, 4104) == 256 + 11 * 17 * 16 * 64 * 4
 

@@ -76,8 +76,8 @@ CASES = [
     ("bf16", (130, 200, 129), (1, 3, 5), False),     # unaligned rows: general kernel
     ("bf16", (16, 520, 300), (0, 0, 0), False),      # small-M vector kernel
     ("bf16", (32, 72, 130), (0, 0, 0), False),       # small-M vector kernel, two row blocks
-    ("bf16", (16, 1032, 2000), (0, 0, 0), True),     # small-M split-K
-    ("bf16", (16, 4352, 1000), (0, 0, 0), True),     # small-M streaming split (K interleaved)
+    ("bf16", (16, 1032, 4100), (0, 0, 0), True),     # small-M split-K
+    ("bf16", (16, 4352, 4100), (0, 0, 0), True),     # small-M streaming split (K interleaved)
     ("bf16", (33, 4104, 4200), (8, 8, 8), True),     # the same, two row blocks, padded rows
     ("bf16", (5, 100, 77), (1, 1, 1), False),        # small-M element-wise kernel
     ("f32", (2100, 2000, 100), (0, 0, 0), False),    # fp32 tiled MFMA, aligned

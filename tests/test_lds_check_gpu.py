@@ -93,10 +93,10 @@ CASES = [
     ("bf16", (300, 264, 200), (0, 0, 0), (0, 1), False, None),     # tiled, B stored N x K (M > 128)
     ("bf16", (300, 264, 200), (8, 8, 8), (1, 1), False, None),     # tiled, both, padded rows
     ("bf16", (16, 520, 300), (0, 0, 0), (0, 0), False, None),      # small-M 64-column ring
-    ("bf16", (17, 64, 1000), (0, 0, 0), (0, 0), True, None),       # small-M ring, split-K
+    ("bf16", (17, 64, 4200), (0, 0, 0), (0, 0), True, None),       # small-M ring, split-K
     ("bf16", (100, 8256, 300), (0, 0, 0), (0, 0), False, None),    # small-M ring, 3 stages (N past one round of 64 x 64 tiles)
-    ("bf16", (16, 520, 300), (0, 0, 0), (0, 1), True, None),       # small-M ring, B stored N x K
-    ("bf16", (16, 4352, 1000), (0, 0, 0), (0, 0), True, None),     # streaming split
+    ("bf16", (16, 520, 4100), (0, 0, 0), (0, 1), True, None),      # small-M ring, B stored N x K, split
+    ("bf16", (16, 4352, 4100), (0, 0, 0), (0, 0), True, None),     # streaming split
     ("bf16", (33, 4104, 4200), (8, 8, 8), (0, 0), True, None),     # streaming split, padded
     ("bf16", (5, 100, 77), (1, 1, 1), (0, 0), False, None),        # small-M element-wise
     ("bf16", (130, 200, 129), (1, 3, 5), (0, 0), False, None),     # unaligned rows

@@ -95,15 +95,15 @@ CASES = [
     ("bf16", (130, 200, 129), (1, 3, 5), (0, 0), False),     # unaligned rows: general kernel
     ("bf16", (16, 520, 300), (0, 0, 0), (0, 0), False),      # small-M vector
     ("bf16", (32, 72, 130), (0, 0, 0), (0, 0), False),       # small-M vector, two row blocks
-    ("bf16", (16, 1032, 2000), (0, 0, 0), (0, 0), True),     # small-M 64-column split
-    ("bf16", (16, 4352, 1000), (0, 0, 0), (0, 0), True),     # small-M streaming split
+    ("bf16", (16, 1032, 4100), (0, 0, 0), (0, 0), True),     # small-M 64-column split
+    ("bf16", (16, 4352, 4100), (0, 0, 0), (0, 0), True),     # small-M streaming split
     ("bf16", (100, 4160, 1500), (8, 8, 8), (0, 0), True),    # streaming split, 7 row blocks, padded
     ("bf16", (5, 100, 77), (1, 1, 1), (0, 0), False),        # small-M element-wise
     ("bf16", (512, 512, 16384), (0, 0, 0), (0, 0), True),    # tiled split-K (M > 128)
     ("bf16", (512, 512, 4096), (0, 0, 0), (0, 0), True),     # few-tile kernel (the workspace unused)
     ("bf16", (300, 264, 200), (0, 0, 0), (1, 0), False),     # tiled, A stored K x M
     ("bf16", (200, 136, 264), (0, 0, 0), (1, 1), False),     # tiled, both transposed
-    ("bf16", (16, 520, 300), (0, 0, 0), (0, 1), True),       # small M, B stored N x K, split
+    ("bf16", (16, 520, 4100), (0, 0, 0), (0, 1), True),      # small M, B stored N x K, split
     ("f32", (2100, 2000, 100), (0, 0, 0), (0, 0), False),    # fp32 tiled copy path
     ("f32", (2100, 2000, 65), (1, 3, 5), (0, 0), False),     # fp32 tiled, unaligned rows
     ("f32", (600, 4100, 300), (4, 8, 12), (0, 0), True),     # fp32 tiled split-K tail, padded

@@ -178,7 +178,7 @@ def test_op_full_size(dtype, ops):
 # vector kernel reads the transposed B directly; unaligned rows fall back to
 # the tiled kernels.
 SMALL_M_TB = [((16, 520, 300), (0, 0, 0), False), ((32, 72, 130), (0, 0, 0), False),
-              ((1, 1032, 4104), (0, 0, 0), True), ((17, 64, 1000), (0, 0, 0), True),
+              ((1, 1032, 4104), (0, 0, 0), True), ((17, 64, 4200), (0, 0, 0), True),
               ((5, 200, 77), (8, 8, 8), False), ((5, 100, 77), (1, 1, 1), False),
               ((3, 1024, 8200), (0, 0, 0), True)]
 

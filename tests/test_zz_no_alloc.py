@@ -47,7 +47,7 @@ def _run(fn_name, A, B, C0, alpha, beta):
 # 64-row tiles, the tiled kernel's split for M > 128 on 128 x 128 tiles, and
 # shapes that do not split: the few-tile kernel's 512 x 2048 x 4096 and a
 # single K chunk).
-SEQUENCE = [((128, 16384, 8192), 1.0, 0.0), ((16, 8192, 8192), 1.0, 0.0), ((16, 4352, 1000), 0.5, 2.0),
+SEQUENCE = [((128, 16384, 8192), 1.0, 0.0), ((16, 8192, 8192), 1.0, 0.0), ((16, 4352, 4100), 0.5, 2.0),
             ((40, 1032, 4104), 1.0, 1.0), ((512, 1024, 8192), 1.0, 0.0), ((512, 2048, 4096), 1.0, 0.0),
             ((16, 16384, 128), 1.0, 0.0)]
 
