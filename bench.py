@@ -63,7 +63,7 @@ SETTLE_SECONDS = 0.25
 EPILOGUE_WORKLOADS = (2, 4)
 # Mid-size shapes whose last round of tiles leaves compute units idle, timed
 # by --all and --only with and without a split-K workspace (seed families
-# 61..67).
+# 61..68).
 def midsize_workloads():
     import gemm_inputs as gi
     return [gi.Workload(61, "gemm_bf16_512x8192x8192", "bf16", 512, 8192, 8192, 1.0, 0.0, "n", "n"),
@@ -76,7 +76,10 @@ def midsize_workloads():
             # 256 tiles of 64 x 64: the bf16 few-tile kernel
             gi.Workload(66, "gemm_bf16_1024x1024x4096", "bf16", 1024, 1024, 4096, 1.0, 0.0, "n", "n"),
             # 272 tiles of 256 x 256: one round of them and a 256-row strip
-            gi.Workload(67, "gemm_bf16_4352x4096x4096", "bf16", 4352, 4096, 4096, 1.0, 0.0, "n", "n")]
+            gi.Workload(67, "gemm_bf16_4352x4096x4096", "bf16", 4352, 4096, 4096, 1.0, 0.0, "n", "n"),
+            # one round of 144 tiles of 256 x 256; with a workspace 576 of
+            # 128 x 128, the last 64 split over K
+            gi.Workload(68, "gemm_bf16_3072x3072x8192", "bf16", 3072, 3072, 8192, 1.0, 0.0, "n", "n")]
 
 
 # Workloads also timed with transposed operand storage (A^T B, A B^T, A^T B^T);
@@ -462,7 +465,7 @@ def main(argv=None) -> int:
     ap.add_argument("--all", action="store_true", help="one JSON line per workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", type=int, default=None,
-                    help="time one workload id (1, 2, 3, 4, 51, 52; 61-67 mid-size) and print its line "
+                    help="time one workload id (1, 2, 3, 4, 51, 52; 61-68 mid-size) and print its line "
                          "(with the split-K line for 52, the bias + GELU line for 2 and 4, "
                          "the transposed-layout lines for 2, 3 and 52)")
     ap.add_argument("--vendor", action="store_true",

@@ -947,8 +947,37 @@ hipError_t launch_bf16_tiled(const GemmArgs<uint16_t>& a, bool dw, void* ws, siz
     return launch_tiles(strip, dw, nullptr, 0, cus, s);
 }
 
+// Products that take 256 x 256 tiles in a single partly full round (129 ..
+// 256 tiles) may instead run 128 x 128 tiles, two per CU, when a workspace
+// lets the last round of those be split over K: 3072^3 has 144 large tiles,
+// or 512 small ones for one full round and 64 more cut into 3 K ranges.
+// Modelled in rounds of 256 x 256 tiles as in tiled_tile, the split ranges of
+// the last round at a lone 128 x 128 tile's rate divided by the ranges.
+// Measured (one MI355X, medians of 7, 256 x 256 tiles against the split):
+// 3072^2 x 8192 165.1 -> 141.3 us, 3072^2 x 4096 90.3 -> 79.4, 2048 x 4608 x
+// 4096 87.1 -> 78.0, 3072 x 3328 x 4096 90.6 -> 85.6, 3072^3 73.5 -> 69.1
+// (A stored K x M: 70.4 -> 66.0; 4-byte rows: 99.6 -> 88.2). With B stored
+// N x K the split ran slower (3072^3: 64.8 -> 90.2 us), so the launcher keeps
+// such products on 256 x 256 tiles; the workspace query, which does not know
+// the layout, still sizes the split for them.
+static bool split128_preferred(int64_t M, int64_t N, int64_t K, int cus) {
+    const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+    if (t256 > kTilePlanCus || 2 * t256 <= kTilePlanCus) return false;
+    const TailSplit plan = plan_tiled128(M, N, K, cus);
+    if (plan.tail == 0) return false;
+    const int64_t full = plan.full / (2 * kTilePlanCus), rem = plan.full % (2 * kTilePlanCus);
+    const double head = 0.61 * (double)full + (rem == 0 ? 0.0 : rem > kTilePlanCus ? 0.61 : 0.49);
+    const double tail = 0.49 * (double)plan.cps / (double)((K + kBK - 1) / kBK);
+    return head + tail < 0.9;
+}
+
 static hipError_t launch_tiles(const GemmArgs<uint16_t>& a, bool dw, void* ws, size_t ws_bytes,
                                int cus, hipStream_t s) {
+    if (ws != nullptr && !a.tb && tiled_tile(a.M, a.N) == 256 && split128_preferred(a.M, a.N, a.K, cus) &&
+        ws_bytes >= tail_workspace(plan_tiled128(a.M, a.N, a.K, cus), 128, 128)) {
+        if (has_epilogue(a)) return launch_cfg<128, 128, 2, 4, true>(a, dw, ws, ws_bytes, cus, s);
+        return launch_cfg<128, 128, 2, 4, false>(a, dw, ws, ws_bytes, cus, s);
+    }
     if (tiled_tile(a.M, a.N) == 128) {
         // At most 160 small tiles (on a full MI355X) and no split over a
         // workspace: 64 x 64 tiles.
@@ -968,7 +997,9 @@ static hipError_t launch_tiles(const GemmArgs<uint16_t>& a, bool dw, void* ws, s
 }
 
 size_t bf16_tiled_workspace(int64_t M, int64_t N, int64_t K, int cus) {
-    if (M < 1 || N < 1 || K < 1 || tiled_tile(M, N) != 128) return 0;
+    if (M < 1 || N < 1 || K < 1) return 0;
+    if (tiled_tile(M, N) == 256)
+        return split128_preferred(M, N, K, cus) ? tail_workspace(plan_tiled128(M, N, K, cus), 128, 128) : 0;
     // A partitioned product (16-byte rows) runs no split.
     if (plan_bf16_partition(M, N, false).by != 0) return 0;
     const TailSplit plan = plan_tiled128(M, N, K, cus);

@@ -167,7 +167,11 @@ gemm_status_t gemm_bf16_ex(int64_t M, int64_t N, int64_t K, float alpha,
  * with 64 KB fp32 partial tiles. Products whose 64 x 64 tiles fit one round
  * of compute units and are at least as many as the split's workgroups run
  * on the few-tile kernel instead (K split over the waves of a workgroup, no
- * workspace): 1024 x 1024 x 4096 needs none.
+ * workspace): 1024 x 1024 x 4096 needs none. Products whose 256 x 256
+ * tiles form one partly full round (129 .. 256 tiles) may run 128 x 128
+ * tiles with a workspace instead, one round of them whole and the rest split,
+ * when a model of the two says it pays (3072 x 3072: 512 tiles and 64 split),
+ * unless B is stored N x K (then the workspace is left unused).
  *
  * gemm_bf16_workspace_size: workspace bytes gemm_bf16_ws needs to split this
  * shape; 0 when it would not split (small M: K below 4096, where the

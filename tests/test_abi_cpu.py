@@ -236,6 +236,13 @@ def test_workspace_size(lib):
     # workspace could split; it runs one round of 256 x 256 tiles and a
     # 256-row strip on the few-tile kernel instead, with no workspace.
     assert dg.gemm_bf16_workspace_size(4352, 4096, 4096) == 0
+    # 3072^2 takes one round of 144 256 x 256 tiles; with a workspace it runs
+    # 576 tiles of 128 x 128 instead: 512 in one round, the last 64 cut into
+    # 3 K ranges of 16 slabs (at K = 3072). 4000^2 (256 large tiles, a full
+    # round) needs none.
+    assert dg.gemm_bf16_workspace_size(3072, 3072, 3072) == 256 + 64 * 3 * 128 * 128 * 4
+    assert dg.gemm_bf16_workspace_size(2900, 3000, 2100) == 256 + 40 * 2 * 128 * 128 * 4
+    assert dg.gemm_bf16_workspace_size(4000, 4000, 2048) == 0
     assert dg.gemm_bf16_workspace_size(16, 2048, 8192) > 0
     assert dg.gemm_bf16_workspace_size(16, 16384, 128) == 0
     assert dg.gemm_bf16_workspace_size(16, 64, 128) == 0
@@ -270,14 +277,16 @@ def test_tiled_workspace_size(lib):
     assert dg.gemm_bf16_workspace_size(1024, 1024, 2048) == 0
     # 129 x 1000 x 8200: 16 tiles, 129 slabs -> 8 ranges of 17 (the last 10).
     assert dg.gemm_bf16_workspace_size(129, 1000, 8200) == 256 + 16 * 8 * tile
+    # One partly full round of 256 x 256 tiles (3072^2 and 3000^2: 144) runs
+    # 576 small tiles with a workspace, the last 64 split: 3072^2 x 8192 in 4
+    # ranges of 32 slabs, 3000^3 (47 slabs) in 2 of 24.
+    assert dg.gemm_bf16_workspace_size(3072, 3072, 8192) == 256 + 64 * 4 * tile
+    assert dg.gemm_bf16_workspace_size(3000, 3000, 3000) == 256 + 64 * 2 * tile
     # No split: one tile per CU already (512 x 8192 and 2048^2: 256 small
-    # tiles), products on 256 x 256 tiles (4096^2; 3072^2 and 3000^2, whose
-    # 144 large tiles beat 576 small ones), fewer than 32 slabs.
+    # tiles), a full round of 256 x 256 tiles (4096^2), fewer than 32 slabs.
     assert dg.gemm_bf16_workspace_size(512, 8192, 8192) == 0
     assert dg.gemm_bf16_workspace_size(2048, 2048, 2048) == 0
     assert dg.gemm_bf16_workspace_size(4096, 4096, 4096) == 0
-    assert dg.gemm_bf16_workspace_size(3072, 3072, 8192) == 0
-    assert dg.gemm_bf16_workspace_size(3000, 3000, 3000) == 0
     assert dg.gemm_bf16_workspace_size(1024, 1024, 1024) == 0
     assert dg.gemm_bf16_workspace_size(300, 520, 1984) == 0
 

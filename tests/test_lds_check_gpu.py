@@ -82,6 +82,7 @@ CASES = [
     ("bf16", (4000, 4000, 136), (8, 8, 8), (1, 1), False, None),   # large tiles, both transposed, padded
     ("bf16", (520, 520, 4100), (0, 0, 0), (0, 0), True, None),     # tiled split-K tail, ragged K
     ("bf16", (520, 520, 4100), (0, 0, 0), (0, 0), False, None),    # same without a workspace: few-tile kernel
+    ("bf16", (2900, 3000, 2100), (2, 2, 2), (1, 0), True, None),   # one round of large tiles as small ones + split tail
     ("bf16", (256, 264, 200), (0, 0, 0), (1, 1), False, None),     # few-tile kernel, both transposed
     ("bf16", (1500, 1528, 136), (8, 0, 0), (0, 0), False, None),   # 64 x 64 tiles (576), 16-byte rows
     ("bf16", (2048, 1500, 300), (0, 0, 0), (0, 0), False, None),   # 192 small tiles, one per CU
