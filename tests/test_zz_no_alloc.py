@@ -45,11 +45,12 @@ def _run(fn_name, A, B, C0, alpha, beta):
 # Consecutive calls on the one scratch: the largest streaming split (128
 # rows, 32 MiB), then smaller ones (streaming split, the 64-column split with
 # 64-row tiles, the tiled kernel's split for M > 128 on 128 x 128 tiles, and
-# shapes that do not split: the few-tile kernel's 512 x 2048 x 4096 and a
+# shapes that do not split: the few-tile kernel's 512 x 2048 x 4096; one
+# round of 256 x 256 tiles run as 128 x 128 tiles with a split tail; a
 # single K chunk).
 SEQUENCE = [((128, 16384, 8192), 1.0, 0.0), ((16, 8192, 8192), 1.0, 0.0), ((16, 4352, 4100), 0.5, 2.0),
             ((40, 1032, 4104), 1.0, 1.0), ((512, 1024, 8192), 1.0, 0.0), ((512, 2048, 4096), 1.0, 0.0),
-            ((16, 16384, 128), 1.0, 0.0)]
+            ((2900, 3000, 2100), 1.0, 0.5), ((16, 16384, 128), 1.0, 0.0)]
 
 
 def test_noalloc_matches_workspace_call_over_consecutive_calls():
